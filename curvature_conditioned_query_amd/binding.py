@@ -1,0 +1,222 @@
+"""ctypes binding of ``libccq.so`` (the C ABI in ``include/ccq.h``).
+
+Argument marshalling only: torch tensors are checked for device, dtype and
+contiguity and handed to the library as raw device pointers together with the
+caller's current HIP stream.  No step of the method runs here, and there is no
+fallback: if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+CCQ_RULE_GLA = 0
+CCQ_RULE_GDN = 1
+CCQ_DTYPE_F32 = 0
+CCQ_DTYPE_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+# Every symbol include/ccq.h declares (kept in one place for the export test).
+EXPORTED_SYMBOLS = (
+    "ccq_fwd_chunked",
+    "ccq_fwd_workspace_bytes",
+    "ccq_decode_step",
+    "ccq_status_string",
+    "ccq_abi_version",
+)
+
+
+class CcqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_status_string(status)})")
+
+
+class FwdParams(ctypes.Structure):
+    """Mirror of ``ccq_fwd_params``."""
+
+    _fields_ = [
+        ("rule", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("segments", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("log_alpha", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("w_lambda", ctypes.c_void_p), ("b_lambda", ctypes.c_void_p),
+        ("S0", ctypes.c_void_p), ("C0", ctypes.c_void_p), ("ksum0", ctypes.c_void_p),
+        ("n0", ctypes.c_void_p),
+        ("o", ctypes.c_void_p),
+        ("S_out", ctypes.c_void_p), ("C_out", ctypes.c_void_p), ("ksum_out", ctypes.c_void_p),
+        ("n_out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def library_path() -> str:
+    return os.environ.get("CCQ_LIBRARY", os.path.join(_HERE, "libccq.so"))
+
+
+def load_library():
+    """Load libccq.so (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m curvature_conditioned_query_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.ccq_fwd_chunked.argtypes = [ctypes.POINTER(FwdParams), vp]
+    lib.ccq_fwd_chunked.restype = ctypes.c_int
+    lib.ccq_fwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdParams)]
+    lib.ccq_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ccq_decode_step.argtypes = [i32, i32, i32, i32, i32, i32] + [vp] * 13
+    lib.ccq_decode_step.restype = ctypes.c_int
+    lib.ccq_status_string.argtypes = [i32]
+    lib.ccq_status_string.restype = ctypes.c_char_p
+    lib.ccq_abi_version.argtypes = []
+    lib.ccq_abi_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load_library().ccq_status_string(status).decode()
+    except Exception:  # pragma: no cover - only used for messages
+        return "?"
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return CCQ_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return CCQ_DTYPE_BF16
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check_dev(name, t, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _rule_code(rule) -> int:
+    if rule in ("gla", CCQ_RULE_GLA):
+        return CCQ_RULE_GLA
+    if rule in ("gdn", CCQ_RULE_GDN):
+        return CCQ_RULE_GDN
+    raise ValueError(f"unknown rule {rule!r}")
+
+
+def make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
+                    carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
+                    workspace=None) -> FwdParams:
+    """Fill a ccq_fwd_params from tensors (carry_in / carry_out: (S, C, ksum, n) or None)."""
+    import torch
+    B, H, T, d_k = q.shape
+    d_v = v.shape[-1]
+    p = FwdParams()
+    p.rule = _rule_code(rule)
+    p.dtype = _dtype_code(q)
+    p.B, p.H, p.T, p.d_k, p.d_v = B, H, T, d_k, d_v
+    p.chunk = chunk
+    p.segments = segments
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta), ("o", o)):
+        _check_dev(name, t, q.dtype)
+    _check_dev("w_lambda", w_lambda, torch.float32)
+    _check_dev("b_lambda", b_lambda, torch.float32)
+    p.q, p.k, p.v, p.log_alpha, p.beta = (_ptr(x) for x in (q, k, v, log_alpha, beta))
+    p.w_lambda, p.b_lambda, p.o = _ptr(w_lambda), _ptr(b_lambda), _ptr(o)
+    if carry_in is not None:
+        S0, C0, m0, n0 = carry_in
+        for name, t, dt in (("S0", S0, torch.float32), ("C0", C0, torch.float32),
+                            ("ksum0", m0, torch.float32), ("n0", n0, torch.int64)):
+            _check_dev(name, t, dt)
+        p.S0, p.C0, p.ksum0, p.n0 = _ptr(S0), _ptr(C0), _ptr(m0), _ptr(n0)
+    if carry_out is not None:
+        S1, C1, m1, n1 = carry_out
+        for name, t, dt in (("S_out", S1, torch.float32), ("C_out", C1, torch.float32),
+                            ("ksum_out", m1, torch.float32), ("n_out", n1, torch.int64)):
+            _check_dev(name, t, dt)
+        p.S_out, p.C_out, p.ksum_out, p.n_out = _ptr(S1), _ptr(C1), _ptr(m1), _ptr(n1)
+    if workspace is not None:
+        _check_dev("workspace", workspace)
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    return p
+
+
+def ccq_fwd_workspace_bytes(p: FwdParams) -> int:
+    return int(load_library().ccq_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
+                    carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
+                    workspace=None, stream=None):
+    """Chunked CCQ prefill through the C ABI.  Allocates o (and the workspace if not
+    given) with torch; returns o."""
+    import torch
+    lib = load_library()
+    if o is None:
+        o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    p = make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
+                        carry_in, carry_out, segments, chunk, workspace)
+    if workspace is None:
+        nbytes = int(lib.ccq_fwd_workspace_bytes(ctypes.byref(p)))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            p.workspace = workspace.data_ptr()
+            p.workspace_bytes = nbytes
+    st = lib.ccq_fwd_chunked(ctypes.byref(p), _stream_handle(stream))
+    if st != 0:
+        raise CcqError(st, "ccq_fwd_chunked")
+    return o
+
+
+def ccq_decode_step(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n,
+                    o=None, stream=None):
+    """One in-place decode step through the C ABI; returns o [N, H, d_v]."""
+    import torch
+    lib = load_library()
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=q.dtype, device=q.device)
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta), ("o", o)):
+        _check_dev(name, t, q.dtype)
+    for name, t, dt in (("w_lambda", w_lambda, torch.float32), ("b_lambda", b_lambda, torch.float32),
+                        ("S", S, torch.float32), ("C", C, torch.float32), ("ksum", ksum, torch.float32),
+                        ("n", n, torch.int64)):
+        _check_dev(name, t, dt)
+    st = lib.ccq_decode_step(_rule_code(rule), _dtype_code(q), N, H, d_k, d_v,
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(w_lambda), _ptr(b_lambda), _ptr(S), _ptr(C), _ptr(ksum), _ptr(n),
+                             _ptr(o), _stream_handle(stream))
+    if st != 0:
+        raise CcqError(st, "ccq_decode_step")
+    return o

@@ -1,0 +1,138 @@
+/*
+ * ccq.h -- C ABI of the MI355X (gfx950) Curvature-Conditioned Query read step.
+ *
+ * The method (gist.science summary of arXiv 2606.01294, "不要阅读一切：一种基于曲率条件
+ * 的线性注意力查询", §2 "理论推导", "机制" and "集成"):
+ *   keys are unit vectors; the running, undecayed key statistics give
+ *     mu_t = (1/t) sum_{j<=t} k_j,  Cbar_t = (1/t) sum_{j<=t} k_j k_j^T,
+ *     Sigma_t = Cbar_t - mu_t mu_t^T;
+ *   the gate is lambda_t = sigmoid(w_lambda . q_t + b_lambda) (one scalar per token and head);
+ *   the cleaned query is q_clean = q_t - lambda_t Sigma_t q_t;
+ *   the write rule is left as it is, and the read is o_t = S_t q_clean with S_t the
+ *   state after token t's write.
+ * Write rules (named by the pages, standard definitions):
+ *   CCQ_RULE_GLA : S_t = S_{t-1} diag(alpha_t) + v_t k_t^T,  alpha_t = exp(log_alpha_t) per key channel;
+ *   CCQ_RULE_GDN : S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T, scalar alpha_t, beta_t.
+ *
+ * Statistic state.  The pages keep one extra d_k x d_k matrix and one d_k vector per head
+ * (summary §2 "机制").  This library stores them as SUMS: C = sum k k^T, ksum = sum k, plus
+ * the token count n, and applies 1/n per token.
+ *
+ * Conventions for every entry point
+ *   - All pointers are DEVICE pointers owned by the caller; the library allocates no memory,
+ *     keeps no pointer after it returns and holds no global mutable state.  Calls are
+ *     reentrant.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default stream) without any
+ *     host synchronisation.  The caller keeps buffers alive until the stream has passed the
+ *     call.
+ *   - Every pointer must be 16-byte aligned.  Tensors are dense, row-major, in the shapes
+ *     given below.
+ *   - Argument errors return a negative ccq_status BEFORE anything is enqueued.  A failed
+ *     launch returns CCQ_ERR_LAUNCH.  Faults inside a kernel surface at the caller's next
+ *     synchronisation; the library does not hide them.
+ *   - Keys must already be L2-normalised (unit keys are the precondition of the eigenvalue
+ *     bound eig(I - lambda Sigma) in [1 - lambda, 1], 10100.com write-up, section "方法解析").
+ *     The library does not normalise them.
+ *   - Supported shapes: d_k == d_v, d in {64, 128} for CCQ_DTYPE_BF16, d == 64 for
+ *     CCQ_DTYPE_F32; chunk == 64 (or 0, meaning 64).  Anything else is CCQ_ERR_UNSUPPORTED.
+ */
+#ifndef CCQ_H_
+#define CCQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CCQ_OK = 0,
+  CCQ_ERR_INVALID_ARG = -1,  /* null required pointer, non-positive size, bad enum, partial carry */
+  CCQ_ERR_UNSUPPORTED = -2,  /* valid request this build has no kernel for (d, dtype, chunk)    */
+  CCQ_ERR_MISALIGNED = -3,   /* a pointer is not 16-byte aligned                                 */
+  CCQ_ERR_LAUNCH = -4,       /* the HIP runtime refused a launch                                 */
+  CCQ_ERR_WORKSPACE = -5     /* workspace missing or smaller than ccq_fwd_workspace_bytes()      */
+} ccq_status;
+
+typedef enum { CCQ_RULE_GLA = 0, CCQ_RULE_GDN = 1 } ccq_rule;
+
+/* Storage dtype of q, k, v, log_alpha, beta and o.  The carry is always fp32. */
+typedef enum { CCQ_DTYPE_F32 = 0, CCQ_DTYPE_BF16 = 1 } ccq_dtype;
+
+/* Arguments of ccq_fwd_chunked.  Zero-initialise, then fill in. */
+typedef struct {
+  int32_t rule;   /* ccq_rule  */
+  int32_t dtype;  /* ccq_dtype */
+  int32_t B, H, T;
+  int32_t d_k, d_v;
+  int32_t chunk;     /* 64, or 0 for the default (64)                                         */
+  int32_t segments;  /* sequence segments per (b, h) chain processed in parallel; 0 = choose  */
+
+  const void *q;         /* [B, H, T, d_k] dtype                                               */
+  const void *k;         /* [B, H, T, d_k] dtype, unit rows                                    */
+  const void *v;         /* [B, H, T, d_v] dtype                                               */
+  const void *log_alpha; /* GLA: [B, H, T, d_k]; GDN: [B, H, T]; dtype; log of the decay       */
+  const void *beta;      /* GDN: [B, H, T] dtype in (0, 1); GLA: must be NULL                  */
+  const float *w_lambda; /* [H, d_k] fp32 gate weights                                          */
+  const float *b_lambda; /* [H] fp32 gate bias (-INFINITY switches the cleaning off exactly)    */
+
+  /* Carry in: all four NULL (start from zeros, n0 = 0) or all four set. */
+  const float *S0;       /* [B, H, d_v, d_k]                                                    */
+  const float *C0;       /* [B, H, d_k, d_k]  sum of k k^T                                      */
+  const float *ksum0;    /* [B, H, d_k]       sum of k                                          */
+  const int64_t *n0;     /* [B, H]            token count                                       */
+
+  void *o;               /* [B, H, T, d_v] dtype, written                                       */
+
+  /* Carry out: all four NULL (not wanted) or all four set.  May alias the carry in. */
+  float *S_out;
+  float *C_out;
+  float *ksum_out;
+  int64_t *n_out;
+
+  void *workspace;        /* device scratch of at least ccq_fwd_workspace_bytes(p) bytes, or  */
+  size_t workspace_bytes; /* NULL / 0 when that function returns 0                            */
+} ccq_fwd_params;
+
+/*
+ * Chunked prefill of one CCQ layer: o for every token and, optionally, the final carry.
+ * The result is the per-token recurrence above evaluated exactly (up to rounding) with
+ * chunks of 64 tokens; the statistics are kept "by the same recurrent or chunked mechanism
+ * as the backbone state" (summary §2 "机制").  A call with a carry in continues the sequence
+ * the carry came from.  T need not be a multiple of 64.
+ * Precondition (GLA): within any 64-token chunk the cumulative log decay of each key channel
+ * stays above -80 on either side of the chunk's midpoint (no fp32 overflow of e^{+-B}).
+ * Returns a ccq_status.
+ */
+int ccq_fwd_chunked(const ccq_fwd_params *p, void *hip_stream);
+
+/* Bytes of device workspace ccq_fwd_chunked needs for these arguments (0 if none).  Depends
+ * only on rule, dtype, B, H, T, d_k, d_v, chunk and segments.  Returns 0 for invalid p too. */
+size_t ccq_fwd_workspace_bytes(const ccq_fwd_params *p);
+
+/*
+ * One decode step for N sequences x H heads, state updated in place:
+ *   n += 1; C += k k^T; ksum += k; Sigma q = C q / n - ksum (ksum . q) / n^2;
+ *   q_clean = q - lambda Sigma q; write rule; o = S q_clean.
+ * q, k: [N, H, d_k] dtype; v: [N, H, d_v] dtype; log_alpha: GLA [N, H, d_k] / GDN [N, H];
+ * beta: GDN [N, H] (GLA: NULL); w_lambda [H, d_k], b_lambda [H] fp32;
+ * S [N, H, d_v, d_k], C [N, H, d_k, d_k], ksum [N, H, d_k] fp32 and n [N, H] int64 are
+ * read and written in place; o [N, H, d_v] dtype is written.  Returns a ccq_status.
+ */
+int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                    const void *q, const void *k, const void *v, const void *log_alpha,
+                    const void *beta, const float *w_lambda, const float *b_lambda, float *S,
+                    float *C, float *ksum, int64_t *n, void *o, void *hip_stream);
+
+/* Static description of a status code (never NULL). */
+const char *ccq_status_string(int32_t status);
+
+/* ABI version of this header: 1. */
+int32_t ccq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCQ_H_ */
