@@ -1,0 +1,148 @@
+// C ABI of libccq.so: argument validation, workspace sizing and kernel dispatch.
+// Declarations and the contract live in include/ccq.h.  Nothing here allocates, keeps
+// state between calls or synchronises the stream.
+#include "ccq.h"
+
+#include <hip/hip_runtime.h>
+
+#include "ccq_internal.hpp"
+
+namespace {
+
+bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+constexpr int kChunk = 64;
+// Target number of (chain, segment) workgroups for the prefill: one per compute unit of
+// an MI355X (256 CUs).  A function of the shape only, so the workspace size never
+// depends on which device is current.
+constexpr int kTargetPrefillGroups = 256;
+
+int supported_d(int dtype, int d) {
+  if (dtype == CCQ_DTYPE_BF16) return d == 64 || d == 128;
+  return d == 64;
+}
+
+// Validates p; on success fills the resolved segment count.
+int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg_out) {
+  if (!p) return CCQ_ERR_INVALID_ARG;
+  if (p->rule != CCQ_RULE_GLA && p->rule != CCQ_RULE_GDN) return CCQ_ERR_INVALID_ARG;
+  if (p->dtype != CCQ_DTYPE_F32 && p->dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
+  if (p->B <= 0 || p->H <= 0 || p->T <= 0 || p->d_k <= 0 || p->d_v <= 0) return CCQ_ERR_INVALID_ARG;
+  if (p->chunk < 0 || p->segments < 0) return CCQ_ERR_INVALID_ARG;
+  if (p->chunk != 0 && p->chunk != kChunk) return CCQ_ERR_UNSUPPORTED;
+  if (p->d_k != p->d_v || !supported_d(p->dtype, p->d_k)) return CCQ_ERR_UNSUPPORTED;
+  if (!p->q || !p->k || !p->v || !p->log_alpha || !p->w_lambda || !p->b_lambda || !p->o)
+    return CCQ_ERR_INVALID_ARG;
+  if ((p->rule == CCQ_RULE_GDN) != (p->beta != nullptr)) return CCQ_ERR_INVALID_ARG;
+  const int nin = (p->S0 != nullptr) + (p->C0 != nullptr) + (p->ksum0 != nullptr) + (p->n0 != nullptr);
+  const int nout = (p->S_out != nullptr) + (p->C_out != nullptr) + (p->ksum_out != nullptr) + (p->n_out != nullptr);
+  if ((nin != 0 && nin != 4) || (nout != 0 && nout != 4)) return CCQ_ERR_INVALID_ARG;
+  const void* ptrs[] = {p->q, p->k, p->v, p->log_alpha, p->beta, p->w_lambda, p->b_lambda, p->S0, p->C0,
+                        p->ksum0, p->n0, p->o, p->S_out, p->C_out, p->ksum_out, p->n_out, p->workspace};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return CCQ_ERR_MISALIGNED;
+  const long long chains = (long long)p->B * p->H;
+  if (chains > (1LL << 24)) return CCQ_ERR_UNSUPPORTED;
+  const int nchunks = (p->T + kChunk - 1) / kChunk;
+  int seg = p->segments;
+  if (seg == 0) {
+    long long want = (kTargetPrefillGroups + chains - 1) / chains;
+    seg = (int)(want < nchunks ? want : nchunks);
+    if (seg < 1) seg = 1;
+  }
+  if (seg > nchunks) seg = nchunks;
+  // Rounds the segment length up to whole chunks and drops empty trailing segments.
+  const int cps = (nchunks + seg - 1) / seg;
+  seg = (nchunks + cps - 1) / cps;
+  if (p->rule == CCQ_RULE_GDN) seg = 1;  // Gated DeltaNet segments are not built yet
+  *segments_out = seg;
+  *chunks_per_seg_out = (p->rule == CCQ_RULE_GDN) ? nchunks : cps;
+  return CCQ_OK;
+}
+
+size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
+  if (seg <= 1) return 0;
+  return (size_t)p->B * p->H * seg * ccq::fwd_slot_bytes(p->d_k);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ccq_abi_version(void) { return 1; }
+
+const char* ccq_status_string(int32_t status) {
+  switch (status) {
+    case CCQ_OK: return "ok";
+    case CCQ_ERR_INVALID_ARG: return "invalid argument";
+    case CCQ_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case CCQ_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case CCQ_ERR_LAUNCH: return "kernel launch failed";
+    case CCQ_ERR_WORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+size_t ccq_fwd_workspace_bytes(const ccq_fwd_params* p) {
+  int seg = 0, cps = 0;
+  if (validate_fwd(p, &seg, &cps) != CCQ_OK) return 0;
+  return fwd_ws_bytes(p, seg);
+}
+
+int ccq_fwd_chunked(const ccq_fwd_params* p, void* hip_stream) {
+  int seg = 0, cps = 0;
+  const int st = validate_fwd(p, &seg, &cps);
+  if (st != CCQ_OK) return st;
+  const size_t need = fwd_ws_bytes(p, seg);
+  if (need > 0 && (p->workspace == nullptr || p->workspace_bytes < need)) return CCQ_ERR_WORKSPACE;
+  ccq::FwdArgs a;
+  a.rule = p->rule;
+  a.dtype = p->dtype;
+  a.B = p->B;
+  a.H = p->H;
+  a.T = p->T;
+  a.d = p->d_k;
+  a.segments = seg;
+  a.chunks_per_segment = cps;
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.log_alpha = p->log_alpha;
+  a.beta = p->beta;
+  a.w_lambda = p->w_lambda;
+  a.b_lambda = p->b_lambda;
+  a.S0 = p->S0;
+  a.C0 = p->C0;
+  a.ksum0 = p->ksum0;
+  a.n0 = p->n0;
+  a.o = p->o;
+  a.S_out = p->S_out;
+  a.C_out = p->C_out;
+  a.ksum_out = p->ksum_out;
+  a.n_out = p->n_out;
+  a.workspace = p->workspace;
+  const hipError_t e = ccq::launch_fwd(a, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
+}
+
+int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v, const void* q,
+                    const void* k, const void* v, const void* log_alpha, const void* beta, const float* w_lambda,
+                    const float* b_lambda, float* S, float* C, float* ksum, int64_t* n, void* o,
+                    void* hip_stream) {
+  if (rule != CCQ_RULE_GLA && rule != CCQ_RULE_GDN) return CCQ_ERR_INVALID_ARG;
+  if (dtype != CCQ_DTYPE_F32 && dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return CCQ_ERR_INVALID_ARG;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return CCQ_ERR_UNSUPPORTED;
+  if ((long long)N * H > 0x7fffffffLL) return CCQ_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !log_alpha || !w_lambda || !b_lambda || !S || !C || !ksum || !n || !o)
+    return CCQ_ERR_INVALID_ARG;
+  if ((rule == CCQ_RULE_GDN) != (beta != nullptr)) return CCQ_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, o};
+  for (const void* pp : ptrs)
+    if (misaligned(pp)) return CCQ_ERR_MISALIGNED;
+  ccq::DecodeArgs a{rule, dtype, N, H, d_k, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, o};
+  const hipError_t e = ccq::launch_decode(a, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
+}
+
+}  // extern "C"

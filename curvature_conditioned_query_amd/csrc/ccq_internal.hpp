@@ -1,0 +1,42 @@
+// Internal launch interface between the C ABI (ccq_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ccq {
+
+struct DecodeArgs {
+  int rule, dtype, N, H, d;
+  const void *q, *k, *v, *log_alpha, *beta;
+  const float *w_lambda, *b_lambda;
+  float *S, *C, *ksum;
+  int64_t* n;
+  void* o;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// One prefill call after validation.  Segment scheme: the T tokens of every (b, h)
+// chain are cut into `segments` contiguous runs of whole chunks.  With more than one
+// segment, a summary kernel condenses every segment but the last, a scan kernel turns
+// the summaries into each segment's carry-in (stored in the workspace), and the main
+// kernel runs all segments in parallel from their carry-ins.
+struct FwdArgs {
+  int rule, dtype, B, H, T, d, segments, chunks_per_segment;
+  const void *q, *k, *v, *log_alpha, *beta;
+  const float *w_lambda, *b_lambda;
+  const float *S0, *C0, *ksum0;
+  const int64_t* n0;
+  void* o;
+  float *S_out, *C_out, *ksum_out;
+  int64_t* n_out;
+  void* workspace;
+};
+
+// Bytes of one segment slot of the workspace (carry of one chain, plus the GLA decay).
+size_t fwd_slot_bytes(int d);
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+}  // namespace ccq

@@ -1,0 +1,106 @@
+"""The C ABI library loads, exports what include/ccq.h declares, and rejects bad
+arguments with the documented status codes before enqueuing anything.  No call
+here reaches a kernel, so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from curvature_conditioned_query_amd import binding
+from curvature_conditioned_query_amd.binding import FwdParams, load_library
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ccq.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, LAUNCH, WORKSPACE = 0, -1, -2, -3, -4, -5
+FAKE = 0x7F0000000000  # aligned, never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ccq_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTED_SYMBOLS)
+    for name in names:
+        assert hasattr(lib, name), f"libccq.so does not export {name}"
+    assert lib.ccq_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, MISALIGNED, LAUNCH, WORKSPACE, 17):
+        s = lib.ccq_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def _params(**kw):
+    p = FwdParams()
+    p.rule, p.dtype, p.B, p.H, p.T, p.d_k, p.d_v, p.chunk = 0, 1, 1, 2, 256, 128, 128, 64
+    p.q = p.k = p.v = p.log_alpha = p.w_lambda = p.b_lambda = p.o = FAKE
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _fwd(lib, p):
+    return lib.ccq_fwd_chunked(ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rule=7), INVALID), (dict(dtype=5), INVALID), (dict(B=0), INVALID), (dict(H=-1), INVALID),
+    (dict(T=0), INVALID), (dict(chunk=32), UNSUPPORTED), (dict(d_k=96, d_v=96), UNSUPPORTED),
+    (dict(d_k=64, d_v=128), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED), (dict(q=None), INVALID),
+    (dict(o=None), INVALID), (dict(beta=FAKE), INVALID), (dict(rule=1), INVALID),
+    (dict(S0=FAKE), INVALID), (dict(S_out=FAKE, C_out=FAKE), INVALID), (dict(k=FAKE + 4), MISALIGNED),
+    (dict(segments=-2), INVALID),
+])
+def test_fwd_argument_errors(lib, kw, code):
+    assert _fwd(lib, _params(**kw)) == code
+    assert lib.ccq_fwd_workspace_bytes(ctypes.byref(_params(**kw))) == 0
+
+
+def test_fwd_null_params(lib):
+    assert lib.ccq_fwd_chunked(None, None) == INVALID
+    assert lib.ccq_fwd_workspace_bytes(None) == 0
+
+
+def test_fwd_workspace_sizing_and_check(lib):
+    p = _params(B=4, H=16, T=4096)
+    need = lib.ccq_fwd_workspace_bytes(ctypes.byref(p))
+    assert need > 0  # 64 chains < 256 target groups: segments in use
+    # too small a workspace is refused before launch
+    p.workspace, p.workspace_bytes = FAKE, need - 16
+    assert _fwd(lib, p) == WORKSPACE
+    p.workspace = None
+    assert _fwd(lib, p) == WORKSPACE
+    # one segment per chain needs none
+    assert lib.ccq_fwd_workspace_bytes(ctypes.byref(_params(B=4, H=16, T=4096, segments=1))) == 0
+    assert lib.ccq_fwd_workspace_bytes(ctypes.byref(_params(B=64, H=16, T=64))) == 0
+
+
+def _dec(lib, rule=0, dtype=1, N=2, H=2, dk=128, dv=128, **ptrs):
+    names = ["q", "k", "v", "log_alpha", "beta", "w_lambda", "b_lambda", "S", "C", "ksum", "n", "o"]
+    vals = {n: FAKE for n in names}
+    vals["beta"] = None if rule == 0 else FAKE
+    vals.update(ptrs)
+    return lib.ccq_decode_step(rule, dtype, N, H, dk, dv, *[vals[n] for n in names], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rule=3), INVALID), (dict(dtype=2), INVALID), (dict(N=0), INVALID), (dict(H=0), INVALID),
+    (dict(dk=32, dv=32), UNSUPPORTED), (dict(dk=128, dv=64), UNSUPPORTED), (dict(q=None), INVALID),
+    (dict(S=None), INVALID), (dict(n=None), INVALID), (dict(beta=FAKE), INVALID),
+    (dict(rule=1, beta=None), INVALID), (dict(C=FAKE + 8), MISALIGNED),
+])
+def test_decode_argument_errors(lib, kw, code):
+    assert _dec(lib, **kw) == code
