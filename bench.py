@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the CCQ read step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--no-cpu] [--no-decode]
+
+A step is one chunked-prefill pass of a CCQ-GLA layer over one batch of synthetic
+input (B=4, H=16, T=4096, d_k=d_v=128, bf16 q/k/v/log-decay, fp32 carry out), with
+the inputs resident in HBM.  ``value`` is prefill tokens/s (B*T per second).  The
+same run times the decode step (256 sequences x 16 heads, d=128, a carry pre-filled
+from an 8K-token prefix) and reports its HBM bandwidth, and times the fp64 CPU
+oracle on a bounded sample of the prefill workload.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
+CHUNK = 64
+PREFILL_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill.hip")
+DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode.hip")
+
+
+# ------------------------------------------------------------------ algorithmic work
+def prefill_work(B, H, T, d, elem_bytes, rule="gla"):
+    """Algorithmic flops and HBM bytes of one prefill pass.
+
+    flops per (token, head): GLA 8 d^2 + 8 L d (full 16x16 MFMA tiles of the L=64 chunk
+    form: Q K^T, Q C0, tril(P) K, Qc S0^T, the intra attention matrix and its product
+    with V, K^T K and the S update); Gated DeltaNet 10 d^2 + 10 L d + L^2/3-ish solve.
+    bytes: q, k, v, log decay read once and o written once, plus the fp32 carry out
+    (S, C, ksum, n) per chain."""
+    th = B * H * T
+    if rule == "gla":
+        flop_th = 8 * d * d + 8 * CHUNK * d
+        in_bytes_th = 4 * d * elem_bytes
+    else:
+        flop_th = 10 * d * d + 12 * CHUNK * d
+        in_bytes_th = 3 * d * elem_bytes + 2 * elem_bytes
+    bytes_th = in_bytes_th + d * elem_bytes
+    carry = 2 * d * d * 4 + d * 4 + 8
+    return th * flop_th, th * bytes_th + B * H * carry
+
+
+def decode_bytes_per_head(d, elem_bytes):
+    """S and C (fp32 d x d) read and written, ksum read and written, n read and written,
+    one token (q, k, v, log alpha) read, o written."""
+    return 4 * d * d * 4 + 2 * d * 4 + 2 * 8 + 4 * d * elem_bytes + d * elem_bytes
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(name, src_sha):
+    """HBM traffic from committed rocprofv3 --pmc summaries, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != src_sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ GPU legs
+def to_dev(x, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(dtype).contiguous()
+
+
+def time_prefill(wl, steps, warmup):
+    import torch
+    from curvature_conditioned_query_amd import ccq_fwd_chunked, load_library
+    from curvature_conditioned_query_amd.inputs import WORKLOADS, workload_inputs
+    load_library()
+    spec = WORKLOADS[wl]
+    x = workload_inputs(wl)
+    tdt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    B, H, T, dk, dv = x.shape
+    q, k, v, g = (to_dev(a, tdt) for a in (x.q, x.k, x.v, x.g))
+    beta = None if x.beta is None else to_dev(x.beta, tdt)
+    w = torch.from_numpy(x.w_lam).cuda()
+    b = torch.from_numpy(x.b_lam).cuda()
+    o = torch.empty((B, H, T, dv), dtype=tdt, device="cuda")
+    cout = (torch.empty((B, H, dv, dk), device="cuda"), torch.empty((B, H, dk, dk), device="cuda"),
+            torch.empty((B, H, dk), device="cuda"), torch.empty((B, H), dtype=torch.int64, device="cuda"))
+    from curvature_conditioned_query_amd.binding import make_fwd_params, ccq_fwd_workspace_bytes
+    p = make_fwd_params(x.rule, q, k, v, g, beta, w, b, o, None, cout)
+    ws_bytes = ccq_fwd_workspace_bytes(p)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    del x
+
+    def step():
+        ccq_fwd_chunked(spec["rule"], q, k, v, g, beta, w, b, o=o, carry_out=cout, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total_ms = ev[0].elapsed_time(ev[steps])
+    segs = int(p.segments) if p.segments else None
+    return dict(spec=spec, shape=(B, H, T, dk, dv), total_ms=total_ms, per_ms=per, wall_s=t_wall,
+                dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs)
+
+
+def time_decode(steps, warmup, seqs_per_batch=32):
+    """Decode workload: 256 sequences x 16 heads, d=128, carry from an 8192-token prefix
+    built by the prefill kernel on device-generated seeded inputs."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_decode_step, ccq_fwd_chunked
+    from curvature_conditioned_query_amd.inputs import WORKLOADS
+    spec = WORKLOADS[4]
+    N, H, T, d = spec["N"], spec["H"], spec["T"], spec["d"]
+    bf = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(spec["seed"])
+    S = torch.empty((N, H, d, d), device="cuda")
+    C = torch.empty((N, H, d, d), device="cuda")
+    m = torch.empty((N, H, d), device="cuda")
+    n = torch.empty((N, H), dtype=torch.int64, device="cuda")
+    w = (torch.randn((H, d), generator=gen, device="cuda") / np.sqrt(d)).float().contiguous()
+    b = torch.full((H,), -2.0, device="cuda")
+    for s0 in range(0, N, seqs_per_batch):
+        nb = min(seqs_per_batch, N - s0)
+        shp = (nb, H, T, d)
+        qq = torch.randn(shp, generator=gen, device="cuda").to(bf)
+        kk = torch.randn(shp, generator=gen, device="cuda")
+        kk = (kk / kk.norm(dim=-1, keepdim=True)).to(bf)
+        vv = torch.randn(shp, generator=gen, device="cuda").to(bf)
+        gg = (torch.nn.functional.logsigmoid(torch.randn(shp, generator=gen, device="cuda")) / 16).to(bf)
+        ccq_fwd_chunked("gla", qq, kk, vv, gg, None, w, b,
+                        carry_out=(S[s0:s0 + nb], C[s0:s0 + nb], m[s0:s0 + nb], n[s0:s0 + nb]))
+        del qq, kk, vv, gg
+    torch.cuda.synchronize()
+    gen.manual_seed(spec["token_seed"])
+    tq = torch.randn((N, H, d), generator=gen, device="cuda").to(bf)
+    tk = torch.randn((N, H, d), generator=gen, device="cuda")
+    tk = (tk / tk.norm(dim=-1, keepdim=True)).to(bf)
+    tv = torch.randn((N, H, d), generator=gen, device="cuda").to(bf)
+    tg = (torch.nn.functional.logsigmoid(torch.randn((N, H, d), generator=gen, device="cuda")) / 16).to(bf)
+    o = torch.empty((N, H, d), dtype=bf, device="cuda")
+
+    def step():
+        ccq_decode_step("gla", tq, tk, tv, tg, None, w, b, S, C, m, n, o=o)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = N * H * decode_bytes_per_head(d, 2)
+    return dict(spec=spec, ms_per_step=ms, bytes_per_step=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                tokens_per_s=N / (ms * 1e-3), n_after=int(n[0, 0].item()))
+
+
+# ------------------------------------------------------------------ CPU oracle leg
+def _oracle_slab(args):
+    import oracle
+    q, k, v, g, beta, w, b, rule = args
+    t = time.perf_counter()
+    oracle.ccq_recurrent(q, k, v, g, beta, w, b, rule)
+    return time.perf_counter() - t
+
+
+def cpu_baseline(wl, tokens, max_workers):
+    """The fp64 recurrent oracle, as it is, on every (b, h) chain of the workload but only the
+    first `tokens` tokens of each; one chain slab per worker process, one BLAS thread each."""
+    import concurrent.futures as cf
+    from curvature_conditioned_query_amd.inputs import workload_inputs
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    x = workload_inputs(wl)
+    B, H, T, dk, dv = x.shape
+    tokens = min(tokens, T)
+    jobs = []
+    for bb in range(B):
+        for hh in range(H):
+            sl = x.slab(bb, hh, 0, tokens)
+            jobs.append((sl.q, sl.k, sl.v, sl.g, sl.beta, sl.w_lam, sl.b_lam, x.rule))
+    workers = max(1, min(max_workers, len(jobs)))
+    t0 = time.perf_counter()
+    with cf.ProcessPoolExecutor(max_workers=workers) as ex:
+        cpu_s = sum(ex.map(_oracle_slab, jobs))
+    wall = time.perf_counter() - t0
+    return dict(value=B * tokens / wall, unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"all {B * H} (b,h) chains of the workload, first {tokens} of {T} tokens each; "
+                       f"fp64 per-token recurrence; {workers} worker processes; {cpu_s:.1f} CPU-s, {wall:.1f} s wall",
+                wall_s=wall, cpu_s=cpu_s)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+# ------------------------------------------------------------------ main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    res = time_prefill(args.workload, args.steps, args.warmup)
+    B, H, T, dk, dv = res["shape"]
+    spec = res["spec"]
+    elem = 2 if res["dtype"] == "bf16" else 4
+    flops, nbytes = prefill_work(B, H, T, dk, elem, spec["rule"])
+    ms = res["total_ms"] / args.steps
+    tok_s = B * T / (ms * 1e-3)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    mfma_peak = BF16_PEAK_TFLOPS if res["dtype"] == "bf16" else FP32_PEAK_TFLOPS
+    intensity = flops / nbytes
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if intensity < ridge else "mfma"
+    src_sha = file_sha(PREFILL_SRC)
+    traffic = measured_traffic(f"traffic_{spec['name']}.json", src_sha)
+    if bound == "hbm":
+        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic)
+    else:
+        roof = dict(bound="mfma", achieved=round(tflops, 1), peak=mfma_peak, unit="TFLOP/s",
+                    frac=round(tflops / mfma_peak, 4), traffic=traffic)
+    roof.update(kernel="ccq_fwd_chunked pass: gla summary + scan + main prefill kernels",
+                algorithmic_bytes=nbytes, algorithmic_flops=flops, avg_launch_ms=round(ms, 4),
+                mfma=dict(achieved=round(tflops, 1), peak=mfma_peak, unit="TFLOP/s",
+                          frac=round(tflops / mfma_peak, 4)))
+    out = {
+        "metric": "CCQ-GLA prefill tokens/s (H16,dk128,T4K) + MFMA util; decode HBM GB/s",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": res["dtype"],
+        "data": "synthetic (seeded normal q, v; unit-normalised keys; logsigmoid(x)/16 log decay; bf16)",
+        "config": {"workload": spec["name"], "rule": spec["rule"], "B": B, "H": H, "T": T, "d_k": dk,
+                   "d_v": dv, "chunk": CHUNK, "segments": res["segments"], "carry": "fp32"},
+        "roofline": roof,
+    }
+    print(f"# prefill {spec['name']}: {ms:.3f} ms/step, {tok_s:.4g} tokens/s, {gbs:.1f} GB/s alg, "
+          f"{tflops:.1f} TFLOP/s alg", file=sys.stderr, flush=True)
+    if not args.no_decode:
+        dres = time_decode(args.decode_steps, 3)
+        dsrc = file_sha(DECODE_SRC)
+        out["decode"] = {
+            "workload": dres["spec"]["name"], "ms_per_step": round(dres["ms_per_step"], 4),
+            "tokens_per_s": round(dres["tokens_per_s"], 1),
+            "roofline": dict(bound="hbm", achieved=round(dres["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(dres["gbs"] / HBM_PEAK_GBS, 4),
+                             traffic=measured_traffic(f"traffic_{dres['spec']['name']}.json", dsrc)),
+            "algorithmic_bytes_per_step": dres["bytes_per_step"],
+        }
+        print(f"# decode: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s", file=sys.stderr, flush=True)
+    if not args.no_cpu:
+        try:
+            ncpu = len(os.sched_getaffinity(0))
+        except AttributeError:
+            ncpu = os.cpu_count() or 1
+        cb = cpu_baseline(args.workload, args.cpu_tokens, min(ncpu, 16))
+        cb["cpu_model"] = cpu_model()
+        out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample", "cpu_model")}
+        print(f"# cpu oracle: {cb['value']:.4g} tokens/s on {cb['cores']} cores ({cb['wall_s']:.1f} s wall)",
+              file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
