@@ -243,6 +243,8 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill leg (profiling the decode kernel alone)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     args = ap.parse_args(argv)
@@ -256,6 +258,10 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
+    if args.no_prefill:
+        dres = time_decode(args.decode_steps, 3)
+        print(f"# decode: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s", file=sys.stderr, flush=True)
+        return 0
     res = time_prefill(args.workload, args.steps, args.warmup)
     B, H, T, dk, dv = res["shape"]
     spec = res["spec"]

@@ -10,9 +10,10 @@
 //
 // Chunk algebra (rows i = 0..63 of a chunk, carry S0, C0 = sum k k^T, m0 = sum k, n0),
 // obtained by unrolling the per-token recurrence inside the chunk:
-//   s_i  = m0 + sum_{j<=i} k_j,  n_i = n0 + i + 1
-//   R    = Q C0 + tril_incl(Q K^T) K                     (row i = C_i q_i)
-//   u_i  = R_i / n_i - s_i (s_i . q_i) / n_i^2           (row i = Sigma_i q_i)
+//   s_i  = m0 + sum_{j<=i} k_j,  n_i = n0 + i + 1,  sq_i = s_i . q_i = m0 . q_i + sum_{j<=i} P_ij
+//   with P = Q K^T, row i of Q C0 + tril_incl(P) K is C_i q_i, and
+//   u_i  = C_i q_i / n_i - s_i sq_i / n_i^2                                  (row i = Sigma_i q_i)
+//        = (Q C0 + tril_incl(P - c 1^T) K)_i / n_i - m0 sq_i / n_i^2,  c_i = sq_i / n_i
 //   qc_i = q_i - lambda_i u_i
 //   B_i  = sum_{j<=i} g_j  (per channel, chunk-local)
 //   O    = (Qc * e^B) S0^T + tril_incl((Qc * e^B)(K * e^-B)^T) V
@@ -21,14 +22,17 @@
 // The intra-chunk decay is factored with the chunk start as reference, so e^{-B} stays
 // finite while B > -80 inside a chunk (the documented precondition).
 //
-// Kernel layout.  One workgroup of D/32 waves per (chain, segment).  Wave w keeps the
-// 32-wide slice [32w, 32w+32) of both fp32 carries as MFMA accumulators: tile (a, jm) of
-// C holds C[16a+4g+r][32w+16jm+l] and tile (a, jm) of S holds S^T[16a+4g+r][32w+16jm+l]
-// (lane l = lane % 16, g = lane / 16, r = element).  Read as an A operand, a pair of such
-// tiles is S (resp. C, which is symmetric) restricted to the wave's rows, so the carry
-// feeds the read-side MFMAs straight from registers and never touches LDS or HBM inside
-// the chain.  Chunk tiles are staged in LDS; the next chunk's global loads are issued into
-// registers before the current chunk is computed.
+// Kernel layout.  One workgroup of D/32 waves per (chain, segment).  Wave w owns the
+// 32-channel slice [32w, 32w+32) of d:
+//  - both fp32 carries live in its MFMA accumulators: tile (a, jm) of C holds
+//    C[16a+4g+r][32w+16jm+l] and tile (a, jm) of S holds S^T[16a+4g+r][32w+16jm+l]
+//    (l = lane % 16, g = lane / 16, r = element).  Read as an A operand, a pair of such
+//    tiles is S (resp. C, which is symmetric) restricted to the wave's rows, so the carry
+//    feeds the read-side MFMAs straight from registers and never leaves them inside a chain;
+//  - it loads its channels of the next chunk's q, k, v and log decay from HBM into MFMA
+//    fragments while the current chunk is computed, and stages them without scalar LDS
+//    traffic: transposes are MFMAs against an identity fragment (exact: x * 1 + 0), and the
+//    cumulative decay over tokens is an MFMA against a lower-triangular ones fragment.
 #include "ccq_device.hpp"
 #include "ccq_internal.hpp"
 
@@ -52,22 +56,24 @@ struct Cfg {
   static constexpr int PAD = 16 / sizeof(T);
   static constexpr int PQ = D + PAD;   // pitch of [64][D] tiles
   static constexpr int PT = kL + PAD;  // pitch of [D][64] and [64][64] tiles
-  static constexpr int PB = D + 4;     // pitch of the fp32 [64][D] decay tile
 };
 
 template <int D, typename T>
 struct Smem {
   using C_ = Cfg<D, T>;
+  static constexpr int LO = (sizeof(T) == 2) ? kL : 1;  // rows of the bf16 lo tiles
   T Qs[kL][C_::PQ];   // q rows
-  T Qa[kL][C_::PQ];   // q_clean * e^B
-  T Ks[kL][C_::PQ];   // k rows, then k * e^-B in place
+  T Qa[kL][C_::PQ];   // q_clean * e^B (hi part for bf16)
+  T Qalo[LO][C_::PQ]; // bf16 only: lo part of q_clean * e^B
+  T Ks[kL][C_::PQ];   // k rows; later k * e^-B (hi part), in place
+  T Klo[LO][C_::PQ];  // bf16 only: lo part of k * e^-B
   T Kt[D][C_::PT];    // k^T
   T Kpt[D][C_::PT];   // (k * e^-B)^T
   T Vt[D][C_::PT];    // v^T
-  T Pm[kL][C_::PT];   // masked Q K^T, then the masked intra-chunk attention matrix
-  float Bs[kL][C_::PB];  // chunk-local cumulative log decay (inclusive)
-  float w[D], m0[D], m1[D], eBL[D], ldec[D];
-  float lam[kL], mq[kL], psum[4][kL];
+  T Pm[kL][C_::PT];   // tril(Q K^T - c 1^T), then the masked intra-chunk attention matrix
+  T Wt[16][C_::PQ];   // rows: w_lambda hi, lo; key sum hi, lo; zeros (B operand of q . [w, m0])
+  float m0[D], m1[D], eBL[D], ldec[D];
+  f32x4 tok[kL];      // per token: lambda, 1/n, sq/n^2, gate logit + b
 };
 
 // Lower-triangular 16x16 tiles of a 64x64 token-token matrix, (row tile, col tile).
@@ -106,6 +112,67 @@ __device__ __forceinline__ void unpack(const u32x4& v, float* out) {
   }
 }
 
+
+// 8 elements of one row from global memory (16 bytes for bf16, 32 for fp32), or zeros.
+template <typename T>
+__device__ __forceinline__ Frag<T> gload_frag(const T* p, bool ok) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    f.v = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(p) : z);
+  } else {
+    const f32x4 lo = ok ? *reinterpret_cast<const f32x4*>(p) : zero4();
+    const f32x4 hi = ok ? *reinterpret_cast<const f32x4*>(p + 4) : zero4();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[4 + e] = hi[e]; }
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_frag(T* p, const Frag<T>& f) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x8*>(p) = f.v;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{f.v[4], f.v[5], f.v[6], f.v[7]};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T cvt(float x) { return (T)x; }
+
+// Identity slice in KORD_CONTIG order: element e of lane (g, l) is 1 where 8g + e == l + 16h.
+// As a B operand against row fragments X[t][k] it yields X[t][16h + n] in the accumulator
+// (4 consecutive tokens per lane); as an A operand against row fragments used as B it
+// yields X[t][16h + 4g + r] (4 consecutive channels per lane).
+template <typename T>
+__device__ __forceinline__ Frag<T> ident_frag(int h, int lane) {
+  Frag<T> f;
+  const int l = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = cvt<T>((8 * g + e == l + 16 * h) ? 1.0f : 0.0f);
+  return f;
+}
+
+// Lower-triangular ones L[t][t'] = (t' <= t) as the A operand, in KORD_ACC order over
+// t' = 32 kk + 16 (e / 4) + 4 g + e % 4, with t = 16 ti + (lane % 16).
+template <typename T>
+__device__ __forceinline__ Frag<T> ltri_frag(int ti, int kk, int lane) {
+  Frag<T> f;
+  const int t = 16 * ti + (lane & 15), g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int tp = 32 * kk + 16 * (e >> 2) + 4 * g + (e & 3);
+    f.v[e] = cvt<T>(tp <= t ? 1.0f : 0.0f);
+  }
+  return f;
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& v) {
+  return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+
 // Ones where token j <= token i, as the B fragment of the inclusive prefix over tokens:
 // B[k = j][n = i] with i = 16 ti + (lane % 16), j = 32 kk + 8 g + e (KORD_CONTIG).
 template <typename T>
@@ -128,14 +195,14 @@ __device__ __forceinline__ Frag<T> causal_ones(int ti, int kk, int lane) {
 template <int D, typename T, int MODE>
 __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
   using C_ = Cfg<D, T>;
-  constexpr int NW = C_::NW, NTH = C_::NTH, NA = C_::NA, NK = C_::NK, VE = C_::VE, NV = C_::NV;
-  constexpr int PQ = C_::PQ, PT = C_::PT, PB = C_::PB;
+  constexpr int NW = C_::NW, NA = C_::NA, NK = C_::NK;
+  constexpr int PQ = C_::PQ, PT = C_::PT;
   constexpr bool MAIN = (MODE == 0);
   constexpr bool kSplit = MAIN && sizeof(T) == 2;  // hi/lo operands for the intra term
-  static_assert(kL * PQ * sizeof(T) <= kL * PB * sizeof(float), "lo tile must fit the decay tile");
   __shared__ Smem<D, T> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int cw = 32 * w;  // first channel of this wave's slice
   const int P = a.segments, cps = a.chunks_per_segment;
   const int per_chain = MAIN ? P : P - 1;
   const int chain = blockIdx.x / per_chain, seg = blockIdx.x % per_chain;
@@ -172,7 +239,7 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
   for (int t = 0; t < NA; ++t) {
 #pragma unroll
     for (int jm = 0; jm < 2; ++jm) {
-      const int row = 32 * w + 16 * jm + l16;
+      const int row = cw + 16 * jm + l16;
       const int col = 16 * t + 4 * g;
       Sacc[t][jm] = Sin ? *reinterpret_cast<const f32x4*>(Sin + (size_t)row * D + col) : zero4();
       Cacc[t][jm] = Cin ? *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col) : zero4();
@@ -185,225 +252,262 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
   float b_lam = 0.f;
   if constexpr (MAIN) b_lam = a.b_lambda[h];
 
-  for (int c = tid; c < D; c += NTH) {
-    sm.m0[c] = min_ ? min_[c] : 0.f;
+  if (tid < D) {
+    const int c = tid;
+    const float m = min_ ? min_[c] : 0.f;
+    sm.m0[c] = m;
     sm.ldec[c] = 0.f;
-    if constexpr (MAIN) sm.w[c] = a.w_lambda[(size_t)h * D + c];
+    if constexpr (MAIN) {
+      const float wv = a.w_lambda[(size_t)h * D + c];
+      const T whi = (T)wv, mhi = (T)m;
+      sm.Wt[0][c] = whi;
+      sm.Wt[1][c] = (T)(wv - (float)whi);
+      sm.Wt[2][c] = mhi;
+      sm.Wt[3][c] = (T)(m - (float)mhi);
+#pragma unroll
+      for (int r = 4; r < 16; ++r) sm.Wt[r][c] = (T)0.f;
+    }
   }
   if constexpr (MAIN) {
-    for (int e = tid; e < kL * PT; e += NTH) (&sm.Pm[0][0])[e] = (T)0.f;
-    for (int e = tid; e < 4 * kL; e += NTH) (&sm.psum[0][0])[e] = 0.f;
+    for (int e = tid; e < kL * PT; e += 2 * D) (&sm.Pm[0][0])[e] = (T)0.f;
   }
 
-  // ---- register prefetch of one chunk (rows >= Lc are zero)
-  u32x4 rq[NV], rk[NV], rv[NV], rg[NV];
+  // ---- register prefetch: this wave's 32 channels of one chunk, as MFMA row fragments
+  // (lane: token 16 ti + l16, channels cw + 8g .. cw + 8g + 7); rows past the end are zero.
+  Frag<T> fq[4], fk[4], fv[4], fg[4];
   auto prefetch = [&](int ch) {
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int vi = tid + j * NTH;
-      const int t = (vi * VE) / D, c = (vi * VE) % D;
-      const size_t off = (tok0 + t0 + t) * D + c;
+    for (int ti = 0; ti < 4; ++ti) {
+      const int t = 16 * ti + l16;
       const bool ok = t < Lc;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      if constexpr (MAIN) rq[j] = ok ? *reinterpret_cast<const u32x4*>(qg + off) : z;
-      rk[j] = ok ? *reinterpret_cast<const u32x4*>(kg + off) : z;
-      rv[j] = ok ? *reinterpret_cast<const u32x4*>(vg + off) : z;
-      rg[j] = ok ? *reinterpret_cast<const u32x4*>(gg + off) : z;
+      const size_t off = ok ? (tok0 + t0 + t) * D + cw + 8 * g : 0;
+      if constexpr (MAIN) fq[ti] = gload_frag<T>(qg + off, ok);
+      fk[ti] = gload_frag<T>(kg + off, ok);
+      fv[ti] = gload_frag<T>(vg + off, ok);
+      fg[ti] = gload_frag<T>(gg + off, ok);
     }
   };
   if (cbeg < cend) prefetch(cbeg);
 
-  f32x4 qlo[4][2];
-  float klo[NV][VE];
+  const Frag<T> I0 = ident_frag<T>(0, lane), I1 = ident_frag<T>(1, lane);
+
   for (int ch = cbeg; ch < cend; ++ch) {
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
 
-    // ---- stage the chunk: q, k rows; k^T, v^T; raw log decay (fp32)
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int vi = tid + j * NTH;
-      const int t = (vi * VE) / D, c = (vi * VE) % D;
-      if constexpr (MAIN) *reinterpret_cast<u32x4*>(&sm.Qs[t][c]) = rq[j];
-      *reinterpret_cast<u32x4*>(&sm.Ks[t][c]) = rk[j];
-      float kf[VE], vf[VE], gf[VE];
-      unpack<T>(rk[j], kf);
-      unpack<T>(rv[j], vf);
-      unpack<T>(rg[j], gf);
-#pragma unroll
-      for (int e = 0; e < VE; ++e) {
-        sm.Kt[c + e][t] = (T)kf[e];
-        sm.Vt[c + e][t] = (T)vf[e];
-        sm.Bs[t][c + e] = gf[e];
-      }
-    }
-    __syncthreads();
-    if (ch + 1 < cend) prefetch(ch + 1);
-
-    // ---- per-token gate and m0 . q  (NW lanes per token, 32 channels each)
-    if constexpr (MAIN) {
-      const int i = w * (kL / NW) + lane / NW;
-      const int p = lane % NW;
-      float wq = 0.f, mq = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < 32; ++e) {
-        const int c = 32 * p + e;
-        const float qv = (float)sm.Qs[i][c];
-        wq += sm.w[c] * qv;
-        mq += sm.m0[c] * qv;
-      }
-      wq = group_sum<NW>(wq);
-      mq = group_sum<NW>(mq);
-      if (p == 0) {
-        sm.lam[i] = sigmoidf(wq + b_lam);
-        sm.mq[i] = mq;
-      }
-    }
-    // ---- cumulative log decay per channel, key sum, chunk decay e^{B_63}
-    if (tid < D) {
-      const int c = tid;
-      float run = 0.f, ks = 0.f;
-#pragma unroll 16
-      for (int t = 0; t < kL; ++t) {
-        run += sm.Bs[t][c];
-        sm.Bs[t][c] = run;
-        ks += (float)sm.Kt[c][t];
-      }
-      sm.m1[c] = sm.m0[c] + ks;
-      sm.eBL[c] = __expf(run);
-      sm.ldec[c] += run;
-    }
-    // ---- P^T = K Q^T on the lower tiles -> Pm[i][j] (masked, j <= i) and row sums
-    if constexpr (MAIN) {
-      for (int idx = w; idx < 10; idx += NW) {
-        const int ti = kTri[idx][0], tj = kTri[idx][1];
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
-          const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
-          mma(acc, A, B);
-        }
-        const int i = 16 * ti + l16;
-        float ps = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * tj + 4 * g + r;
-          acc[r] = (j <= i) ? acc[r] : 0.f;
-          ps += acc[r];
-        }
-        ps += __shfl_xor(ps, 16, 64);
-        ps += __shfl_xor(ps, 32, 64);
-        if (g == 0) sm.psum[tj][i] = ps;
-        st4<T>(&sm.Pm[i][16 * tj + 4 * g], acc);
-      }
-    }
-    __syncthreads();
-
-    // ---- cleaned query for the wave's 32 channels (MAIN), k * e^-B in both layouts
-    if constexpr (MAIN) {
-      f32x4 R[2][4], Sp[2][4];
-#pragma unroll
-      for (int jm = 0; jm < 2; ++jm)
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) R[jm][ti] = Sp[jm][ti] = zero4();
-      // Q C0 (A operand straight from the carry accumulators)
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const Frag<T> A0 = acc_frag<T>(Cacc[2 * kk][0], Cacc[2 * kk + 1][0]);
-        const Frag<T> A1 = acc_frag<T>(Cacc[2 * kk][1], Cacc[2 * kk + 1][1]);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const Frag<T> B = lds_frag<T, KORD_ACC>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
-          mma(R[0][ti], A0, B);
-          mma(R[1][ti], A1, B);
-        }
-      }
-      // tril(Q K^T) K and the inclusive key prefix sum_{j<=i} k_j
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const Frag<T> A0 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, 32 * w, 32 * kk, lane);
-        const Frag<T> A1 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, 32 * w + 16, 32 * kk, lane);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          if (kk == 1 && ti < 2) continue;  // tokens 32..63 never precede tokens 0..31
-          const Frag<T> Bp = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
-          const Frag<T> Bo = causal_ones<T>(ti, kk, lane);
-          mma(R[0][ti], A0, Bp);
-          mma(R[1][ti], A1, Bp);
-          mma(Sp[0][ti], A0, Bo);
-          mma(Sp[1][ti], A1, Bo);
-        }
-      }
-      // u = R / n - s (s . q) / n^2;  qc = q - lambda u;  Qa = qc * e^B.  For bf16 operands
-      // Qa is kept as hi + lo (lo = bf16(x - hi)): the intra-chunk attention matrix is a sum
-      // of few, possibly cancelling products when little of the sequence has been read.
+    // ---- stage this wave's channels: rows, transposes, cumulative decay, k e^-B transposed
+    {
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const int i = 16 * ti + l16;
-        const float inv_n = 1.0f / (float)(nb + i + 1);
-        const float sq = sm.mq[i] + sm.psum[0][i] + sm.psum[1][i] + sm.psum[2][i] + sm.psum[3][i];
-        const float coef = sq * inv_n * inv_n;
-        const float lam = sm.lam[i];
+        const int t = 16 * ti + l16;
+        if constexpr (MAIN) st_frag<T>(&sm.Qs[t][cw + 8 * g], fq[ti]);
+        st_frag<T>(&sm.Ks[t][cw + 8 * g], fk[ti]);
+        f32x4 V0 = zero4(), V1 = zero4();
+        mma(V0, fv[ti], I0);
+        mma(V1, fv[ti], I1);
+        st4<T>(&sm.Vt[cw + l16][16 * ti + 4 * g], V0);
+        st4<T>(&sm.Vt[cw + 16 + l16][16 * ti + 4 * g], V1);
+      }
+      // one 16-channel half at a time keeps the transposes' registers down
 #pragma unroll
-        for (int jm = 0; jm < 2; ++jm) {
-          const int m = 32 * w + 16 * jm + 4 * g;
-          const f32x4 q4 = ld4<T>(&sm.Qs[i][m]);
-          const f32x4 b4 = *reinterpret_cast<const f32x4*>(&sm.Bs[i][m]);
-          f32x4 qa;
+      for (int hh = 0; hh < 2; ++hh) {
+        const Frag<T>& Ih = hh ? I1 : I0;
+        const int c = cw + 16 * hh + l16;
+        f32x4 KT[4], GT[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          KT[ti] = GT[ti] = zero4();
+          mma(KT[ti], fk[ti], Ih);  // KT[ti][r] = k at token 16 ti + 4 g + r, channel c
+          mma(GT[ti], fg[ti], Ih);
+          st4<T>(&sm.Kt[c][16 * ti + 4 * g], KT[ti]);
+        }
+        const Frag<T> G0 = acc_frag<T>(GT[0], GT[1]);
+        const Frag<T> G1 = acc_frag<T>(GT[2], GT[3]);
+        float ks = 0.f;
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+          f32x4 Bc = zero4();
+          mma(Bc, ltri_frag<T>(ti, 0, lane), G0);
+          if (ti >= 2) mma(Bc, ltri_frag<T>(ti, 1, lane), G1);
+          // Bc[r] = cumulative log decay at token 16 ti + 4 g + r, channel c
+          f32x4 kp;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float s = Sp[jm][ti][r] + sm.m0[m + r];
-            const float u = R[jm][ti][r] * inv_n - s * coef;
-            qa[r] = (q4[r] - lam * u) * __expf(b4[r]);
+            kp[r] = KT[ti][r] * __expf(-Bc[r]);
+            ks += KT[ti][r];
           }
-          st4<T>(&sm.Qa[i][m], qa);
-          if constexpr (kSplit) qlo[ti][jm] = qa - ld4<T>(&sm.Qa[i][m]);
+          st4<T>(&sm.Kpt[c][16 * ti + 4 * g], kp);
+          if (ti == 3 && g == 3) {
+            sm.eBL[c] = __expf(Bc[3]);
+            sm.ldec[c] += Bc[3];
+          }
         }
+        ks += __shfl_xor(ks, 16, 64);
+        ks += __shfl_xor(ks, 32, 64);
+        if (g == 0) sm.m1[c] = sm.m0[c] + ks;
       }
-      // k * e^-B, row-major, hi in place (nothing reads Ks in this phase); lo kept in registers
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int vi = tid + j * NTH;
-        const int t = (vi * VE) / D, c = (vi * VE) % D;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          const float kp = (float)sm.Ks[t][c + e] * __expf(-sm.Bs[t][c + e]);
-          const T hi = (T)kp;
-          sm.Ks[t][c + e] = hi;
-          if constexpr (kSplit) klo[j][e] = kp - (float)hi;
-        }
+      // the summary pass has registers to spare: its next chunk's loads go out now
+      if constexpr (!MAIN) {
+        if (ch + 1 < cend) prefetch(ch + 1);
       }
-    }
-    // (k * e^-B)^T
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int vi = tid + j * NTH;
-      const int c = (vi * VE) / kL, t = (vi * VE) % kL;
-#pragma unroll
-      for (int e = 0; e < VE; ++e) sm.Kpt[c][t + e] = (T)((float)sm.Kt[c][t + e] * __expf(-sm.Bs[t + e][c]));
     }
     __syncthreads();
 
     if constexpr (MAIN) {
-      if constexpr (kSplit) {
-        // lo parts into tiles nobody reads any more: Qa lo over q rows, (k e^-B) lo over the decay tile
-        T* Klo = reinterpret_cast<T*>(&sm.Bs[0][0]);
+      // ---- one 16-token row tile per wave: gate logit and m0 . q, then the row tile of
+      // P = Q K^T, its inclusive row sums, and Pm = tril(P - c 1^T) with c_i = sq_i / n_i
+      for (int it = w; it < 4; it += NW) {
+        {
+          f32x4 acc = zero4();  // [q] x [w_hi, w_lo, m0_hi, m0_lo]
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+          for (int kk = 0; kk < NK; ++kk) {
+            const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * it, 32 * kk, lane);
+            const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Wt[0][0], PQ, 0, 32 * kk, lane);
+            mma(acc, A, B);
+          }
 #pragma unroll
-          for (int jm = 0; jm < 2; ++jm) st4<T>(&sm.Qs[16 * ti + l16][32 * w + 16 * jm + 4 * g], qlo[ti][jm]);
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          const int vi = tid + j * NTH;
-          const int t = (vi * VE) / D, c = (vi * VE) % D;
-#pragma unroll
-          for (int e = 0; e < VE; ++e) Klo[t * PQ + c + e] = (T)klo[j][e];
+          for (int r = 0; r < 4; ++r) {
+            const float x = acc[r] + __shfl_down(acc[r], 1, 64);  // hi + lo columns
+            const int i = 16 * it + 4 * g + r;
+            if (l16 == 0) sm.tok[i][3] = x + b_lam;
+            if (l16 == 2) sm.tok[i][1] = x;  // m0 . q, parked until the row sums are known
+          }
         }
-        __syncthreads();
+        const int i = 16 * it + l16;  // this lane's token in the P tiles below
+        f32x4 Pt[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+          Pt[tj] = zero4();
+          if (tj > it) continue;
+#pragma unroll
+          for (int kk = 0; kk < NK; ++kk) {
+            const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+            const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * it, 32 * kk, lane);
+            mma(Pt[tj], A, B);
+          }
+          // Pt[tj][r] = P[i][16 tj + 4 g + r]
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool keep = 16 * tj + 4 * g + r <= i;
+            Pt[tj][r] = keep ? Pt[tj][r] : 0.f;
+            rs += Pt[tj][r];
+          }
+        }
+        rs += __shfl_xor(rs, 16, 64);
+        rs += __shfl_xor(rs, 32, 64);
+        const float gate = sm.tok[i][3];
+        const float sq = sm.tok[i][1] + rs;
+        const float inv_n = __builtin_amdgcn_rcpf((float)(nb + i + 1));
+        const float cbar = sq * inv_n;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+          if (tj > it) continue;
+          f32x4 pc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pc[r] = (16 * tj + 4 * g + r <= i) ? Pt[tj][r] - cbar : 0.f;
+          st4<T>(&sm.Pm[i][16 * tj + 4 * g], pc);
+        }
+        if (g == 0) sm.tok[i] = f32x4{sigmoidf(gate), inv_n, cbar * inv_n, gate};
       }
+      __syncthreads();
+
+      // ---- cleaned query for the wave's 32 channels, and k * e^-B
+      {
+        f32x4 R[2][4];
+#pragma unroll
+        for (int jm = 0; jm < 2; ++jm)
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) R[jm][ti] = zero4();
+        // Q C0 (A operand straight from the carry accumulators)
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          const Frag<T> A0 = acc_frag<T>(Cacc[2 * kk][0], Cacc[2 * kk + 1][0]);
+          const Frag<T> A1 = acc_frag<T>(Cacc[2 * kk][1], Cacc[2 * kk + 1][1]);
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) {
+            const Frag<T> B = lds_frag<T, KORD_ACC>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
+            mma(R[0][ti], A0, B);
+            mma(R[1][ti], A1, B);
+          }
+        }
+        // + tril(P - c 1^T) K
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const Frag<T> A0 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw, 32 * kk, lane);
+          const Frag<T> A1 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw + 16, 32 * kk, lane);
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) {
+            if (kk == 1 && ti < 2) continue;  // tokens 32..63 never precede tokens 0..31
+            const Frag<T> Bp = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
+            mma(R[0][ti], A0, Bp);
+            mma(R[1][ti], A1, Bp);
+          }
+        }
+        // R[jm][ti][r]: channel cw + 16 jm + 4 g + r, token 16 ti + l16.  The cumulative decay
+        // in the same layout, from the chunk's log-decay rows still in registers:
+        // Bc^T = (G^T)(L^T) with G^T read off the transposes of the rows.
+#pragma unroll
+        for (int jm = 0; jm < 2; ++jm) {
+          const Frag<T>& Ih = jm ? I1 : I0;
+          f32x4 GT[4];
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) {
+            GT[ti] = zero4();
+            mma(GT[ti], fg[ti], Ih);
+          }
+          const Frag<T> Ga = acc_frag<T>(GT[0], GT[1]);
+          const Frag<T> Gb = acc_frag<T>(GT[2], GT[3]);
+          const int m = cw + 16 * jm + 4 * g;
+          const f32x4 m04 = *reinterpret_cast<const f32x4*>(&sm.m0[m]);
+#pragma unroll
+          for (int ti = 0; ti < 4; ++ti) {
+            f32x4 BT = zero4();
+            mma(BT, Ga, ltri_frag<T>(ti, 0, lane));
+            if (ti >= 2) mma(BT, Gb, ltri_frag<T>(ti, 1, lane));
+            const int i = 16 * ti + l16;
+            const f32x4 ts = sm.tok[i];  // lambda, 1/n, sq/n^2
+            const f32x4 q4 = ld4<T>(&sm.Qs[i][m]);
+            f32x4 qa;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float u = R[jm][ti][r] * ts[1] - m04[r] * ts[2];
+              qa[r] = (q4[r] - ts[0] * u) * __expf(BT[r]);
+            }
+            // k * e^-B at the same (token, channel) positions: identity A against the k rows
+            f32x4 KC = zero4();
+            mma(KC, Ih, fk[ti]);
+            f32x4 kp;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) kp[r] = KC[r] * __expf(-BT[r]);
+            // bf16: hi + lo (the intra-chunk attention is a sum of few, possibly cancelling
+            // products when little of the sequence has been read)
+            const bf16x4 qh = to_bf16x4(qa), kh = to_bf16x4(kp);
+            if constexpr (kSplit) {
+              *reinterpret_cast<bf16x4*>(&sm.Qa[i][m]) = qh;
+              *reinterpret_cast<bf16x4*>(&sm.Ks[i][m]) = kh;
+              f32x4 ql, kl;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                ql[r] = qa[r] - (float)qh[r];
+                kl[r] = kp[r] - (float)kh[r];
+              }
+              st4<T>(&sm.Qalo[i][m], ql);
+              st4<T>(&sm.Klo[i][m], kl);
+            } else {
+              st4<T>(&sm.Qa[i][m], qa);
+              st4<T>(&sm.Ks[i][m], kp);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // the chunk's row fragments are consumed: next chunk's loads go out now, behind the
+      // intra-chunk read, the output store and the carry update
+      if (ch + 1 < cend) prefetch(ch + 1);
+
       // ---- intra-chunk attention (Qc e^B)(K e^-B)^T on the lower tiles -> Pm (masked)
       for (int idx = w; idx < 10; idx += NW) {
         const int ti = kTri[idx][0], tj = kTri[idx][1];
@@ -414,8 +518,8 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
           const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
           mma(acc, A, B);
           if constexpr (kSplit) {
-            const Frag<T> Al = lds_frag<T, KORD_CONTIG>(reinterpret_cast<const T*>(&sm.Bs[0][0]), PQ, 16 * tj, 32 * kk, lane);
-            const Frag<T> Bl = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
+            const Frag<T> Al = lds_frag<T, KORD_CONTIG>(&sm.Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
+            const Frag<T> Bl = lds_frag<T, KORD_CONTIG>(&sm.Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
             mma(acc, A, Bl);
             mma(acc, Al, B);
           }
@@ -446,8 +550,8 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const Frag<T> A0 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, 32 * w, 32 * kk, lane);
-        const Frag<T> A1 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, 32 * w + 16, 32 * kk, lane);
+        const Frag<T> A0 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw, 32 * kk, lane);
+        const Frag<T> A1 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw + 16, 32 * kk, lane);
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           if (kk == 1 && ti < 2) continue;
@@ -462,7 +566,7 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
         const int i = 16 * ti + l16;
         if (i < Lc) {
 #pragma unroll
-          for (int jm = 0; jm < 2; ++jm) st4<T>(og + (tok0 + t0 + i) * D + 32 * w + 16 * jm + 4 * g, O[jm][ti]);
+          for (int jm = 0; jm < 2; ++jm) st4<T>(og + (tok0 + t0 + i) * D + cw + 16 * jm + 4 * g, O[jm][ti]);
         }
       }
     }
@@ -470,10 +574,10 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
     // ---- carry update: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const Frag<T> Bk0 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, 32 * w, 32 * kk, lane);
-      const Frag<T> Bk1 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, 32 * w + 16, 32 * kk, lane);
-      const Frag<T> Bv0 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, 32 * w, 32 * kk, lane);
-      const Frag<T> Bv1 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, 32 * w + 16, 32 * kk, lane);
+      const Frag<T> Bk0 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw, 32 * kk, lane);
+      const Frag<T> Bk1 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw + 16, 32 * kk, lane);
+      const Frag<T> Bv0 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw, 32 * kk, lane);
+      const Frag<T> Bv1 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw + 16, 32 * kk, lane);
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
         const Frag<T> Ak = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, 16 * t, 32 * kk, lane);
@@ -490,7 +594,15 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
       Sacc[t][0] *= e4;
       Sacc[t][1] *= e4;
     }
-    if (tid < D) sm.m0[tid] = sm.m1[tid];
+    if (tid < D) {
+      const float m = sm.m1[tid];
+      sm.m0[tid] = m;
+      if constexpr (MAIN) {
+        const T mhi = (T)m;
+        sm.Wt[2][tid] = mhi;
+        sm.Wt[3][tid] = (T)(m - (float)mhi);
+      }
+    }
     nb += Lc;
     __syncthreads();
   }
@@ -519,15 +631,15 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
     for (int t = 0; t < NA; ++t) {
 #pragma unroll
       for (int jm = 0; jm < 2; ++jm) {
-        const int row = 32 * w + 16 * jm + l16;
+        const int row = cw + 16 * jm + l16;
         const int col = 16 * t + 4 * g;
         *reinterpret_cast<f32x4*>(Sout + (size_t)row * D + col) = Sacc[t][jm];
         *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t][jm];
       }
     }
-    for (int c = tid; c < D; c += NTH) {
-      mout[c] = sm.m0[c];
-      if (ldout != nullptr) ldout[c] = sm.ldec[c];
+    if (tid < D) {
+      mout[tid] = sm.m0[tid];
+      if (ldout != nullptr) ldout[tid] = sm.ldec[tid];
     }
   }
 }
