@@ -247,6 +247,9 @@ def main(argv=None):
                     help="skip the prefill leg (profiling the decode kernel alone)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (3 times), the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
@@ -258,6 +261,14 @@ def main(argv=None):
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.no_prefill:
         dres = time_decode(args.decode_steps, 3)
         print(f"# decode: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s", file=sys.stderr, flush=True)

@@ -22,17 +22,22 @@
 // The intra-chunk decay is factored with the chunk start as reference, so e^{-B} stays
 // finite while B > -80 inside a chunk (the documented precondition).
 //
-// Kernel layout.  One workgroup of D/32 waves per (chain, segment).  Wave w owns the
-// 32-channel slice [32w, 32w+32) of d:
-//  - both fp32 carries live in its MFMA accumulators: tile (a, jm) of C holds
-//    C[16a+4g+r][32w+16jm+l] and tile (a, jm) of S holds S^T[16a+4g+r][32w+16jm+l]
-//    (l = lane % 16, g = lane / 16, r = element).  Read as an A operand, a pair of such
-//    tiles is S (resp. C, which is symmetric) restricted to the wave's rows, so the carry
-//    feeds the read-side MFMAs straight from registers and never leaves them inside a chain;
-//  - it loads its channels of the next chunk's q, k, v and log decay from HBM into MFMA
-//    fragments while the current chunk is computed, and stages them without scalar LDS
-//    traffic: transposes are MFMAs against an identity fragment (exact: x * 1 + 0), and the
-//    cumulative decay over tokens is an MFMA against a lower-triangular ones fragment.
+// Kernel layout.  One workgroup of D/16 waves per (chain, segment) -- 8 waves at d = 128,
+// two per SIMD, so one wave's vector and LDS work overlaps the other's matrix work.
+// Wave w owns the 16 channels [16w, 16w + 16) of d:
+//  - both fp32 carries live in its MFMA accumulators: tile a of C holds C[16a+4g+r][16w+l]
+//    and tile a of S holds S^T[16a+4g+r][16w+l] (l = lane % 16, g = lane / 16, r =
+//    element).  Read as an A operand, a pair of such tiles is S (resp. C, which is
+//    symmetric) restricted to the wave's rows, so the carry feeds the read-side MFMAs
+//    straight from registers and never leaves them inside a chain;
+//  - every chunk tile sits in LDS row-major ([token][channel]); operands whose contraction
+//    runs over tokens (K^T, V^T, (K e^-B)^T) are read with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16), so staging is plain 16-byte row writes;
+//  - the wave pair sharing a 32-channel block loads that block's rows of the next chunk
+//    (q and k for the first wave, v and log decay for the second) into registers while the
+//    current chunk is computed; the cumulative decay over tokens is an MFMA against a
+//    lower-triangular ones fragment, channel selection an MFMA against an identity fragment
+//    (exact: x * 1 + 0).
 #include "ccq_device.hpp"
 #include "ccq_internal.hpp"
 
@@ -47,37 +52,30 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int D, typename T>
 struct Cfg {
-  static constexpr int NW = D / 32;        // waves per workgroup
-  static constexpr int NTH = 64 * NW;      // threads per workgroup (= 2D)
-  static constexpr int NA = D / 16;        // 16-wide tiles along d
-  static constexpr int NK = D / 32;        // K-steps of 32 along d
-  static constexpr int VE = 16 / sizeof(T);  // elements per 16-byte vector
-  static constexpr int NV = (kL * D) / (NTH * VE);  // 16-byte vectors per thread per tile
-  static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int PQ = D + PAD;   // pitch of [64][D] tiles
-  static constexpr int PT = kL + PAD;  // pitch of [D][64] and [64][64] tiles
+  static constexpr int NW = D / 16;          // waves per workgroup (16 channels each)
+  static constexpr int NA = D / 16;          // 16-wide tiles along d
+  static constexpr int NK = D / 32;          // K-steps of 32 along d
+  static constexpr int PQ = D + 16 / sizeof(T);    // pitch of [64][D] row tiles
+  static constexpr int PT = kL + 16 / sizeof(T);   // pitch of the [64][64] token tile
+  static constexpr int LO = (sizeof(T) == 2) ? kL : 1;  // rows of the bf16 lo tiles
 };
 
 template <int D, typename T>
 struct Smem {
   using C_ = Cfg<D, T>;
-  static constexpr int LO = (sizeof(T) == 2) ? kL : 1;  // rows of the bf16 lo tiles
-  T Qs[kL][C_::PQ];   // q rows
-  T Qa[kL][C_::PQ];   // q_clean * e^B (hi part for bf16)
-  T Qalo[LO][C_::PQ]; // bf16 only: lo part of q_clean * e^B
-  T Ks[kL][C_::PQ];   // k rows; later k * e^-B (hi part), in place
-  T Klo[LO][C_::PQ];  // bf16 only: lo part of k * e^-B
-  T Kt[D][C_::PT];    // k^T
-  T Kpt[D][C_::PT];   // (k * e^-B)^T
-  T Vt[D][C_::PT];    // v^T
-  T Pm[kL][C_::PT];   // tril(Q K^T - c 1^T), then the masked intra-chunk attention matrix
-  T Wt[16][C_::PQ];   // rows: w_lambda hi, lo; key sum hi, lo; zeros (B operand of q . [w, m0])
+  T Qs[kL][C_::PQ];    // q rows
+  T Ks[kL][C_::PQ];    // k rows
+  T Vs[kL][C_::PQ];    // v rows
+  T Gs[kL][C_::PQ];    // log decay rows
+  T Kp[kL][C_::PQ];    // k * e^-B rows (hi part for bf16)
+  T Klo[C_::LO][C_::PQ];   // bf16 only: lo part of k * e^-B
+  T Qa[kL][C_::PQ];    // q_clean * e^B rows (hi part for bf16)
+  T Qalo[C_::LO][C_::PQ];  // bf16 only: lo part of q_clean * e^B
+  T Pm[kL][C_::PT];    // tril(Q K^T - c 1^T), then the masked intra-chunk attention matrix
+  T Wt[4][C_::PQ];     // w_lambda hi, lo; key sum hi, lo (B operand of q . [w, m0])
   float m0[D], m1[D], eBL[D], ldec[D];
-  f32x4 tok[kL];      // per token: lambda, 1/n, sq/n^2, gate logit + b
+  f32x4 tok[kL];       // per token: lambda, 1/n, sq/n^2, gate logit + b
 };
-
-// Lower-triangular 16x16 tiles of a 64x64 token-token matrix, (row tile, col tile).
-__constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 template <typename T>
 __device__ __forceinline__ void st4(T* p, const f32x4& v) {
@@ -97,21 +95,6 @@ __device__ __forceinline__ f32x4 ld4(const T* p) {
     return *reinterpret_cast<const f32x4*>(p);
   }
 }
-
-// 16-byte vector of T as floats (VE = 8 for bf16, 4 for fp32).
-template <typename T>
-__device__ __forceinline__ void unpack(const u32x4& v, float* out) {
-  if constexpr (sizeof(T) == 2) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = (float)b[e];
-  } else {
-    const f32x4 f = __builtin_bit_cast(f32x4, v);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = f[e];
-  }
-}
-
 
 // 8 elements of one row from global memory (16 bytes for bf16, 32 for fp32), or zeros.
 template <typename T>
@@ -139,6 +122,29 @@ __device__ __forceinline__ void st_frag(T* p, const Frag<T>& f) {
   }
 }
 
+// Fragment whose K index runs down the rows of a row-major LDS tile X[row][col]: lane
+// (g, i = lane % 16) receives X[k0 + 8g + e][n0 + i] for e = 0..7 (KORD_CONTIG).  As a B
+// operand that is X[k][n]; as an A operand it is X^T.  For bf16 it is two gfx950
+// transposing reads: within each 16-lane group, lane s points at row k0+8g+s/4, column
+// n0+4(s%4), and lane i receives element i%4 of lanes i/4, i/4+4, i/4+8, i/4+12.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+template <typename T>
+__device__ __forceinline__ Frag<T> tr_frag(const T* X, int pitch, int k0, int n0, int lane) {
+  Frag<T> f;
+  const int g = lane >> 4, i = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    const T* p = X + (k0 + 8 * g + (i >> 2)) * pitch + n0 + 4 * (i & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * pitch));
+    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const T* p = X + (k0 + 8 * g) * pitch + n0 + i;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = p[e * pitch];
+  }
+  return f;
+}
+
 template <typename T>
 __device__ __forceinline__ T cvt(float x) { return (T)x; }
 
@@ -155,8 +161,8 @@ __device__ __forceinline__ Frag<T> ident_frag(int h, int lane) {
   return f;
 }
 
-// Lower-triangular ones L[t][t'] = (t' <= t) as the A operand, in KORD_ACC order over
-// t' = 32 kk + 16 (e / 4) + 4 g + e % 4, with t = 16 ti + (lane % 16).
+// Lower-triangular ones L[t][t'] = (t' <= t), t = 16 ti + (lane % 16), over
+// t' = 32 kk + 16 (e / 4) + 4 g + e % 4 (KORD_ACC).
 template <typename T>
 __device__ __forceinline__ Frag<T> ltri_frag(int ti, int kk, int lane) {
   Frag<T> f;
@@ -173,27 +179,13 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& v) {
   return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
 }
 
-// Ones where token j <= token i, as the B fragment of the inclusive prefix over tokens:
-// B[k = j][n = i] with i = 16 ti + (lane % 16), j = 32 kk + 8 g + e (KORD_CONTIG).
-template <typename T>
-__device__ __forceinline__ Frag<T> causal_ones(int ti, int kk, int lane) {
-  Frag<T> f;
-  const int i = 16 * ti + (lane & 15);
-  const int j0 = 32 * kk + 8 * (lane >> 4);
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f.v[e] = (__bf16)((j0 + e <= i) ? 1.0f : 0.0f);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) f.v[e] = (j0 + e <= i) ? 1.0f : 0.0f;
-  }
-  return f;
-}
+// Lower-triangular 16x16 tiles of a 64x64 token-token matrix, (row tile, col tile).
+__constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
 
 // MODE 0: full read (o for every token) from the segment's carry-in, carry out at the end.
 // MODE 1: segment summary from a zero carry (C, S, ksum and total log decay), no outputs.
 template <int D, typename T, int MODE>
-__global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
+__global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, NK = C_::NK;
   constexpr int PQ = C_::PQ, PT = C_::PT;
@@ -202,7 +194,9 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
   __shared__ Smem<D, T> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int cw = 32 * w;  // first channel of this wave's slice
+  const int cw = 16 * w;       // this wave's 16 channels
+  const int hb = w & 1;        // which half of its 32-channel block
+  const int cb = cw - 16 * hb; // first channel of the block
   const int P = a.segments, cps = a.chunks_per_segment;
   const int per_chain = MAIN ? P : P - 1;
   const int chain = blockIdx.x / per_chain, seg = blockIdx.x % per_chain;
@@ -219,7 +213,7 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
   const size_t slot_f = 2 * (size_t)D * D + 2 * D;
 
   // ---- carry in
-  f32x4 Cacc[NA][2], Sacc[NA][2];
+  f32x4 Cacc[NA], Sacc[NA];
   const float* Sin = nullptr;
   const float* Cin = nullptr;
   const float* min_ = nullptr;
@@ -235,14 +229,13 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
       min_ = a.ksum0 + (size_t)chain * D;
     }
   }
+  {
+    const int row = cw + l16;
 #pragma unroll
-  for (int t = 0; t < NA; ++t) {
-#pragma unroll
-    for (int jm = 0; jm < 2; ++jm) {
-      const int row = cw + 16 * jm + l16;
+    for (int t = 0; t < NA; ++t) {
       const int col = 16 * t + 4 * g;
-      Sacc[t][jm] = Sin ? *reinterpret_cast<const f32x4*>(Sin + (size_t)row * D + col) : zero4();
-      Cacc[t][jm] = Cin ? *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col) : zero4();
+      Sacc[t] = Sin ? *reinterpret_cast<const f32x4*>(Sin + (size_t)row * D + col) : zero4();
+      Cacc[t] = Cin ? *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col) : zero4();
     }
   }
   int64_t nb = (int64_t)cbeg * kL;  // tokens before this chunk (count base)
@@ -264,17 +257,18 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
       sm.Wt[1][c] = (T)(wv - (float)whi);
       sm.Wt[2][c] = mhi;
       sm.Wt[3][c] = (T)(m - (float)mhi);
-#pragma unroll
-      for (int r = 4; r < 16; ++r) sm.Wt[r][c] = (T)0.f;
     }
   }
   if constexpr (MAIN) {
-    for (int e = tid; e < kL * PT; e += 2 * D) (&sm.Pm[0][0])[e] = (T)0.f;
+    for (int e = tid; e < kL * PT; e += 64 * NW) (&sm.Pm[0][0])[e] = (T)0.f;
   }
 
-  // ---- register prefetch: this wave's 32 channels of one chunk, as MFMA row fragments
-  // (lane: token 16 ti + l16, channels cw + 8g .. cw + 8g + 7); rows past the end are zero.
-  Frag<T> fq[4], fk[4], fv[4], fg[4];
+  // ---- register prefetch of the block's rows of one chunk, as MFMA row fragments (lane:
+  // token 16 ti + l16, channels cb + 8g .. cb + 8g + 7): q and k for the first wave of the
+  // pair, v and log decay for the second; rows past the end of the sequence are zero.
+  Frag<T> fa[4], fb[4];
+  const T* srcA = hb ? vg : qg;
+  const T* srcB = hb ? gg : kg;
   auto prefetch = [&](int ch) {
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
@@ -282,89 +276,100 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
     for (int ti = 0; ti < 4; ++ti) {
       const int t = 16 * ti + l16;
       const bool ok = t < Lc;
-      const size_t off = ok ? (tok0 + t0 + t) * D + cw + 8 * g : 0;
-      if constexpr (MAIN) fq[ti] = gload_frag<T>(qg + off, ok);
-      fk[ti] = gload_frag<T>(kg + off, ok);
-      fv[ti] = gload_frag<T>(vg + off, ok);
-      fg[ti] = gload_frag<T>(gg + off, ok);
+      const size_t off = ok ? (tok0 + t0 + t) * D + cb + 8 * g : 0;
+      if (MAIN || hb == 1) fa[ti] = gload_frag<T>(srcA + off, ok);
+      fb[ti] = gload_frag<T>(srcB + off, ok);
     }
   };
   if (cbeg < cend) prefetch(cbeg);
 
-  const Frag<T> I0 = ident_frag<T>(0, lane), I1 = ident_frag<T>(1, lane);
+  const Frag<T> Ih = ident_frag<T>(hb, lane);
 
   for (int ch = cbeg; ch < cend; ++ch) {
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
 
-    // ---- stage this wave's channels: rows, transposes, cumulative decay, k e^-B transposed
-    {
+    // ---- stage rows: q and k by the first wave of each pair, v and log decay by the second
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) {
-        const int t = 16 * ti + l16;
-        if constexpr (MAIN) st_frag<T>(&sm.Qs[t][cw + 8 * g], fq[ti]);
-        st_frag<T>(&sm.Ks[t][cw + 8 * g], fk[ti]);
-        f32x4 V0 = zero4(), V1 = zero4();
-        mma(V0, fv[ti], I0);
-        mma(V1, fv[ti], I1);
-        st4<T>(&sm.Vt[cw + l16][16 * ti + 4 * g], V0);
-        st4<T>(&sm.Vt[cw + 16 + l16][16 * ti + 4 * g], V1);
+    for (int ti = 0; ti < 4; ++ti) {
+      const int t = 16 * ti + l16;
+      if (hb == 0) {
+        if constexpr (MAIN) st_frag<T>(&sm.Qs[t][cb + 8 * g], fa[ti]);
+        st_frag<T>(&sm.Ks[t][cb + 8 * g], fb[ti]);
+      } else {
+        st_frag<T>(&sm.Vs[t][cb + 8 * g], fa[ti]);
+        st_frag<T>(&sm.Gs[t][cb + 8 * g], fb[ti]);
       }
-      // one 16-channel half at a time keeps the transposes' registers down
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const Frag<T>& Ih = hh ? I1 : I0;
-        const int c = cw + 16 * hh + l16;
-        f32x4 KT[4], GT[4];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          KT[ti] = GT[ti] = zero4();
-          mma(KT[ti], fk[ti], Ih);  // KT[ti][r] = k at token 16 ti + 4 g + r, channel c
-          mma(GT[ti], fg[ti], Ih);
-          st4<T>(&sm.Kt[c][16 * ti + 4 * g], KT[ti]);
-        }
-        const Frag<T> G0 = acc_frag<T>(GT[0], GT[1]);
-        const Frag<T> G1 = acc_frag<T>(GT[2], GT[3]);
-        float ks = 0.f;
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          f32x4 Bc = zero4();
-          mma(Bc, ltri_frag<T>(ti, 0, lane), G0);
-          if (ti >= 2) mma(Bc, ltri_frag<T>(ti, 1, lane), G1);
-          // Bc[r] = cumulative log decay at token 16 ti + 4 g + r, channel c
-          f32x4 kp;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            kp[r] = KT[ti][r] * __expf(-Bc[r]);
-            ks += KT[ti][r];
-          }
-          st4<T>(&sm.Kpt[c][16 * ti + 4 * g], kp);
-          if (ti == 3 && g == 3) {
-            sm.eBL[c] = __expf(Bc[3]);
-            sm.ldec[c] += Bc[3];
-          }
-        }
-        ks += __shfl_xor(ks, 16, 64);
-        ks += __shfl_xor(ks, 32, 64);
-        if (g == 0) sm.m1[c] = sm.m0[c] + ks;
-      }
-      // the summary pass has registers to spare: its next chunk's loads go out now
-      if constexpr (!MAIN) {
-        if (ch + 1 < cend) prefetch(ch + 1);
-      }
+    }
+    if constexpr (!MAIN) {
+      if (ch + 1 < cend) prefetch(ch + 1);
     }
     __syncthreads();
 
+    // ---- own channels: cumulative decay (4 consecutive channels per lane), k e^-B, key sum,
+    // chunk decay.  BT[ti][r] = B at token 16 ti + l16, channel cw + 4g + r.
+    f32x4 BT[4];
+    {
+      f32x4 GT[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        GT[ti] = zero4();  // log alpha at token 16 ti + 4 g + r, channel cw + l16
+        mma(GT[ti], lds_frag<T, KORD_CONTIG>(&sm.Gs[0][0], PQ, 16 * ti, cb, lane), Ih);
+      }
+      const Frag<T> Ga = acc_frag<T>(GT[0], GT[1]);
+      const Frag<T> Gb = acc_frag<T>(GT[2], GT[3]);
+      f32x4 ks = zero4();
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        BT[ti] = zero4();
+        mma(BT[ti], Ga, ltri_frag<T>(ti, 0, lane));
+        if (ti >= 2) mma(BT[ti], Gb, ltri_frag<T>(ti, 1, lane));
+        f32x4 KC = zero4();  // k at token 16 ti + l16, channel cw + 4g + r
+        mma(KC, Ih, lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * ti, cb, lane));
+        ks += KC;
+        f32x4 kp;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kp[r] = KC[r] * __expf(-BT[ti][r]);
+        const int t = 16 * ti + l16;
+        if constexpr (kSplit) {
+          const bf16x4 kh = to_bf16x4(kp);
+          *reinterpret_cast<bf16x4*>(&sm.Kp[t][cw + 4 * g]) = kh;
+          f32x4 kl;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) kl[r] = kp[r] - (float)kh[r];
+          st4<T>(&sm.Klo[t][cw + 4 * g], kl);
+        } else {
+          st4<T>(&sm.Kp[t][cw + 4 * g], kp);
+        }
+      }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ks[r] += __shfl_xor(ks[r], off, 64);
+      }
+      const int c = cw + 4 * g;
+      if (l16 == 0) *reinterpret_cast<f32x4*>(&sm.m1[c]) = *reinterpret_cast<const f32x4*>(&sm.m0[c]) + ks;
+      if (l16 == 15) {  // token 63
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          sm.eBL[c + r] = __expf(BT[3][r]);
+          sm.ldec[c + r] += BT[3][r];
+        }
+      }
+    }
+    if constexpr (!MAIN) __syncthreads();
+
     if constexpr (MAIN) {
-      // ---- one 16-token row tile per wave: gate logit and m0 . q, then the row tile of
-      // P = Q K^T, its inclusive row sums, and Pm = tril(P - c 1^T) with c_i = sq_i / n_i
+      // ---- one 16-token row tile per wave (waves 0..3): gate logit and m0 . q, then the row
+      // tile of P = Q K^T, its inclusive row sums, and Pm = tril(P - c 1^T), c_i = sq_i / n_i
       for (int it = w; it < 4; it += NW) {
         {
-          f32x4 acc = zero4();  // [q] x [w_hi, w_lo, m0_hi, m0_lo]
+          f32x4 acc = zero4();  // [q] x [w_hi, w_lo, m0_hi, m0_lo]; B rows 4..15 are zero
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk) {
             const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * it, 32 * kk, lane);
-            const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Wt[0][0], PQ, 0, 32 * kk, lane);
+            Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Wt[0][0], PQ, (l16 < 4 ? 0 : -l16), 32 * kk, lane);
+            if (l16 >= 4) B = Frag<T>{};
             mma(acc, A, B);
           }
 #pragma unroll
@@ -391,8 +396,7 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
           // Pt[tj][r] = P[i][16 tj + 4 g + r]
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const bool keep = 16 * tj + 4 * g + r <= i;
-            Pt[tj][r] = keep ? Pt[tj][r] : 0.f;
+            Pt[tj][r] = (16 * tj + 4 * g + r <= i) ? Pt[tj][r] : 0.f;
             rs += Pt[tj][r];
           }
         }
@@ -414,92 +418,55 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
       }
       __syncthreads();
 
-      // ---- cleaned query for the wave's 32 channels, and k * e^-B
+      // ---- cleaned query for the wave's 16 channels: R = Q C0 + tril(P - c 1^T) K
       {
-        f32x4 R[2][4];
+        f32x4 R[4];
 #pragma unroll
-        for (int jm = 0; jm < 2; ++jm)
-#pragma unroll
-          for (int ti = 0; ti < 4; ++ti) R[jm][ti] = zero4();
-        // Q C0 (A operand straight from the carry accumulators)
+        for (int ti = 0; ti < 4; ++ti) R[ti] = zero4();
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          const Frag<T> A0 = acc_frag<T>(Cacc[2 * kk][0], Cacc[2 * kk + 1][0]);
-          const Frag<T> A1 = acc_frag<T>(Cacc[2 * kk][1], Cacc[2 * kk + 1][1]);
+          const Frag<T> A = acc_frag<T>(Cacc[2 * kk], Cacc[2 * kk + 1]);
 #pragma unroll
           for (int ti = 0; ti < 4; ++ti) {
             const Frag<T> B = lds_frag<T, KORD_ACC>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
-            mma(R[0][ti], A0, B);
-            mma(R[1][ti], A1, B);
+            mma(R[ti], A, B);
           }
         }
-        // + tril(P - c 1^T) K
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const Frag<T> A0 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw, 32 * kk, lane);
-          const Frag<T> A1 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw + 16, 32 * kk, lane);
+          const Frag<T> A = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, cw, lane);  // K^T, own rows
 #pragma unroll
           for (int ti = 0; ti < 4; ++ti) {
             if (kk == 1 && ti < 2) continue;  // tokens 32..63 never precede tokens 0..31
-            const Frag<T> Bp = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
-            mma(R[0][ti], A0, Bp);
-            mma(R[1][ti], A1, Bp);
+            const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
+            mma(R[ti], A, B);
           }
         }
-        // R[jm][ti][r]: channel cw + 16 jm + 4 g + r, token 16 ti + l16.  The cumulative decay
-        // in the same layout, from the chunk's log-decay rows still in registers:
-        // Bc^T = (G^T)(L^T) with G^T read off the transposes of the rows.
+        // R[ti][r]: channel cw + 4 g + r, token 16 ti + l16
+        const int m = cw + 4 * g;
+        const f32x4 m04 = *reinterpret_cast<const f32x4*>(&sm.m0[m]);
 #pragma unroll
-        for (int jm = 0; jm < 2; ++jm) {
-          const Frag<T>& Ih = jm ? I1 : I0;
-          f32x4 GT[4];
+        for (int ti = 0; ti < 4; ++ti) {
+          const int i = 16 * ti + l16;
+          const f32x4 ts = sm.tok[i];  // lambda, 1/n, sq/n^2
+          const f32x4 q4 = ld4<T>(&sm.Qs[i][m]);
+          f32x4 qa;
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) {
-            GT[ti] = zero4();
-            mma(GT[ti], fg[ti], Ih);
+          for (int r = 0; r < 4; ++r) {
+            const float u = R[ti][r] * ts[1] - m04[r] * ts[2];
+            qa[r] = (q4[r] - ts[0] * u) * __expf(BT[ti][r]);
           }
-          const Frag<T> Ga = acc_frag<T>(GT[0], GT[1]);
-          const Frag<T> Gb = acc_frag<T>(GT[2], GT[3]);
-          const int m = cw + 16 * jm + 4 * g;
-          const f32x4 m04 = *reinterpret_cast<const f32x4*>(&sm.m0[m]);
+          // bf16: hi + lo (the intra-chunk attention is a sum of few, possibly cancelling
+          // products when little of the sequence has been read)
+          if constexpr (kSplit) {
+            const bf16x4 qh = to_bf16x4(qa);
+            *reinterpret_cast<bf16x4*>(&sm.Qa[i][m]) = qh;
+            f32x4 ql;
 #pragma unroll
-          for (int ti = 0; ti < 4; ++ti) {
-            f32x4 BT = zero4();
-            mma(BT, Ga, ltri_frag<T>(ti, 0, lane));
-            if (ti >= 2) mma(BT, Gb, ltri_frag<T>(ti, 1, lane));
-            const int i = 16 * ti + l16;
-            const f32x4 ts = sm.tok[i];  // lambda, 1/n, sq/n^2
-            const f32x4 q4 = ld4<T>(&sm.Qs[i][m]);
-            f32x4 qa;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float u = R[jm][ti][r] * ts[1] - m04[r] * ts[2];
-              qa[r] = (q4[r] - ts[0] * u) * __expf(BT[r]);
-            }
-            // k * e^-B at the same (token, channel) positions: identity A against the k rows
-            f32x4 KC = zero4();
-            mma(KC, Ih, fk[ti]);
-            f32x4 kp;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) kp[r] = KC[r] * __expf(-BT[r]);
-            // bf16: hi + lo (the intra-chunk attention is a sum of few, possibly cancelling
-            // products when little of the sequence has been read)
-            const bf16x4 qh = to_bf16x4(qa), kh = to_bf16x4(kp);
-            if constexpr (kSplit) {
-              *reinterpret_cast<bf16x4*>(&sm.Qa[i][m]) = qh;
-              *reinterpret_cast<bf16x4*>(&sm.Ks[i][m]) = kh;
-              f32x4 ql, kl;
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                ql[r] = qa[r] - (float)qh[r];
-                kl[r] = kp[r] - (float)kh[r];
-              }
-              st4<T>(&sm.Qalo[i][m], ql);
-              st4<T>(&sm.Klo[i][m], kl);
-            } else {
-              st4<T>(&sm.Qa[i][m], qa);
-              st4<T>(&sm.Ks[i][m], kp);
-            }
+            for (int r = 0; r < 4; ++r) ql[r] = qa[r] - (float)qh[r];
+            st4<T>(&sm.Qalo[i][m], ql);
+          } else {
+            st4<T>(&sm.Qa[i][m], qa);
           }
         }
       }
@@ -514,7 +481,7 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+          const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Kp[0][0], PQ, 16 * tj, 32 * kk, lane);
           const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
           mma(acc, A, B);
           if constexpr (kSplit) {
@@ -531,69 +498,52 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
       }
       __syncthreads();
 
-      // ---- O^T for the wave's 32 value rows: S0 (Qc e^B)^T + V^T A^T
-      f32x4 O[2][4];
+      // ---- O^T for the wave's 16 value rows: S0 (Qc e^B)^T + V^T A^T
+      f32x4 O[4];
 #pragma unroll
-      for (int jm = 0; jm < 2; ++jm)
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) O[jm][ti] = zero4();
+      for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const Frag<T> A0 = acc_frag<T>(Sacc[2 * kk][0], Sacc[2 * kk + 1][0]);
-        const Frag<T> A1 = acc_frag<T>(Sacc[2 * kk][1], Sacc[2 * kk + 1][1]);
+        const Frag<T> A = acc_frag<T>(Sacc[2 * kk], Sacc[2 * kk + 1]);
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           const Frag<T> B = lds_frag<T, KORD_ACC>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
-          mma(O[0][ti], A0, B);
-          mma(O[1][ti], A1, B);
+          mma(O[ti], A, B);
         }
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const Frag<T> A0 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw, 32 * kk, lane);
-        const Frag<T> A1 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw + 16, 32 * kk, lane);
+        const Frag<T> A = tr_frag<T>(&sm.Vs[0][0], PQ, 32 * kk, cw, lane);  // V^T, own rows
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           if (kk == 1 && ti < 2) continue;
           const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
-          mma(O[0][ti], A0, B);
-          mma(O[1][ti], A1, B);
+          mma(O[ti], A, B);
         }
       }
       T* og = static_cast<T*>(a.o);
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
         const int i = 16 * ti + l16;
-        if (i < Lc) {
-#pragma unroll
-          for (int jm = 0; jm < 2; ++jm) st4<T>(og + (tok0 + t0 + i) * D + cw + 16 * jm + 4 * g, O[jm][ti]);
-        }
+        if (i < Lc) st4<T>(og + (tok0 + t0 + i) * D + cw + 4 * g, O[ti]);
       }
     }
 
     // ---- carry update: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const Frag<T> Bk0 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw, 32 * kk, lane);
-      const Frag<T> Bk1 = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, cw + 16, 32 * kk, lane);
-      const Frag<T> Bv0 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw, 32 * kk, lane);
-      const Frag<T> Bv1 = lds_frag<T, KORD_CONTIG>(&sm.Vt[0][0], PT, cw + 16, 32 * kk, lane);
+      const Frag<T> Bk = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
+      const Frag<T> Bv = tr_frag<T>(&sm.Vs[0][0], PQ, 32 * kk, cw, lane);  // V[t][own channel]
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
-        const Frag<T> Ak = lds_frag<T, KORD_CONTIG>(&sm.Kt[0][0], PT, 16 * t, 32 * kk, lane);
-        const Frag<T> Ap = lds_frag<T, KORD_CONTIG>(&sm.Kpt[0][0], PT, 16 * t, 32 * kk, lane);
-        mma(Cacc[t][0], Ak, Bk0);
-        mma(Cacc[t][1], Ak, Bk1);
-        mma(Sacc[t][0], Ap, Bv0);
-        mma(Sacc[t][1], Ap, Bv1);
+        const Frag<T> Ak = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, 16 * t, lane);  // K^T rows 16t..
+        const Frag<T> Ap = tr_frag<T>(&sm.Kp[0][0], PQ, 32 * kk, 16 * t, lane);  // (K e^-B)^T
+        mma(Cacc[t], Ak, Bk);
+        mma(Sacc[t], Ap, Bv);
       }
     }
 #pragma unroll
-    for (int t = 0; t < NA; ++t) {
-      const f32x4 e4 = *reinterpret_cast<const f32x4*>(&sm.eBL[16 * t + 4 * g]);
-      Sacc[t][0] *= e4;
-      Sacc[t][1] *= e4;
-    }
+    for (int t = 0; t < NA; ++t) Sacc[t] *= *reinterpret_cast<const f32x4*>(&sm.eBL[16 * t + 4 * g]);
     if (tid < D) {
       const float m = sm.m1[tid];
       sm.m0[tid] = m;
@@ -627,15 +577,12 @@ __global__ __launch_bounds__(2 * D) void gla_prefill_kernel(FwdArgs a) {
     ldout = mout + D;
   }
   if (Sout != nullptr) {
+    const int row = cw + l16;
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
-#pragma unroll
-      for (int jm = 0; jm < 2; ++jm) {
-        const int row = cw + 16 * jm + l16;
-        const int col = 16 * t + 4 * g;
-        *reinterpret_cast<f32x4*>(Sout + (size_t)row * D + col) = Sacc[t][jm];
-        *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t][jm];
-      }
+      const int col = 16 * t + 4 * g;
+      *reinterpret_cast<f32x4*>(Sout + (size_t)row * D + col) = Sacc[t];
+      *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t];
     }
     if (tid < D) {
       mout[tid] = sm.m0[tid];
@@ -689,12 +636,13 @@ template <int D, typename T>
 static hipError_t launch_gla(const FwdArgs& a, hipStream_t s) {
   const int chains = a.B * a.H;
   const int P = a.segments;
+  const dim3 block(4 * D);
   if (P > 1) {
-    hipLaunchKernelGGL((gla_prefill_kernel<D, T, 1>), dim3((unsigned)(chains * (P - 1))), dim3(2 * D), 0, s, a);
+    hipLaunchKernelGGL((gla_prefill_kernel<D, T, 1>), dim3((unsigned)(chains * (P - 1))), block, 0, s, a);
     const int nf4 = (2 * D * D + D) / 4;
     hipLaunchKernelGGL((gla_scan_kernel<D>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
   }
-  hipLaunchKernelGGL((gla_prefill_kernel<D, T, 0>), dim3((unsigned)(chains * P)), dim3(2 * D), 0, s, a);
+  hipLaunchKernelGGL((gla_prefill_kernel<D, T, 0>), dim3((unsigned)(chains * P)), block, 0, s, a);
   return hipGetLastError();
 }
 
