@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     v_s[tid] = ldf(vg, tid);
     if constexpr (RULE == 0) al_s[tid] = __expf(ldf(static_cast<const T*>(a.log_alpha), (size_t)head * D + tid));
   }
-  __syncthreads();
+  lds_barrier();
 
   // Wave 0: updated key sum, the gate, and ksum_new . q.
   if (tid < 64) {
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       *reinterpret_cast<f32x4*>(Sg + (size_t)row * D + 4 * col4) = sr[i];
     }
   }
-  __syncthreads();  // r_s, kn_s and scal complete
+  lds_barrier();  // r_s, kn_s and scal complete
 
   if (tid < D) {
     const float lam = scal[0], msq = scal[1], nf = scal[2];
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const float u = r_s[tid] * inv_n - kn_s[tid] * (msq * inv_n * inv_n);
     qt_s[tid] = q_s[tid] - lam * u;
   }
-  __syncthreads();
+  lds_barrier();
 
   const f32x4 qt4 = *reinterpret_cast<const f32x4*>(qt_s + 4 * col4);
   T* og = static_cast<T*>(a.o) + (size_t)head * D;

@@ -44,7 +44,14 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// Workgroup barrier that publishes LDS writes only.  __syncthreads() also fences global
+// memory, i.e. waits for every outstanding global load and store of the wave (in-flight
+// prefetches, output stores); the kernels here never exchange data between waves through
+// global memory, so waiting for the LDS counter is enough.  The "memory" clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------- MFMA tiles
 

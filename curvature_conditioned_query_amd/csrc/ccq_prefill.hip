@@ -179,8 +179,14 @@ __device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& v) {
   return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
 }
 
-// Lower-triangular 16x16 tiles of a 64x64 token-token matrix, (row tile, col tile).
-__constant__ int8_t kTri[10][2] = {{0, 0}, {1, 0}, {1, 1}, {2, 0}, {2, 1}, {2, 2}, {3, 0}, {3, 1}, {3, 2}, {3, 3}};
+// Lower-triangular 16x16 tiles of a 64x64 token-token matrix, numbered row by row:
+// idx -> (row tile, col tile) = (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ... (3,3).  Computed
+// rather than read from a table: a memory read here would wait behind the in-flight prefetch.
+__device__ __forceinline__ int tri_row(int idx) { return (idx >= 1) + (idx >= 3) + (idx >= 6); }
+__device__ __forceinline__ int tri_col(int idx) {
+  const int r = tri_row(idx);
+  return idx - r * (r + 1) / 2;
+}
 
 // MODE 0: full read (o for every token) from the segment's carry-in, carry out at the end.
 // MODE 1: segment summary from a zero carry (C, S, ksum and total log decay), no outputs.
@@ -238,6 +244,8 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
       Cacc[t] = Cin ? *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col) : zero4();
     }
   }
+  // the carry-in loads complete here, so nothing in the chunk loop waits on them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int64_t nb = (int64_t)cbeg * kL;  // tokens before this chunk (count base)
   if constexpr (MAIN) {
     if (a.n0 != nullptr) nb += a.n0[chain];
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
     if constexpr (!MAIN) {
       if (ch + 1 < cend) prefetch(ch + 1);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- own channels: cumulative decay (4 consecutive channels per lane), k e^-B, key sum,
     // chunk decay.  BT[ti][r] = B at token 16 ti + l16, channel cw + 4g + r.
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
         }
       }
     }
-    if constexpr (!MAIN) __syncthreads();
+    if constexpr (!MAIN) lds_barrier();
 
     if constexpr (MAIN) {
       // ---- one 16-token row tile per wave (waves 0..3): gate logit and m0 . q, then the row
@@ -416,7 +424,7 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
         }
         if (g == 0) sm.tok[i] = f32x4{sigmoidf(gate), inv_n, cbar * inv_n, gate};
       }
-      __syncthreads();
+      lds_barrier();
 
       // ---- cleaned query for the wave's 16 channels: R = Q C0 + tril(P - c 1^T) K
       {
@@ -470,14 +478,14 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       // the chunk's row fragments are consumed: next chunk's loads go out now, behind the
       // intra-chunk read, the output store and the carry update
       if (ch + 1 < cend) prefetch(ch + 1);
 
       // ---- intra-chunk attention (Qc e^B)(K e^-B)^T on the lower tiles -> Pm (masked)
       for (int idx = w; idx < 10; idx += NW) {
-        const int ti = kTri[idx][0], tj = kTri[idx][1];
+        const int ti = tri_row(idx), tj = tri_col(idx);
         f32x4 acc = zero4();
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
@@ -496,7 +504,7 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
         for (int r = 0; r < 4; ++r) acc[r] = (16 * tj + 4 * g + r <= i) ? acc[r] : 0.f;
         st4<T>(&sm.Pm[i][16 * tj + 4 * g], acc);
       }
-      __syncthreads();
+      lds_barrier();
 
       // ---- O^T for the wave's 16 value rows: S0 (Qc e^B)^T + V^T A^T
       f32x4 O[4];
@@ -554,7 +562,7 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
       }
     }
     nb += Lc;
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- carry out
