@@ -55,6 +55,17 @@ def prefill_work(B, H, T, d, elem_bytes, rule="gla"):
     return th * flop_th, th * bytes_th + B * H * carry
 
 
+def main_kernel_bytes(B, H, T, d, elem_bytes, segments):
+    """Algorithmic HBM bytes of one launch of the main prefill kernel: q, k, v, log decay read
+    and o written once, the carry-in of every segment after the first read from the workspace
+    (S, C, ksum in fp32), and the final carry (S, C, ksum, n) written."""
+    chains = B * H
+    tokens = 5 * B * H * T * d * elem_bytes
+    slot_in = (2 * d * d + d) * 4
+    carry_out = 2 * d * d * 4 + d * 4 + 8
+    return tokens + chains * (max(segments, 1) - 1) * slot_in + chains * carry_out
+
+
 def decode_bytes_per_head(d, elem_bytes):
     """S and C (fp32 d x d) read and written, ksum read and written, n read and written,
     one token (q, k, v, log alpha) read, o written."""
@@ -109,8 +120,12 @@ def time_prefill(wl, steps, warmup):
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     del x
 
-    def step():
-        ccq_fwd_chunked(spec["rule"], q, k, v, g, beta, w, b, o=o, carry_out=cout, workspace=ws)
+    hip = HipEvents(4 * steps)
+
+    def step(i=None):
+        pe = None if i is None else hip.slice(4 * i, 4)
+        ccq_fwd_chunked(spec["rule"], q, k, v, g, beta, w, b, o=o, carry_out=cout, workspace=ws,
+                        phase_events=pe)
 
     for _ in range(warmup):
         step()
@@ -121,15 +136,54 @@ def time_prefill(wl, steps, warmup):
     t_wall = time.perf_counter()
     ev[0].record(stream)
     for i in range(steps):
-        step()
+        step(i)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
     total_ms = ev[0].elapsed_time(ev[steps])
-    segs = int(p.segments) if p.segments else None
+    # per-kernel launch durations from the events the library records on its stream
+    phases = {name: float(np.mean([hip.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(steps)]))
+              for a, name in enumerate(("summary", "scan", "main"))}
+    hip.destroy()
+    # segments the library resolved: its workspace holds one (2 d^2 + 2 d) fp32 slot per
+    # (chain, segment) when there is more than one segment
+    segs = int(p.segments) if p.segments else (ws_bytes // (B * H * (2 * dk * dk + 2 * dk) * 4) or 1)
     return dict(spec=spec, shape=(B, H, T, dk, dv), total_ms=total_ms, per_ms=per, wall_s=t_wall,
-                dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs)
+                dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs, phase_ms=phases)
+
+
+class HipEvents:
+    """Plain hipEvent_t handles from the HIP runtime torch has loaded (same soname, so the
+    same runtime instance the kernels are launched through)."""
+
+    def __init__(self, n):
+        import ctypes
+        self._ct = ctypes
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev[i] = h
+
+    def slice(self, i, n):
+        ct = self._ct
+        return ct.cast(ct.byref(self.ev, i * ct.sizeof(ct.c_void_p)), ct.POINTER(ct.c_void_p))
+
+    def elapsed_ms(self, i, j):
+        ms = self._ct.c_float()
+        if self.rt.hipEventElapsedTime(self._ct.byref(ms), self.ev[i], self.ev[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self):
+        for h in self.ev:
+            self.rt.hipEventDestroy(h)
 
 
 def time_decode(steps, warmup, seqs_per_batch=32):
@@ -240,7 +294,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3])
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 3])
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
@@ -248,8 +302,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
-                    help="also run a plain device copy of MIB MiB (3 times), the reference for scaling "
-                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
+                    help="also run a plain streaming kernel over MIB MiB (torch.neg, 3 times), the reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
@@ -266,7 +320,7 @@ def main(argv=None):
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)  # streams n*4 bytes in and n*4 bytes out
         torch.cuda.synchronize()
         del src, dst
     if args.no_prefill:
@@ -287,17 +341,27 @@ def main(argv=None):
     ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     bound = "hbm" if intensity < ridge else "mfma"
     src_sha = file_sha(PREFILL_SRC)
+    # Roofline of the dominant kernel, the main prefill kernel (one launch per pass): its
+    # algorithmic bytes and the method's flops over its own average launch duration.
+    main_ms = res["phase_ms"]["main"]
+    main_bytes = main_kernel_bytes(B, H, T, dk, elem, res["segments"] or 1)
+    k_gbs = main_bytes / (main_ms * 1e-3) / 1e9
+    k_tflops = flops / (main_ms * 1e-3) / 1e12
     traffic = measured_traffic(f"traffic_{spec['name']}.json", src_sha)
     if bound == "hbm":
-        roof = dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic)
+        roof = dict(bound="hbm", achieved=round(k_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(k_gbs / HBM_PEAK_GBS, 4), traffic=traffic)
     else:
-        roof = dict(bound="mfma", achieved=round(tflops, 1), peak=mfma_peak, unit="TFLOP/s",
-                    frac=round(tflops / mfma_peak, 4), traffic=traffic)
-    roof.update(kernel="ccq_fwd_chunked pass: gla summary + scan + main prefill kernels",
-                algorithmic_bytes=nbytes, algorithmic_flops=flops, avg_launch_ms=round(ms, 4),
-                mfma=dict(achieved=round(tflops, 1), peak=mfma_peak, unit="TFLOP/s",
-                          frac=round(tflops / mfma_peak, 4)))
+        roof = dict(bound="mfma", achieved=round(k_tflops, 1), peak=mfma_peak, unit="TFLOP/s",
+                    frac=round(k_tflops / mfma_peak, 4), traffic=traffic)
+    roof.update(kernel=f"gla_prefill_kernel<{dk},{'bf16' if elem == 2 else 'f32'},main>",
+                avg_launch_ms=round(main_ms, 4), algorithmic_bytes_per_launch=main_bytes,
+                algorithmic_flops_per_launch=flops,
+                mfma=dict(achieved=round(k_tflops, 1), peak=mfma_peak, unit="TFLOP/s",
+                          frac=round(k_tflops / mfma_peak, 4)),
+                pass_ms={k: round(v, 4) for k, v in res["phase_ms"].items()},
+                whole_pass=dict(bytes=nbytes, gbs=round(gbs, 1), tflops=round(tflops, 1),
+                                hbm_frac=round(gbs / HBM_PEAK_GBS, 4)))
     out = {
         "metric": "CCQ-GLA prefill tokens/s (H16,dk128,T4K) + MFMA util; decode HBM GB/s",
         "value": round(tok_s, 1),
@@ -316,7 +380,8 @@ def main(argv=None):
         "roofline": roof,
     }
     print(f"# prefill {spec['name']}: {ms:.3f} ms/step, {tok_s:.4g} tokens/s, {gbs:.1f} GB/s alg, "
-          f"{tflops:.1f} TFLOP/s alg", file=sys.stderr, flush=True)
+          f"{tflops:.1f} TFLOP/s alg; kernels (ms) " +
+          ", ".join(f"{k} {v:.4f}" for k, v in res["phase_ms"].items()), file=sys.stderr, flush=True)
     if not args.no_decode:
         dres = time_decode(args.decode_steps, 3)
         dsrc = file_sha(DECODE_SRC)

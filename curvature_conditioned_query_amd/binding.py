@@ -53,6 +53,7 @@ class FwdParams(ctypes.Structure):
         ("S_out", ctypes.c_void_p), ("C_out", ctypes.c_void_p), ("ksum_out", ctypes.c_void_p),
         ("n_out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("phase_events", ctypes.c_void_p),
     ]
 
 
@@ -177,9 +178,10 @@ def ccq_fwd_workspace_bytes(p: FwdParams) -> int:
 
 def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
                     carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, phase_events=None):
     """Chunked CCQ prefill through the C ABI.  Allocates o (and the workspace if not
-    given) with torch; returns o."""
+    given) with torch; returns o.  ``phase_events``: optional ctypes array of 4 hipEvent_t
+    handles recorded around the kernels of the pass."""
     import torch
     lib = load_library()
     if o is None:
@@ -192,6 +194,8 @@ def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
             p.workspace = workspace.data_ptr()
             p.workspace_bytes = nbytes
+    if phase_events is not None:
+        p.phase_events = ctypes.cast(phase_events, ctypes.c_void_p)
     st = lib.ccq_fwd_chunked(ctypes.byref(p), _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_fwd_chunked")

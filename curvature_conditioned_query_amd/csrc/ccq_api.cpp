@@ -54,9 +54,9 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
   // Rounds the segment length up to whole chunks and drops empty trailing segments.
   const int cps = (nchunks + seg - 1) / seg;
   seg = (nchunks + cps - 1) / cps;
-  if (p->rule == CCQ_RULE_GDN) seg = 1;  // Gated DeltaNet segments are not built yet
+  if (p->rule == CCQ_RULE_GDN) return CCQ_ERR_UNSUPPORTED;  // no Gated DeltaNet prefill kernel yet
   *segments_out = seg;
-  *chunks_per_seg_out = (p->rule == CCQ_RULE_GDN) ? nchunks : cps;
+  *chunks_per_seg_out = cps;
   return CCQ_OK;
 }
 
@@ -69,7 +69,7 @@ size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 1; }
+int32_t ccq_abi_version(void) { return 2; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -121,6 +121,7 @@ int ccq_fwd_chunked(const ccq_fwd_params* p, void* hip_stream) {
   a.ksum_out = p->ksum_out;
   a.n_out = p->n_out;
   a.workspace = p->workspace;
+  a.events = p->phase_events;
   const hipError_t e = ccq::launch_fwd(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }

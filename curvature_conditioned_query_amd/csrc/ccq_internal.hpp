@@ -33,6 +33,7 @@ struct FwdArgs {
   float *S_out, *C_out, *ksum_out;
   int64_t* n_out;
   void* workspace;
+  void* const* events;  // optional: 4 hipEvent_t around the kernels of the pass
 };
 
 // Bytes of one segment slot of the workspace (carry of one chain, plus the GLA decay).

@@ -191,7 +191,7 @@ __device__ __forceinline__ int tri_col(int idx) {
 // MODE 0: full read (o for every token) from the segment's carry-in, carry out at the end.
 // MODE 1: segment summary from a zero carry (C, S, ksum and total log decay), no outputs.
 template <int D, typename T, int MODE>
-__global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
+__device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, NK = C_::NK;
   constexpr int PQ = C_::PQ, PT = C_::PT;
@@ -599,6 +599,16 @@ __global__ __launch_bounds__(4 * D) void gla_prefill_kernel(FwdArgs a) {
   }
 }
 
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
+  gla_prefill_body<D, T, 1>(a);
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
+  gla_prefill_body<D, T, 0>(a);
+}
+
 // Exclusive scan of segment summaries into carry-ins, in place.  Slot p holds the summary
 // of segment p (p < P-1) and receives the carry-in of segment p (p <= P-1):
 //   carry_in[0] = carry0;  carry_in[p+1] = (S_in[p] diag(e^{ldec[p]}) + dS[p], C + dC, m + dm).
@@ -640,18 +650,31 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
   }
 }
 
+// Records the caller's timing event `i` (if any) on the stream.
+static hipError_t record_event(const FwdArgs& a, int i, hipStream_t s) {
+  if (a.events == nullptr) return hipSuccess;
+  return hipEventRecord(static_cast<hipEvent_t>(a.events[i]), s);
+}
+
 template <int D, typename T>
 static hipError_t launch_gla(const FwdArgs& a, hipStream_t s) {
   const int chains = a.B * a.H;
   const int P = a.segments;
   const dim3 block(4 * D);
+  if (record_event(a, 0, s) != hipSuccess) return hipErrorLaunchFailure;
   if (P > 1) {
-    hipLaunchKernelGGL((gla_prefill_kernel<D, T, 1>), dim3((unsigned)(chains * (P - 1))), block, 0, s, a);
+    hipLaunchKernelGGL((gla_summary_kernel<D, T>), dim3((unsigned)(chains * (P - 1))), block, 0, s, a);
+    if (record_event(a, 1, s) != hipSuccess) return hipErrorLaunchFailure;
     const int nf4 = (2 * D * D + D) / 4;
     hipLaunchKernelGGL((gla_scan_kernel<D>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
+  } else if (record_event(a, 1, s) != hipSuccess) {
+    return hipErrorLaunchFailure;
   }
-  hipLaunchKernelGGL((gla_prefill_kernel<D, T, 0>), dim3((unsigned)(chains * P)), block, 0, s, a);
-  return hipGetLastError();
+  if (record_event(a, 2, s) != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL((gla_main_kernel<D, T>), dim3((unsigned)(chains * P)), block, 0, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return record_event(a, 3, s);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {

@@ -93,6 +93,12 @@ typedef struct {
 
   void *workspace;        /* device scratch of at least ccq_fwd_workspace_bytes(p) bytes, or  */
   size_t workspace_bytes; /* NULL / 0 when that function returns 0                            */
+
+  /* Optional per-kernel timing: NULL, or an array of 4 caller-created hipEvent_t that are
+   * recorded on hip_stream before the segment-summary kernel, after it, after the carry scan
+   * and after the main kernel.  With one segment the first three are recorded together,
+   * just before the main kernel.  A failed record returns CCQ_ERR_LAUNCH. */
+  void *const *phase_events;
 } ccq_fwd_params;
 
 /*
@@ -128,7 +134,7 @@ int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int32_t ccq_abi_version(void);
 
 #ifdef __cplusplus
