@@ -52,9 +52,12 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
   }
   if (seg > nchunks) seg = nchunks;
   // Rounds the segment length up to whole chunks and drops empty trailing segments.
-  const int cps = (nchunks + seg - 1) / seg;
+  int cps = (nchunks + seg - 1) / seg;
   seg = (nchunks + cps - 1) / cps;
-  if (p->rule == CCQ_RULE_GDN) return CCQ_ERR_UNSUPPORTED;  // no Gated DeltaNet prefill kernel yet
+  if (p->rule == CCQ_RULE_GDN) {  // Gated DeltaNet: one segment per chain
+    seg = 1;
+    cps = nchunks;
+  }
   *segments_out = seg;
   *chunks_per_seg_out = cps;
   return CCQ_OK;

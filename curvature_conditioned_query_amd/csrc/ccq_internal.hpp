@@ -39,5 +39,7 @@ struct FwdArgs {
 // Bytes of one segment slot of the workspace (carry of one chain, plus the GLA decay).
 size_t fwd_slot_bytes(int d);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+// Gated DeltaNet prefill (one segment per chain).
+hipError_t launch_gdn(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace ccq

@@ -1,0 +1,289 @@
+// Helpers and rule-independent phases shared by the chunked-prefill kernels (gfx950).
+//
+// Tiles of a 64-token chunk sit in LDS row-major ([token][channel]).  The CCQ statistics
+// part of a chunk does not depend on the write rule: it is the gate, the causal Gram
+// matrix P = Q K^T with its row sums, and the cleaned query (gist.science summary of
+// arXiv 2606.01294, §2 "理论推导" and §2 "机制"):
+//   s_i  = m0 + sum_{j<=i} k_j,  n_i = n0 + i + 1,  sq_i = s_i . q_i = m0 . q_i + sum_{j<=i} P_ij
+//   u_i  = (Q C0 + tril_incl(P - c 1^T) K)_i / n_i - m0 sq_i / n_i^2,  c_i = sq_i / n_i
+//        (row i of Q C0 + tril_incl(P) K is C_i q_i, so u_i = Sigma_i q_i)
+//   qc_i = q_i - lambda_i u_i,  lambda_i = sigmoid(w . q_i + b)
+// Any shared-memory struct with the members used below (Qs, Ks, Wt, Pm, tok, m0, Qa, Qalo)
+// can host them.
+#pragma once
+
+#include "ccq_device.hpp"
+
+namespace ccq {
+
+constexpr int kL = 64;  // chunk length
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D, typename T>
+struct Cfg {
+  static constexpr int NW = D / 16;          // waves per workgroup (16 channels each)
+  static constexpr int NA = D / 16;          // 16-wide tiles along d
+  static constexpr int NK = D / 32;          // K-steps of 32 along d
+  static constexpr int PQ = D + 16 / sizeof(T);    // pitch of [64][D] row tiles
+  static constexpr int PT = kL + 16 / sizeof(T);   // pitch of the [64][64] token tile
+  static constexpr int LO = (sizeof(T) == 2) ? kL : 1;  // rows of the bf16 lo tiles
+};
+
+template <typename T>
+__device__ __forceinline__ void st4(T* p, const f32x4& v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  } else {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+}
+
+// 8 elements of one row from global memory (16 bytes for bf16, 32 for fp32), or zeros.
+template <typename T>
+__device__ __forceinline__ Frag<T> gload_frag(const T* p, bool ok) {
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    f.v = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(p) : z);
+  } else {
+    const f32x4 lo = ok ? *reinterpret_cast<const f32x4*>(p) : zero4();
+    const f32x4 hi = ok ? *reinterpret_cast<const f32x4*>(p + 4) : zero4();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[4 + e] = hi[e]; }
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ void st_frag(T* p, const Frag<T>& f) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<bf16x8*>(p) = f.v;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{f.v[4], f.v[5], f.v[6], f.v[7]};
+  }
+}
+
+// Fragment whose K index runs down the rows of a row-major LDS tile X[row][col]: lane
+// (g, i = lane % 16) receives X[k0 + 8g + e][n0 + i] for e = 0..7 (KORD_CONTIG).  As a B
+// operand that is X[k][n]; as an A operand it is X^T.  For bf16 it is two gfx950
+// transposing reads: within each 16-lane group, lane s points at row k0+8g+s/4, column
+// n0+4(s%4), and lane i receives element i%4 of lanes i/4, i/4+4, i/4+8, i/4+12.
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+template <typename T>
+__device__ __forceinline__ Frag<T> tr_frag(const T* X, int pitch, int k0, int n0, int lane) {
+  Frag<T> f;
+  const int g = lane >> 4, i = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    const T* p = X + (k0 + 8 * g + (i >> 2)) * pitch + n0 + 4 * (i & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * pitch));
+    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const T* p = X + (k0 + 8 * g) * pitch + n0 + i;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = p[e * pitch];
+  }
+  return f;
+}
+
+// As tr_frag, in KORD_ACC order: lane (g, i) receives X[k0 + 16 (e / 4) + 4 g + e % 4][n0 + i],
+// the K order of an operand built from a pair of accumulator tiles (acc_frag).
+template <typename T>
+__device__ __forceinline__ Frag<T> tr_frag_acc(const T* X, int pitch, int k0, int n0, int lane) {
+  Frag<T> f;
+  const int g = lane >> 4, i = lane & 15;
+  if constexpr (sizeof(T) == 2) {
+    const T* p = X + (k0 + 4 * g + (i >> 2)) * pitch + n0 + 4 * (i & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * pitch));
+    f.v = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    const T* p = X + (k0 + 4 * g) * pitch + n0 + i;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = p[(16 * (e >> 2) + (e & 3)) * pitch];
+  }
+  return f;
+}
+
+template <typename T>
+__device__ __forceinline__ T cvt(float x) { return (T)x; }
+
+// Identity slice in KORD_CONTIG order: element e of lane (g, l) is 1 where 8g + e == l + 16h.
+// As a B operand against row fragments X[t][k] it yields X[t][16h + n] in the accumulator
+// (4 consecutive tokens per lane); as an A operand against row fragments used as B it
+// yields X[t][16h + 4g + r] (4 consecutive channels per lane).
+template <typename T>
+__device__ __forceinline__ Frag<T> ident_frag(int h, int lane) {
+  Frag<T> f;
+  const int l = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = cvt<T>((8 * g + e == l + 16 * h) ? 1.0f : 0.0f);
+  return f;
+}
+
+// Lower-triangular ones L[t][t'] = (t' <= t), t = 16 ti + (lane % 16), over
+// t' = 32 kk + 16 (e / 4) + 4 g + e % 4 (KORD_ACC).
+template <typename T>
+__device__ __forceinline__ Frag<T> ltri_frag(int ti, int kk, int lane) {
+  Frag<T> f;
+  const int t = 16 * ti + (lane & 15), g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int tp = 32 * kk + 16 * (e >> 2) + 4 * g + (e & 3);
+    f.v[e] = cvt<T>(tp <= t ? 1.0f : 0.0f);
+  }
+  return f;
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(const f32x4& v) {
+  return bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+}
+
+// Lower-triangular 16x16 tiles of a 64x64 token-token matrix, numbered row by row:
+// idx -> (row tile, col tile) = (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ... (3,3).  Computed
+// rather than read from a table: a memory read here would wait behind the in-flight prefetch.
+__device__ __forceinline__ int tri_row(int idx) { return (idx >= 1) + (idx >= 3) + (idx >= 6); }
+__device__ __forceinline__ int tri_col(int idx) {
+  const int r = tri_row(idx);
+  return idx - r * (r + 1) / 2;
+}
+
+// Gate logit and m0 . q, then the row tile of P = Q K^T, its inclusive row sums and
+// Pm = tril(P - c 1^T), for the 16-token row tiles it = w, w + NW, ... < 4 (waves 0..3 at
+// d >= 64).  Writes sm.Pm and sm.tok[i] = {lambda_i, 1/n_i, sq_i / n_i^2, logit_i}; nb is
+// the number of tokens before the chunk.  Needs Qs, Ks, Wt staged; Pm rows must be zero
+// above the diagonal tiles.
+template <int D, typename T, typename SM>
+__device__ __forceinline__ void ccq_gram_rows(SM& sm, int w, int lane, int64_t nb, float b_lam) {
+  using C_ = Cfg<D, T>;
+  constexpr int NW = C_::NW, NK = C_::NK, PQ = C_::PQ;
+  const int g = lane >> 4, l16 = lane & 15;
+  for (int it = w; it < 4; it += NW) {
+    {
+      f32x4 acc = zero4();  // [q] x [w_hi, w_lo, m0_hi, m0_lo]; B rows 4..15 are zero
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * it, 32 * kk, lane);
+        Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Wt[0][0], PQ, (l16 < 4 ? 0 : -l16), 32 * kk, lane);
+        if (l16 >= 4) B = Frag<T>{};
+        mma(acc, A, B);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = acc[r] + __shfl_down(acc[r], 1, 64);  // hi + lo columns
+        const int i = 16 * it + 4 * g + r;
+        if (l16 == 0) sm.tok[i][3] = x + b_lam;
+        if (l16 == 2) sm.tok[i][1] = x;  // m0 . q, parked until the row sums are known
+      }
+    }
+    const int i = 16 * it + l16;  // this lane's token in the P tiles below
+    f32x4 Pt[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      Pt[tj] = zero4();
+      if (tj > it) continue;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+        const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * it, 32 * kk, lane);
+        mma(Pt[tj], A, B);
+      }
+      // Pt[tj][r] = P[i][16 tj + 4 g + r]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Pt[tj][r] = (16 * tj + 4 * g + r <= i) ? Pt[tj][r] : 0.f;
+        rs += Pt[tj][r];
+      }
+    }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+    const float gate = sm.tok[i][3];
+    const float sq = sm.tok[i][1] + rs;
+    const float inv_n = __builtin_amdgcn_rcpf((float)(nb + i + 1));
+    const float cbar = sq * inv_n;
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) {
+      if (tj > it) continue;
+      f32x4 pc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pc[r] = (16 * tj + 4 * g + r <= i) ? Pt[tj][r] - cbar : 0.f;
+      st4<T>(&sm.Pm[i][16 * tj + 4 * g], pc);
+    }
+    if (g == 0) sm.tok[i] = f32x4{sigmoidf(gate), inv_n, cbar * inv_n, gate};
+  }
+}
+
+// R = Q C0 + tril(P - c 1^T) K for the wave's channels cw .. cw + 15 (C0 from the wave's
+// carry accumulators), then u and the cleaned query; stores qc_i * scale(ti, r) to Qa (and
+// its bf16 low part to Qalo when SPLIT) at token i = 16 ti + l16, channel cw + 4 g + r.
+// Needs Qs, Ks, Pm and tok from ccq_gram_rows.
+template <int D, typename T, bool SPLIT, typename SM, typename Scale>
+__device__ __forceinline__ void ccq_clean_query(SM& sm, const f32x4* Cacc, int cw, int lane, Scale scale) {
+  using C_ = Cfg<D, T>;
+  constexpr int NK = C_::NK, PQ = C_::PQ, PT = C_::PT;
+  const int g = lane >> 4, l16 = lane & 15;
+  f32x4 R[4];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) R[ti] = zero4();
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const Frag<T> A = acc_frag<T>(Cacc[2 * kk], Cacc[2 * kk + 1]);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      const Frag<T> B = lds_frag<T, KORD_ACC>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
+      mma(R[ti], A, B);
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const Frag<T> A = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, cw, lane);  // K^T, own rows
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      if (kk == 1 && ti < 2) continue;  // tokens 32..63 never precede tokens 0..31
+      const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
+      mma(R[ti], A, B);
+    }
+  }
+  // R[ti][r]: channel cw + 4 g + r, token 16 ti + l16
+  const int m = cw + 4 * g;
+  const f32x4 m04 = *reinterpret_cast<const f32x4*>(&sm.m0[m]);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
+    const int i = 16 * ti + l16;
+    const f32x4 ts = sm.tok[i];  // lambda, 1/n, sq/n^2
+    const f32x4 q4 = ld4<T>(&sm.Qs[i][m]);
+    f32x4 qa;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float u = R[ti][r] * ts[1] - m04[r] * ts[2];
+      qa[r] = (q4[r] - ts[0] * u) * scale(ti, r);
+    }
+    // bf16: hi + lo (the intra-chunk attention is a sum of few, possibly cancelling
+    // products when little of the sequence has been read)
+    if constexpr (SPLIT) {
+      const bf16x4 qh = to_bf16x4(qa);
+      *reinterpret_cast<bf16x4*>(&sm.Qa[i][m]) = qh;
+      f32x4 ql;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ql[r] = qa[r] - (float)qh[r];
+      st4<T>(&sm.Qalo[i][m], ql);
+    } else {
+      st4<T>(&sm.Qa[i][m], qa);
+    }
+  }
+}
+
+}  // namespace ccq

@@ -62,7 +62,7 @@ def _fwd(lib, p):
     (dict(d_k=64, d_v=128), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED), (dict(q=None), INVALID),
     (dict(o=None), INVALID), (dict(beta=FAKE), INVALID), (dict(rule=1), INVALID),
     (dict(S0=FAKE), INVALID), (dict(S_out=FAKE, C_out=FAKE), INVALID), (dict(k=FAKE + 4), MISALIGNED),
-    (dict(segments=-2), INVALID), (dict(rule=1, beta=FAKE), UNSUPPORTED),
+    (dict(segments=-2), INVALID),
 ])
 def test_fwd_argument_errors(lib, kw, code):
     assert _fwd(lib, _params(**kw)) == code

@@ -1,0 +1,121 @@
+"""Chunked-prefill parity on the Gated DeltaNet backbone: HIP kernel through the C ABI vs the
+fp64 oracle.  Same tolerances as the GLA prefill (normwise per (b, h) slab): 1e-4 for fp32
+inputs, 2e-2 for bf16 inputs with fp32 carry, on o and on the final carry."""
+
+import numpy as np
+import pytest
+
+from curvature_conditioned_query_amd.inputs import gdn_inputs, structured_inputs, workload_inputs
+from oracle import Carry, normwise_error
+
+from gpu_util import up_carry
+from test_gpu_prefill import check, gpu_prefill, oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T", [1, 2, 17, 63, 64, 65, 130, 200])
+def test_gdn_ragged_lengths_fp32(T):
+    x = gdn_inputs(2, 2, T, 64, 140 + T, "f32")
+    o, c = gpu_prefill(x)
+    o_ref, c_ref = oracle(x)
+    check(x, o, c, o_ref, c_ref, tag=f"gdn T={T}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 2, 64, 65, 300])
+def test_gdn_bf16_shapes(d, T):
+    x = gdn_inputs(2, 3, T, d, 160 + T + d, "bf16")
+    o, c = gpu_prefill(x)
+    o_ref, c_ref = oracle(x)
+    check(x, o, c, o_ref, c_ref, tag=f"gdn d={d} T={T}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gdn_carry_resume_and_alias(dtype):
+    """prefill(T1) -> carry -> prefill(T2) from it == prefill(T1 + T2); carry out may alias in."""
+    d = 64
+    x = gdn_inputs(2, 2, 230, d, 188, dtype)
+    o_ref, c_ref = oracle(x)
+    x1, x2 = (gdn_inputs(2, 2, 230, d, 188, dtype) for _ in range(2))
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(x1, name, getattr(x, name)[:, :, :100])
+        setattr(x2, name, getattr(x, name)[:, :, 100:])
+    o1, c1 = gpu_prefill(x1)
+    carry = Carry(c1[0], c1[1], c1[2], c1[3])
+    for alias in (False, True):
+        o2, c2 = gpu_prefill(x2, carry=carry, alias=alias)
+        check(x, np.concatenate([o1, o2], axis=2), c2, o_ref, c_ref, tag=f"gdn resume alias={alias}")
+
+
+def test_gdn_carry_in_from_oracle_prefix():
+    x0 = gdn_inputs(1, 2, 150, 64, 191, "f32")
+    _, pre = oracle(x0)
+    (_, (S, C, m, n)) = up_carry(pre)
+    carry = Carry(S, C, m, n)
+    x = gdn_inputs(1, 2, 333, 64, 192, "f32")
+    o_ref, c_ref = oracle(x, carry)
+    o, c = gpu_prefill(x, carry=carry)
+    check(x, o, c, o_ref, c_ref, tag="gdn carry-in")
+
+
+def test_gdn_segments_request_is_one_pass():
+    """A Gated DeltaNet call runs one segment per chain whatever is asked: no workspace, and
+    the same result for any requested count."""
+    x = gdn_inputs(1, 2, 300, 64, 193, "f32")
+    o1, c1 = gpu_prefill(x, segments=1)
+    o4, c4 = gpu_prefill(x, segments=4)
+    assert np.array_equal(o1, o4)
+    for a, b in zip(c1, c4):
+        assert np.array_equal(a, b)
+
+
+def test_gdn_lambda_zero_is_backbone():
+    x = gdn_inputs(1, 2, 190, 64, 194, "f32")
+    x.b_lam[:] = -np.inf
+    o, c = gpu_prefill(x)
+    o_ref, c_ref = oracle(x)
+    check(x, o, c, o_ref, c_ref, tag="gdn lambda=0")
+
+
+@pytest.mark.parametrize("dtype,tol_delta", [("f32", 1e-3), ("bf16", 5e-2)])
+def test_gdn_structured_keys_ccq_delta(dtype, tol_delta):
+    """Low-rank haystack keys plus needles, lambda ~ 0.5: the GPU's CCQ delta o(b) - o(b=-inf)
+    must match the oracle's (bf16 bound as for the GLA case)."""
+    d = 64 if dtype == "f32" else 128
+    T = 256 if dtype == "f32" else 1024
+    x = structured_inputs("gdn", 1, 2, T, d, 3002, dtype)
+    x0 = structured_inputs("gdn", 1, 2, T, d, 3002, dtype)
+    x0.b_lam[:] = -np.inf
+    o, c = gpu_prefill(x)
+    o0, _ = gpu_prefill(x0)
+    o_ref, c_ref = oracle(x)
+    o0_ref, _ = oracle(x0)
+    check(x, o, c, o_ref, c_ref, tag="gdn structured")
+    dref = o_ref - o0_ref
+    frac = np.abs(dref).max() / np.abs(o_ref).max()
+    ed = normwise_error(o - o0, dref)
+    print(f"gdn structured {dtype}: delta/o {frac:.3f} delta err {ed:.3e}", flush=True)
+    assert frac > 0.05
+    assert ed <= tol_delta
+
+
+def test_gdn_deterministic():
+    x = gdn_inputs(2, 2, 300, 128, 195, "bf16")
+    o1, c1 = gpu_prefill(x)
+    o2, c2 = gpu_prefill(x)
+    assert np.array_equal(o1, o2)
+    for a, b in zip(c1, c2):
+        assert np.array_equal(a, b)
+
+
+def test_gdn_full_size_workload_sampled():
+    """B=4, H=16, T=4096, d=128 bf16: every chain on the GPU, sampled chains vs the oracle."""
+    x = workload_inputs(2)
+    o, c = gpu_prefill(x)
+    assert np.all(np.isfinite(o))
+    for (b, h) in [(0, 0), (3, 15), (1, 9)]:
+        xs = x.slab(b, h)
+        o_ref, c_ref = oracle(xs)
+        cs = tuple(a[b:b + 1, h:h + 1] for a in c)
+        check(xs, o[b:b + 1, h:h + 1], cs, o_ref, c_ref, tag=f"workload2 chain ({b},{h})")
