@@ -32,6 +32,7 @@ FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 CHUNK = 64
 PREFILL_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill.hip")
 DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode.hip")
+GDN_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill_gdn.hip")
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -40,7 +41,9 @@ def prefill_work(B, H, T, d, elem_bytes, rule="gla"):
 
     flops per (token, head): GLA 8 d^2 + 8 L d (full 16x16 MFMA tiles of the L=64 chunk
     form: Q K^T, Q C0, tril(P) K, Qc S0^T, the intra attention matrix and its product
-    with V, K^T K and the S update); Gated DeltaNet 10 d^2 + 10 L d + L^2/3-ish solve.
+    with V, K^T K and the S update); Gated DeltaNet 10 d^2 + 14 L d (the CCQ part as for GLA,
+    plus K K^T, U = T diag(beta) V, W = T diag(beta gamma) K, Qc K^T and its product with Delta
+    on L x L tiles, W S0^T, Qc S0^T and the S update on d x d; the L^3/3 solve is not counted).
     bytes: q, k, v, log decay read once and o written once, plus the fp32 carry out
     (S, C, ksum, n) per chain."""
     th = B * H * T
@@ -48,19 +51,21 @@ def prefill_work(B, H, T, d, elem_bytes, rule="gla"):
         flop_th = 8 * d * d + 8 * CHUNK * d
         in_bytes_th = 4 * d * elem_bytes
     else:
-        flop_th = 10 * d * d + 12 * CHUNK * d
+        flop_th = 10 * d * d + 14 * CHUNK * d
         in_bytes_th = 3 * d * elem_bytes + 2 * elem_bytes
     bytes_th = in_bytes_th + d * elem_bytes
     carry = 2 * d * d * 4 + d * 4 + 8
     return th * flop_th, th * bytes_th + B * H * carry
 
 
-def main_kernel_bytes(B, H, T, d, elem_bytes, segments):
-    """Algorithmic HBM bytes of one launch of the main prefill kernel: q, k, v, log decay read
-    and o written once, the carry-in of every segment after the first read from the workspace
-    (S, C, ksum in fp32), and the final carry (S, C, ksum, n) written."""
+def main_kernel_bytes(B, H, T, d, elem_bytes, segments, rule="gla"):
+    """Algorithmic HBM bytes of one launch of the main prefill kernel: q, k, v and the gates
+    (GLA: log decay per key channel; GDN: log alpha and beta per token) read and o written
+    once, the carry-in of every segment after the first read from the workspace (S, C, ksum
+    in fp32), and the final carry (S, C, ksum, n) written."""
     chains = B * H
-    tokens = 5 * B * H * T * d * elem_bytes
+    per_th = (5 * d if rule == "gla" else 4 * d + 2) * elem_bytes
+    tokens = B * H * T * per_th
     slot_in = (2 * d * d + d) * 4
     carry_out = 2 * d * d * 4 + d * 4 + 8
     return tokens + chains * (max(segments, 1) - 1) * slot_in + chains * carry_out
@@ -297,6 +302,7 @@ def main(argv=None):
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 3])
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet prefill leg")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill leg (profiling the decode kernel alone)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -344,7 +350,7 @@ def main(argv=None):
     # Roofline of the dominant kernel, the main prefill kernel (one launch per pass): its
     # algorithmic bytes and the method's flops over its own average launch duration.
     main_ms = res["phase_ms"]["main"]
-    main_bytes = main_kernel_bytes(B, H, T, dk, elem, res["segments"] or 1)
+    main_bytes = main_kernel_bytes(B, H, T, dk, elem, res["segments"] or 1, spec["rule"])
     k_gbs = main_bytes / (main_ms * 1e-3) / 1e9
     k_tflops = flops / (main_ms * 1e-3) / 1e12
     traffic = measured_traffic(f"traffic_{spec['name']}.json", src_sha)
@@ -382,6 +388,30 @@ def main(argv=None):
     print(f"# prefill {spec['name']}: {ms:.3f} ms/step, {tok_s:.4g} tokens/s, {gbs:.1f} GB/s alg, "
           f"{tflops:.1f} TFLOP/s alg; kernels (ms) " +
           ", ".join(f"{k} {v:.4f}" for k, v in res["phase_ms"].items()), file=sys.stderr, flush=True)
+    if not args.no_gdn:
+        gres = time_prefill(2, args.steps, args.warmup)
+        gB, gH, gT, gd, _ = gres["shape"]
+        g_ms = gres["total_ms"] / args.steps
+        g_flops, g_bytes = prefill_work(gB, gH, gT, gd, 2, "gdn")
+        g_main = gres["phase_ms"]["main"]
+        g_kbytes = main_kernel_bytes(gB, gH, gT, gd, 2, 1, "gdn")
+        g_gbs = g_kbytes / (g_main * 1e-3) / 1e9
+        g_tf = g_flops / (g_main * 1e-3) / 1e12
+        gsrc = file_sha(GDN_SRC)
+        out["gdn"] = {
+            "workload": gres["spec"]["name"], "ms_per_step": round(g_ms, 4),
+            "tokens_per_s": round(gB * gT / (g_ms * 1e-3), 1), "segments": 1,
+            "roofline": dict(bound="hbm", achieved=round(g_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(g_gbs / HBM_PEAK_GBS, 4),
+                             traffic=measured_traffic(f"traffic_{gres['spec']['name']}.json", gsrc),
+                             kernel=f"gdn_main_kernel<{gd},bf16>", avg_launch_ms=round(g_main, 4),
+                             algorithmic_bytes_per_launch=g_kbytes, algorithmic_flops_per_launch=g_flops,
+                             mfma=dict(achieved=round(g_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                                       frac=round(g_tf / BF16_PEAK_TFLOPS, 4))),
+        }
+        print(f"# prefill {gres['spec']['name']}: {g_ms:.3f} ms/step, {gB * gT / (g_ms * 1e-3):.4g} tokens/s, "
+              f"main kernel {g_main:.4f} ms, {g_gbs:.1f} GB/s alg, {g_tf:.1f} TFLOP/s alg",
+              file=sys.stderr, flush=True)
     if not args.no_decode:
         dres = time_decode(args.decode_steps, 3)
         dsrc = file_sha(DECODE_SRC)

@@ -8,24 +8,28 @@
 //   GLA: S <- S diag(alpha) + v k^T;   GDN: S <- alpha S (I - beta k k^T) + beta v k^T
 //   o = S q_clean  (S after the write)
 //
-// Memory-bound: every head moves its fp32 C and S (2 x d^2 x 4 bytes) in and out once.
-// One 256-thread workgroup per head.  Thread t owns float4 column group (t mod d/4) of
-// rows t/(d/4) + i*(256/(d/4)); every load of C and S is issued before the first
-// barrier, so a workgroup has its whole 2 x d^2 x 4 bytes in flight at once.  Rows are
-// reduced across the d/4 lanes that share them with xor shuffles inside a wave.
+// Memory-bound: every head moves its fp32 C and S (2 x d^2 x 4 bytes) in and out once, with
+// non-temporal loads and stores (the state is touched once per step and is far larger than
+// the caches).  One workgroup of NT threads per head (1024 at d = 128).  The per-token operands (q, k, v,
+// gates, ksum, n, w_lambda) are loaded first and the state after them, so the waits for the
+// small operands never wait for the state (the vector-memory counter drains in order);
+// then thread t owns float4 column group (t mod d/4) of rows t/(d/4) + i*(NT/(d/4)), with
+// every load of C and S in flight before the first use.  Rows are reduced across the d/4
+// lanes that share them with xor shuffles inside a wave; d-long dot products are reduced
+// per wave and summed from LDS.
 #include "ccq_device.hpp"
 #include "ccq_internal.hpp"
 
 namespace ccq {
 
-constexpr int kDecodeThreads = 256;
-
-template <int D, typename T, int RULE>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
-  constexpr int C4 = D / 4;                 // float4 per row
-  constexpr int RPI = kDecodeThreads / C4;  // rows covered per iteration
-  constexpr int IT = D / RPI;               // iterations per thread
+template <int D, typename T, int RULE, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
+  constexpr int C4 = D / 4;       // float4 per row
+  constexpr int RPI = NT / C4;    // rows covered per iteration
+  constexpr int IT = D / RPI;     // iterations per thread
+  constexpr int NWV = (D + 63) / 64;  // waves holding the d-long vectors
   static_assert(C4 <= 64 && (64 % C4) == 0, "a row must sit inside one wave");
+  static_assert(IT * RPI == D, "rows must tile the workgroup");
 
   const int head = blockIdx.x;  // (sequence, head) pair, 0 .. N*H-1
   const int h = head % a.H;
@@ -34,60 +38,61 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
   const int row0 = tid / C4;
 
   __shared__ float q_s[D], k_s[D], v_s[D], al_s[D], kn_s[D], r_s[D], qt_s[D];
-  __shared__ float scal[4];  // lambda, msq, n (as float), k.q (unused by GLA)
+  __shared__ float part[2][NWV];  // per-wave partial w . q and ksum_new . q
+  __shared__ float nf_s;
 
-  const T* qg = static_cast<const T*>(a.q) + (size_t)head * D;
-  const T* kg = static_cast<const T*>(a.k) + (size_t)head * D;
-  const T* vg = static_cast<const T*>(a.v) + (size_t)head * D;
+  // ---- per-token operands first (every thread loads; threads past d repeat an index)
+  const int c = tid % D;
+  const T qraw = static_cast<const T*>(a.q)[(size_t)head * D + c];
+  const T kraw = static_cast<const T*>(a.k)[(size_t)head * D + c];
+  const T vraw = static_cast<const T*>(a.v)[(size_t)head * D + c];
+  const T graw = (RULE == 0) ? static_cast<const T*>(a.log_alpha)[(size_t)head * D + c]
+                             : static_cast<const T*>(a.log_alpha)[head];
+  const T braw = (RULE == 1) ? static_cast<const T*>(a.beta)[head] : T(0.f);
+  const float mv = a.ksum[(size_t)head * D + c];
+  const float wv = a.w_lambda[(size_t)h * D + c];
+  const int64_t n0 = a.n[head];
+  const float b_lam = a.b_lambda[h];
+
+  // ---- then the state
   float* Cg = a.C + (size_t)head * D * D;
   float* Sg = a.S + (size_t)head * D * D;
-
-  // Issue the state loads first: they are the bandwidth.
   f32x4 cr[IT], sr[IT];
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int row = row0 + i * RPI;
-    cr[i] = *reinterpret_cast<const f32x4*>(Cg + (size_t)row * D + 4 * col4);
-  }
+  for (int i = 0; i < IT; ++i) cr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Cg + (size_t)(row0 + i * RPI) * D + 4 * col4));
 #pragma unroll
-  for (int i = 0; i < IT; ++i) {
-    const int row = row0 + i * RPI;
-    sr[i] = *reinterpret_cast<const f32x4*>(Sg + (size_t)row * D + 4 * col4);
-  }
-
+  for (int i = 0; i < IT; ++i) sr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sg + (size_t)(row0 + i * RPI) * D + 4 * col4));
+  // nothing that uses the operands above may be scheduled before the state loads are issued
+  __builtin_amdgcn_sched_barrier(0);
+  const float qv = to_f32(qraw), kv = to_f32(kraw), vv = to_f32(vraw);
   float alpha_s = 1.f, beta_s = 0.f;
   if constexpr (RULE == 1) {
-    alpha_s = __expf(ldf(static_cast<const T*>(a.log_alpha), head));
-    beta_s = ldf(static_cast<const T*>(a.beta), head);
+    alpha_s = __expf(to_f32(graw));
+    beta_s = to_f32(braw);
   }
+
+  // ---- token vectors to LDS, updated key sum and count, partial dot products
   if (tid < D) {
-    q_s[tid] = ldf(qg, tid);
-    k_s[tid] = ldf(kg, tid);
-    v_s[tid] = ldf(vg, tid);
-    if constexpr (RULE == 0) al_s[tid] = __expf(ldf(static_cast<const T*>(a.log_alpha), (size_t)head * D + tid));
+    const float kn = mv + kv;
+    q_s[tid] = qv;
+    k_s[tid] = kv;
+    v_s[tid] = vv;
+    if constexpr (RULE == 0) al_s[tid] = __expf(to_f32(graw));
+    kn_s[tid] = kn;
+    a.ksum[(size_t)head * D + tid] = kn;
+    const float pw = group_sum<64>(wv * qv);
+    const float pm = group_sum<64>(kn * qv);
+    if ((tid & 63) == 0) {
+      part[0][tid >> 6] = pw;
+      part[1][tid >> 6] = pm;
+    }
+  }
+  if (tid == 0) {
+    const int64_t n1 = n0 + 1;
+    a.n[head] = n1;
+    nf_s = (float)n1;
   }
   lds_barrier();
-
-  // Wave 0: updated key sum, the gate, and ksum_new . q.
-  if (tid < 64) {
-    float wq = 0.f, msq = 0.f;
-    for (int c = tid; c < D; c += 64) {
-      const float kn = a.ksum[(size_t)head * D + c] + k_s[c];
-      a.ksum[(size_t)head * D + c] = kn;
-      kn_s[c] = kn;
-      wq += a.w_lambda[(size_t)h * D + c] * q_s[c];
-      msq += kn * q_s[c];
-    }
-    wq = group_sum<64>(wq);
-    msq = group_sum<64>(msq);
-    if (tid == 0) {
-      const int64_t n1 = a.n[head] + 1;
-      a.n[head] = n1;
-      scal[0] = sigmoidf(wq + a.b_lambda[h]);
-      scal[1] = msq;
-      scal[2] = (float)n1;
-    }
-  }
 
   const f32x4 k4 = *reinterpret_cast<const f32x4*>(k_s + 4 * col4);
   const f32x4 q4 = *reinterpret_cast<const f32x4*>(q_s + 4 * col4);
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     const int row = row0 + i * RPI;
     const float kr = k_s[row];
     f32x4 cn = cr[i] + kr * k4;
-    *reinterpret_cast<f32x4*>(Cg + (size_t)row * D + 4 * col4) = cn;
+    __builtin_nontemporal_store(cn, reinterpret_cast<f32x4*>(Cg + (size_t)row * D + 4 * col4));
     float pr = cn[0] * q4[0] + cn[1] * q4[1] + cn[2] * q4[2] + cn[3] * q4[3];
     pr = group_sum<C4>(pr);
     if (col4 == 0) r_s[row] = pr;
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
     for (int i = 0; i < IT; ++i) {
       const int row = row0 + i * RPI;
       sr[i] = sr[i] * a4 + v_s[row] * k4;
-      *reinterpret_cast<f32x4*>(Sg + (size_t)row * D + 4 * col4) = sr[i];
+      __builtin_nontemporal_store(sr[i], reinterpret_cast<f32x4*>(Sg + (size_t)row * D + 4 * col4));
     }
   } else {
 #pragma unroll
@@ -120,14 +125,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
       float sk = sr[i][0] * k4[0] + sr[i][1] * k4[1] + sr[i][2] * k4[2] + sr[i][3] * k4[3];
       sk = group_sum<C4>(sk);
       sr[i] = alpha_s * (sr[i] - (beta_s * sk) * k4) + (beta_s * v_s[row]) * k4;
-      *reinterpret_cast<f32x4*>(Sg + (size_t)row * D + 4 * col4) = sr[i];
+      __builtin_nontemporal_store(sr[i], reinterpret_cast<f32x4*>(Sg + (size_t)row * D + 4 * col4));
     }
   }
-  lds_barrier();  // r_s, kn_s and scal complete
+  lds_barrier();  // r_s complete
 
   if (tid < D) {
-    const float lam = scal[0], msq = scal[1], nf = scal[2];
-    const float inv_n = 1.0f / nf;
+    float wq = 0.f, msq = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWV; ++v) {
+      wq += part[0][v];
+      msq += part[1][v];
+    }
+    const float lam = sigmoidf(wq + b_lam);
+    const float inv_n = 1.0f / nf_s;
     const float u = r_s[tid] * inv_n - kn_s[tid] * (msq * inv_n * inv_n);
     qt_s[tid] = q_s[tid] - lam * u;
   }
@@ -146,11 +157,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs a) {
 
 template <int D, typename T>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.N * a.H)), block(kDecodeThreads);
+  constexpr int NT = 8 * D;  // 1024 threads at d = 128: 4 float4 of C and of S per thread
+  const dim3 grid((unsigned)(a.N * a.H)), block(NT);
   if (a.rule == 0)
-    hipLaunchKernelGGL((decode_kernel<D, T, 0>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, T, 0, NT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, T, 1>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<D, T, 1, NT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
