@@ -360,7 +360,7 @@ def main(argv=None):
     else:
         roof = dict(bound="mfma", achieved=round(k_tflops, 1), peak=mfma_peak, unit="TFLOP/s",
                     frac=round(k_tflops / mfma_peak, 4), traffic=traffic)
-    roof.update(kernel=f"gla_prefill_kernel<{dk},{'bf16' if elem == 2 else 'f32'},main>",
+    roof.update(kernel=f"gla_main_kernel<{dk},{'bf16' if elem == 2 else 'f32'}>",
                 avg_launch_ms=round(main_ms, 4), algorithmic_bytes_per_launch=main_bytes,
                 algorithmic_flops_per_launch=flops,
                 mfma=dict(achieved=round(k_tflops, 1), peak=mfma_peak, unit="TFLOP/s",

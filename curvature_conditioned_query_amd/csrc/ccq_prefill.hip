@@ -49,18 +49,19 @@ size_t fwd_slot_bytes(int d) { return (size_t)(2 * d * d + 2 * d) * sizeof(float
 template <int D, typename T>
 struct Smem {
   using C_ = Cfg<D, T>;
-  T Qs[kL][C_::PQ];    // q rows
-  T Ks[kL][C_::PQ];    // k rows
-  T Vs[kL][C_::PQ];    // v rows
-  T Gs[kL][C_::PQ];    // log decay rows
-  T Kp[kL][C_::PQ];    // k * e^-B rows (hi part for bf16)
-  T Klo[C_::LO][C_::PQ];   // bf16 only: lo part of k * e^-B
-  T Qa[kL][C_::PQ];    // q_clean * e^B rows (hi part for bf16)
-  T Qalo[C_::LO][C_::PQ];  // bf16 only: lo part of q_clean * e^B
-  T Pm[kL][C_::PT];    // tril(Q K^T - c 1^T), then the masked intra-chunk attention matrix
-  T Wt[4][C_::PQ];     // w_lambda hi, lo; key sum hi, lo (B operand of q . [w, m0])
+  T Qs[kL][C_::PQ];     // q rows
+  T Gs[kL][C_::PQ];     // log decay rows
+  // Chunk c keeps its k rows in X[c % 2] and v rows in Y[c % 2]; the other halves hold the
+  // bf16 low parts of k e^-B and q_clean e^B while the intra-chunk attention is formed, and
+  // then receive the next chunk's k and v.
+  T X[2][kL][C_::PQ];
+  T Y[2][kL][C_::PQ];
+  T Kp[kL][C_::PQ];     // k * e^-B rows (hi part for bf16)
+  T Qa[kL][C_::PQ];     // q_clean * e^B rows (hi part for bf16)
+  T Pm[kL][C_::PT];     // tril(Q K^T - c 1^T), then the masked intra-chunk attention matrix
+  T Wt[4][C_::PQ];      // w_lambda hi, lo; key sum hi, lo (B operand of q . [w, m0])
   float m0[D], m1[D], eBL[D], ldec[D];
-  f32x4 tok[kL];       // per token: lambda, 1/n, sq/n^2, gate logit + b
+  f32x4 tok[kL];        // per token: lambda, 1/n, sq/n^2, gate logit + b
 };
 
 // MODE 0: full read (o for every token) from the segment's carry-in, carry out at the end.
@@ -146,25 +147,20 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     for (int e = tid; e < kL * PT; e += 64 * NW) (&sm.Pm[0][0])[e] = (T)0.f;
   }
 
-  // ---- register prefetch of the block's rows of one chunk, as MFMA row fragments (lane:
-  // token 16 ti + l16, channels cb + 8g .. cb + 8g + 7): q and k for the first wave of the
-  // pair, v and log decay for the second; rows past the end of the sequence are zero.
-  Frag<T> fa[4], fb[4];
-  const T* srcA = hb ? vg : qg;
-  const T* srcB = hb ? gg : kg;
-  auto prefetch = [&](int ch) {
-    const int t0 = ch * kL;
-    const int Lc = min(kL, a.T - t0);
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const int t = 16 * ti + l16;
-      const bool ok = t < Lc;
-      const size_t off = ok ? (tok0 + t0 + t) * D + cb + 8 * g : 0;
-      if (MAIN || hb == 1) fa[ti] = gload_frag<T>(srcA + off, ok);
-      fb[ti] = gload_frag<T>(srcB + off, ok);
-    }
+  // ---- chunk tiles go straight from HBM to LDS (no registers involved), each as soon as the
+  // previous chunk has finished reading the buffer it lands in: log decay after the gate and
+  // Gram rows, q after the cleaned query, k and v (bf16) after the intra-chunk attention or
+  // (fp32, summary) at the start of the previous chunk.
+  auto chunk_len = [&](int ch) { return min(kL, a.T - ch * kL); };
+  auto dma_rows = [&](T (*dst)[PQ], const T* g, int ch) {
+    dma_tile<D, T, PQ>(dst, g + (tok0 + (size_t)ch * kL) * D, chunk_len(ch), w, NW, lane);
   };
-  if (cbeg < cend) prefetch(cbeg);
+  if (cbeg < cend) {
+    if constexpr (MAIN) dma_rows(sm.Qs, qg, cbeg);
+    dma_rows(sm.Gs, gg, cbeg);
+    dma_rows(sm.X[cbeg & 1], kg, cbeg);
+    dma_rows(sm.Y[cbeg & 1], vg, cbeg);
+  }
 
   const Frag<T> Ih = ident_frag<T>(hb, lane);
 
@@ -172,22 +168,28 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
 
-    // ---- stage rows: q and k by the first wave of each pair, v and log decay by the second
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const int t = 16 * ti + l16;
-      if (hb == 0) {
-        if constexpr (MAIN) st_frag<T>(&sm.Qs[t][cb + 8 * g], fa[ti]);
-        st_frag<T>(&sm.Ks[t][cb + 8 * g], fb[ti]);
-      } else {
-        st_frag<T>(&sm.Vs[t][cb + 8 * g], fa[ti]);
-        st_frag<T>(&sm.Gs[t][cb + 8 * g], fb[ti]);
+    T (*Ks)[PQ] = sm.X[ch & 1];
+    T (*Vs)[PQ] = sm.Y[ch & 1];
+    T (*Klo)[PQ] = sm.X[(ch + 1) & 1];   // bf16 only
+    T (*Qalo)[PQ] = sm.Y[(ch + 1) & 1];  // bf16 only
+
+    // ---- this chunk's tiles have landed (own loads, then everyone's); rows past the end of
+    // the sequence are zeroed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (Lc < kL) {
+      if constexpr (MAIN) zero_tail<D, T, PQ>(sm.Qs, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(sm.Gs, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(Ks, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(Vs, Lc, tid, 64 * NW);
+      lds_barrier();
+    }
+    if constexpr (!kSplit) {
+      if (ch + 1 < cend) {
+        dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
+        dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
       }
     }
-    if constexpr (!MAIN) {
-      if (ch + 1 < cend) prefetch(ch + 1);
-    }
-    lds_barrier();
 
     // ---- own channels: cumulative decay (4 consecutive channels per lane), k e^-B, key sum,
     // chunk decay.  BT[ti][r] = B at token 16 ti + l16, channel cw + 4g + r.
@@ -208,7 +210,7 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
         mma(BT[ti], Ga, ltri_frag<T>(ti, 0, lane));
         if (ti >= 2) mma(BT[ti], Gb, ltri_frag<T>(ti, 1, lane));
         f32x4 KC = zero4();  // k at token 16 ti + l16, channel cw + 4g + r
-        mma(KC, Ih, lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * ti, cb, lane));
+        mma(KC, Ih, lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * ti, cb, lane));
         ks += KC;
         f32x4 kp;
 #pragma unroll
@@ -220,7 +222,7 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
           f32x4 kl;
 #pragma unroll
           for (int r = 0; r < 4; ++r) kl[r] = kp[r] - (float)kh[r];
-          st4<T>(&sm.Klo[t][cw + 4 * g], kl);
+          st4<T>(&Klo[t][cw + 4 * g], kl);
         } else {
           st4<T>(&sm.Kp[t][cw + 4 * g], kp);
         }
@@ -240,17 +242,19 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
         }
       }
     }
-    if constexpr (!MAIN) lds_barrier();
+    if constexpr (!MAIN) {
+      lds_barrier();
+      if (ch + 1 < cend) dma_rows(sm.Gs, gg, ch + 1);
+    }
 
     if constexpr (MAIN) {
-      ccq_gram_rows<D, T>(sm, w, lane, nb, b_lam);
+      ccq_gram_rows<D, T>(sm, Ks, w, lane, nb, b_lam);
       lds_barrier();
+      if (ch + 1 < cend) dma_rows(sm.Gs, gg, ch + 1);
 
-      ccq_clean_query<D, T, kSplit>(sm, Cacc, cw, lane, [&](int ti, int r) { return __expf(BT[ti][r]); });
+      ccq_clean_query<D, T, kSplit>(sm, Ks, Qalo, Cacc, cw, lane, [&](int ti, int r) { return __expf(BT[ti][r]); });
       lds_barrier();
-      // the chunk's row fragments are consumed: next chunk's loads go out now, behind the
-      // intra-chunk read, the output store and the carry update
-      if (ch + 1 < cend) prefetch(ch + 1);
+      if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);
 
       // ---- intra-chunk attention (Qc e^B)(K e^-B)^T on the lower tiles -> Pm (masked)
       for (int idx = w; idx < 10; idx += NW) {
@@ -262,8 +266,8 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
           const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
           mma(acc, A, B);
           if constexpr (kSplit) {
-            const Frag<T> Al = lds_frag<T, KORD_CONTIG>(&sm.Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
-            const Frag<T> Bl = lds_frag<T, KORD_CONTIG>(&sm.Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
+            const Frag<T> Al = lds_frag<T, KORD_CONTIG>(&Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
+            const Frag<T> Bl = lds_frag<T, KORD_CONTIG>(&Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
             mma(acc, A, Bl);
             mma(acc, Al, B);
           }
@@ -274,6 +278,12 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
         st4<T>(&sm.Pm[i][16 * tj + 4 * g], acc);
       }
       lds_barrier();
+      if constexpr (kSplit) {  // the low parts are consumed: their buffers take the next k, v
+        if (ch + 1 < cend) {
+          dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
+          dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
+        }
+      }
 
       // ---- O^T for the wave's 16 value rows: S0 (Qc e^B)^T + V^T A^T
       f32x4 O[4];
@@ -290,7 +300,7 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const Frag<T> A = tr_frag<T>(&sm.Vs[0][0], PQ, 32 * kk, cw, lane);  // V^T, own rows
+        const Frag<T> A = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);  // V^T, own rows
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
           if (kk == 1 && ti < 2) continue;
@@ -309,11 +319,11 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     // ---- carry update: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const Frag<T> Bk = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
-      const Frag<T> Bv = tr_frag<T>(&sm.Vs[0][0], PQ, 32 * kk, cw, lane);  // V[t][own channel]
+      const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
+      const Frag<T> Bv = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);  // V[t][own channel]
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
-        const Frag<T> Ak = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, 16 * t, lane);  // K^T rows 16t..
+        const Frag<T> Ak = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane);  // K^T rows 16t..
         const Frag<T> Ap = tr_frag<T>(&sm.Kp[0][0], PQ, 32 * kk, 16 * t, lane);  // (K e^-B)^T
         mma(Cacc[t], Ak, Bk);
         mma(Sacc[t], Ap, Bv);

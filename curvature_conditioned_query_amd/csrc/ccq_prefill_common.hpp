@@ -8,8 +8,8 @@
 //   u_i  = (Q C0 + tril_incl(P - c 1^T) K)_i / n_i - m0 sq_i / n_i^2,  c_i = sq_i / n_i
 //        (row i of Q C0 + tril_incl(P) K is C_i q_i, so u_i = Sigma_i q_i)
 //   qc_i = q_i - lambda_i u_i,  lambda_i = sigmoid(w . q_i + b)
-// Any shared-memory struct with the members used below (Qs, Ks, Wt, Pm, tok, m0, Qa, Qalo)
-// can host them.
+// Any shared-memory struct with the members used below (Qs, Wt, Pm, tok, m0, Qa) can host
+// them; the key tile and the bf16 low part of the cleaned query are passed in.
 #pragma once
 
 #include "ccq_device.hpp"
@@ -49,16 +49,21 @@ __device__ __forceinline__ f32x4 ld4(const T* p) {
   }
 }
 
-// 8 elements of one row from global memory (16 bytes for bf16, 32 for fp32), or zeros.
+// 8 elements of one row from global memory (16 bytes for bf16, 32 for fp32), or zeros.  The
+// load is always issued (p must be a valid address either way) and the zeros are selected
+// per lane afterwards, so no branch guards it.
 template <typename T>
 __device__ __forceinline__ Frag<T> gload_frag(const T* p, bool ok) {
   Frag<T> f;
   if constexpr (sizeof(T) == 2) {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    f.v = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(p) : z);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(p);
+    f.v = __builtin_bit_cast(bf16x8, ok ? x : z);
   } else {
-    const f32x4 lo = ok ? *reinterpret_cast<const f32x4*>(p) : zero4();
-    const f32x4 hi = ok ? *reinterpret_cast<const f32x4*>(p + 4) : zero4();
+    const f32x4 lo_ = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 hi_ = *reinterpret_cast<const f32x4*>(p + 4);
+    const f32x4 lo = ok ? lo_ : zero4();
+    const f32x4 hi = ok ? hi_ : zero4();
 #pragma unroll
     for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[4 + e] = hi[e]; }
   }
@@ -160,13 +165,49 @@ __device__ __forceinline__ int tri_col(int idx) {
   return idx - r * (r + 1) / 2;
 }
 
+// Rows 0..63 of one chunk of a [token][D] tensor (src = its row 0) straight into an LDS tile
+// of pitch PQ with gfx950's global_load_lds_dwordx4, which writes lane i's 16 bytes to the
+// LDS address M0 + 16 i.  Instruction j of a tile therefore fills the tile's 16-byte units
+// [64 j, 64 j + 64); unit u is row u / U, slot u % U of a row of U units, the last
+// U - D * sizeof(T) / 16 of them padding.  Padding slots and rows at or past Lc (beyond the
+// end of the sequence) load row 0 instead: the padding is never read and the rows past the
+// end are zeroed by zero_tail once the loads have landed.  Waves w, w + nw, ... issue the
+// tile's U instructions.
+// The instruction is issued from inline assembly so that the compiler does not track it:
+// its wait-count pass would otherwise make every later LDS read that it cannot prove
+// disjoint from the (runtime-selected) destination wait for the load.  Callers therefore
+// wait themselves: s_waitcnt vmcnt(0), then a barrier, before the tile is read.  Loads the
+// compiler does issue are still waited for correctly (the counter drains in order, so loads
+// it does not know about only make its own waits stricter).
+template <int D, typename T, int PQ>
+__device__ __forceinline__ void dma_tile(T (*dst)[PQ], const T* src, int Lc, int w, int nw, int lane) {
+  constexpr int U = PQ * (int)sizeof(T) / 16, DU = D * (int)sizeof(T) / 16, EPU = 16 / (int)sizeof(T);
+  static_assert(PQ * sizeof(T) % 16 == 0, "rows must be whole 16-byte units");
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) T*)&dst[0][0];
+  for (int j = w; j < U; j += nw) {
+    const int u = 64 * j + lane;
+    const int row = u / U, slot = u - row * U;
+    const bool ok = row < Lc && slot < DU;
+    const T* p = src + (ok ? row * D + slot * EPU : 0);
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)j);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p) : "memory", "m0");
+  }
+}
+
+// Zeroes rows Lc..63 of an LDS tile (the rows of a chunk past the end of the sequence).
+template <int D, typename T, int PQ>
+__device__ __forceinline__ void zero_tail(T (*dst)[PQ], int Lc, int tid, int nthreads) {
+  for (int e = tid; e < (kL - Lc) * D; e += nthreads) dst[Lc + e / D][e % D] = (T)0.f;
+}
+
 // Gate logit and m0 . q, then the row tile of P = Q K^T, its inclusive row sums and
 // Pm = tril(P - c 1^T), for the 16-token row tiles it = w, w + NW, ... < 4 (waves 0..3 at
 // d >= 64).  Writes sm.Pm and sm.tok[i] = {lambda_i, 1/n_i, sq_i / n_i^2, logit_i}; nb is
 // the number of tokens before the chunk.  Needs Qs, Ks, Wt staged; Pm rows must be zero
 // above the diagonal tiles.
 template <int D, typename T, typename SM>
-__device__ __forceinline__ void ccq_gram_rows(SM& sm, int w, int lane, int64_t nb, float b_lam) {
+__device__ __forceinline__ void ccq_gram_rows(SM& sm, const T (*Ks)[Cfg<D, T>::PQ], int w, int lane, int64_t nb,
+                                              float b_lam) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NK = C_::NK, PQ = C_::PQ;
   const int g = lane >> 4, l16 = lane & 15;
@@ -197,7 +238,7 @@ __device__ __forceinline__ void ccq_gram_rows(SM& sm, int w, int lane, int64_t n
       if (tj > it) continue;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+        const Frag<T> A = lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
         const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qs[0][0], PQ, 16 * it, 32 * kk, lane);
         mma(Pt[tj], A, B);
       }
@@ -231,7 +272,8 @@ __device__ __forceinline__ void ccq_gram_rows(SM& sm, int w, int lane, int64_t n
 // its bf16 low part to Qalo when SPLIT) at token i = 16 ti + l16, channel cw + 4 g + r.
 // Needs Qs, Ks, Pm and tok from ccq_gram_rows.
 template <int D, typename T, bool SPLIT, typename SM, typename Scale>
-__device__ __forceinline__ void ccq_clean_query(SM& sm, const f32x4* Cacc, int cw, int lane, Scale scale) {
+__device__ __forceinline__ void ccq_clean_query(SM& sm, const T (*Ks)[Cfg<D, T>::PQ], T (*Qalo)[Cfg<D, T>::PQ],
+                                                const f32x4* Cacc, int cw, int lane, Scale scale) {
   using C_ = Cfg<D, T>;
   constexpr int NK = C_::NK, PQ = C_::PQ, PT = C_::PT;
   const int g = lane >> 4, l16 = lane & 15;
@@ -249,7 +291,7 @@ __device__ __forceinline__ void ccq_clean_query(SM& sm, const f32x4* Cacc, int c
   }
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    const Frag<T> A = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, cw, lane);  // K^T, own rows
+    const Frag<T> A = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K^T, own rows
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       if (kk == 1 && ti < 2) continue;  // tokens 32..63 never precede tokens 0..31
@@ -279,7 +321,7 @@ __device__ __forceinline__ void ccq_clean_query(SM& sm, const f32x4* Cacc, int c
       f32x4 ql;
 #pragma unroll
       for (int r = 0; r < 4; ++r) ql[r] = qa[r] - (float)qh[r];
-      st4<T>(&sm.Qalo[i][m], ql);
+      st4<T>(&Qalo[i][m], ql);
     } else {
       st4<T>(&sm.Qa[i][m], qa);
     }

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
 
     // ---- gate and Gram rows (waves 0..3); A = beta Gam (K K^T) below the diagonal and the key
     // sums (the other waves at d = 128, all of them at d = 64)
-    ccq_gram_rows<D, T>(sm, w, lane, nb, b_lam);
+    ccq_gram_rows<D, T>(sm, sm.Ks, w, lane, nb, b_lam);
     {
       constexpr int kw0 = (NW >= 8) ? 4 : 0, kws = NW - kw0;
       if (w >= kw0) {
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sm.Tb[blk][i][c] = tcol[i];
     }
-    ccq_clean_query<D, T, kSplit>(sm, Cacc, cw, lane, [](int, int) { return 1.0f; });
+    ccq_clean_query<D, T, kSplit>(sm, sm.Ks, sm.Qalo, Cacc, cw, lane, [](int, int) { return 1.0f; });
     f32x4 X[4];  // X[b][r] at token 16 b + 4 g + r, value channel cw + l16
 #pragma unroll
     for (int b = 0; b < 4; ++b) X[b] = zero4();
