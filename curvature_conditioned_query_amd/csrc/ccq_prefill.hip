@@ -248,11 +248,15 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     }
 
     if constexpr (MAIN) {
-      ccq_gram_rows<D, T>(sm, Ks, w, lane, nb, b_lam);
+      // gate and Gram rows on waves 0..3 while every wave forms Q C0 for its channels
+      ccq_gram_rows<D, T, NW>(sm, Ks, w, lane, nb, b_lam);
+      f32x4 R[1][4];
+      ccq_query_carry<D, T, 1>(sm, [&](int, int t) -> const f32x4& { return Cacc[t]; }, lane, R);
       lds_barrier();
       if (ch + 1 < cend) dma_rows(sm.Gs, gg, ch + 1);
 
-      ccq_clean_query<D, T, kSplit>(sm, Ks, Qalo, Cacc, cw, lane, [&](int ti, int r) { return __expf(BT[ti][r]); });
+      ccq_clean_query<D, T, 1, kSplit>(sm, Ks, Qalo, R, cw, lane,
+                                       [&](int, int ti, int r) { return __expf(BT[ti][r]); });
       lds_barrier();
       if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);
 
@@ -260,16 +264,23 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
       for (int idx = w; idx < 10; idx += NW) {
         const int ti = tri_row(idx), tj = tri_col(idx);
         f32x4 acc = zero4();
+        Frag<T> Af[NK], Bf[NK], Alf[NK], Blf[NK];
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-          const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Kp[0][0], PQ, 16 * tj, 32 * kk, lane);
-          const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
-          mma(acc, A, B);
+          Af[kk] = lds_frag<T, KORD_CONTIG>(&sm.Kp[0][0], PQ, 16 * tj, 32 * kk, lane);
+          Bf[kk] = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
           if constexpr (kSplit) {
-            const Frag<T> Al = lds_frag<T, KORD_CONTIG>(&Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
-            const Frag<T> Bl = lds_frag<T, KORD_CONTIG>(&Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
-            mma(acc, A, Bl);
-            mma(acc, Al, B);
+            Alf[kk] = lds_frag<T, KORD_CONTIG>(&Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
+            Blf[kk] = lds_frag<T, KORD_CONTIG>(&Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          mma(acc, Af[kk], Bf[kk]);
+          if constexpr (kSplit) {
+            mma(acc, Af[kk], Blf[kk]);
+            mma(acc, Alf[kk], Bf[kk]);
           }
         }
         const int i = 16 * ti + l16;
@@ -291,12 +302,13 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
       for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const Frag<T> A = acc_frag<T>(Sacc[2 * kk], Sacc[2 * kk + 1]);
+        Frag<T> Bq[4];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          const Frag<T> B = lds_frag<T, KORD_ACC>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
-          mma(O[ti], A, B);
-        }
+        for (int ti = 0; ti < 4; ++ti) Bq[ti] = lds_frag<T, KORD_ACC>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
+        const Frag<T> A = acc_frag<T>(Sacc[2 * kk], Sacc[2 * kk + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) mma(O[ti], A, Bq[ti]);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -322,11 +334,19 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
       const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
       const Frag<T> Bv = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);  // V[t][own channel]
 #pragma unroll
-      for (int t = 0; t < NA; ++t) {
-        const Frag<T> Ak = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane);  // K^T rows 16t..
-        const Frag<T> Ap = tr_frag<T>(&sm.Kp[0][0], PQ, 32 * kk, 16 * t, lane);  // (K e^-B)^T
-        mma(Cacc[t], Ak, Bk);
-        mma(Sacc[t], Ap, Bv);
+      for (int t0_ = 0; t0_ < NA; t0_ += 4) {
+        Frag<T> Ak[4], Ap[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          Ak[u] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
+          Ap[u] = tr_frag<T>(&sm.Kp[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          mma(Cacc[t0_ + u], Ak[u], Bk);
+          mma(Sacc[t0_ + u], Ap[u], Bv);
+        }
       }
     }
 #pragma unroll

@@ -201,17 +201,16 @@ __device__ __forceinline__ void zero_tail(T (*dst)[PQ], int Lc, int tid, int nth
 }
 
 // Gate logit and m0 . q, then the row tile of P = Q K^T, its inclusive row sums and
-// Pm = tril(P - c 1^T), for the 16-token row tiles it = w, w + NW, ... < 4 (waves 0..3 at
-// d >= 64).  Writes sm.Pm and sm.tok[i] = {lambda_i, 1/n_i, sq_i / n_i^2, logit_i}; nb is
-// the number of tokens before the chunk.  Needs Qs, Ks, Wt staged; Pm rows must be zero
-// above the diagonal tiles.
-template <int D, typename T, typename SM>
+// Pm = tril(P - c 1^T), for the 16-token row tiles it = w, w + NWAVES, ... < 4.  Writes
+// sm.Pm and sm.tok[i] = {lambda_i, 1/n_i, sq_i / n_i^2, logit_i}; nb is the number of tokens
+// before the chunk.  Needs Qs, Ks, Wt staged; Pm rows must be zero above the diagonal tiles.
+template <int D, typename T, int NWAVES, typename SM>
 __device__ __forceinline__ void ccq_gram_rows(SM& sm, const T (*Ks)[Cfg<D, T>::PQ], int w, int lane, int64_t nb,
                                               float b_lam) {
   using C_ = Cfg<D, T>;
-  constexpr int NW = C_::NW, NK = C_::NK, PQ = C_::PQ;
+  constexpr int NK = C_::NK, PQ = C_::PQ;
   const int g = lane >> 4, l16 = lane & 15;
-  for (int it = w; it < 4; it += NW) {
+  for (int it = w; it < 4; it += NWAVES) {
     {
       f32x4 acc = zero4();  // [q] x [w_hi, w_lo, m0_hi, m0_lo]; B rows 4..15 are zero
 #pragma unroll
@@ -267,63 +266,84 @@ __device__ __forceinline__ void ccq_gram_rows(SM& sm, const T (*Ks)[Cfg<D, T>::P
   }
 }
 
-// R = Q C0 + tril(P - c 1^T) K for the wave's channels cw .. cw + 15 (C0 from the wave's
-// carry accumulators), then u and the cleaned query; stores qc_i * scale(ti, r) to Qa (and
-// its bf16 low part to Qalo when SPLIT) at token i = 16 ti + l16, channel cw + 4 g + r.
-// Needs Qs, Ks, Pm and tok from ccq_gram_rows.
-template <int D, typename T, bool SPLIT, typename SM, typename Scale>
-__device__ __forceinline__ void ccq_clean_query(SM& sm, const T (*Ks)[Cfg<D, T>::PQ], T (*Qalo)[Cfg<D, T>::PQ],
-                                                const f32x4* Cacc, int cw, int lane, Scale scale) {
+// R = Q C0 for the wave's NH 16-channel groups cw + 16 h .. + 15 (C0 from the wave's carry
+// accumulators: ctile(h, t) is the tile holding C[cw + 16 h + l16][16 t + 4 g + r]):
+// R[h][ti][r] at channel cw + 16 h + 4 g + r, token 16 ti + l16.  Needs only Qs, so it can run
+// beside ccq_gram_rows.  The Q fragments are read once for all NH groups.
+template <int D, typename T, int NH, typename SM, typename CTile>
+__device__ __forceinline__ void ccq_query_carry(SM& sm, CTile ctile, int lane, f32x4 (&R)[NH][4]) {
   using C_ = Cfg<D, T>;
-  constexpr int NK = C_::NK, PQ = C_::PQ, PT = C_::PT;
-  const int g = lane >> 4, l16 = lane & 15;
-  f32x4 R[4];
+  constexpr int NK = C_::NK, PQ = C_::PQ;
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti) R[ti] = zero4();
+  for (int h = 0; h < NH; ++h)
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) R[h][ti] = zero4();
 #pragma unroll
   for (int kk = 0; kk < NK; ++kk) {
-    const Frag<T> A = acc_frag<T>(Cacc[2 * kk], Cacc[2 * kk + 1]);
+    Frag<T> A[NH];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const Frag<T> B = lds_frag<T, KORD_ACC>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
-      mma(R[ti], A, B);
-    }
+    for (int h = 0; h < NH; ++h) A[h] = acc_frag<T>(ctile(h, 2 * kk), ctile(h, 2 * kk + 1));
+    Frag<T> Bq[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) Bq[ti] = lds_frag<T, KORD_ACC>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) mma(R[h][ti], A[h], Bq[ti]);
   }
+}
+
+// R += tril(P - c 1^T) K (R from ccq_query_carry), then u and the cleaned query; stores
+// qc_i * scale(h, ti, r) to Qa (and its bf16 low part to Qalo when SPLIT) at token
+// i = 16 ti + l16, channel cw + 16 h + 4 g + r.  Needs Qs, Ks, Pm and tok from ccq_gram_rows.
+template <int D, typename T, int NH, bool SPLIT, typename SM, typename Scale>
+__device__ __forceinline__ void ccq_clean_query(SM& sm, const T (*Ks)[Cfg<D, T>::PQ], T (*Qalo)[Cfg<D, T>::PQ],
+                                                f32x4 (&R)[NH][4], int cw, int lane, Scale scale) {
+  using C_ = Cfg<D, T>;
+  constexpr int PT = C_::PT, PQ = C_::PQ;
+  const int g = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    const Frag<T> A = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K^T, own rows
+    Frag<T> A[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) A[h] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw + 16 * h, lane);  // K^T, own rows
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       if (kk == 1 && ti < 2) continue;  // tokens 32..63 never precede tokens 0..31
       const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
-      mma(R[ti], A, B);
+#pragma unroll
+      for (int h = 0; h < NH; ++h) mma(R[h][ti], A[h], B);
     }
   }
-  // R[ti][r]: channel cw + 4 g + r, token 16 ti + l16
-  const int m = cw + 4 * g;
-  const f32x4 m04 = *reinterpret_cast<const f32x4*>(&sm.m0[m]);
+  // R[h][ti][r]: channel cw + 16 h + 4 g + r, token 16 ti + l16
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti) {
-    const int i = 16 * ti + l16;
-    const f32x4 ts = sm.tok[i];  // lambda, 1/n, sq/n^2
-    const f32x4 q4 = ld4<T>(&sm.Qs[i][m]);
-    f32x4 qa;
+  for (int h = 0; h < NH; ++h) {
+    const int m = cw + 16 * h + 4 * g;
+    const f32x4 m04 = *reinterpret_cast<const f32x4*>(&sm.m0[m]);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float u = R[ti][r] * ts[1] - m04[r] * ts[2];
-      qa[r] = (q4[r] - ts[0] * u) * scale(ti, r);
-    }
-    // bf16: hi + lo (the intra-chunk attention is a sum of few, possibly cancelling
-    // products when little of the sequence has been read)
-    if constexpr (SPLIT) {
-      const bf16x4 qh = to_bf16x4(qa);
-      *reinterpret_cast<bf16x4*>(&sm.Qa[i][m]) = qh;
-      f32x4 ql;
+    for (int ti = 0; ti < 4; ++ti) {
+      const int i = 16 * ti + l16;
+      const f32x4 ts = sm.tok[i];  // lambda, 1/n, sq/n^2
+      const f32x4 q4 = ld4<T>(&sm.Qs[i][m]);
+      f32x4 qa;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ql[r] = qa[r] - (float)qh[r];
-      st4<T>(&Qalo[i][m], ql);
-    } else {
-      st4<T>(&sm.Qa[i][m], qa);
+      for (int r = 0; r < 4; ++r) {
+        const float u = R[h][ti][r] * ts[1] - m04[r] * ts[2];
+        qa[r] = (q4[r] - ts[0] * u) * scale(h, ti, r);
+      }
+      // bf16: hi + lo (the intra-chunk attention is a sum of few, possibly cancelling
+      // products when little of the sequence has been read)
+      if constexpr (SPLIT) {
+        const bf16x4 qh = to_bf16x4(qa);
+        *reinterpret_cast<bf16x4*>(&sm.Qa[i][m]) = qh;
+        f32x4 ql;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ql[r] = qa[r] - (float)qh[r];
+        st4<T>(&Qalo[i][m], ql);
+      } else {
+        st4<T>(&sm.Qa[i][m], qa);
+      }
     }
   }
 }

@@ -33,7 +33,7 @@ template <int D, typename T>
 struct GdnSmem {
   using C_ = Cfg<D, T>;
   T Qs[kL][C_::PQ];        // q rows
-  T Ks[kL][C_::PQ];        // k rows
+  T Ks[2][kL][C_::PQ];     // k rows of chunk c in Ks[c % 2]; the other half receives chunk c + 1
   T Vs[kL][C_::PQ];        // v rows
   T Qa[kL][C_::PQ];        // cleaned query (hi part for bf16)
   T Qalo[C_::LO][C_::PQ];  // bf16 only: lo part of the cleaned query
@@ -56,8 +56,6 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int cw = 16 * w;        // this wave's 16 channels
-  const int hb = w & 1;         // which half of its 32-channel block
-  const int cb = cw - 16 * hb;  // first channel of the block
   const int chain = blockIdx.x;
   const int h = chain % a.H;
   const int nchunks = (a.T + kL - 1) / kL;
@@ -95,49 +93,40 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   }
   for (int e = tid; e < kL * PT; e += 64 * NW) (&sm.Pm[0][0])[e] = (T)0.f;
 
-  // ---- register prefetch of one chunk: q and k rows (first wave of each pair), v rows
-  // (second wave); wave 1 also takes the per-token log alpha and beta (lane = token).
-  // Rows past the end of the sequence are zero (beta = 0 makes their deltas zero).
-  Frag<T> fa[4], fb[4];
+  // ---- chunk tiles go straight from HBM to LDS (no registers involved): k of the next chunk
+  // at the start of a chunk (it has its own buffer), q and v once the cleaned query and X
+  // are formed.  Wave 1 keeps the per-token log alpha and beta of the next chunk in registers
+  // (lane = token).  Rows past the end of the sequence are zeroed (beta = 0 then makes their
+  // deltas zero).
+  auto chunk_len = [&](int c) { return min(kL, a.T - c * kL); };
+  auto dma_rows = [&](T (*dst)[PQ], const T* src, int c) {
+    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, lane);
+  };
   float sg = 0.f, sb = 0.f;
-  auto prefetch = [&](int ch) {
-    const int t0 = ch * kL;
-    const int Lc = min(kL, a.T - t0);
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const int t = 16 * ti + l16;
-      const bool ok = t < Lc;
-      const size_t off = ok ? (tok0 + t0 + t) * D + cb + 8 * g : 0;
-      if (hb == 0) {
-        fa[ti] = gload_frag<T>(qg + off, ok);
-        fb[ti] = gload_frag<T>(kg + off, ok);
-      } else {
-        fa[ti] = gload_frag<T>(vg + off, ok);
-      }
-    }
+  auto load_gates = [&](int c) {
     if (w == 1) {
-      const bool ok = lane < Lc;
-      sg = ok ? ldf(gg, tok0 + t0 + lane) : 0.f;
-      sb = ok ? ldf(bg, tok0 + t0 + lane) : 0.f;
+      const bool ok = lane < chunk_len(c);
+      const size_t i = tok0 + (size_t)c * kL + (ok ? lane : 0);
+      const float x = ldf(gg, i), y = ldf(bg, i);
+      sg = ok ? x : 0.f;
+      sb = ok ? y : 0.f;
     }
   };
-  if (nchunks > 0) prefetch(0);
+  if (nchunks > 0) {
+    dma_rows(sm.Qs, qg, 0);
+    dma_rows(sm.Ks[0], kg, 0);
+    dma_rows(sm.Vs, vg, 0);
+    load_gates(0);
+  }
 
   for (int ch = 0; ch < nchunks; ++ch) {
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
+    T (*Ks)[PQ] = sm.Ks[ch & 1];
 
-    // ---- stage rows; chunk-local log gamma by an inclusive scan over the lanes of wave 1
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const int t = 16 * ti + l16;
-      if (hb == 0) {
-        st_frag<T>(&sm.Qs[t][cb + 8 * g], fa[ti]);
-        st_frag<T>(&sm.Ks[t][cb + 8 * g], fb[ti]);
-      } else {
-        st_frag<T>(&sm.Vs[t][cb + 8 * g], fa[ti]);
-      }
-    }
+    // ---- this chunk's tiles have landed; chunk-local log gamma by an inclusive scan over the
+    // lanes of wave 1; rows past the end of the sequence are zeroed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (w == 1) {
       float x = sg;
 #pragma unroll
@@ -149,10 +138,17 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
       sm.beta[lane] = sb;
     }
     lds_barrier();
+    if (Lc < kL) {
+      zero_tail<D, T, PQ>(sm.Qs, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(Ks, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(sm.Vs, Lc, tid, 64 * NW);
+      lds_barrier();
+    }
+    if (ch + 1 < nchunks) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1);
 
     // ---- gate and Gram rows (waves 0..3); A = beta Gam (K K^T) below the diagonal and the key
     // sums (the other waves at d = 128, all of them at d = 64)
-    ccq_gram_rows<D, T>(sm, sm.Ks, w, lane, nb, b_lam);
+    ccq_gram_rows<D, T, NW>(sm, Ks, w, lane, nb, b_lam);
     {
       constexpr int kw0 = (NW >= 8) ? 4 : 0, kws = NW - kw0;
       if (w >= kw0) {
@@ -161,8 +157,8 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
           f32x4 acc = zero4();  // k_j . k_i at j = 16 tj + 4 g + r, i = 16 ti + l16
 #pragma unroll
           for (int kk = 0; kk < NK; ++kk) {
-            const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
-            const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * ti, 32 * kk, lane);
+            const Frag<T> A = lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+            const Frag<T> B = lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * ti, 32 * kk, lane);
             mma(acc, A, B);
           }
           const int i = 16 * ti + l16, j0 = 16 * tj + 4 * g;
@@ -178,7 +174,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
         const int c = (tid - 2 * D) >> 1, half = tid & 1;
         float s = 0.f;
 #pragma unroll 8
-        for (int t = 32 * half; t < 32 * half + 32; ++t) s += to_f32(sm.Ks[t][c]);
+        for (int t = 32 * half; t < 32 * half + 32; ++t) s += to_f32(Ks[t][c]);
         s += __shfl_xor(s, 1, 64);
         if (half == 0) sm.m1[c] = sm.m0[c] + s;
       }
@@ -205,7 +201,9 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sm.Tb[blk][i][c] = tcol[i];
     }
-    ccq_clean_query<D, T, kSplit>(sm, sm.Ks, sm.Qalo, Cacc, cw, lane, [](int, int) { return 1.0f; });
+    f32x4 R[1][4];
+    ccq_query_carry<D, T, 1>(sm, [&](int, int t) -> const f32x4& { return Cacc[t]; }, lane, R);
+    ccq_clean_query<D, T, 1, kSplit>(sm, Ks, sm.Qalo, R, cw, lane, [](int, int, int) { return 1.0f; });
     f32x4 X[4];  // X[b][r] at token 16 b + 4 g + r, value channel cw + l16
 #pragma unroll
     for (int b = 0; b < 4; ++b) X[b] = zero4();
@@ -213,7 +211,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     for (int kk = 0; kk < NK; ++kk) {
       const Frag<T> Bs = acc_frag<T>(Sacc[2 * kk], Sacc[2 * kk + 1]);  // S0^T, own columns
 #pragma unroll
-      for (int b = 0; b < 4; ++b) mma(X[b], lds_frag<T, KORD_ACC>(&sm.Ks[0][0], PQ, 16 * b, 32 * kk, lane), Bs);
+      for (int b = 0; b < 4; ++b) mma(X[b], lds_frag<T, KORD_ACC>(&Ks[0][0], PQ, 16 * b, 32 * kk, lane), Bs);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -224,7 +222,11 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
       for (int r = 0; r < 4; ++r) X[b][r] = bt[r] * (to_f32(sm.Vs[j0 + r][cw + l16]) - __expf(lg[r]) * X[b][r]);
     }
     lds_barrier();
-    if (ch + 1 < nchunks) prefetch(ch + 1);
+    if (ch + 1 < nchunks) {  // q and v of this chunk are no longer read
+      dma_rows(sm.Qs, qg, ch + 1);
+      dma_rows(sm.Vs, vg, ch + 1);
+      load_gates(ch + 1);
+    }
 
     // ---- M = tril(Qc K^T) * Gam on the lower tiles -> Pm; Delta on the wave's columns
     for (int idx = w; idx < 10; idx += NW) {
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
       f32x4 acc = zero4();  // qc_i . k_j at j = 16 tj + 4 g + r, i = 16 ti + l16
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        const Frag<T> A = lds_frag<T, KORD_CONTIG>(&sm.Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+        const Frag<T> A = lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
         mma(acc, A, lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane));
         if constexpr (kSplit) mma(acc, A, lds_frag<T, KORD_CONTIG>(&sm.Qalo[0][0], PQ, 16 * ti, 32 * kk, lane));
       }
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     for (int t = 0; t < NA; ++t) Sacc[t] *= gL;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const Frag<T> Bk = tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
+      const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
       f32x4 d0 = Dl[2 * kk], d1 = Dl[2 * kk + 1];
       const f32x4 lg0 = *reinterpret_cast<const f32x4*>(&sm.lgam[32 * kk + 4 * g]);
       const f32x4 lg1 = *reinterpret_cast<const f32x4*>(&sm.lgam[32 * kk + 16 + 4 * g]);
@@ -307,8 +309,8 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
       const Frag<T> Bd = acc_frag<T>(d0, d1);  // diag(gamma_L / gamma) Delta, own columns
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
-        mma(Cacc[t], tr_frag<T>(&sm.Ks[0][0], PQ, 32 * kk, 16 * t, lane), Bk);
-        mma(Sacc[t], tr_frag_acc<T>(&sm.Ks[0][0], PQ, 32 * kk, 16 * t, lane), Bd);
+        mma(Cacc[t], tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane), Bk);
+        mma(Sacc[t], tr_frag_acc<T>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane), Bd);
       }
     }
     if (tid < D) {
