@@ -151,9 +151,10 @@ def time_prefill(wl, steps, warmup):
     phases = {name: float(np.mean([hip.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(steps)]))
               for a, name in enumerate(("summary", "scan", "main"))}
     hip.destroy()
-    # segments the library resolved: its workspace holds one (2 d^2 + 2 d) fp32 slot per
-    # (chain, segment) when there is more than one segment
-    segs = int(p.segments) if p.segments else (ws_bytes // (B * H * (2 * dk * dk + 2 * dk) * 4) or 1)
+    # segments the library resolved: its workspace holds one fp32 slot per (chain, segment)
+    # when there is more than one segment (GLA: S, C, ksum, log decay; GDN: S, C, ksum, M)
+    slot = (2 * dk * dk + 2 * dk) * 4 if spec["rule"] == "gla" else (3 * dk * dk + dk) * 4
+    segs = int(p.segments) if p.segments else (ws_bytes // (B * H * slot) or 1)
     return dict(spec=spec, shape=(B, H, T, dk, dv), total_ms=total_ms, per_ms=per, wall_s=t_wall,
                 dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs, phase_ms=phases)
 
@@ -394,13 +395,14 @@ def main(argv=None):
         g_ms = gres["total_ms"] / args.steps
         g_flops, g_bytes = prefill_work(gB, gH, gT, gd, 2, "gdn")
         g_main = gres["phase_ms"]["main"]
-        g_kbytes = main_kernel_bytes(gB, gH, gT, gd, 2, 1, "gdn")
+        g_kbytes = main_kernel_bytes(gB, gH, gT, gd, 2, gres["segments"] or 1, "gdn")
         g_gbs = g_kbytes / (g_main * 1e-3) / 1e9
         g_tf = g_flops / (g_main * 1e-3) / 1e12
         gsrc = file_sha(GDN_SRC)
         out["gdn"] = {
             "workload": gres["spec"]["name"], "ms_per_step": round(g_ms, 4),
-            "tokens_per_s": round(gB * gT / (g_ms * 1e-3), 1), "segments": 1,
+            "tokens_per_s": round(gB * gT / (g_ms * 1e-3), 1), "segments": gres["segments"],
+            "pass_ms": {k: round(v, 4) for k, v in gres["phase_ms"].items()},
             "roofline": dict(bound="hbm", achieved=round(g_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=round(g_gbs / HBM_PEAK_GBS, 4),
                              traffic=measured_traffic(f"traffic_{gres['spec']['name']}.json", gsrc),

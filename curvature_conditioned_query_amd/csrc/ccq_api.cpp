@@ -54,10 +54,6 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
   // Rounds the segment length up to whole chunks and drops empty trailing segments.
   int cps = (nchunks + seg - 1) / seg;
   seg = (nchunks + cps - 1) / cps;
-  if (p->rule == CCQ_RULE_GDN) {  // Gated DeltaNet: one segment per chain
-    seg = 1;
-    cps = nchunks;
-  }
   *segments_out = seg;
   *chunks_per_seg_out = cps;
   return CCQ_OK;
@@ -65,7 +61,8 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
 
 size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
   if (seg <= 1) return 0;
-  return (size_t)p->B * p->H * seg * ccq::fwd_slot_bytes(p->d_k);
+  const size_t slot = (p->rule == CCQ_RULE_GDN) ? ccq::gdn_slot_bytes(p->d_k) : ccq::fwd_slot_bytes(p->d_k);
+  return (size_t)p->B * p->H * seg * slot;
 }
 
 }  // namespace

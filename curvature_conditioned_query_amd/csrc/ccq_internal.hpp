@@ -36,10 +36,12 @@ struct FwdArgs {
   void* const* events;  // optional: 4 hipEvent_t around the kernels of the pass
 };
 
-// Bytes of one segment slot of the workspace (carry of one chain, plus the GLA decay).
+// Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
+// Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).
 size_t fwd_slot_bytes(int d);
+size_t gdn_slot_bytes(int d);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-// Gated DeltaNet prefill (one segment per chain).
+// Gated DeltaNet prefill.
 hipError_t launch_gdn(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace ccq

@@ -269,8 +269,9 @@ __device__ __forceinline__ void ccq_gram_rows(SM& sm, const T (*Ks)[Cfg<D, T>::P
 // R = Q C0 for the wave's NH 16-channel groups cw + 16 h .. + 15 (C0 from the wave's carry
 // accumulators: ctile(h, t) is the tile holding C[cw + 16 h + l16][16 t + 4 g + r]):
 // R[h][ti][r] at channel cw + 16 h + 4 g + r, token 16 ti + l16.  Needs only Qs, so it can run
-// beside ccq_gram_rows.  The Q fragments are read once for all NH groups.
-template <int D, typename T, int NH, typename SM, typename CTile>
+// beside ccq_gram_rows.  The Q fragments are read once for all NH groups (as one block ahead of
+// their MFMAs when BATCH).
+template <int D, typename T, int NH, bool BATCH = true, typename SM, typename CTile>
 __device__ __forceinline__ void ccq_query_carry(SM& sm, CTile ctile, int lane, f32x4 (&R)[NH][4]) {
   using C_ = Cfg<D, T>;
   constexpr int NK = C_::NK, PQ = C_::PQ;
@@ -286,7 +287,7 @@ __device__ __forceinline__ void ccq_query_carry(SM& sm, CTile ctile, int lane, f
     Frag<T> Bq[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) Bq[ti] = lds_frag<T, KORD_ACC>(&sm.Qs[0][0], PQ, 16 * ti, 32 * kk, lane);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (BATCH) __builtin_amdgcn_sched_barrier(0);  // the four reads go out together
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
