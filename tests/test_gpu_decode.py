@@ -76,3 +76,43 @@ def test_decode_lambda_zero_is_backbone(gpu_lib):
         tok["v"].astype(np.float64)[..., :, None] * tok["k"].astype(np.float64)[..., None, :]
     ref = np.einsum("nhvk,nhk->nhv", S_new, tok["q"].astype(np.float64))
     assert normwise_error(down(o), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("rule", ["gla", "gdn"])
+def test_decode_full_size_sampled(gpu_lib, rule):
+    """The benchmark's decode shape and launch (256 sequences x 16 heads, d = 128, bf16 token,
+    fp32 state, n = 8192).  Carries are built on the device and are consistent: 64 unit keys per
+    head, each counted 128 times (C = 128 sum k k^T, ksum = 128 sum k, n = 8192), S random.  One
+    step runs over every head; sampled heads are checked against the oracle step from the same
+    carry values."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_decode_step as gpu_step
+    N, H, d, reps, m_keys = 256, 16, 128, 128, 64
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    K = torch.randn((N, H, m_keys, d), generator=gen, device="cuda")
+    K = K / K.norm(dim=-1, keepdim=True)
+    C = (reps * (K.transpose(-1, -2).contiguous() @ K)).contiguous()
+    m = (reps * K.sum(dim=2)).contiguous()
+    n = torch.full((N, H), reps * m_keys, dtype=torch.int64, device="cuda")
+    S = (torch.randn((N, H, d, d), generator=gen, device="cuda") / np.sqrt(d)).contiguous()
+    del K
+    tok = decode_tokens(rule, N, H, d, 4243, "bf16")
+    sample = [(0, 0), (255, 15), (100, 7), (31, 3)]
+    before = {(i, h): tuple(t[i, h].double().cpu().numpy() for t in (S, C, m)) + (int(n[i, h]),) for i, h in sample}
+    o = gpu_step(rule, up(tok["q"], "bf16"), up(tok["k"], "bf16"), up(tok["v"], "bf16"), up(tok["g"], "bf16"),
+                 up(tok["beta"], "bf16"), torch.from_numpy(tok["w_lam"]).cuda(),
+                 torch.from_numpy(tok["b_lam"]).cuda(), S, C, m, n)
+    torch.cuda.synchronize()
+    assert bool(torch.all(n == reps * m_keys + 1))
+    for (i, h) in sample:
+        S0, C0, m0, n0 = before[(i, h)]
+        carry = Carry(S0[None, None], C0[None, None], m0[None, None], np.array([[n0]], np.int64))
+        pick = lambda a: None if a is None else a[i:i + 1, h:h + 1]  # noqa: E731
+        o_ref, ref = ccq_decode_step(pick(tok["q"]), pick(tok["k"]), pick(tok["v"]), pick(tok["g"]),
+                                     pick(tok["beta"]), tok["w_lam"][h:h + 1], tok["b_lam"][h:h + 1], rule, carry)
+        err = normwise_error(down(o[i:i + 1, h:h + 1]), o_ref)
+        print(f"decode full-size {rule} head ({i},{h}): o err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"]
+        assert normwise_error(down(S[i:i + 1, h:h + 1]), ref.S) <= STATE_TOL
+        assert normwise_error(down(C[i:i + 1, h:h + 1]), ref.C) <= STATE_TOL
+        assert normwise_error(down(m[i:i + 1, h:h + 1])[:, :, :, None], ref.m[:, :, :, None]) <= STATE_TOL
