@@ -344,19 +344,17 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     ccq_query_carry<D, T, 1, false>(sm, [&](int, int t) -> const f32x4& { return Cacc[t]; }, lane, R);
     lds_barrier();
 
-    // ---- inverses of the diagonal blocks (last wave), cleaned query, X = beta (V - gamma K S0^T)
+    // ---- inverses of the diagonal blocks (last wave), cleaned query
     if (w == NW - 1) gdn_diag_inverse<D, T>(sm, lane);
     ccq_clean_query<D, T, 1, kSplit>(sm, Ks, sm.Qalo, R, cw, lane, [](int, int, int) { return 1.0f; });
+    lds_barrier();
+    if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);  // q of this chunk is no longer read
+
+    // ---- X = beta (V - gamma K S0^T) and Delta on the wave's columns; M = tril(Qc K^T) * Gam
+    // on the lower tiles -> Pm
     f32x4 X[4];
     gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, X);
-    lds_barrier();
-    if (ch + 1 < cend) {  // q and v of this chunk are no longer read
-      dma_rows(sm.Qs, qg, ch + 1);
-      dma_rows(sm.Vs, vg, ch + 1);
-      load_gates(ch + 1);
-    }
 
-    // ---- M = tril(Qc K^T) * Gam on the lower tiles -> Pm; Delta on the wave's columns
     for (int idx = w; idx < 10; idx += NW) {
       const int ti = tri_row(idx), tj = tri_col(idx);
       f32x4 acc = zero4();  // qc_i . k_j at j = 16 tj + 4 g + r, i = 16 ti + l16
@@ -377,6 +375,10 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     f32x4 Dl[4];  // Delta[b][r] at token 16 b + 4 g + r, value channel cw + l16 (fp32)
     gdn_solve<D, T>(sm, X, lane, Dl);
     lds_barrier();
+    if (ch + 1 < cend) {  // v of this chunk is no longer read
+      dma_rows(sm.Vs, vg, ch + 1);
+      load_gates(ch + 1);
+    }
 
     // ---- O^T for the wave's 16 value rows: gamma * S0 Qc^T + Delta^T M^T
     f32x4 O[4];
@@ -544,57 +546,73 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
 
 // S part, in fp32: slot p holds dS_p and M_p (p < P-1) and receives S_in[p] (p <= P-1):
 //   S_in[0] = S0 (or 0),  S_in[p+1] = S_in[p] M_p + dS_p.
-// Workgroup (16-row block rb of S, chain); thread (row = tid / 16, column group tid % 16)
-// computes columns tid % 16 + 16 j of its row.  M_p and the rows of S_in[p] are staged in LDS.
+// Workgroup (16-row block rb of S, chain), D/32 waves: wave w computes the two 16x16 output
+// tiles at columns 32 w .. 32 w + 31 with fp32 MFMAs (v_mfma_f32_16x16x4_f32, one K-slice of 4
+// per instruction), the A operand (rows of S_in[p]) and B operand (M_p) read from LDS, eight
+// K-slices of operands at a time.  The running rows live in the accumulators: lane (g, l)
+// holds rows 4 g + r, column n0 + 16 t + l.
 template <int D>
-__global__ __launch_bounds__(256) void gdn_scan_state_kernel(FwdArgs a) {
-  constexpr int NJ = D / 16;
-  __shared__ float Ms[D][D + 1];
-  __shared__ __attribute__((aligned(16))) float Rs[16][D];
+__global__ __launch_bounds__(2 * D) void gdn_scan_state_kernel(FwdArgs a) {
+  constexpr int NT = 2 * D, KB = 8;
+  __shared__ float Ss[16][D + 4];
+  __shared__ float Ms[D][D + 4];
   const int rb = blockIdx.x, chain = blockIdx.y, tid = threadIdx.x;
-  const int row = tid >> 4, c0 = tid & 15;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int P = a.segments;
   const size_t slot_f = gdn_slot_floats(D);
   float* base = static_cast<float*>(a.workspace) + (size_t)chain * P * slot_f;
-  const int srow = 16 * rb + row;
-  float run[NJ];
+  const int n0 = 32 * w;
+  auto elem = [&](int t, int r) { return (size_t)(16 * rb + 4 * g + r) * D + n0 + 16 * t + l16; };
+  f32x4 run[2];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    run[j] = (a.S0 != nullptr) ? a.S0[(size_t)chain * D * D + (size_t)srow * D + c0 + 16 * j] : 0.f;
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) run[t][r] = (a.S0 != nullptr) ? a.S0[(size_t)chain * D * D + elem(t, r)] : 0.f;
   for (int p = 0; p < P; ++p) {
     float* slot = base + (size_t)p * slot_f;
-    float d[NJ];
+    f32x4 dS[2];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) d[j] = (p < P - 1) ? slot[(size_t)srow * D + c0 + 16 * j] : 0.f;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) slot[(size_t)srow * D + c0 + 16 * j] = run[j];
+      for (int r = 0; r < 4; ++r) {
+        dS[t][r] = (p < P - 1) ? slot[elem(t, r)] : 0.f;
+        slot[elem(t, r)] = run[t][r];
+      }
     if (p == P - 1) break;
-    const float* M = slot + 2 * (size_t)D * D + D;
     // M_p: every load in flight before the first LDS store
-    constexpr int NV = D * D / 4 / 256;  // float4 per thread
+    constexpr int NV = D * D / 4 / NT;
+    const float* M = slot + 2 * (size_t)D * D + D;
     f32x4 mv[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) mv[i] = *reinterpret_cast<const f32x4*>(M + 4 * (size_t)(tid + 256 * i));
-    __syncthreads();  // the previous step's reads of Ms and Rs are done
+    for (int v = 0; v < NV; ++v) mv[v] = *reinterpret_cast<const f32x4*>(M + 4 * (size_t)(tid + NT * v));
+    __syncthreads();  // the previous step's reads of Ss and Ms are done
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = 4 * (tid + 256 * i);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ms[(e + r) / D][(e + r) % D] = mv[i][r];
+    for (int v = 0; v < NV; ++v) {
+      const int e = 4 * (tid + NT * v);
+      *reinterpret_cast<f32x4*>(&Ms[e / D][e % D]) = mv[v];
     }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) Rs[row][c0 + 16 * j] = run[j];
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ss[4 * g + r][n0 + 16 * t + l16] = run[t][r];
     __syncthreads();
-    // NJ independent accumulators; the row of S_in[p] is read four columns at a time
+    run[0] = dS[0];
+    run[1] = dS[1];
+    for (int k0 = 0; k0 < D / 4; k0 += KB) {
+      float av[KB], b0[KB], b1[KB];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) run[j] = d[j];
-#pragma unroll 4
-    for (int k = 0; k < D; k += 4) {
-      const f32x4 r4 = *reinterpret_cast<const f32x4*>(&Rs[row][k]);
+      for (int u = 0; u < KB; ++u) {
+        const int kk = k0 + u;
+        av[u] = Ss[l16][4 * kk + g];
+        b0[u] = Ms[4 * kk + g][n0 + l16];
+        b1[u] = Ms[4 * kk + g][n0 + 16 + l16];
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) run[j] = fmaf(r4[e], Ms[k + e][c0 + 16 * j], run[j]);
+      for (int u = 0; u < KB; ++u) {
+        run[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], b0[u], run[0], 0, 0, 0);
+        run[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], b1[u], run[1], 0, 0, 0);
+      }
     }
   }
 }
@@ -632,7 +650,7 @@ static hipError_t launch_gdn_t(const FwdArgs& a, hipStream_t s) {
   if (P > 1) {
     hipLaunchKernelGGL((gdn_summary_kernel<D, T>), dim3((unsigned)(chains * (P - 1))), dim3(4 * D), 0, s, a);
     if (rec(1) != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL((gdn_scan_state_kernel<D>), dim3(D / 16, (unsigned)chains), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gdn_scan_state_kernel<D>), dim3(D / 16, (unsigned)chains), dim3(2 * D), 0, s, a);
     hipLaunchKernelGGL((gdn_scan_sum_kernel<D>), dim3((unsigned)((D * D + D + 255) / 256), (unsigned)chains), dim3(256),
                        0, s, a);
   } else if (rec(1) != hipSuccess) {
