@@ -26,6 +26,7 @@ __all__ = [
     "Carry",
     "sigmoid",
     "key_covariance",
+    "unit_keys",
     "ccq_recurrent",
     "ccq_chunked",
     "ccq_decode_step",
@@ -78,6 +79,18 @@ def key_covariance(K: np.ndarray) -> np.ndarray:
     mu = K.sum(axis=0) / t
     Cbar = K.T @ K / t
     return Cbar - np.outer(mu, mu)
+
+
+def unit_keys(k, eps: float = 1e-12) -> np.ndarray:
+    """Keys scaled to unit L2 norm along the last axis, k / max(|k|, eps), in fp64.
+
+    Unit keys are the precondition of the method's eigenvalue bound (10100.com write-up,
+    section "方法解析"); when a caller asks the library to normalise, this is the definition
+    it is held to (the eps floor, which keeps an all-zero key at zero, is this library's
+    reading: the pages are silent on it)."""
+    k = np.asarray(k, dtype=f64)
+    nrm = np.sqrt(np.sum(k * k, axis=-1, keepdims=True))
+    return k / np.maximum(nrm, eps)
 
 
 def _as64(x):

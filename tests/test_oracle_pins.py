@@ -19,7 +19,7 @@ from scipy.special import expit
 from curvature_conditioned_query_amd.inputs import (bf16_bits, bf16_round, gdn_inputs, gla_inputs,
                                                     structured_inputs)
 from oracle import (Carry, ccq_chunked, ccq_decode_step, ccq_recurrent, gla_closed_form_carry,
-                    key_covariance, normwise_error)
+                    key_covariance, normwise_error, unit_keys)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
 
@@ -371,3 +371,23 @@ def test_generators_are_seeded_and_unit_keys():
     assert np.all(np.abs(np.linalg.norm(f.k.astype(np.float64), axis=-1) - 1) < 1e-6)
     gd = gdn_inputs(1, 2, 16, 8, 5, "f32")
     assert np.all((gd.beta > 0) & (gd.beta < 1)) and np.all(gd.g < 0)
+
+
+def test_unit_keys_definition():
+    """unit_keys: norm 1 along the last axis, direction kept, zero key stays zero, invariant to a
+    positive rescale, idempotent -- pinned without re-typing the formula."""
+    rng = np.random.default_rng(31)
+    k = rng.standard_normal((2, 3, 5, 16)) * rng.uniform(0.1, 7.0, size=(2, 3, 5, 1))
+    k[0, 1, 2] = 0.0
+    u = unit_keys(k)
+    n = np.linalg.norm(u, axis=-1)
+    mask = np.ones_like(n, dtype=bool)
+    mask[0, 1, 2] = False
+    assert np.allclose(n[mask], 1.0, atol=1e-14)
+    assert np.array_equal(u[0, 1, 2], np.zeros(16))
+    cos = np.sum(u * k, axis=-1)[mask] / np.linalg.norm(k, axis=-1)[mask]
+    assert np.allclose(cos, 1.0, atol=1e-14)  # same direction
+    assert np.allclose(unit_keys(3.5 * k), u, atol=1e-15)
+    assert np.allclose(unit_keys(u), u, atol=1e-15)
+    # a hand case: (3, 4) -> (0.6, 0.8)
+    assert np.allclose(unit_keys(np.array([3.0, 4.0])), [0.6, 0.8], atol=1e-15)
