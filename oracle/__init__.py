@@ -35,4 +35,5 @@ from .ccq import (  # noqa: F401
     key_covariance,
     normwise_error,
     sigmoid,
+    unit_keys,
 )
