@@ -54,6 +54,7 @@ class FwdParams(ctypes.Structure):
         ("n_out", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("phase_events", ctypes.c_void_p),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -78,7 +79,7 @@ def load_library():
     lib.ccq_fwd_chunked.restype = ctypes.c_int
     lib.ccq_fwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdParams)]
     lib.ccq_fwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.ccq_decode_step.argtypes = [i32, i32, i32, i32, i32, i32] + [vp] * 13
+    lib.ccq_decode_step.argtypes = [i32, i32, i32, i32, i32, i32] + [vp] * 12 + [i32, vp]
     lib.ccq_decode_step.restype = ctypes.c_int
     lib.ccq_status_string.argtypes = [i32]
     lib.ccq_status_string.restype = ctypes.c_char_p
@@ -134,9 +135,12 @@ def _rule_code(rule) -> int:
     raise ValueError(f"unknown rule {rule!r}")
 
 
+FLAG_NORMALIZE_KEYS = 1  # CCQ_FLAG_NORMALIZE_KEYS
+
+
 def make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
                     carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
-                    workspace=None) -> FwdParams:
+                    workspace=None, normalize_keys: bool = False) -> FwdParams:
     """Fill a ccq_fwd_params from tensors (carry_in / carry_out: (S, C, ksum, n) or None)."""
     import torch
     B, H, T, d_k = q.shape
@@ -147,6 +151,7 @@ def make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
     p.B, p.H, p.T, p.d_k, p.d_v = B, H, T, d_k, d_v
     p.chunk = chunk
     p.segments = segments
+    p.flags = FLAG_NORMALIZE_KEYS if normalize_keys else 0
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta), ("o", o)):
         _check_dev(name, t, q.dtype)
     _check_dev("w_lambda", w_lambda, torch.float32)
@@ -178,16 +183,17 @@ def ccq_fwd_workspace_bytes(p: FwdParams) -> int:
 
 def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
                     carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
-                    workspace=None, stream=None, phase_events=None):
+                    workspace=None, stream=None, phase_events=None, normalize_keys: bool = False):
     """Chunked CCQ prefill through the C ABI.  Allocates o (and the workspace if not
     given) with torch; returns o.  ``phase_events``: optional ctypes array of 4 hipEvent_t
-    handles recorded around the kernels of the pass."""
+    handles recorded around the kernels of the pass.  ``normalize_keys``: the kernels scale
+    every key to unit L2 norm first (CCQ_FLAG_NORMALIZE_KEYS)."""
     import torch
     lib = load_library()
     if o is None:
         o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     p = make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
-                        carry_in, carry_out, segments, chunk, workspace)
+                        carry_in, carry_out, segments, chunk, workspace, normalize_keys)
     if workspace is None:
         nbytes = int(lib.ccq_fwd_workspace_bytes(ctypes.byref(p)))
         if nbytes:
@@ -203,8 +209,9 @@ def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
 
 
 def ccq_decode_step(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n,
-                    o=None, stream=None):
-    """One in-place decode step through the C ABI; returns o [N, H, d_v]."""
+                    o=None, stream=None, normalize_keys: bool = False):
+    """One in-place decode step through the C ABI; returns o [N, H, d_v].  ``normalize_keys``:
+    the kernel scales the key to unit L2 norm first (CCQ_FLAG_NORMALIZE_KEYS)."""
     import torch
     lib = load_library()
     N, H, d_k = q.shape
@@ -220,7 +227,7 @@ def ccq_decode_step(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ks
     st = lib.ccq_decode_step(_rule_code(rule), _dtype_code(q), N, H, d_k, d_v,
                              _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                              _ptr(w_lambda), _ptr(b_lambda), _ptr(S), _ptr(C), _ptr(ksum), _ptr(n),
-                             _ptr(o), _stream_handle(stream))
+                             _ptr(o), FLAG_NORMALIZE_KEYS if normalize_keys else 0, _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_decode_step")
     return o

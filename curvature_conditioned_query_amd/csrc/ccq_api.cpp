@@ -29,6 +29,7 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
   if (p->dtype != CCQ_DTYPE_F32 && p->dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
   if (p->B <= 0 || p->H <= 0 || p->T <= 0 || p->d_k <= 0 || p->d_v <= 0) return CCQ_ERR_INVALID_ARG;
   if (p->chunk < 0 || p->segments < 0) return CCQ_ERR_INVALID_ARG;
+  if (p->flags & ~CCQ_FLAG_NORMALIZE_KEYS) return CCQ_ERR_INVALID_ARG;
   if (p->chunk != 0 && p->chunk != kChunk) return CCQ_ERR_UNSUPPORTED;
   if (p->d_k != p->d_v || !supported_d(p->dtype, p->d_k)) return CCQ_ERR_UNSUPPORTED;
   if (!p->q || !p->k || !p->v || !p->log_alpha || !p->w_lambda || !p->b_lambda || !p->o)
@@ -69,7 +70,7 @@ size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 2; }
+int32_t ccq_abi_version(void) { return 3; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -122,6 +123,7 @@ int ccq_fwd_chunked(const ccq_fwd_params* p, void* hip_stream) {
   a.n_out = p->n_out;
   a.workspace = p->workspace;
   a.events = p->phase_events;
+  a.flags = p->flags;
   const hipError_t e = ccq::launch_fwd(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }
@@ -129,10 +131,11 @@ int ccq_fwd_chunked(const ccq_fwd_params* p, void* hip_stream) {
 int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v, const void* q,
                     const void* k, const void* v, const void* log_alpha, const void* beta, const float* w_lambda,
                     const float* b_lambda, float* S, float* C, float* ksum, int64_t* n, void* o,
-                    void* hip_stream) {
+                    int32_t flags, void* hip_stream) {
   if (rule != CCQ_RULE_GLA && rule != CCQ_RULE_GDN) return CCQ_ERR_INVALID_ARG;
   if (dtype != CCQ_DTYPE_F32 && dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
   if (N <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return CCQ_ERR_INVALID_ARG;
+  if (flags & ~CCQ_FLAG_NORMALIZE_KEYS) return CCQ_ERR_INVALID_ARG;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return CCQ_ERR_UNSUPPORTED;
   if ((long long)N * H > 0x7fffffffLL) return CCQ_ERR_UNSUPPORTED;
   if (!q || !k || !v || !log_alpha || !w_lambda || !b_lambda || !S || !C || !ksum || !n || !o)
@@ -141,7 +144,7 @@ int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d
   const void* ptrs[] = {q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, o};
   for (const void* pp : ptrs)
     if (misaligned(pp)) return CCQ_ERR_MISALIGNED;
-  ccq::DecodeArgs a{rule, dtype, N, H, d_k, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, o};
+  ccq::DecodeArgs a{rule, dtype, N, H, d_k, flags, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, o};
   const hipError_t e = ccq::launch_decode(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }

@@ -22,7 +22,7 @@
 
 namespace ccq {
 
-template <int D, typename T, int RULE, int NT>
+template <int D, typename T, int RULE, int NT, bool NORM>
 __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
   constexpr int C4 = D / 4;       // float4 per row
   constexpr int RPI = NT / C4;    // rows covered per iteration
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
   const int row0 = tid / C4;
 
   __shared__ float q_s[D], k_s[D], v_s[D], al_s[D], kn_s[D], r_s[D], qt_s[D];
-  __shared__ float part[2][NWV];  // per-wave partial w . q and ksum_new . q
+  __shared__ float part[3][NWV];  // per-wave partial w . q, ksum_new . q and (NORM) k . k
   __shared__ float nf_s;
 
   // ---- per-token operands first (every thread loads; threads past d repeat an index)
@@ -64,7 +64,19 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
   for (int i = 0; i < IT; ++i) sr[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sg + (size_t)(row0 + i * RPI) * D + 4 * col4));
   // nothing that uses the operands above may be scheduled before the state loads are issued
   __builtin_amdgcn_sched_barrier(0);
-  const float qv = to_f32(qraw), kv = to_f32(kraw), vv = to_f32(vraw);
+  const float qv = to_f32(qraw), vv = to_f32(vraw);
+  float kv = to_f32(kraw);
+  if constexpr (NORM) {  // k / max(|k|, 1e-12), the d-long sum reduced per wave and from LDS
+    if (tid < D) {
+      const float pk = group_sum<64>(kv * kv);
+      if ((tid & 63) == 0) part[2][tid >> 6] = pk;
+    }
+    lds_barrier();
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWV; ++v) ss += part[2][v];
+    kv *= __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+  }
   float alpha_s = 1.f, beta_s = 0.f;
   if constexpr (RULE == 1) {
     alpha_s = __expf(to_f32(graw));
@@ -159,10 +171,18 @@ template <int D, typename T>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t s) {
   constexpr int NT = 8 * D;  // 1024 threads at d = 128: 4 float4 of C and of S per thread
   const dim3 grid((unsigned)(a.N * a.H)), block(NT);
-  if (a.rule == 0)
-    hipLaunchKernelGGL((decode_kernel<D, T, 0, NT>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, T, 1, NT>), grid, block, 0, s, a);
+  const bool norm = (a.flags & kFlagNormalizeKeys) != 0;
+  if (a.rule == 0) {
+    if (norm)
+      hipLaunchKernelGGL((decode_kernel<D, T, 0, NT, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, T, 0, NT, false>), grid, block, 0, s, a);
+  } else {
+    if (norm)
+      hipLaunchKernelGGL((decode_kernel<D, T, 1, NT, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, T, 1, NT, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -8,7 +8,7 @@
 namespace ccq {
 
 struct DecodeArgs {
-  int rule, dtype, N, H, d;
+  int rule, dtype, N, H, d, flags;
   const void *q, *k, *v, *log_alpha, *beta;
   const float *w_lambda, *b_lambda;
   float *S, *C, *ksum;
@@ -34,7 +34,10 @@ struct FwdArgs {
   int64_t* n_out;
   void* workspace;
   void* const* events;  // optional: 4 hipEvent_t around the kernels of the pass
+  int flags;             // ccq_flag bits
 };
+
+constexpr int kFlagNormalizeKeys = 1;
 
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).

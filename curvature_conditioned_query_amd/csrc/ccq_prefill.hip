@@ -184,6 +184,10 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
       zero_tail<D, T, PQ>(Vs, Lc, tid, 64 * NW);
       lds_barrier();
     }
+    if (a.flags & kFlagNormalizeKeys) {
+      normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
+      lds_barrier();
+    }
     if constexpr (!kSplit) {
       if (ch + 1 < cend) {
         dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);

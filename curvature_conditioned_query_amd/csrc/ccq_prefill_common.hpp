@@ -200,6 +200,29 @@ __device__ __forceinline__ void zero_tail(T (*dst)[PQ], int Lc, int tid, int nth
   for (int e = tid; e < (kL - Lc) * D; e += nthreads) dst[Lc + e / D][e % D] = (T)0.f;
 }
 
+// Scales rows 0..63 of an LDS key tile to unit L2 norm, k / max(|k|, 1e-12) in fp32 (the
+// library-side normalisation asked for with the normalise-keys flag), 16 lanes per row.
+// Every thread of the workgroup takes part; rows of zeros stay zero.  The caller puts a
+// barrier after it.
+template <int D, typename T, int PQ>
+__device__ __forceinline__ void normalize_rows(T (*K)[PQ], int tid, int nthreads) {
+  constexpr int EPL = D / 16;  // elements per lane
+  const int sub = tid & 15;
+  for (int row = tid >> 4; row < kL; row += nthreads >> 4) {
+    float x[EPL];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      x[e] = to_f32(K[row][sub * EPL + e]);
+      ss += x[e] * x[e];
+    }
+    ss = group_sum<16>(ss);
+    const float inv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-24f));
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) K[row][sub * EPL + e] = (T)(x[e] * inv);
+  }
+}
+
 // Gate logit and m0 . q, then the row tile of P = Q K^T, its inclusive row sums and
 // Pm = tril(P - c 1^T), for the 16-token row tiles it = w, w + NWAVES, ... < 4.  Writes
 // sm.Pm and sm.tok[i] = {lambda_i, 1/n_i, sq_i / n_i^2, logit_i}; nb is the number of tokens

@@ -330,6 +330,10 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
       zero_tail<D, T, PQ>(sm.Vs, Lc, tid, 64 * NW);
       lds_barrier();
     }
+    if (a.flags & kFlagNormalizeKeys) {
+      normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
+      lds_barrier();
+    }
     if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1);
 
     // ---- gate and Gram rows (waves 0..3) and Q C0 (every wave); A = beta Gam (K K^T) below
@@ -499,6 +503,10 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (w == 1) gdn_gates<D, T>(sm, sg, sb, lane);
     lds_barrier();
+    if (a.flags & kFlagNormalizeKeys) {
+      normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
+      lds_barrier();
+    }
     if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1);
 
     gdn_build_A<D, T>(sm, Ks, w, NW, lane);

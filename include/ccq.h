@@ -30,9 +30,9 @@
  *   - Argument errors return a negative ccq_status BEFORE anything is enqueued.  A failed
  *     launch returns CCQ_ERR_LAUNCH.  Faults inside a kernel surface at the caller's next
  *     synchronisation; the library does not hide them.
- *   - Keys must already be L2-normalised (unit keys are the precondition of the eigenvalue
- *     bound eig(I - lambda Sigma) in [1 - lambda, 1], 10100.com write-up, section "方法解析").
- *     The library does not normalise them.
+ *   - Keys must be L2-normalised (unit keys are the precondition of the eigenvalue bound
+ *     eig(I - lambda Sigma) in [1 - lambda, 1], 10100.com write-up, section "方法解析"): either
+ *     by the caller, or by the library when CCQ_FLAG_NORMALIZE_KEYS is set.
  *   - Supported shapes: d_k == d_v, d in {64, 128} for CCQ_DTYPE_BF16, d == 64 for
  *     CCQ_DTYPE_F32; chunk == 64 (or 0, meaning 64).  Anything else is CCQ_ERR_UNSUPPORTED.
  */
@@ -59,6 +59,12 @@ typedef enum { CCQ_RULE_GLA = 0, CCQ_RULE_GDN = 1 } ccq_rule;
 
 /* Storage dtype of q, k, v, log_alpha, beta and o.  The carry is always fp32. */
 typedef enum { CCQ_DTYPE_F32 = 0, CCQ_DTYPE_BF16 = 1 } ccq_dtype;
+
+/* Option bits (ccq_fwd_params.flags, ccq_decode_step's flags).
+ * CCQ_FLAG_NORMALIZE_KEYS: the library scales every key to unit L2 norm, k / max(|k|, 1e-12)
+ * computed in fp32 from the stored key, before any use (statistics, gate, read and write).
+ * Without it keys are used as given and must already be unit vectors. */
+typedef enum { CCQ_FLAG_NORMALIZE_KEYS = 1 } ccq_flag;
 
 /* Arguments of ccq_fwd_chunked.  Zero-initialise, then fill in. */
 typedef struct {
@@ -99,6 +105,8 @@ typedef struct {
    * and after the main kernel.  With one segment the first three are recorded together,
    * just before the main kernel.  A failed record returns CCQ_ERR_LAUNCH. */
   void *const *phase_events;
+
+  int32_t flags;          /* ccq_flag bits; unknown bits are CCQ_ERR_INVALID_ARG            */
 } ccq_fwd_params;
 
 /*
@@ -124,17 +132,18 @@ size_t ccq_fwd_workspace_bytes(const ccq_fwd_params *p);
  * q, k: [N, H, d_k] dtype; v: [N, H, d_v] dtype; log_alpha: GLA [N, H, d_k] / GDN [N, H];
  * beta: GDN [N, H] (GLA: NULL); w_lambda [H, d_k], b_lambda [H] fp32;
  * S [N, H, d_v, d_k], C [N, H, d_k, d_k], ksum [N, H, d_k] fp32 and n [N, H] int64 are
- * read and written in place; o [N, H, d_v] dtype is written.  Returns a ccq_status.
+ * read and written in place; o [N, H, d_v] dtype is written.  flags: ccq_flag bits.
+ * Returns a ccq_status.
  */
 int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                     const void *q, const void *k, const void *v, const void *log_alpha,
                     const void *beta, const float *w_lambda, const float *b_lambda, float *S,
-                    float *C, float *ksum, int64_t *n, void *o, void *hip_stream);
+                    float *C, float *ksum, int64_t *n, void *o, int32_t flags, void *hip_stream);
 
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int32_t ccq_abi_version(void);
 
 #ifdef __cplusplus

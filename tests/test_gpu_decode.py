@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from curvature_conditioned_query_amd.inputs import decode_tokens, gdn_inputs, gla_inputs, structured_inputs
-from oracle import Carry, ccq_decode_step, ccq_recurrent, normwise_error
+from oracle import Carry, ccq_decode_step, ccq_recurrent, normwise_error, unit_keys
 
 from gpu_util import down, up, up_carry
 
@@ -116,3 +116,33 @@ def test_decode_full_size_sampled(gpu_lib, rule):
         assert normwise_error(down(S[i:i + 1, h:h + 1]), ref.S) <= STATE_TOL
         assert normwise_error(down(C[i:i + 1, h:h + 1]), ref.C) <= STATE_TOL
         assert normwise_error(down(m[i:i + 1, h:h + 1])[:, :, :, None], ref.m[:, :, :, None]) <= STATE_TOL
+
+
+@pytest.mark.parametrize("rule", ["gla", "gdn"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_normalize_keys_flag(gpu_lib, rule, dtype):
+    """Raw key (any scale, one all-zero) with the normalise-keys flag == oracle step on the unit key."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_decode_step as gpu_step
+    N, H, d = 3, 2, 128
+    carry = _prefix_carry(rule, N, H, d, 29, 901)
+    (S, C, m, n), (S64, C64, m64, n64) = up_carry(carry)
+    tok = decode_tokens(rule, N, H, d, 902, dtype)
+    rng = np.random.default_rng(903)
+    k_raw = (tok["k"] * rng.uniform(0.05, 20.0, size=(N, H, 1))).astype(np.float32)
+    k_raw[2, 1] = 0.0
+    if dtype == "bf16":
+        from curvature_conditioned_query_amd.inputs import bf16_round
+        k_raw = bf16_round(k_raw)
+    o = gpu_step(rule, up(tok["q"], dtype), up(k_raw, dtype), up(tok["v"], dtype), up(tok["g"], dtype),
+                 up(tok["beta"], dtype), torch.from_numpy(tok["w_lam"]).cuda(),
+                 torch.from_numpy(tok["b_lam"]).cuda(), S, C, m, n, normalize_keys=True)
+    torch.cuda.synchronize()
+    o_ref, ref = ccq_decode_step(tok["q"], unit_keys(k_raw), tok["v"], tok["g"], tok["beta"], tok["w_lam"],
+                                 tok["b_lam"], rule, Carry(S64, C64, m64, n64))
+    err = normwise_error(down(o), o_ref)
+    print(f"decode normalize-keys {rule} {dtype}: o err {err:.3e}", flush=True)
+    assert err <= TOL[dtype]
+    # fp32 state: the bf16 key is normalised in fp32 on both sides up to the oracle's fp64
+    assert normwise_error(down(C), ref.C) <= (STATE_TOL if dtype == "f32" else 1e-4)
+    assert normwise_error(down(S), ref.S) <= (STATE_TOL if dtype == "f32" else 1e-4)

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from curvature_conditioned_query_amd.inputs import gdn_inputs, gla_inputs, structured_inputs, workload_inputs
-from oracle import Carry, ccq_recurrent, normwise_error
+from oracle import Carry, ccq_recurrent, normwise_error, unit_keys
 
 from gpu_util import down, up, up_carry, upload_inputs
 
@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def gpu_prefill(x, segments=0, carry=None, want_carry=True, alias=False):
+def gpu_prefill(x, segments=0, carry=None, want_carry=True, alias=False, normalize_keys=False):
     """Run ccq_fwd_chunked on PrefillInputs x; returns (o, (S, C, ksum, n)) as numpy."""
     import torch
     from curvature_conditioned_query_amd import ccq_fwd_chunked
@@ -34,7 +34,7 @@ def gpu_prefill(x, segments=0, carry=None, want_carry=True, alias=False):
             cout = (torch.empty((B, H, dv, dk), device="cuda"), torch.empty((B, H, dk, dk), device="cuda"),
                     torch.empty((B, H, dk), device="cuda"), torch.empty((B, H), dtype=torch.int64, device="cuda"))
     o = ccq_fwd_chunked(x.rule, d["q"], d["k"], d["v"], d["g"], d["beta"], d["w"], d["b"],
-                        carry_in=cin, carry_out=cout, segments=segments)
+                        carry_in=cin, carry_out=cout, segments=segments, normalize_keys=normalize_keys)
     torch.cuda.synchronize()
     res = None if cout is None else tuple(down(t) for t in cout)
     return down(o), res
@@ -188,3 +188,26 @@ def test_full_size_workload_sampled(wl, chains):
         xs = x.slab(b, h)
         cs = tuple(a[b:b + 1, h:h + 1] for a in c)
         check(xs, o[b:b + 1, h:h + 1], cs, o_ref, c_ref, tag=f"workload{wl} chain ({b},{h})")
+
+
+@pytest.mark.parametrize("rule", ["gla", "gdn"])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_normalize_keys_flag(rule, dtype, d):
+    """With the normalise-keys flag the kernels take raw keys (any scale, some all-zero) and
+    must give the oracle's result on unit_keys(k)."""
+    gen = gla_inputs if rule == "gla" else gdn_inputs
+    x = gen(2, 2, 150, d, 321 + d, dtype)
+    rng = np.random.default_rng(77)
+    scale = rng.uniform(0.05, 20.0, size=x.k.shape[:-1] + (1,)).astype(np.float32)
+    k_raw = x.k * scale
+    k_raw[0, 1, 5] = 0.0
+    k_raw[1, 0, 70] = 0.0
+    if dtype == "bf16":
+        from curvature_conditioned_query_amd.inputs import bf16_round
+        k_raw = bf16_round(k_raw)
+    x.k = k_raw
+    o, c = gpu_prefill(x, segments=2, normalize_keys=True)
+    xr = gen(2, 2, 150, d, 321 + d, dtype)
+    xr.k = unit_keys(k_raw)
+    o_ref, c_ref = oracle(xr)
+    check(x, o, c, o_ref, c_ref, tag=f"normalize-keys {rule}")
