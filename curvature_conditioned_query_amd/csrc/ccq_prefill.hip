@@ -32,12 +32,12 @@
 //    straight from registers and never leaves them inside a chain;
 //  - every chunk tile sits in LDS row-major ([token][channel]); operands whose contraction
 //    runs over tokens (K^T, V^T, (K e^-B)^T) are read with the gfx950 transposing LDS read
-//    (ds_read_b64_tr_b16), so staging is plain 16-byte row writes;
-//  - the wave pair sharing a 32-channel block loads that block's rows of the next chunk
-//    (q and k for the first wave, v and log decay for the second) into registers while the
-//    current chunk is computed; the cumulative decay over tokens is an MFMA against a
-//    lower-triangular ones fragment, channel selection an MFMA against an identity fragment
-//    (exact: x * 1 + 0).
+//    (ds_read_b64_tr_b16), so no transposed copy is ever written;
+//  - the next chunk's q, k, v and log decay go straight from HBM to LDS
+//    (global_load_lds_dwordx4), each as soon as the buffer it lands in is free, so no
+//    registers hold prefetched rows;
+//  - the cumulative decay over tokens is an MFMA against a lower-triangular ones fragment,
+//    channel selection an MFMA against an identity fragment (exact: x * 1 + 0).
 #include "ccq_internal.hpp"
 #include "ccq_prefill_common.hpp"
 

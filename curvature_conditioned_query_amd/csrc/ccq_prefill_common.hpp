@@ -18,8 +18,6 @@ namespace ccq {
 
 constexpr int kL = 64;  // chunk length
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 template <int D, typename T>
 struct Cfg {
   static constexpr int NW = D / 16;          // waves per workgroup (16 channels each)
@@ -46,37 +44,6 @@ __device__ __forceinline__ f32x4 ld4(const T* p) {
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
   } else {
     return *reinterpret_cast<const f32x4*>(p);
-  }
-}
-
-// 8 elements of one row from global memory (16 bytes for bf16, 32 for fp32), or zeros.  The
-// load is always issued (p must be a valid address either way) and the zeros are selected
-// per lane afterwards, so no branch guards it.
-template <typename T>
-__device__ __forceinline__ Frag<T> gload_frag(const T* p, bool ok) {
-  Frag<T> f;
-  if constexpr (sizeof(T) == 2) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 x = *reinterpret_cast<const u32x4*>(p);
-    f.v = __builtin_bit_cast(bf16x8, ok ? x : z);
-  } else {
-    const f32x4 lo_ = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 hi_ = *reinterpret_cast<const f32x4*>(p + 4);
-    const f32x4 lo = ok ? lo_ : zero4();
-    const f32x4 hi = ok ? hi_ : zero4();
-#pragma unroll
-    for (int e = 0; e < 4; ++e) { f.v[e] = lo[e]; f.v[4 + e] = hi[e]; }
-  }
-  return f;
-}
-
-template <typename T>
-__device__ __forceinline__ void st_frag(T* p, const Frag<T>& f) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<bf16x8*>(p) = f.v;
-  } else {
-    *reinterpret_cast<f32x4*>(p) = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{f.v[4], f.v[5], f.v[6], f.v[7]};
   }
 }
 
