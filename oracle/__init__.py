@@ -34,6 +34,8 @@ from .ccq import (  # noqa: F401
     gla_closed_form_carry,
     key_covariance,
     normwise_error,
+    pack_upper,
     sigmoid,
     unit_keys,
+    unpack_upper,
 )

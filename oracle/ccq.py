@@ -32,6 +32,8 @@ __all__ = [
     "ccq_decode_step",
     "gla_closed_form_carry",
     "normwise_error",
+    "pack_upper",
+    "unpack_upper",
 ]
 
 f64 = np.float64
@@ -278,6 +280,36 @@ def gla_closed_form_carry(k, v, g) -> Carry:
     m = k.sum(axis=-2)
     n = np.full(k.shape[:2], T, dtype=np.int64)
     return Carry(S, C, m, n)
+
+
+def pack_upper(C) -> np.ndarray:
+    """Packed form of a symmetric [..., d, d] statistic: its upper triangle, row by row
+    (C[0][0..d-1], C[1][1..d-1], ..., C[d-1][d-1]), d (d + 1) / 2 entries.
+
+    The second-moment sum is the one state of the method that is symmetric (a sum of k k^T,
+    gist.science summary §2 "理论推导"); keeping one triangle is the compact statistic state
+    the 10100.com write-up's section "代价与边界" motivates by the memory the extra
+    d_k x d_k matrix costs at inference.  The row order is this library's reading: the pages
+    fix no layout."""
+    C = np.asarray(C)
+    d = C.shape[-1]
+    if C.shape[-2] != d:
+        raise ValueError("pack_upper takes square matrices")
+    iu, ju = np.triu_indices(d)
+    return C[..., iu, ju]
+
+
+def unpack_upper(p, d: int) -> np.ndarray:
+    """Inverse of ``pack_upper``: the symmetric [..., d, d] matrix whose upper triangle,
+    row by row, is p[..., :d (d + 1) / 2]."""
+    p = np.asarray(p)
+    if p.shape[-1] != d * (d + 1) // 2:
+        raise ValueError(f"a packed {d}x{d} triangle has {d * (d + 1) // 2} entries, got {p.shape[-1]}")
+    out = np.zeros(p.shape[:-1] + (d, d), dtype=p.dtype)
+    iu, ju = np.triu_indices(d)
+    out[..., iu, ju] = p
+    out[..., ju, iu] = p
+    return out
 
 
 def normwise_error(x, y) -> float:

@@ -32,6 +32,8 @@ MUTATIONS = {
                            "st.C = 0.9 * st.C + kt[..., :, None] * kt[..., None, :]"),
     "stats_skip_current_token": ("st.C = st.C + kt[..., :, None] * kt[..., None, :]\n        st.m = st.m + kt",
                                  "pass"),
+    "packed_lower_triangle": ("    iu, ju = np.triu_indices(d)\n    return C[..., iu, ju]",
+                              "    iu, ju = np.tril_indices(d)\n    return C[..., iu, ju]"),
 }
 
 
@@ -57,6 +59,11 @@ def _pins_hold(m) -> bool:
         for t in range(1, 7):
             if not np.allclose(rec["sigma"][0, 0, t - 1], np.cov(K[:t].T, bias=True), atol=1e-12):
                 return False
+        # packed statistic: the upper triangle row by row (hand case; C is symmetric, so the
+        # lower triangle row by row would give 1 2 4 3 5 6)
+        C3 = np.array([[1.0, 2.0, 3.0], [2.0, 4.0, 5.0], [3.0, 5.0, 6.0]])
+        if not np.array_equal(m.pack_upper(C3), [1.0, 2.0, 3.0, 4.0, 5.0, 6.0]):
+            return False
         # gate formula on the raw query
         x = gla_inputs(1, 1, 5, 4, 3, "f32")
         _, _, rec = m.ccq_recurrent(x.q, x.k, x.v, x.g, None, x.w_lam, x.b_lam, "gla", record=True)

@@ -19,7 +19,7 @@ from scipy.special import expit
 from curvature_conditioned_query_amd.inputs import (bf16_bits, bf16_round, gdn_inputs, gla_inputs,
                                                     structured_inputs)
 from oracle import (Carry, ccq_chunked, ccq_decode_step, ccq_recurrent, gla_closed_form_carry,
-                    key_covariance, normwise_error, unit_keys)
+                    key_covariance, normwise_error, pack_upper, unit_keys, unpack_upper)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
 
@@ -391,3 +391,42 @@ def test_unit_keys_definition():
     assert np.allclose(unit_keys(u), u, atol=1e-15)
     # a hand case: (3, 4) -> (0.6, 0.8)
     assert np.allclose(unit_keys(np.array([3.0, 4.0])), [0.6, 0.8], atol=1e-15)
+
+
+def test_pack_upper_layout():
+    """pack_upper: a hand case, the position of every entry against the closed-form offset of a
+    row-by-row upper triangle, the entry count, and the weighted-sum invariant (off-diagonal
+    entries stand for two matrix entries)."""
+    C3 = np.array([[1.0, 2.0, 3.0], [2.0, 4.0, 5.0], [3.0, 5.0, 6.0]])
+    assert np.array_equal(pack_upper(C3), [1.0, 2.0, 3.0, 4.0, 5.0, 6.0])
+    d = 7
+    # entry (i, j), i <= j, tagged by a value that names it
+    M = np.array([[100.0 * min(i, j) + max(i, j) for j in range(d)] for i in range(d)])
+    p = pack_upper(M)
+    assert p.shape == (d * (d + 1) // 2,)
+    for i in range(d):
+        for j in range(i, d):
+            off = i * d - i * (i - 1) // 2 + (j - i)
+            assert p[off] == 100.0 * i + j, (i, j, off)
+    rng = np.random.default_rng(41)
+    K = rng.standard_normal((2, 3, 20, 16))
+    C = np.swapaxes(K, -1, -2) @ K
+    pc = pack_upper(C)
+    diag = np.array([1.0 if i == j else 2.0 for i in range(16) for j in range(i, 16)])
+    assert np.allclose((pc * diag).sum(axis=-1), C.sum(axis=(-1, -2)), rtol=1e-13)
+
+
+def test_unpack_upper_round_trip():
+    """unpack_upper inverts pack_upper exactly on symmetric matrices (batched), returns a
+    symmetric matrix for any packed vector, and rejects a wrong length."""
+    rng = np.random.default_rng(42)
+    K = rng.standard_normal((3, 2, 40, 12)).astype(np.float32)
+    C = np.swapaxes(K, -1, -2) @ K
+    C = (C + np.swapaxes(C, -1, -2)) / 2
+    assert np.array_equal(unpack_upper(pack_upper(C), 12), C)
+    p = rng.standard_normal(12 * 13 // 2)
+    U = unpack_upper(p, 12)
+    assert np.array_equal(U, U.T)
+    assert np.array_equal(pack_upper(U), p)
+    with pytest.raises(ValueError):
+        unpack_upper(p[:-1], 12)
