@@ -71,10 +71,12 @@ def main_kernel_bytes(B, H, T, d, elem_bytes, segments, rule="gla"):
     return tokens + chains * (max(segments, 1) - 1) * slot_in + chains * carry_out
 
 
-def decode_bytes_per_head(d, elem_bytes):
-    """S and C (fp32 d x d) read and written, ksum read and written, n read and written,
-    one token (q, k, v, log alpha) read, o written."""
-    return 4 * d * d * 4 + 2 * d * 4 + 2 * 8 + 4 * d * elem_bytes + d * elem_bytes
+def decode_bytes_per_head(d, elem_bytes, packed_cov=False):
+    """S (fp32 d x d) and C (fp32 d x d, or its d (d + 1) / 2 packed upper triangle) read and
+    written, ksum read and written, n read and written, one token (q, k, v, log alpha) read,
+    o written."""
+    c_floats = d * (d + 1) // 2 if packed_cov else d * d
+    return 2 * (d * d + c_floats) * 4 + 2 * d * 4 + 2 * 8 + 4 * d * elem_bytes + d * elem_bytes
 
 
 def file_sha(path):
@@ -192,9 +194,10 @@ class HipEvents:
             self.rt.hipEventDestroy(h)
 
 
-def time_decode(steps, warmup, seqs_per_batch=32):
+def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False):
     """Decode workload: 256 sequences x 16 heads, d=128, carry from an 8192-token prefix
-    built by the prefill kernel on device-generated seeded inputs."""
+    built by the prefill kernel on device-generated seeded inputs.  packed_cov: the statistic
+    C is kept as its packed upper triangle (prefill writes it so, decode updates it so)."""
     import torch
     from curvature_conditioned_query_amd import ccq_decode_step, ccq_fwd_chunked
     from curvature_conditioned_query_amd.inputs import WORKLOADS
@@ -204,7 +207,7 @@ def time_decode(steps, warmup, seqs_per_batch=32):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(spec["seed"])
     S = torch.empty((N, H, d, d), device="cuda")
-    C = torch.empty((N, H, d, d), device="cuda")
+    C = torch.empty((N, H, d * (d + 1) // 2) if packed_cov else (N, H, d, d), device="cuda")
     m = torch.empty((N, H, d), device="cuda")
     n = torch.empty((N, H), dtype=torch.int64, device="cuda")
     w = (torch.randn((H, d), generator=gen, device="cuda") / np.sqrt(d)).float().contiguous()
@@ -218,7 +221,8 @@ def time_decode(steps, warmup, seqs_per_batch=32):
         vv = torch.randn(shp, generator=gen, device="cuda").to(bf)
         gg = (torch.nn.functional.logsigmoid(torch.randn(shp, generator=gen, device="cuda")) / 16).to(bf)
         ccq_fwd_chunked("gla", qq, kk, vv, gg, None, w, b,
-                        carry_out=(S[s0:s0 + nb], C[s0:s0 + nb], m[s0:s0 + nb], n[s0:s0 + nb]))
+                        carry_out=(S[s0:s0 + nb], C[s0:s0 + nb], m[s0:s0 + nb], n[s0:s0 + nb]),
+                        packed_cov=packed_cov)
         del qq, kk, vv, gg
     torch.cuda.synchronize()
     gen.manual_seed(spec["token_seed"])
@@ -230,7 +234,7 @@ def time_decode(steps, warmup, seqs_per_batch=32):
     o = torch.empty((N, H, d), dtype=bf, device="cuda")
 
     def step():
-        ccq_decode_step("gla", tq, tk, tv, tg, None, w, b, S, C, m, n, o=o)
+        ccq_decode_step("gla", tq, tk, tv, tg, None, w, b, S, C, m, n, o=o, packed_cov=packed_cov)
 
     for _ in range(warmup):
         step()
@@ -243,9 +247,11 @@ def time_decode(steps, warmup, seqs_per_batch=32):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    nbytes = N * H * decode_bytes_per_head(d, 2)
-    return dict(spec=spec, ms_per_step=ms, bytes_per_step=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
-                tokens_per_s=N / (ms * 1e-3), n_after=int(n[0, 0].item()))
+    nbytes = N * H * decode_bytes_per_head(d, 2, packed_cov)
+    name = spec["name"].replace("decode-", "decode-packed-") if packed_cov else spec["name"]
+    del S, C, m, n
+    return dict(spec=spec, name=name, ms_per_step=ms, bytes_per_step=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
+                tokens_per_s=N / (ms * 1e-3))
 
 
 # ------------------------------------------------------------------ CPU oracle leg
@@ -331,8 +337,10 @@ def main(argv=None):
         torch.cuda.synchronize()
         del src, dst
     if args.no_prefill:
-        dres = time_decode(args.decode_steps, 3)
-        print(f"# decode: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s", file=sys.stderr, flush=True)
+        for packed in (False, True):
+            dres = time_decode(args.decode_steps, 3, packed_cov=packed)
+            print(f"# {dres['name']}: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s",
+                  file=sys.stderr, flush=True)
         return 0
     res = time_prefill(args.workload, args.steps, args.warmup)
     B, H, T, dk, dv = res["shape"]
@@ -415,17 +423,19 @@ def main(argv=None):
               f"main kernel {g_main:.4f} ms, {g_gbs:.1f} GB/s alg, {g_tf:.1f} TFLOP/s alg",
               file=sys.stderr, flush=True)
     if not args.no_decode:
-        dres = time_decode(args.decode_steps, 3)
         dsrc = file_sha(DECODE_SRC)
-        out["decode"] = {
-            "workload": dres["spec"]["name"], "ms_per_step": round(dres["ms_per_step"], 4),
-            "tokens_per_s": round(dres["tokens_per_s"], 1),
-            "roofline": dict(bound="hbm", achieved=round(dres["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=round(dres["gbs"] / HBM_PEAK_GBS, 4),
-                             traffic=measured_traffic(f"traffic_{dres['spec']['name']}.json", dsrc)),
-            "algorithmic_bytes_per_step": dres["bytes_per_step"],
-        }
-        print(f"# decode: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s", file=sys.stderr, flush=True)
+        for key, packed in (("decode", False), ("decode_packed", True)):
+            dres = time_decode(args.decode_steps, 3, packed_cov=packed)
+            out[key] = {
+                "workload": dres["name"], "ms_per_step": round(dres["ms_per_step"], 4),
+                "tokens_per_s": round(dres["tokens_per_s"], 1), "packed_cov": packed,
+                "roofline": dict(bound="hbm", achieved=round(dres["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                                 frac=round(dres["gbs"] / HBM_PEAK_GBS, 4),
+                                 traffic=measured_traffic(f"traffic_{dres['name']}.json", dsrc)),
+                "algorithmic_bytes_per_step": dres["bytes_per_step"],
+            }
+            print(f"# {dres['name']}: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s",
+                  file=sys.stderr, flush=True)
     if not args.no_cpu:
         try:
             ncpu = len(os.sched_getaffinity(0))

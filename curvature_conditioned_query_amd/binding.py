@@ -136,12 +136,28 @@ def _rule_code(rule) -> int:
 
 
 FLAG_NORMALIZE_KEYS = 1  # CCQ_FLAG_NORMALIZE_KEYS
+FLAG_PACKED_COV = 2  # CCQ_FLAG_PACKED_COV
+
+
+def _flags(normalize_keys: bool, packed_cov: bool) -> int:
+    return (FLAG_NORMALIZE_KEYS if normalize_keys else 0) | (FLAG_PACKED_COV if packed_cov else 0)
+
+
+def _check_numel(name, t, n):
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
+
+
+def cov_numel(d_k: int, packed_cov: bool) -> int:
+    """Floats per head of the second-moment state: d_k^2, or d_k (d_k + 1) / 2 packed."""
+    return d_k * (d_k + 1) // 2 if packed_cov else d_k * d_k
 
 
 def make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
                     carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
-                    workspace=None, normalize_keys: bool = False) -> FwdParams:
-    """Fill a ccq_fwd_params from tensors (carry_in / carry_out: (S, C, ksum, n) or None)."""
+                    workspace=None, normalize_keys: bool = False, packed_cov: bool = False) -> FwdParams:
+    """Fill a ccq_fwd_params from tensors (carry_in / carry_out: (S, C, ksum, n) or None; C is
+    [B, H, d_k, d_k], or its packed upper triangle [B, H, d_k (d_k + 1) / 2] with packed_cov)."""
     import torch
     B, H, T, d_k = q.shape
     d_v = v.shape[-1]
@@ -151,7 +167,7 @@ def make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
     p.B, p.H, p.T, p.d_k, p.d_v = B, H, T, d_k, d_v
     p.chunk = chunk
     p.segments = segments
-    p.flags = FLAG_NORMALIZE_KEYS if normalize_keys else 0
+    p.flags = _flags(normalize_keys, packed_cov)
     for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta), ("o", o)):
         _check_dev(name, t, q.dtype)
     _check_dev("w_lambda", w_lambda, torch.float32)
@@ -163,12 +179,20 @@ def make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
         for name, t, dt in (("S0", S0, torch.float32), ("C0", C0, torch.float32),
                             ("ksum0", m0, torch.float32), ("n0", n0, torch.int64)):
             _check_dev(name, t, dt)
+        _check_numel("S0", S0, B * H * d_v * d_k)
+        _check_numel("C0", C0, B * H * cov_numel(d_k, packed_cov))
+        _check_numel("ksum0", m0, B * H * d_k)
+        _check_numel("n0", n0, B * H)
         p.S0, p.C0, p.ksum0, p.n0 = _ptr(S0), _ptr(C0), _ptr(m0), _ptr(n0)
     if carry_out is not None:
         S1, C1, m1, n1 = carry_out
         for name, t, dt in (("S_out", S1, torch.float32), ("C_out", C1, torch.float32),
                             ("ksum_out", m1, torch.float32), ("n_out", n1, torch.int64)):
             _check_dev(name, t, dt)
+        _check_numel("S_out", S1, B * H * d_v * d_k)
+        _check_numel("C_out", C1, B * H * cov_numel(d_k, packed_cov))
+        _check_numel("ksum_out", m1, B * H * d_k)
+        _check_numel("n_out", n1, B * H)
         p.S_out, p.C_out, p.ksum_out, p.n_out = _ptr(S1), _ptr(C1), _ptr(m1), _ptr(n1)
     if workspace is not None:
         _check_dev("workspace", workspace)
@@ -183,17 +207,19 @@ def ccq_fwd_workspace_bytes(p: FwdParams) -> int:
 
 def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
                     carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
-                    workspace=None, stream=None, phase_events=None, normalize_keys: bool = False):
+                    workspace=None, stream=None, phase_events=None, normalize_keys: bool = False,
+                    packed_cov: bool = False):
     """Chunked CCQ prefill through the C ABI.  Allocates o (and the workspace if not
     given) with torch; returns o.  ``phase_events``: optional ctypes array of 4 hipEvent_t
     handles recorded around the kernels of the pass.  ``normalize_keys``: the kernels scale
-    every key to unit L2 norm first (CCQ_FLAG_NORMALIZE_KEYS)."""
+    every key to unit L2 norm first (CCQ_FLAG_NORMALIZE_KEYS).  ``packed_cov``: the carry's
+    C is the packed upper triangle (CCQ_FLAG_PACKED_COV)."""
     import torch
     lib = load_library()
     if o is None:
         o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     p = make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
-                        carry_in, carry_out, segments, chunk, workspace, normalize_keys)
+                        carry_in, carry_out, segments, chunk, workspace, normalize_keys, packed_cov)
     if workspace is None:
         nbytes = int(lib.ccq_fwd_workspace_bytes(ctypes.byref(p)))
         if nbytes:
@@ -209,9 +235,10 @@ def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
 
 
 def ccq_decode_step(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n,
-                    o=None, stream=None, normalize_keys: bool = False):
+                    o=None, stream=None, normalize_keys: bool = False, packed_cov: bool = False):
     """One in-place decode step through the C ABI; returns o [N, H, d_v].  ``normalize_keys``:
-    the kernel scales the key to unit L2 norm first (CCQ_FLAG_NORMALIZE_KEYS)."""
+    the kernel scales the key to unit L2 norm first (CCQ_FLAG_NORMALIZE_KEYS).  ``packed_cov``:
+    C is the packed upper triangle [N, H, d_k (d_k + 1) / 2] (CCQ_FLAG_PACKED_COV)."""
     import torch
     lib = load_library()
     N, H, d_k = q.shape
@@ -224,10 +251,14 @@ def ccq_decode_step(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ks
                         ("S", S, torch.float32), ("C", C, torch.float32), ("ksum", ksum, torch.float32),
                         ("n", n, torch.int64)):
         _check_dev(name, t, dt)
+    _check_numel("S", S, N * H * d_v * d_k)
+    _check_numel("C", C, N * H * cov_numel(d_k, packed_cov))
+    _check_numel("ksum", ksum, N * H * d_k)
+    _check_numel("n", n, N * H)
     st = lib.ccq_decode_step(_rule_code(rule), _dtype_code(q), N, H, d_k, d_v,
                              _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                              _ptr(w_lambda), _ptr(b_lambda), _ptr(S), _ptr(C), _ptr(ksum), _ptr(n),
-                             _ptr(o), FLAG_NORMALIZE_KEYS if normalize_keys else 0, _stream_handle(stream))
+                             _ptr(o), _flags(normalize_keys, packed_cov), _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_decode_step")
     return o

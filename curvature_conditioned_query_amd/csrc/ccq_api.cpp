@@ -7,6 +7,9 @@
 
 #include "ccq_internal.hpp"
 
+static_assert(CCQ_FLAG_NORMALIZE_KEYS == ccq::kFlagNormalizeKeys && CCQ_FLAG_PACKED_COV == ccq::kFlagPackedCov,
+              "flag bits of the header and the kernels agree");
+
 namespace {
 
 bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -29,7 +32,7 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
   if (p->dtype != CCQ_DTYPE_F32 && p->dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
   if (p->B <= 0 || p->H <= 0 || p->T <= 0 || p->d_k <= 0 || p->d_v <= 0) return CCQ_ERR_INVALID_ARG;
   if (p->chunk < 0 || p->segments < 0) return CCQ_ERR_INVALID_ARG;
-  if (p->flags & ~CCQ_FLAG_NORMALIZE_KEYS) return CCQ_ERR_INVALID_ARG;
+  if (p->flags & ~(CCQ_FLAG_NORMALIZE_KEYS | CCQ_FLAG_PACKED_COV)) return CCQ_ERR_INVALID_ARG;
   if (p->chunk != 0 && p->chunk != kChunk) return CCQ_ERR_UNSUPPORTED;
   if (p->d_k != p->d_v || !supported_d(p->dtype, p->d_k)) return CCQ_ERR_UNSUPPORTED;
   if (!p->q || !p->k || !p->v || !p->log_alpha || !p->w_lambda || !p->b_lambda || !p->o)
@@ -70,7 +73,7 @@ size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 3; }
+int32_t ccq_abi_version(void) { return 4; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -135,7 +138,7 @@ int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d
   if (rule != CCQ_RULE_GLA && rule != CCQ_RULE_GDN) return CCQ_ERR_INVALID_ARG;
   if (dtype != CCQ_DTYPE_F32 && dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
   if (N <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return CCQ_ERR_INVALID_ARG;
-  if (flags & ~CCQ_FLAG_NORMALIZE_KEYS) return CCQ_ERR_INVALID_ARG;
+  if (flags & ~(CCQ_FLAG_NORMALIZE_KEYS | CCQ_FLAG_PACKED_COV)) return CCQ_ERR_INVALID_ARG;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return CCQ_ERR_UNSUPPORTED;
   if ((long long)N * H > 0x7fffffffLL) return CCQ_ERR_UNSUPPORTED;
   if (!q || !k || !v || !log_alpha || !w_lambda || !b_lambda || !S || !C || !ksum || !n || !o)

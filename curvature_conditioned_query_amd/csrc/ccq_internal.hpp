@@ -38,6 +38,14 @@ struct FwdArgs {
 };
 
 constexpr int kFlagNormalizeKeys = 1;
+constexpr int kFlagPackedCov = 2;  // C0 / C_out / decode C hold the packed upper triangle
+
+// Index of entry (i, j) of a symmetric d x d matrix stored as its upper triangle, row by row:
+// row r starts at r d - r (r - 1) / 2.
+__host__ __device__ inline int packed_index(int i, int j, int d) {
+  const int r = i < j ? i : j, c = i < j ? j : i;
+  return r * d - r * (r - 1) / 2 + (c - r);
+}
 
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).

@@ -95,10 +95,14 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
   const size_t slot_f = 2 * (size_t)D * D + 2 * D;
 
   // ---- carry in
+  // the caller's C0 / C_out may be the packed upper triangle (the workspace slots never are)
+  const bool cpacked = (a.flags & kFlagPackedCov) != 0;
+  constexpr size_t kTri = (size_t)D * (D + 1) / 2;
   f32x4 Cacc[NA], Sacc[NA];
   const float* Sin = nullptr;
   const float* Cin = nullptr;
   const float* min_ = nullptr;
+  bool cin_packed = false;
   if constexpr (MAIN) {
     if (P > 1) {
       const float* slot = slots + ((size_t)chain * P + seg) * slot_f;
@@ -107,7 +111,8 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
       min_ = slot + 2 * (size_t)D * D;
     } else if (a.S0 != nullptr) {
       Sin = a.S0 + (size_t)chain * D * D;
-      Cin = a.C0 + (size_t)chain * D * D;
+      cin_packed = cpacked;
+      Cin = a.C0 + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
       min_ = a.ksum0 + (size_t)chain * D;
     }
   }
@@ -117,7 +122,12 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     for (int t = 0; t < NA; ++t) {
       const int col = 16 * t + 4 * g;
       Sacc[t] = Sin ? *reinterpret_cast<const f32x4*>(Sin + (size_t)row * D + col) : zero4();
-      Cacc[t] = Cin ? *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col) : zero4();
+      if (Cin == nullptr)
+        Cacc[t] = zero4();
+      else if (cin_packed)
+        Cacc[t] = ld_packed4<D>(Cin, row, col);
+      else
+        Cacc[t] = *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col);
     }
   }
   // the carry-in loads complete here, so nothing in the chunk loop waits on them
@@ -373,10 +383,12 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
   float* Cout = nullptr;
   float* mout = nullptr;
   float* ldout = nullptr;
+  bool cout_packed = false;
   if constexpr (MAIN) {
     if (seg == P - 1 && a.S_out != nullptr) {
       Sout = a.S_out + (size_t)chain * D * D;
-      Cout = a.C_out + (size_t)chain * D * D;
+      cout_packed = cpacked;
+      Cout = a.C_out + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
       mout = a.ksum_out + (size_t)chain * D;
       if (tid == 0) a.n_out[chain] = nb;
     }
@@ -393,7 +405,10 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     for (int t = 0; t < NA; ++t) {
       const int col = 16 * t + 4 * g;
       *reinterpret_cast<f32x4*>(Sout + (size_t)row * D + col) = Sacc[t];
-      *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t];
+      if (cout_packed)
+        st_packed4<D>(Cout, row, col, Cacc[t]);
+      else
+        *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t];
     }
     if (tid < D) {
       mout[tid] = sm.m0[tid];
@@ -437,7 +452,12 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
       src = a.C0 + (size_t)chain * D * D + (f - (size_t)D * D);
     else
       src = a.ksum0 + (size_t)chain * D + (f - 2 * (size_t)D * D);
-    run = *reinterpret_cast<const f32x4*>(src);
+    if (!isS && f < 2 * (size_t)D * D && (a.flags & kFlagPackedCov)) {
+      const int e = (int)(f - (size_t)D * D);
+      run = ld_packed4<D>(a.C0 + (size_t)chain * D * (D + 1) / 2, e / D, e % D);
+    } else {
+      run = *reinterpret_cast<const f32x4*>(src);
+    }
   }
   for (int p = 0; p < P; ++p) {
     float* slot = base + (size_t)p * slot_f;

@@ -161,6 +161,26 @@ __device__ __forceinline__ void dma_tile(T (*dst)[PQ], const T* src, int Lc, int
   }
 }
 
+// C[row][col .. col + 3] of a symmetric D x D matrix held as its packed upper triangle (the
+// caller's carry with the packed-statistics flag).
+template <int D>
+__device__ __forceinline__ f32x4 ld_packed4(const float* p, int row, int col) {
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = p[packed_index(row, col + e, D)];
+  return v;
+}
+
+// The entries of C[row][col .. col + 3] on or above the diagonal, into a packed upper
+// triangle.  Lanes that together hold every (row, col) of C once write every entry of the
+// triangle once.
+template <int D>
+__device__ __forceinline__ void st_packed4(float* p, int row, int col, const f32x4& v) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (row <= col + e) p[packed_index(row, col + e, D)] = v[e];
+}
+
 // Zeroes rows Lc..63 of an LDS tile (the rows of a chunk past the end of the sequence).
 template <int D, typename T, int PQ>
 __device__ __forceinline__ void zero_tail(T (*dst)[PQ], int Lc, int tid, int nthreads) {

@@ -250,9 +250,13 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   const T* bg = static_cast<const T*>(a.beta);
 
   // ---- carry in: the segment's slot when there are segments, else the caller's carry
+  // the caller's C0 / C_out may be the packed upper triangle (the workspace slots never are)
+  const bool cpacked = (a.flags & kFlagPackedCov) != 0;
+  constexpr size_t kTri = (size_t)D * (D + 1) / 2;
   const float* Sin = nullptr;
   const float* Cin = nullptr;
   const float* min_ = nullptr;
+  bool cin_packed = false;
   if (P > 1) {
     const float* slot = static_cast<const float*>(a.workspace) + ((size_t)chain * P + seg) * gdn_slot_floats(D);
     Sin = slot;
@@ -260,7 +264,8 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     min_ = slot + 2 * (size_t)D * D;
   } else if (a.S0 != nullptr) {
     Sin = a.S0 + (size_t)chain * D * D;
-    Cin = a.C0 + (size_t)chain * D * D;
+    cin_packed = cpacked;
+    Cin = a.C0 + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
     min_ = a.ksum0 + (size_t)chain * D;
   }
   f32x4 Cacc[NA], Sacc[NA];
@@ -270,7 +275,12 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     for (int t = 0; t < NA; ++t) {
       const int col = 16 * t + 4 * g;
       Sacc[t] = Sin ? *reinterpret_cast<const f32x4*>(Sin + (size_t)row * D + col) : zero4();
-      Cacc[t] = Cin ? *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col) : zero4();
+      if (Cin == nullptr)
+        Cacc[t] = zero4();
+      else if (cin_packed)
+        Cacc[t] = ld_packed4<D>(Cin, row, col);
+      else
+        Cacc[t] = *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -429,13 +439,16 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   // ---- carry out (last segment)
   if (seg == P - 1 && a.S_out != nullptr) {
     float* Sout = a.S_out + (size_t)chain * D * D;
-    float* Cout = a.C_out + (size_t)chain * D * D;
+    float* Cout = a.C_out + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
     const int row = cw + l16;
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
       const int col = 16 * t + 4 * g;
       *reinterpret_cast<f32x4*>(Sout + (size_t)row * D + col) = Sacc[t];
-      *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t];
+      if (cpacked)
+        st_packed4<D>(Cout, row, col, Cacc[t]);
+      else
+        *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t];
     }
     if (tid < D) a.ksum_out[(size_t)chain * D + tid] = sm.m0[tid];
     if (tid == 0) a.n_out[chain] = nb;
@@ -635,8 +648,14 @@ __global__ __launch_bounds__(256) void gdn_scan_sum_kernel(FwdArgs a) {
   const size_t slot_f = gdn_slot_floats(D);
   float* base = static_cast<float*>(a.workspace) + (size_t)chain * P * slot_f + (size_t)D * D;
   float run = 0.f;
-  if (a.S0 != nullptr)
-    run = (f < (size_t)D * D) ? a.C0[(size_t)chain * D * D + f] : a.ksum0[(size_t)chain * D + (f - (size_t)D * D)];
+  if (a.S0 != nullptr) {
+    if (f >= (size_t)D * D)
+      run = a.ksum0[(size_t)chain * D + (f - (size_t)D * D)];
+    else if (a.flags & kFlagPackedCov)
+      run = a.C0[(size_t)chain * D * (D + 1) / 2 + packed_index((int)f / D, (int)f % D, D)];
+    else
+      run = a.C0[(size_t)chain * D * D + f];
+  }
   for (int p = 0; p < P; ++p) {
     float* v = base + (size_t)p * slot_f + f;
     const float d = (p < P - 1) ? *v : 0.f;

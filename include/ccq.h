@@ -63,8 +63,16 @@ typedef enum { CCQ_DTYPE_F32 = 0, CCQ_DTYPE_BF16 = 1 } ccq_dtype;
 /* Option bits (ccq_fwd_params.flags, ccq_decode_step's flags).
  * CCQ_FLAG_NORMALIZE_KEYS: the library scales every key to unit L2 norm, k / max(|k|, 1e-12)
  * computed in fp32 from the stored key, before any use (statistics, gate, read and write).
- * Without it keys are used as given and must already be unit vectors. */
-typedef enum { CCQ_FLAG_NORMALIZE_KEYS = 1 } ccq_flag;
+ * Without it keys are used as given and must already be unit vectors.
+ * CCQ_FLAG_PACKED_COV: the second-moment sum C, which is symmetric, is passed as its upper
+ * triangle only: d_k (d_k + 1) / 2 fp32 entries per head, row by row (C[0][0..d_k-1],
+ * C[1][1..d_k-1], ..., C[d_k-1][d_k-1]), so entry C[i][j], i <= j, sits at index
+ * i d_k - i (i - 1) / 2 + (j - i).  It applies to C0 and C_out of ccq_fwd_chunked and to C
+ * of ccq_decode_step, whose per-head stride becomes d_k (d_k + 1) / 2.  The statistics
+ * are the extra state the method keeps per head (summary §2 "机制"); the 10100.com
+ * write-up's section "代价与边界" names that state's memory as the method's inference cost,
+ * and the packed form moves about half of C's bytes in a decode step. */
+typedef enum { CCQ_FLAG_NORMALIZE_KEYS = 1, CCQ_FLAG_PACKED_COV = 2 } ccq_flag;
 
 /* Arguments of ccq_fwd_chunked.  Zero-initialise, then fill in. */
 typedef struct {
@@ -85,7 +93,7 @@ typedef struct {
 
   /* Carry in: all four NULL (start from zeros, n0 = 0) or all four set. */
   const float *S0;       /* [B, H, d_v, d_k]                                                    */
-  const float *C0;       /* [B, H, d_k, d_k]  sum of k k^T                                      */
+  const float *C0;       /* [B, H, d_k, d_k]  sum of k k^T  ([B, H, d_k (d_k+1)/2] packed)      */
   const float *ksum0;    /* [B, H, d_k]       sum of k                                          */
   const int64_t *n0;     /* [B, H]            token count                                       */
 
@@ -93,7 +101,7 @@ typedef struct {
 
   /* Carry out: all four NULL (not wanted) or all four set.  May alias the carry in. */
   float *S_out;
-  float *C_out;
+  float *C_out;          /* same layout as C0                                                    */
   float *ksum_out;
   int64_t *n_out;
 
@@ -112,8 +120,8 @@ typedef struct {
 /*
  * Chunked prefill of one CCQ layer: o for every token and, optionally, the final carry.
  * The result is the per-token recurrence above evaluated exactly (up to rounding) with
- * chunks of 64 tokens; the statistics are kept "by the same recurrent or chunked mechanism
- * as the backbone state" (summary §2 "机制").  A call with a carry in continues the sequence
+ * chunks of 64 tokens; the statistics are carried chunk by chunk exactly as the backbone's
+ * state is (summary §2 "机制").  A call with a carry in continues the sequence
  * the carry came from.  T need not be a multiple of 64.
  * Precondition (GLA): within any 64-token chunk the cumulative log decay of each key channel
  * stays above -80 on either side of the chunk's midpoint (no fp32 overflow of e^{+-B}).
@@ -131,8 +139,9 @@ size_t ccq_fwd_workspace_bytes(const ccq_fwd_params *p);
  *   q_clean = q - lambda Sigma q; write rule; o = S q_clean.
  * q, k: [N, H, d_k] dtype; v: [N, H, d_v] dtype; log_alpha: GLA [N, H, d_k] / GDN [N, H];
  * beta: GDN [N, H] (GLA: NULL); w_lambda [H, d_k], b_lambda [H] fp32;
- * S [N, H, d_v, d_k], C [N, H, d_k, d_k], ksum [N, H, d_k] fp32 and n [N, H] int64 are
- * read and written in place; o [N, H, d_v] dtype is written.  flags: ccq_flag bits.
+ * S [N, H, d_v, d_k], C [N, H, d_k, d_k] (with CCQ_FLAG_PACKED_COV: [N, H, d_k (d_k+1)/2]),
+ * ksum [N, H, d_k] fp32 and n [N, H] int64 are read and written in place; o [N, H, d_v]
+ * dtype is written.  flags: ccq_flag bits; unknown bits are CCQ_ERR_INVALID_ARG.
  * Returns a ccq_status.
  */
 int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
@@ -143,7 +152,7 @@ int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 int32_t ccq_abi_version(void);
 
 #ifdef __cplusplus

@@ -5,9 +5,9 @@ Two forms are kept, both in float64 NumPy:
 * ``ccq_recurrent`` is the plain per-token definition.  It is THE oracle the
   HIP path is compared against.
 * ``ccq_chunked`` is the same result reached by unrolling the recurrence inside
-  chunks of L tokens (the pages say the statistics are kept by "the same
-  recurrent or chunked mechanism as the backbone", gist.science summary §2
-  "机制").  It exists to pin that algebra against the plain definition.
+  chunks of L tokens (the statistics may follow the backbone's own recurrent or
+  chunked form, gist.science summary §2 "机制").  It exists to pin that algebra
+  against the plain definition.
 
 Notation follows the pages: keys k_t (unit norm), queries q_t, values v_t; the
 running undecayed statistics are the key sum m, the second-moment sum C and the

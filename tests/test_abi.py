@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 3
+    assert lib.ccq_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -62,7 +62,7 @@ def _fwd(lib, p):
     (dict(d_k=64, d_v=128), UNSUPPORTED), (dict(dtype=0), UNSUPPORTED), (dict(q=None), INVALID),
     (dict(o=None), INVALID), (dict(beta=FAKE), INVALID), (dict(rule=1), INVALID),
     (dict(S0=FAKE), INVALID), (dict(S_out=FAKE, C_out=FAKE), INVALID), (dict(k=FAKE + 4), MISALIGNED),
-    (dict(segments=-2), INVALID), (dict(flags=2), INVALID), (dict(flags=-1), INVALID),
+    (dict(segments=-2), INVALID), (dict(flags=4), INVALID), (dict(flags=-1), INVALID),
 ])
 def test_fwd_argument_errors(lib, kw, code):
     assert _fwd(lib, _params(**kw)) == code
@@ -100,7 +100,7 @@ def _dec(lib, rule=0, dtype=1, N=2, H=2, dk=128, dv=128, flags=0, **ptrs):
     (dict(rule=3), INVALID), (dict(dtype=2), INVALID), (dict(N=0), INVALID), (dict(H=0), INVALID),
     (dict(dk=32, dv=32), UNSUPPORTED), (dict(dk=128, dv=64), UNSUPPORTED), (dict(q=None), INVALID),
     (dict(S=None), INVALID), (dict(n=None), INVALID), (dict(beta=FAKE), INVALID),
-    (dict(rule=1, beta=None), INVALID), (dict(C=FAKE + 8), MISALIGNED), (dict(flags=4), INVALID),
+    (dict(rule=1, beta=None), INVALID), (dict(C=FAKE + 8), MISALIGNED), (dict(flags=4), INVALID), (dict(flags=8), INVALID),
 ])
 def test_decode_argument_errors(lib, kw, code):
     assert _dec(lib, **kw) == code

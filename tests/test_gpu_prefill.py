@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from curvature_conditioned_query_amd.inputs import gdn_inputs, gla_inputs, structured_inputs, workload_inputs
-from oracle import Carry, ccq_recurrent, normwise_error, unit_keys
+from oracle import Carry, ccq_recurrent, normwise_error, pack_upper, unit_keys, unpack_upper
 
 from gpu_util import down, up, up_carry, upload_inputs
 
@@ -17,8 +17,11 @@ pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def gpu_prefill(x, segments=0, carry=None, want_carry=True, alias=False, normalize_keys=False):
-    """Run ccq_fwd_chunked on PrefillInputs x; returns (o, (S, C, ksum, n)) as numpy."""
+def gpu_prefill(x, segments=0, carry=None, want_carry=True, alias=False, normalize_keys=False,
+                packed_cov=False):
+    """Run ccq_fwd_chunked on PrefillInputs x; returns (o, (S, C, ksum, n)) as numpy.  With
+    packed_cov the carry's C goes in and comes out as the packed upper triangle; it is returned
+    unpacked to the full matrix."""
     import torch
     from curvature_conditioned_query_amd import ccq_fwd_chunked
     d = upload_inputs(x)
@@ -26,17 +29,24 @@ def gpu_prefill(x, segments=0, carry=None, want_carry=True, alias=False, normali
     cin = None
     if carry is not None:
         cin, _ = up_carry(carry)
+        if packed_cov:
+            Cp = pack_upper(np.asarray(carry.C, np.float32))
+            cin = (cin[0], torch.from_numpy(np.ascontiguousarray(Cp)).cuda(), cin[2], cin[3])
     cout = None
     if want_carry:
         if alias and cin is not None:
             cout = cin
         else:
-            cout = (torch.empty((B, H, dv, dk), device="cuda"), torch.empty((B, H, dk, dk), device="cuda"),
+            cshape = (B, H, dk * (dk + 1) // 2) if packed_cov else (B, H, dk, dk)
+            cout = (torch.empty((B, H, dv, dk), device="cuda"), torch.empty(cshape, device="cuda"),
                     torch.empty((B, H, dk), device="cuda"), torch.empty((B, H), dtype=torch.int64, device="cuda"))
     o = ccq_fwd_chunked(x.rule, d["q"], d["k"], d["v"], d["g"], d["beta"], d["w"], d["b"],
-                        carry_in=cin, carry_out=cout, segments=segments, normalize_keys=normalize_keys)
+                        carry_in=cin, carry_out=cout, segments=segments, normalize_keys=normalize_keys,
+                        packed_cov=packed_cov)
     torch.cuda.synchronize()
     res = None if cout is None else tuple(down(t) for t in cout)
+    if res is not None and packed_cov:
+        res = (res[0], unpack_upper(res[1], dk), res[2], res[3])
     return down(o), res
 
 
@@ -211,3 +221,26 @@ def test_normalize_keys_flag(rule, dtype, d):
     xr.k = unit_keys(k_raw)
     o_ref, c_ref = oracle(xr)
     check(x, o, c, o_ref, c_ref, tag=f"normalize-keys {rule}")
+
+
+@pytest.mark.parametrize("rule", ["gla", "gdn"])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("segments", [1, 3])
+def test_packed_cov_carry(rule, dtype, d, segments):
+    """The packed-statistics flag: C0 and C_out as the packed upper triangle, with and without
+    segments (the carry scan reads the packed C0), carry out separate from and aliasing the carry
+    in; o and the carry match the oracle's continuation from the same carry."""
+    gen = gla_inputs if rule == "gla" else gdn_inputs
+    x0 = gen(1, 2, 150, d, 95, "f32")
+    _, pre = oracle(x0)
+    (_, (S, C, m, n)) = up_carry(pre)
+    carry = Carry(S, C, m, n)
+    x = gen(1, 2, 333, d, 96, dtype)
+    o_ref, c_ref = oracle(x, carry)
+    for alias in (False, True):
+        o, c = gpu_prefill(x, carry=carry, segments=segments, alias=alias, packed_cov=True)
+        check(x, o, c, o_ref, c_ref, tag=f"packed C seg={segments} alias={alias}")
+    # from a zero carry: the packed C_out holds the sum of k k^T
+    o, c = gpu_prefill(x, segments=segments, packed_cov=True)
+    o_ref0, c_ref0 = oracle(x)
+    check(x, o, c, o_ref0, c_ref0, tag=f"packed C out seg={segments}")
