@@ -60,19 +60,18 @@ struct Smem {
   T Qa[kL][C_::PQ];     // q_clean * e^B rows (hi part for bf16)
   T Pm[kL][C_::PT];     // tril(Q K^T - c 1^T), then the masked intra-chunk attention matrix
   T Wt[4][C_::PQ];      // w_lambda hi, lo; key sum hi, lo (B operand of q . [w, m0])
-  float m0[D], m1[D], eBL[D], ldec[D];
+  float m0[D], m1[D], eBL[D];
   f32x4 tok[kL];        // per token: lambda, 1/n, sq/n^2, gate logit + b
 };
 
-// MODE 0: full read (o for every token) from the segment's carry-in, carry out at the end.
-// MODE 1: segment summary from a zero carry (C, S, ksum and total log decay), no outputs.
-template <int D, typename T, int MODE>
-__device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
+// Full read (o for every token) of one (chain, segment) from the segment's carry-in, carry
+// out at the end of the chain.
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, NK = C_::NK;
   constexpr int PQ = C_::PQ, PT = C_::PT;
-  constexpr bool MAIN = (MODE == 0);
-  constexpr bool kSplit = MAIN && sizeof(T) == 2;  // hi/lo operands for the intra term
+  constexpr bool kSplit = sizeof(T) == 2;  // hi/lo operands for the intra term
   __shared__ Smem<D, T> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
@@ -80,8 +79,7 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
   const int hb = w & 1;        // which half of its 32-channel block
   const int cb = cw - 16 * hb; // first channel of the block
   const int P = a.segments, cps = a.chunks_per_segment;
-  const int per_chain = MAIN ? P : P - 1;
-  const int chain = blockIdx.x / per_chain, seg = blockIdx.x % per_chain;
+  const int chain = blockIdx.x / P, seg = blockIdx.x % P;
   const int h = chain % a.H;
   const int nchunks = (a.T + kL - 1) / kL;
   const int cbeg = seg * cps;
@@ -103,18 +101,16 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
   const float* Cin = nullptr;
   const float* min_ = nullptr;
   bool cin_packed = false;
-  if constexpr (MAIN) {
-    if (P > 1) {
-      const float* slot = slots + ((size_t)chain * P + seg) * slot_f;
-      Sin = slot;
-      Cin = slot + (size_t)D * D;
-      min_ = slot + 2 * (size_t)D * D;
-    } else if (a.S0 != nullptr) {
-      Sin = a.S0 + (size_t)chain * D * D;
-      cin_packed = cpacked;
-      Cin = a.C0 + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
-      min_ = a.ksum0 + (size_t)chain * D;
-    }
+  if (P > 1) {
+    const float* slot = slots + ((size_t)chain * P + seg) * slot_f;
+    Sin = slot;
+    Cin = slot + (size_t)D * D;
+    min_ = slot + 2 * (size_t)D * D;
+  } else if (a.S0 != nullptr) {
+    Sin = a.S0 + (size_t)chain * D * D;
+    cin_packed = cpacked;
+    Cin = a.C0 + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
+    min_ = a.ksum0 + (size_t)chain * D;
   }
   {
     const int row = cw + l16;
@@ -133,40 +129,32 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
   // the carry-in loads complete here, so nothing in the chunk loop waits on them
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int64_t nb = (int64_t)cbeg * kL;  // tokens before this chunk (count base)
-  if constexpr (MAIN) {
-    if (a.n0 != nullptr) nb += a.n0[chain];
-  }
-  float b_lam = 0.f;
-  if constexpr (MAIN) b_lam = a.b_lambda[h];
+  if (a.n0 != nullptr) nb += a.n0[chain];
+  const float b_lam = a.b_lambda[h];
 
   if (tid < D) {
     const int c = tid;
     const float m = min_ ? min_[c] : 0.f;
     sm.m0[c] = m;
-    sm.ldec[c] = 0.f;
-    if constexpr (MAIN) {
-      const float wv = a.w_lambda[(size_t)h * D + c];
-      const T whi = (T)wv, mhi = (T)m;
-      sm.Wt[0][c] = whi;
-      sm.Wt[1][c] = (T)(wv - (float)whi);
-      sm.Wt[2][c] = mhi;
-      sm.Wt[3][c] = (T)(m - (float)mhi);
-    }
+    const float wv = a.w_lambda[(size_t)h * D + c];
+    const T whi = (T)wv, mhi = (T)m;
+    sm.Wt[0][c] = whi;
+    sm.Wt[1][c] = (T)(wv - (float)whi);
+    sm.Wt[2][c] = mhi;
+    sm.Wt[3][c] = (T)(m - (float)mhi);
   }
-  if constexpr (MAIN) {
-    for (int e = tid; e < kL * PT; e += 64 * NW) (&sm.Pm[0][0])[e] = (T)0.f;
-  }
+  for (int e = tid; e < kL * PT; e += 64 * NW) (&sm.Pm[0][0])[e] = (T)0.f;
 
   // ---- chunk tiles go straight from HBM to LDS (no registers involved), each as soon as the
   // previous chunk has finished reading the buffer it lands in: log decay after the gate and
-  // Gram rows, q after the cleaned query, k and v (bf16) after the intra-chunk attention or
-  // (fp32, summary) at the start of the previous chunk.
+  // Gram rows, q after the cleaned query, k and v after the intra-chunk attention (bf16) or at
+  // the start of the previous chunk (fp32).
   auto chunk_len = [&](int ch) { return min(kL, a.T - ch * kL); };
   auto dma_rows = [&](T (*dst)[PQ], const T* g, int ch) {
     dma_tile<D, T, PQ>(dst, g + (tok0 + (size_t)ch * kL) * D, chunk_len(ch), w, NW, lane);
   };
   if (cbeg < cend) {
-    if constexpr (MAIN) dma_rows(sm.Qs, qg, cbeg);
+    dma_rows(sm.Qs, qg, cbeg);
     dma_rows(sm.Gs, gg, cbeg);
     dma_rows(sm.X[cbeg & 1], kg, cbeg);
     dma_rows(sm.Y[cbeg & 1], vg, cbeg);
@@ -188,7 +176,7 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     if (Lc < kL) {
-      if constexpr (MAIN) zero_tail<D, T, PQ>(sm.Qs, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(sm.Qs, Lc, tid, 64 * NW);
       zero_tail<D, T, PQ>(sm.Gs, Lc, tid, 64 * NW);
       zero_tail<D, T, PQ>(Ks, Lc, tid, 64 * NW);
       zero_tail<D, T, PQ>(Vs, Lc, tid, 64 * NW);
@@ -252,94 +240,86 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           sm.eBL[c + r] = __expf(BT[3][r]);
-          sm.ldec[c + r] += BT[3][r];
         }
       }
     }
-    if constexpr (!MAIN) {
-      lds_barrier();
-      if (ch + 1 < cend) dma_rows(sm.Gs, gg, ch + 1);
-    }
+    // gate and Gram rows on waves 0..3 while every wave forms Q C0 for its channels
+    ccq_gram_rows<D, T, NW>(sm, Ks, w, lane, nb, b_lam);
+    f32x4 R[1][4];
+    ccq_query_carry<D, T, 1>(sm, [&](int, int t) -> const f32x4& { return Cacc[t]; }, lane, R);
+    lds_barrier();
+    if (ch + 1 < cend) dma_rows(sm.Gs, gg, ch + 1);
 
-    if constexpr (MAIN) {
-      // gate and Gram rows on waves 0..3 while every wave forms Q C0 for its channels
-      ccq_gram_rows<D, T, NW>(sm, Ks, w, lane, nb, b_lam);
-      f32x4 R[1][4];
-      ccq_query_carry<D, T, 1>(sm, [&](int, int t) -> const f32x4& { return Cacc[t]; }, lane, R);
-      lds_barrier();
-      if (ch + 1 < cend) dma_rows(sm.Gs, gg, ch + 1);
+    ccq_clean_query<D, T, 1, kSplit>(sm, Ks, Qalo, R, cw, lane,
+                                     [&](int, int ti, int r) { return __expf(BT[ti][r]); });
+    lds_barrier();
+    if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);
 
-      ccq_clean_query<D, T, 1, kSplit>(sm, Ks, Qalo, R, cw, lane,
-                                       [&](int, int ti, int r) { return __expf(BT[ti][r]); });
-      lds_barrier();
-      if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);
-
-      // ---- intra-chunk attention (Qc e^B)(K e^-B)^T on the lower tiles -> Pm (masked)
-      for (int idx = w; idx < 10; idx += NW) {
-        const int ti = tri_row(idx), tj = tri_col(idx);
-        f32x4 acc = zero4();
-        Frag<T> Af[NK], Bf[NK], Alf[NK], Blf[NK];
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          Af[kk] = lds_frag<T, KORD_CONTIG>(&sm.Kp[0][0], PQ, 16 * tj, 32 * kk, lane);
-          Bf[kk] = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
-          if constexpr (kSplit) {
-            Alf[kk] = lds_frag<T, KORD_CONTIG>(&Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
-            Blf[kk] = lds_frag<T, KORD_CONTIG>(&Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-          mma(acc, Af[kk], Bf[kk]);
-          if constexpr (kSplit) {
-            mma(acc, Af[kk], Blf[kk]);
-            mma(acc, Alf[kk], Bf[kk]);
-          }
-        }
-        const int i = 16 * ti + l16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = (16 * tj + 4 * g + r <= i) ? acc[r] : 0.f;
-        st4<T>(&sm.Pm[i][16 * tj + 4 * g], acc);
-      }
-      lds_barrier();
-      if constexpr (kSplit) {  // the low parts are consumed: their buffers take the next k, v
-        if (ch + 1 < cend) {
-          dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
-          dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
-        }
-      }
-
-      // ---- O^T for the wave's 16 value rows: S0 (Qc e^B)^T + V^T A^T
-      f32x4 O[4];
-#pragma unroll
-      for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
+    // ---- intra-chunk attention (Qc e^B)(K e^-B)^T on the lower tiles -> Pm (masked)
+    for (int idx = w; idx < 10; idx += NW) {
+      const int ti = tri_row(idx), tj = tri_col(idx);
+      f32x4 acc = zero4();
+      Frag<T> Af[NK], Bf[NK], Alf[NK], Blf[NK];
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) {
-        Frag<T> Bq[4];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) Bq[ti] = lds_frag<T, KORD_ACC>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
-        const Frag<T> A = acc_frag<T>(Sacc[2 * kk], Sacc[2 * kk + 1]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) mma(O[ti], A, Bq[ti]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const Frag<T> A = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);  // V^T, own rows
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-          if (kk == 1 && ti < 2) continue;
-          const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
-          mma(O[ti], A, B);
+        Af[kk] = lds_frag<T, KORD_CONTIG>(&sm.Kp[0][0], PQ, 16 * tj, 32 * kk, lane);
+        Bf[kk] = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
+        if constexpr (kSplit) {
+          Alf[kk] = lds_frag<T, KORD_CONTIG>(&Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
+          Blf[kk] = lds_frag<T, KORD_CONTIG>(&Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
         }
       }
-      T* og = static_cast<T*>(a.o);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        mma(acc, Af[kk], Bf[kk]);
+        if constexpr (kSplit) {
+          mma(acc, Af[kk], Blf[kk]);
+          mma(acc, Alf[kk], Bf[kk]);
+        }
+      }
+      const int i = 16 * ti + l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = (16 * tj + 4 * g + r <= i) ? acc[r] : 0.f;
+      st4<T>(&sm.Pm[i][16 * tj + 4 * g], acc);
+    }
+    lds_barrier();
+    if constexpr (kSplit) {  // the low parts are consumed: their buffers take the next k, v
+      if (ch + 1 < cend) {
+        dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
+        dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
+      }
+    }
+
+    // ---- O^T for the wave's 16 value rows: S0 (Qc e^B)^T + V^T A^T
+    f32x4 O[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      Frag<T> Bq[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) Bq[ti] = lds_frag<T, KORD_ACC>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
+      const Frag<T> A = acc_frag<T>(Sacc[2 * kk], Sacc[2 * kk + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) mma(O[ti], A, Bq[ti]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const Frag<T> A = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);  // V^T, own rows
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
-        const int i = 16 * ti + l16;
-        if (i < Lc) st4<T>(og + (tok0 + t0 + i) * D + cw + 4 * g, O[ti]);
+        if (kk == 1 && ti < 2) continue;
+        const Frag<T> B = lds_frag<T, KORD_CONTIG>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane);
+        mma(O[ti], A, B);
       }
+    }
+    T* og = static_cast<T*>(a.o);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      const int i = 16 * ti + l16;
+      if (i < Lc) st4<T>(og + (tok0 + t0 + i) * D + cw + 4 * g, O[ti]);
     }
 
     // ---- carry update: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
@@ -368,63 +348,198 @@ __device__ __forceinline__ void gla_prefill_body(const FwdArgs a) {
     if (tid < D) {
       const float m = sm.m1[tid];
       sm.m0[tid] = m;
-      if constexpr (MAIN) {
-        const T mhi = (T)m;
-        sm.Wt[2][tid] = mhi;
-        sm.Wt[3][tid] = (T)(m - (float)mhi);
-      }
+      const T mhi = (T)m;
+      sm.Wt[2][tid] = mhi;
+      sm.Wt[3][tid] = (T)(m - (float)mhi);
     }
     nb += Lc;
     lds_barrier();
   }
 
-  // ---- carry out
-  float* Sout = nullptr;
-  float* Cout = nullptr;
-  float* mout = nullptr;
-  float* ldout = nullptr;
-  bool cout_packed = false;
-  if constexpr (MAIN) {
-    if (seg == P - 1 && a.S_out != nullptr) {
-      Sout = a.S_out + (size_t)chain * D * D;
-      cout_packed = cpacked;
-      Cout = a.C_out + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
-      mout = a.ksum_out + (size_t)chain * D;
-      if (tid == 0) a.n_out[chain] = nb;
-    }
-  } else {
-    float* slot = slots + ((size_t)chain * P + seg) * slot_f;
-    Sout = slot;
-    Cout = slot + (size_t)D * D;
-    mout = slot + 2 * (size_t)D * D;
-    ldout = mout + D;
-  }
-  if (Sout != nullptr) {
+  // ---- carry out (last segment of the chain)
+  if (seg == P - 1 && a.S_out != nullptr) {
+    float* Sout = a.S_out + (size_t)chain * D * D;
+    float* Cout = a.C_out + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
     const int row = cw + l16;
 #pragma unroll
     for (int t = 0; t < NA; ++t) {
       const int col = 16 * t + 4 * g;
       *reinterpret_cast<f32x4*>(Sout + (size_t)row * D + col) = Sacc[t];
-      if (cout_packed)
+      if (cpacked)
         st_packed4<D>(Cout, row, col, Cacc[t]);
       else
         *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t];
     }
-    if (tid < D) {
-      mout[tid] = sm.m0[tid];
-      if (ldout != nullptr) ldout[tid] = sm.ldec[tid];
-    }
+    if (tid < D) a.ksum_out[(size_t)chain * D + tid] = sm.m0[tid];
+    if (tid == 0) a.n_out[chain] = nb;
   }
 }
 
+// ---------------------------------------------------------------- segment summaries
+
+// Segment summary (segments 0 .. P-2 of a chain, which always consist of whole chunks): from
+// a zero carry, C = sum K^T K and S^T = sum over chunks of diag(e^{B_63}) (S^T + (K e^-B)^T V)
+// (the carry update of the chunk algebra above), the key sum and the total log decay.
+// Nothing here depends on the queries, so the chunk loop is software-pipelined with one
+// barrier per chunk: in chunk i's interval every wave forms chunk i+1's decayed keys
+// (cumulative decay by MFMA, k e^-B, e^{B_63}) while it accumulates chunk i into the carries,
+// and the values of chunk i+1 and the keys and log decay of chunk i+2 stream into LDS.  Keys
+// are triple-buffered (chunk i feeds K^T K while chunk i+1 feeds the decay and chunk i+2
+// lands), the rest double-buffered.
 template <int D, typename T>
-__global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
-  gla_prefill_body<D, T, 1>(a);
-}
+struct SumSmem {
+  using C_ = Cfg<D, T>;
+  T Ks[3][kL][C_::PQ];
+  T Vs[2][kL][C_::PQ];
+  T Gs[2][kL][C_::PQ];
+  T Kp[2][kL][C_::PQ];  // k e^-B
+  float eBL[2][D];      // e^{B_63} per key channel
+};
 
 template <int D, typename T>
-__global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
-  gla_prefill_body<D, T, 0>(a);
+__global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
+  using C_ = Cfg<D, T>;
+  constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
+  __shared__ SumSmem<D, T> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int cw = 16 * w, hb = w & 1, cb = cw - 16 * hb;
+  const int P = a.segments, n = a.chunks_per_segment;
+  const int chain = blockIdx.x / (P - 1), seg = blockIdx.x % (P - 1);
+  const int cbeg = seg * n;
+  const size_t tok0 = (size_t)chain * (size_t)a.T;
+  const T* kg = static_cast<const T*>(a.k);
+  const T* vg = static_cast<const T*>(a.v);
+  const T* gg = static_cast<const T*>(a.log_alpha);
+  const bool norm = (a.flags & kFlagNormalizeKeys) != 0;
+  auto dma = [&](T (*dst)[PQ], const T* src, int i) {
+    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w, NW, lane);
+  };
+
+  f32x4 Cacc[NA], Sacc[NA];
+#pragma unroll
+  for (int t = 0; t < NA; ++t) Cacc[t] = Sacc[t] = zero4();
+  f32x4 ksum = zero4(), ldec = zero4();  // own channels cw + 4g + r (ldec valid where l16 == 15)
+  const Frag<T> Ih = ident_frag<T>(hb, lane);
+
+  // Chunk i's decayed keys into Kp[i & 1] and e^{B_63} into eBL[i & 1], for the wave's own
+  // channels; BT[ti][r] = B at token 16 ti + l16, channel cw + 4g + r.
+  auto decay_keys = [&](int i) {
+    T (*Ks)[PQ] = sm.Ks[i % 3];
+    T (*Gs)[PQ] = sm.Gs[i & 1];
+    T (*Kp)[PQ] = sm.Kp[i & 1];
+    f32x4 GT[4], KC[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      GT[ti] = zero4();  // log alpha at token 16 ti + 4 g + r, channel cw + l16
+      mma(GT[ti], lds_frag<T, KORD_CONTIG>(&Gs[0][0], PQ, 16 * ti, cb, lane), Ih);
+      KC[ti] = zero4();  // k at token 16 ti + l16, channel cw + 4g + r
+      mma(KC[ti], Ih, lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * ti, cb, lane));
+    }
+    const Frag<T> Ga = acc_frag<T>(GT[0], GT[1]);
+    const Frag<T> Gb = acc_frag<T>(GT[2], GT[3]);
+    f32x4 BT[4], ks = zero4();
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      BT[ti] = zero4();
+      mma(BT[ti], Ga, ltri_frag<T>(ti, 0, lane));
+      if (ti >= 2) mma(BT[ti], Gb, ltri_frag<T>(ti, 1, lane));
+      ks += KC[ti];
+      f32x4 kp;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kp[r] = KC[ti][r] * __expf(-BT[ti][r]);
+      st4<T>(&Kp[16 * ti + l16][cw + 4 * g], kp);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ks[r] += __shfl_xor(ks[r], off, 64);
+    }
+    ksum += ks;
+    ldec += BT[3];
+    if (l16 == 15) {  // token 63
+      const int c = cw + 4 * g;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.eBL[i & 1][c + r] = __expf(BT[3][r]);
+    }
+  };
+
+  // prologue: chunks 0 and 1 of keys and log decay, chunk 0 of values; chunk 0's decay
+  dma(sm.Ks[0], kg, 0);
+  dma(sm.Gs[0], gg, 0);
+  dma(sm.Vs[0], vg, 0);
+  if (n > 1) {
+    dma(sm.Ks[1], kg, 1);
+    dma(sm.Gs[1], gg, 1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (norm) {
+    normalize_rows<D, T, PQ>(sm.Ks[0], tid, 64 * NW);
+    if (n > 1) normalize_rows<D, T, PQ>(sm.Ks[1], tid, 64 * NW);
+    lds_barrier();
+  }
+  decay_keys(0);
+  lds_barrier();
+
+  for (int i = 0; i < n; ++i) {
+    // every buffer written here was last read in the previous interval
+    if (i + 1 < n) dma(sm.Vs[(i + 1) & 1], vg, i + 1);
+    if (i + 2 < n) {
+      dma(sm.Ks[(i + 2) % 3], kg, i + 2);
+      dma(sm.Gs[i & 1], gg, i + 2);
+    }
+    if (i + 1 < n) decay_keys(i + 1);
+
+    // carry update of chunk i: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
+    T (*Ks)[PQ] = sm.Ks[i % 3];
+    T (*Kp)[PQ] = sm.Kp[i & 1];
+    T (*Vs)[PQ] = sm.Vs[i & 1];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);
+      const Frag<T> Bv = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);
+#pragma unroll
+      for (int t0_ = 0; t0_ < NA; t0_ += 4) {
+        Frag<T> Ak[4], Ap[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          Ak[u] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
+          Ap[u] = tr_frag<T>(&Kp[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          mma(Cacc[t0_ + u], Ak[u], Bk);
+          mma(Sacc[t0_ + u], Ap[u], Bv);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NA; ++t) Sacc[t] *= *reinterpret_cast<const f32x4*>(&sm.eBL[i & 1][16 * t + 4 * g]);
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (norm && i + 2 < n) {  // chunk i+2's keys have landed: unit rows before their first use
+      normalize_rows<D, T, PQ>(sm.Ks[(i + 2) % 3], tid, 64 * NW);
+      lds_barrier();
+    }
+  }
+
+  // slot of (chain, seg): S | C | ksum | log decay
+  float* slot = static_cast<float*>(a.workspace) + ((size_t)chain * P + seg) * (2 * (size_t)D * D + 2 * D);
+  {
+    const int row = cw + l16;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      const int col = 16 * t + 4 * g;
+      *reinterpret_cast<f32x4*>(slot + (size_t)row * D + col) = Sacc[t];
+      *reinterpret_cast<f32x4*>(slot + (size_t)D * D + (size_t)row * D + col) = Cacc[t];
+    }
+    const int c = cw + 4 * g;
+    if (l16 == 0) *reinterpret_cast<f32x4*>(slot + 2 * (size_t)D * D + c) = ksum;
+    if (l16 == 15) *reinterpret_cast<f32x4*>(slot + 2 * (size_t)D * D + D + c) = ldec;
+  }
 }
 
 // Exclusive scan of segment summaries into carry-ins, in place.  Slot p holds the summary
