@@ -21,6 +21,10 @@ Sources, cited by page title and section:
   GLA, S_t = S_{t-1} diag(alpha_t) + v_t k_t^T with alpha per key channel, and
   Gated DeltaNet, S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
 
+* The key-covariance subspace diagnostic (``subspace.py``) follows the 10100.com
+  write-up's section "记忆体检" (Δμ: needle vs distractor alignment with the top-16
+  eigen-subspace of the key covariance).
+
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, brute force, library routines and hand-derived fixtures
 (``tests/golden``).  No function is left "parity unpinned".
@@ -39,3 +43,4 @@ from .ccq import (  # noqa: F401
     unit_keys,
     unpack_upper,
 )
+from .subspace import covariance_from_sums, delta_mu, subspace_alignment, top_eigen  # noqa: F401
