@@ -254,6 +254,59 @@ def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False):
                 tokens_per_s=N / (ms * 1e-3))
 
 
+def time_subspace(calls, warmup, r=16):
+    """Key-covariance subspace diagnostic on B=4, H=16, T=4096, d=128 bf16 keys with 16 leading
+    directions and a needle every 64 tokens; the statistics come from a GLA prefill of those
+    keys (the carry), the call computes eigenvalues, the top-16 basis, every key's alignment
+    and Δμ per head."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_fwd_chunked, ccq_key_subspace
+    from curvature_conditioned_query_amd.inputs import subspace_keys
+    B, H, T, d = 4, 16, 4096, 128
+    k_np, needle_np = subspace_keys(B, H, T, d, 1005, "bf16")
+    bf = torch.bfloat16
+    k = torch.from_numpy(k_np).cuda().to(bf)
+    needle = torch.from_numpy(needle_np).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(1005)
+    q = torch.randn((B, H, T, d), generator=gen, device="cuda").to(bf)
+    v = torch.randn((B, H, T, d), generator=gen, device="cuda").to(bf)
+    g = (torch.nn.functional.logsigmoid(torch.randn((B, H, T, d), generator=gen, device="cuda")) / 16).to(bf)
+    w = (torch.randn((H, d), generator=gen, device="cuda") / np.sqrt(d)).contiguous()
+    b = torch.full((H,), -2.0, device="cuda")
+    S = torch.empty((B, H, d, d), device="cuda")
+    C = torch.empty((B, H, d * (d + 1) // 2), device="cuda")
+    m = torch.empty((B, H, d), device="cuda")
+    n = torch.empty((B, H), dtype=torch.int64, device="cuda")
+    ccq_fwd_chunked("gla", q, k, v, g, None, w, b, carry_out=(S, C, m, n), packed_cov=True)
+    for _ in range(warmup):
+        out = ccq_key_subspace(C, m, n, k, r=r, needle=needle, packed_cov=True)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        out = ccq_key_subspace(C, m, n, k, r=r, needle=needle, packed_cov=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    dmu = out[3].float().cpu().numpy()
+    sweeps = torch.empty((B, H), dtype=torch.int32, device="cuda")
+    ccq_key_subspace(C, m, n, k, r=r, needle=needle, packed_cov=True, sweeps=sweeps)
+    torch.cuda.synchronize()
+    sw = sweeps.cpu().numpy()
+    return dict(name=f"ccq-key-subspace-B{B}H{H}T{T}d{d}-r{r}", ms=ms, heads=B * H, tokens=B * T,
+                delta_mu_mean=float(np.nanmean(dmu)), sweeps=sw, flops=float(sw.sum()) * jacobi_sweep_flops(d))
+
+
+def jacobi_sweep_flops(d):
+    """Algorithmic fp32 flops of one sweep of the parallel Jacobi method on a d x d symmetric
+    matrix with eigenvectors: d - 1 steps, each rotating the d/2 (d/2 - 1)/2 off-diagonal
+    2 x 2 blocks on both sides (24 flops), the d/2 diagonal blocks (4) and two rows of the
+    eigenvector matrix per pair (6 per column)."""
+    npairs = d // 2
+    return (d - 1) * (npairs * (npairs - 1) // 2 * 24 + npairs * 4 + npairs * d * 6)
+
+
 # ------------------------------------------------------------------ CPU oracle leg
 def _oracle_slab(args):
     import oracle
@@ -312,6 +365,8 @@ def main(argv=None):
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet prefill leg")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill leg (profiling the decode kernel alone)")
+    ap.add_argument("--no-subspace", action="store_true", help="skip the key-subspace diagnostic leg")
+    ap.add_argument("--subspace-only", action="store_true", help="run the key-subspace diagnostic leg alone")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -336,6 +391,11 @@ def main(argv=None):
             torch.neg(src, out=dst)  # streams n*4 bytes in and n*4 bytes out
         torch.cuda.synchronize()
         del src, dst
+    if args.subspace_only:
+        sres = time_subspace(5, 1)
+        print(f"# {sres['name']}: {sres['ms']:.3f} ms/call, sweeps {sres['sweeps'].min()}..{sres['sweeps'].max()}, "
+              f"{sres['flops'] / (sres['ms'] * 1e-3) / 1e12:.3f} TFLOP/s", file=sys.stderr, flush=True)
+        return 0
     if args.no_prefill:
         for packed in (False, True):
             dres = time_decode(args.decode_steps, 3, packed_cov=packed)
@@ -436,6 +496,22 @@ def main(argv=None):
             }
             print(f"# {dres['name']}: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s",
                   file=sys.stderr, flush=True)
+    if not args.no_subspace:
+        sres = time_subspace(5, 1)
+        s_tf = sres["flops"] / (sres["ms"] * 1e-3) / 1e12
+        out["subspace"] = {"workload": sres["name"], "ms_per_call": round(sres["ms"], 4),
+                           "heads_per_s": round(sres["heads"] / (sres["ms"] * 1e-3), 1),
+                           "delta_mu_mean": round(sres["delta_mu_mean"], 4),
+                           "sweeps": {"min": int(sres["sweeps"].min()), "max": int(sres["sweeps"].max()),
+                                      "mean": round(float(sres["sweeps"].mean()), 2)},
+                           "roofline": dict(bound="alu", achieved=round(s_tf, 3), peak=FP32_PEAK_TFLOPS,
+                                            unit="TFLOP/s", frac=round(s_tf / FP32_PEAK_TFLOPS, 5),
+                                            traffic=None, kernel="subspace_eigen_kernel<128> (with the "
+                                            "alignment and delta kernels in the timed call)",
+                                            algorithmic_flops_per_call=sres["flops"])}
+        print(f"# {sres['name']}: {sres['ms']:.3f} ms/call (eigen-decomposition of {sres['heads']} heads, "
+              f"alignment of {sres['tokens']} tokens x 16 heads), mean delta-mu {sres['delta_mu_mean']:+.4f}",
+              file=sys.stderr, flush=True)
     if not args.no_cpu:
         try:
             ncpu = len(os.sched_getaffinity(0))

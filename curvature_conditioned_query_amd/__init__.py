@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     ccq_decode_step,
     ccq_fwd_chunked,
     ccq_fwd_workspace_bytes,
+    ccq_key_subspace,
     library_path,
     load_library,
 )

@@ -25,6 +25,7 @@ EXPORTED_SYMBOLS = (
     "ccq_fwd_chunked",
     "ccq_fwd_workspace_bytes",
     "ccq_decode_step",
+    "ccq_key_subspace",
     "ccq_status_string",
     "ccq_abi_version",
 )
@@ -81,6 +82,8 @@ def load_library():
     lib.ccq_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ccq_decode_step.argtypes = [i32, i32, i32, i32, i32, i32] + [vp] * 12 + [i32, vp]
     lib.ccq_decode_step.restype = ctypes.c_int
+    lib.ccq_key_subspace.argtypes = [i32] * 6 + [vp] * 10 + [i32, vp]
+    lib.ccq_key_subspace.restype = ctypes.c_int
     lib.ccq_status_string.argtypes = [i32]
     lib.ccq_status_string.restype = ctypes.c_char_p
     lib.ccq_abi_version.argtypes = []
@@ -262,3 +265,42 @@ def ccq_decode_step(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ks
     if st != 0:
         raise CcqError(st, "ccq_decode_step")
     return o
+
+
+def ccq_key_subspace(C, ksum, n, k, r: int = 16, needle=None, packed_cov: bool = False, stream=None,
+                     sweeps=None):
+    """Key-covariance subspace diagnostic through the C ABI (see ``ccq_key_subspace`` in ccq.h).
+    C [B, H, d, d] (or packed [B, H, d (d + 1) / 2]), ksum [B, H, d], n [B, H] int64: the
+    statistics; k [B, H, T, d]: the keys to score; needle [B, H, T] bool / uint8 or None;
+    sweeps: optional int32 [B, H] tensor that receives the Jacobi sweep counts.
+    Returns (eigvals [B, H, d], basis [B, H, r, d], align [B, H, T], delta_mu [B, H] or None),
+    allocated with torch on k's device."""
+    import torch
+    lib = load_library()
+    B, H, T, d = k.shape
+    _check_dev("k", k)
+    for name, t, dt in (("C", C, torch.float32), ("ksum", ksum, torch.float32), ("n", n, torch.int64)):
+        _check_dev(name, t, dt)
+    _check_numel("C", C, B * H * cov_numel(d, packed_cov))
+    _check_numel("ksum", ksum, B * H * d)
+    _check_numel("n", n, B * H)
+    dev = k.device
+    eig = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    basis = torch.empty((B, H, r, d), dtype=torch.float32, device=dev)
+    align = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    if sweeps is not None:
+        _check_dev("sweeps", sweeps, torch.int32)
+        _check_numel("sweeps", sweeps, B * H)
+    dmu = None
+    nd = None
+    if needle is not None:
+        nd = needle.to(torch.uint8).contiguous()
+        _check_dev("needle", nd)
+        _check_numel("needle", nd, B * H * T)
+        dmu = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = lib.ccq_key_subspace(_dtype_code(k), B, H, T, d, r, _ptr(C), _ptr(ksum), _ptr(n), _ptr(k), _ptr(nd),
+                              _ptr(eig), _ptr(basis), _ptr(align), _ptr(dmu), _ptr(sweeps),
+                              FLAG_PACKED_COV if packed_cov else 0, _stream_handle(stream))
+    if st != 0:
+        raise CcqError(st, "ccq_key_subspace")
+    return eig, basis, align, dmu

@@ -47,6 +47,19 @@ __host__ __device__ inline int packed_index(int i, int j, int d) {
   return r * d - r * (r - 1) / 2 + (c - r);
 }
 
+// Key-covariance subspace diagnostic (one call after validation).
+constexpr int kMaxSubspaceRank = 32;
+struct SubspaceArgs {
+  int dtype, B, H, T, d, r, flags;
+  const float *C, *ksum;
+  const int64_t* n;
+  const void* k;
+  const uint8_t* needle;
+  float *eigvals, *basis, *align, *delta_mu;
+  int32_t* sweeps;
+};
+hipError_t launch_subspace(const SubspaceArgs& a, hipStream_t stream);
+
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).
 size_t fwd_slot_bytes(int d);

@@ -415,6 +415,23 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
   auto dma = [&](T (*dst)[PQ], const T* src, int i) {
     dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w, NW, lane);
   };
+  // the m-th load instruction this wave issues for a tile (waves w, w + NW, ... share a tile)
+  auto dma_part = [&](T (*dst)[PQ], const T* src, int i, int m) {
+    dma_unit<D, T, PQ>(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w + NW * m, lane);
+  };
+  constexpr int kParts = (PQ * (int)sizeof(T) / 16 + NW - 1) / NW;  // instructions per wave and tile
+  // Loads of an interval in the order they are issued, one instruction at a time between
+  // compute steps: values of chunk i+1, then keys and log decay of chunk i+2.
+  auto issue = [&](int i, int q) {
+    if (q < kParts) {
+      if (i + 1 < n) dma_part(sm.Vs[(i + 1) & 1], vg, i + 1, q);
+    } else if (q < 2 * kParts) {
+      if (i + 2 < n) dma_part(sm.Ks[(i + 2) % 3], kg, i + 2, q - kParts);
+    } else if (q < 3 * kParts) {
+      if (i + 2 < n) dma_part(sm.Gs[i & 1], gg, i + 2, q - 2 * kParts);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   f32x4 Cacc[NA], Sacc[NA];
 #pragma unroll
@@ -483,13 +500,13 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
   lds_barrier();
 
   for (int i = 0; i < n; ++i) {
-    // every buffer written here was last read in the previous interval
-    if (i + 1 < n) dma(sm.Vs[(i + 1) & 1], vg, i + 1);
-    if (i + 2 < n) {
-      dma(sm.Ks[(i + 2) % 3], kg, i + 2);
-      dma(sm.Gs[i & 1], gg, i + 2);
-    }
+    // Every buffer a load writes here was last read in the previous interval.  The loads are
+    // spread over the interval one instruction at a time: a burst of them stalls the issuing
+    // waves while the CU's vector-memory path drains it.
+    issue(i, 0);
     if (i + 1 < n) decay_keys(i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(i, 1);
 
     // carry update of chunk i: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
     T (*Ks)[PQ] = sm.Ks[i % 3];
@@ -513,8 +530,11 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
           mma(Cacc[t0_ + u], Ak[u], Bk);
           mma(Sacc[t0_ + u], Ap[u], Bv);
         }
+        issue(i, 2 + kk * (NA / 4) + t0_ / 4);
       }
     }
+#pragma unroll
+    for (int q = 2 + 2 * (NA / 4); q < 3 * kParts; ++q) issue(i, q);
 #pragma unroll
     for (int t = 0; t < NA; ++t) Sacc[t] *= *reinterpret_cast<const f32x4*>(&sm.eBL[i & 1][16 * t + 4 * g]);
 

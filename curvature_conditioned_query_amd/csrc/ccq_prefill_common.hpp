@@ -146,19 +146,25 @@ __device__ __forceinline__ int tri_col(int idx) {
 // wait themselves: s_waitcnt vmcnt(0), then a barrier, before the tile is read.  Loads the
 // compiler does issue are still waited for correctly (the counter drains in order, so loads
 // it does not know about only make its own waits stricter).
+// Instruction j (0 <= j < PQ * sizeof(T) / 16) of such a tile load; does nothing for larger j.
 template <int D, typename T, int PQ>
-__device__ __forceinline__ void dma_tile(T (*dst)[PQ], const T* src, int Lc, int w, int nw, int lane) {
+__device__ __forceinline__ void dma_unit(T (*dst)[PQ], const T* src, int Lc, int j, int lane) {
   constexpr int U = PQ * (int)sizeof(T) / 16, DU = D * (int)sizeof(T) / 16, EPU = 16 / (int)sizeof(T);
   static_assert(PQ * sizeof(T) % 16 == 0, "rows must be whole 16-byte units");
+  if (j >= U) return;
   const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) T*)&dst[0][0];
-  for (int j = w; j < U; j += nw) {
-    const int u = 64 * j + lane;
-    const int row = u / U, slot = u - row * U;
-    const bool ok = row < Lc && slot < DU;
-    const T* p = src + (ok ? row * D + slot * EPU : 0);
-    const unsigned m0 = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)j);
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p) : "memory", "m0");
-  }
+  const int u = 64 * j + lane;
+  const int row = u / U, slot = u - row * U;
+  const bool ok = row < Lc && slot < DU;
+  const T* p = src + (ok ? row * D + slot * EPU : 0);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)j);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p) : "memory", "m0");
+}
+
+template <int D, typename T, int PQ>
+__device__ __forceinline__ void dma_tile(T (*dst)[PQ], const T* src, int Lc, int w, int nw, int lane) {
+  constexpr int U = PQ * (int)sizeof(T) / 16;
+  for (int j = w; j < U; j += nw) dma_unit<D, T, PQ>(dst, src, Lc, j, lane);
 }
 
 // C[row][col .. col + 3] of a symmetric D x D matrix held as its packed upper triangle (the

@@ -38,6 +38,7 @@ __all__ = [
     "gdn_inputs",
     "structured_inputs",
     "decode_tokens",
+    "subspace_keys",
     "WORKLOADS",
     "workload_inputs",
 ]
@@ -182,6 +183,31 @@ def structured_inputs(rule: str, B: int, H: int, T: int, d: int, seed: int,
     return PrefillInputs(rule, dtype, _store(q, dtype), _store(k, dtype), _store(v, dtype),
                          _store(g, dtype), beta, w.astype(np.float32),
                          np.full((H,), b_lam, dtype=np.float32))
+
+
+def subspace_keys(B: int, H: int, T: int, d: int, seed: int, dtype: str = "bf16", rank: int = 16,
+                  needle_every: int = 64):
+    """Keys for the key-covariance subspace diagnostic, and their needle mask.
+
+    Haystack keys are normalize(Q diag(s) z + 0.1 eps) with Q a random d x rank orthonormal
+    basis per head and s spread evenly over [2, 1], so the key covariance has ``rank``
+    distinct leading eigenvalues well above the rest; every ``needle_every``-th key is a
+    random unit vector (a needle, mostly off that subspace).  A stand-in for the retrieval
+    prompts of the 10100.com write-up's section "记忆体检".  Returns (k [B, H, T, d] stored
+    in dtype, as fp32; needle [B, H, T] bool)."""
+    rng = np.random.default_rng(seed)
+    G = rng.standard_normal((B, H, d, rank))
+    Q, _ = np.linalg.qr(G)
+    s = np.linspace(2.0, 1.0, rank)
+    z = rng.standard_normal((B, H, T, rank))
+    eps = rng.standard_normal((B, H, T, d))
+    k = np.einsum("bhdr,bhtr->bhtd", Q * s, z) + 0.1 * eps
+    needle = np.zeros((B, H, T), dtype=bool)
+    if needle_every > 0:
+        needle[:, :, needle_every - 1::needle_every] = True
+        k[needle] = rng.standard_normal((int(needle.sum()), d))
+    k = _unit_rows(k.astype(np.float32))
+    return _store(k, dtype), needle
 
 
 def decode_tokens(rule: str, N: int, H: int, d: int, seed: int, dtype: str = "bf16"):

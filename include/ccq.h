@@ -149,10 +149,38 @@ int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d
                     const void *beta, const float *w_lambda, const float *b_lambda, float *S,
                     float *C, float *ksum, int64_t *n, void *o, int32_t flags, void *hip_stream);
 
+/*
+ * Key-covariance subspace diagnostic (the geometric check of the 10100.com write-up, section
+ * "记忆体检": Δμ, how much less needle keys than distractor keys align with the top-16
+ * eigen-subspace of the key covariance; negative means the needle lies off the high-variance
+ * directions).  Per (b, h):
+ *   Sigma = C / n - mu mu^T with mu = ksum / n (the statistics of the read step; C, ksum, n as
+ *           carried by ccq_fwd_chunked / ccq_decode_step; n <= 0 gives Sigma = 0),
+ *   eigvals [B, H, d_k]    : the eigenvalues of Sigma, descending,
+ *   basis   [B, H, r, d_k] : the top-r unit eigenvectors as rows, each with its largest-
+ *                            magnitude entry positive (the lowest index among equal ones),
+ *   align   [B, H, T]      : a_t = |basis k_t|^2 / |k_t|^2 for every key k_t of k
+ *                            ([B, H, T, d_k] dtype; a_t = 0 for a zero key),
+ *   delta_mu [B, H]        : mean a_t over tokens with needle[b][h][t] != 0 minus the mean over
+ *                            the others (NaN when either set is empty); needle [B, H, T] uint8,
+ *   sweeps  [B, H] int32   : Jacobi sweeps the head took (optional, may be NULL).
+ * needle and delta_mu are both NULL (no Δμ) or both set; sweeps may be NULL; every other
+ * pointer is required.
+ * flags: CCQ_FLAG_PACKED_COV (C packed as for the other entry points); other bits are
+ * CCQ_ERR_INVALID_ARG.  1 <= r <= min(32, d_k); d_k in {64, 128}; B * H <= 65535; dtype as for
+ * the other entry points.  The eigenvectors come from the cyclic Jacobi method in fp32 (to about 1e-6 of the
+ * largest eigenvalue); the subspace, and with it a_t, is well defined when eigenvalue r
+ * exceeds eigenvalue r + 1.  Returns a ccq_status.
+ */
+int ccq_key_subspace(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d_k, int32_t r,
+                     const float *C, const float *ksum, const int64_t *n, const void *k,
+                     const uint8_t *needle, float *eigvals, float *basis, float *align,
+                     float *delta_mu, int32_t *sweeps, int32_t flags, void *hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 4. */
+/* ABI version of this header: 5. */
 int32_t ccq_abi_version(void);
 
 #ifdef __cplusplus

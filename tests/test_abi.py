@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 4
+    assert lib.ccq_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -104,3 +104,23 @@ def _dec(lib, rule=0, dtype=1, N=2, H=2, dk=128, dv=128, flags=0, **ptrs):
 ])
 def test_decode_argument_errors(lib, kw, code):
     assert _dec(lib, **kw) == code
+
+
+def _sub(lib, dtype=1, B=2, H=2, T=100, dk=128, r=16, flags=0, **ptrs):
+    names = ["C", "ksum", "n", "k", "needle", "eigvals", "basis", "align", "delta_mu", "sweeps"]
+    vals = {n: FAKE for n in names}
+    vals["sweeps"] = None
+    vals.update(ptrs)
+    return lib.ccq_key_subspace(dtype, B, H, T, dk, r, *[vals[n] for n in names], flags, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), INVALID), (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(r=0), INVALID),
+    (dict(dk=64, r=65), INVALID), (dict(r=33), UNSUPPORTED), (dict(dk=96, r=8), UNSUPPORTED),
+    (dict(B=300, H=300), UNSUPPORTED), (dict(C=None), INVALID), (dict(k=None), INVALID),
+    (dict(basis=None), INVALID), (dict(align=None), INVALID), (dict(needle=None), INVALID),
+    (dict(delta_mu=None), INVALID), (dict(flags=1), INVALID), (dict(flags=4), INVALID),
+    (dict(ksum=FAKE + 4), MISALIGNED), (dict(needle=FAKE + 1), MISALIGNED), (dict(sweeps=FAKE + 4), MISALIGNED),
+])
+def test_subspace_argument_errors(lib, kw, code):
+    assert _sub(lib, **kw) == code
