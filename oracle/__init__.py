@@ -21,6 +21,8 @@ Sources, cited by page title and section:
   GLA, S_t = S_{t-1} diag(alpha_t) + v_t k_t^T with alpha per key channel, and
   Gated DeltaNet, S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
 
+* The gradients of the recurrence (``grad.py``): the forward step once more in plain
+  PyTorch fp64, differentiated by torch.autograd, pinned to finite differences.
 * The key-covariance subspace diagnostic (``subspace.py``) follows the 10100.com
   write-up's section "记忆体检" (Δμ: needle vs distractor alignment with the top-16
   eigen-subspace of the key covariance).
@@ -44,3 +46,4 @@ from .ccq import (  # noqa: F401
     unpack_upper,
 )
 from .subspace import covariance_from_sums, delta_mu, subspace_alignment, top_eigen  # noqa: F401
+from .grad import ccq_sequence_backward, ccq_step_backward, ccq_step_torch  # noqa: F401
