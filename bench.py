@@ -32,6 +32,7 @@ FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 CHUNK = 64
 PREFILL_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill.hip")
 DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode.hip")
+BACKWARD_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_step_backward.hip")
 GDN_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill_gdn.hip")
 
 
@@ -298,6 +299,66 @@ def time_subspace(calls, warmup, r=16):
                 delta_mu_mean=float(np.nanmean(dmu)), sweeps=sw, flops=float(sw.sum()) * jacobi_sweep_flops(d))
 
 
+def step_backward_bytes_per_head(d, elem_bytes):
+    """Algorithmic HBM bytes of one backward step per (sequence, head): S, C and the adjoints dS,
+    dC (fp32 d x d) read, dS and dC written back; the token (q, k, v, log alpha) and w_lambda
+    read; ksum, n, d_o read, dksum read and written; dq, dk, dv, dlog_alpha, dw_lambda (fp32 d)
+    and db_lambda written."""
+    return 6 * d * d * 4 + 4 * d * elem_bytes + d * 4 + d * 4 + 8 + d * 4 + 2 * d * 4 + 5 * d * 4 + 4
+
+
+def time_step_backward(steps, warmup, rule="gla"):
+    """Backward of one recurrence step over the decode workload's shape (256 sequences x 16 heads,
+    d = 128, bf16 token, fp32 state and adjoints), K times in a row (the adjoints are updated in
+    place, as when walking a sequence backwards)."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_step_backward
+    N, H, d = 256, 16, 128
+    gen = torch.Generator(device="cuda").manual_seed(1006)
+    bf = torch.bfloat16
+    K = torch.randn((N, H, 32, d), generator=gen, device="cuda")
+    K = K / K.norm(dim=-1, keepdim=True)
+    C = 64 * (K.transpose(-1, -2).contiguous() @ K)
+    C = ((C + C.transpose(-1, -2)) / 2).contiguous()
+    m = (64 * K.sum(dim=2)).contiguous()
+    del K
+    n = torch.full((N, H), 2048, dtype=torch.int64, device="cuda")
+    S = (torch.randn((N, H, d, d), generator=gen, device="cuda") / np.sqrt(d)).contiguous()
+    dS = torch.zeros((N, H, d, d), device="cuda")
+    dC = torch.zeros((N, H, d, d), device="cuda")
+    dm = torch.zeros((N, H, d), device="cuda")
+    do = torch.randn((N, H, d), generator=gen, device="cuda")
+    q = torch.randn((N, H, d), generator=gen, device="cuda").to(bf)
+    k = torch.randn((N, H, d), generator=gen, device="cuda")
+    k = (k / k.norm(dim=-1, keepdim=True)).to(bf)
+    v = torch.randn((N, H, d), generator=gen, device="cuda").to(bf)
+    if rule == "gla":
+        g = (torch.nn.functional.logsigmoid(torch.randn((N, H, d), generator=gen, device="cuda")) / 16).to(bf)
+        beta = None
+    else:
+        g = (-torch.nn.functional.softplus(torch.randn((N, H), generator=gen, device="cuda")) / 8).to(bf)
+        beta = torch.sigmoid(torch.randn((N, H), generator=gen, device="cuda")).to(bf)
+    w = (torch.randn((H, d), generator=gen, device="cuda") / np.sqrt(d)).contiguous()
+    b = torch.full((H,), -2.0, device="cuda")
+
+    def step():
+        ccq_step_backward(rule, q, k, v, g, beta, w, b, S, C, m, n, do, dS, dC, dm)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = N * H * step_backward_bytes_per_head(d, 2)
+    return dict(name=f"ccq-{rule}-step-backward-N{N}H{H}d{d}", ms=ms, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
 def jacobi_sweep_flops(d):
     """Algorithmic fp32 flops of one sweep of the parallel Jacobi method on a d x d symmetric
     matrix with eigenvectors: d - 1 steps, each rotating the d/2 (d/2 - 1)/2 off-diagonal
@@ -366,6 +427,8 @@ def main(argv=None):
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill leg (profiling the decode kernel alone)")
     ap.add_argument("--no-subspace", action="store_true", help="skip the key-subspace diagnostic leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the step-backward leg")
+    ap.add_argument("--backward-only", action="store_true", help="run the step-backward leg alone")
     ap.add_argument("--subspace-only", action="store_true", help="run the key-subspace diagnostic leg alone")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
@@ -391,6 +454,12 @@ def main(argv=None):
             torch.neg(src, out=dst)  # streams n*4 bytes in and n*4 bytes out
         torch.cuda.synchronize()
         del src, dst
+    if args.backward_only:
+        for rule in ("gla", "gdn"):
+            bres = time_step_backward(args.decode_steps, 3, rule)
+            print(f"# {bres['name']}: {bres['ms'] * 1e3:.1f} us/step, {bres['gbs']:.1f} GB/s", file=sys.stderr,
+                  flush=True)
+        return 0
     if args.subspace_only:
         sres = time_subspace(5, 1)
         print(f"# {sres['name']}: {sres['ms']:.3f} ms/call, sweeps {sres['sweeps'].min()}..{sres['sweeps'].max()}, "
@@ -496,6 +565,19 @@ def main(argv=None):
             }
             print(f"# {dres['name']}: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s",
                   file=sys.stderr, flush=True)
+    if not args.no_backward:
+        bsrc = file_sha(BACKWARD_SRC)
+        out["step_backward"] = {}
+        for rule in ("gla", "gdn"):
+            bres = time_step_backward(args.decode_steps, 3, rule)
+            out["step_backward"][rule] = {
+                "workload": bres["name"], "ms_per_step": round(bres["ms"], 4),
+                "roofline": dict(bound="hbm", achieved=round(bres["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                                 frac=round(bres["gbs"] / HBM_PEAK_GBS, 4),
+                                 traffic=measured_traffic(f"traffic_{bres['name']}.json", bsrc)),
+                "algorithmic_bytes_per_step": bres["bytes"]}
+            print(f"# {bres['name']}: {bres['ms'] * 1e3:.1f} us/step, {bres['gbs']:.1f} GB/s", file=sys.stderr,
+                  flush=True)
     if not args.no_subspace:
         sres = time_subspace(5, 1)
         s_tf = sres["flops"] / (sres["ms"] * 1e-3) / 1e12

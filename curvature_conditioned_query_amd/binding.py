@@ -26,6 +26,7 @@ EXPORTED_SYMBOLS = (
     "ccq_fwd_workspace_bytes",
     "ccq_decode_step",
     "ccq_key_subspace",
+    "ccq_step_backward",
     "ccq_status_string",
     "ccq_abi_version",
 )
@@ -84,6 +85,8 @@ def load_library():
     lib.ccq_decode_step.restype = ctypes.c_int
     lib.ccq_key_subspace.argtypes = [i32] * 6 + [vp] * 10 + [i32, vp]
     lib.ccq_key_subspace.restype = ctypes.c_int
+    lib.ccq_step_backward.argtypes = [i32] * 6 + [vp] * 22 + [i32, vp]
+    lib.ccq_step_backward.restype = ctypes.c_int
     lib.ccq_status_string.argtypes = [i32]
     lib.ccq_status_string.restype = ctypes.c_char_p
     lib.ccq_abi_version.argtypes = []
@@ -304,3 +307,42 @@ def ccq_key_subspace(C, ksum, n, k, r: int = 16, needle=None, packed_cov: bool =
     if st != 0:
         raise CcqError(st, "ccq_key_subspace")
     return eig, basis, align, dmu
+
+
+def ccq_step_backward(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, d_o, dS, dC, dksum,
+                      stream=None):
+    """Backward of one recurrence step through the C ABI (see ``ccq_step_backward`` in ccq.h).
+    The carry before the step (S, C, ksum, n), the token and d_o are inputs; dS, dC, dksum (fp32)
+    hold the adjoint of the carry after the step and are overwritten with the adjoint before it.
+    Returns a dict of fp32 tensors: dq, dk, dv, dlog_alpha, dbeta (GDN), dw_lambda [N, H, d_k],
+    db_lambda [N, H] (per sequence)."""
+    import torch
+    lib = load_library()
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("beta", beta)):
+        _check_dev(name, t, q.dtype)
+    for name, t, dt in (("w_lambda", w_lambda, torch.float32), ("b_lambda", b_lambda, torch.float32),
+                        ("S", S, torch.float32), ("C", C, torch.float32), ("ksum", ksum, torch.float32),
+                        ("n", n, torch.int64), ("d_o", d_o, torch.float32), ("dS", dS, torch.float32),
+                        ("dC", dC, torch.float32), ("dksum", dksum, torch.float32)):
+        _check_dev(name, t, dt)
+    for name, t, cnt in (("S", S, N * H * d_v * d_k), ("C", C, N * H * d_k * d_k), ("ksum", ksum, N * H * d_k),
+                         ("n", n, N * H), ("d_o", d_o, N * H * d_v), ("dS", dS, N * H * d_v * d_k),
+                         ("dC", dC, N * H * d_k * d_k), ("dksum", dksum, N * H * d_k)):
+        _check_numel(name, t, cnt)
+    rule_c = _rule_code(rule)
+    dev = q.device
+    f = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((N, H, d_k), **f), dk=torch.empty((N, H, d_k), **f), dv=torch.empty((N, H, d_v), **f),
+               dlog_alpha=torch.empty((N, H, d_k) if rule_c == CCQ_RULE_GLA else (N, H), **f),
+               dbeta=None if rule_c == CCQ_RULE_GLA else torch.empty((N, H), **f),
+               dw_lambda=torch.empty((N, H, d_k), **f), db_lambda=torch.empty((N, H), **f))
+    st = lib.ccq_step_backward(rule_c, _dtype_code(q), N, H, d_k, d_v, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                               _ptr(beta), _ptr(w_lambda), _ptr(b_lambda), _ptr(S), _ptr(C), _ptr(ksum), _ptr(n),
+                               _ptr(d_o), _ptr(dS), _ptr(dC), _ptr(dksum), _ptr(out["dq"]), _ptr(out["dk"]),
+                               _ptr(out["dv"]), _ptr(out["dlog_alpha"]), _ptr(out["dbeta"]), _ptr(out["dw_lambda"]),
+                               _ptr(out["db_lambda"]), 0, _stream_handle(stream))
+    if st != 0:
+        raise CcqError(st, "ccq_step_backward")
+    return out

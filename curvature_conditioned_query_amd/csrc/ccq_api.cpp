@@ -73,7 +73,7 @@ size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 5; }
+int32_t ccq_abi_version(void) { return 6; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -170,6 +170,34 @@ int ccq_key_subspace(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d_k
   ccq::SubspaceArgs a{dtype, B, H, T, d_k, r, flags, C, ksum, n, k, needle, eigvals, basis, align, delta_mu,
                       sweeps};
   const hipError_t e = ccq::launch_subspace(a, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
+}
+
+int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v, const void* q,
+                      const void* k, const void* v, const void* log_alpha, const void* beta, const float* w_lambda,
+                      const float* b_lambda, const float* S, const float* C, const float* ksum, const int64_t* n,
+                      const float* d_o, float* dS, float* dC, float* dksum, float* dq, float* dk, float* dv,
+                      float* dlog_alpha, float* dbeta, float* dw_lambda, float* db_lambda, int32_t flags,
+                      void* hip_stream) {
+  if (rule != CCQ_RULE_GLA && rule != CCQ_RULE_GDN) return CCQ_ERR_INVALID_ARG;
+  if (dtype != CCQ_DTYPE_F32 && dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
+  if (N <= 0 || H <= 0 || d_k <= 0 || d_v <= 0) return CCQ_ERR_INVALID_ARG;
+  if (flags & ~(CCQ_FLAG_NORMALIZE_KEYS | CCQ_FLAG_PACKED_COV)) return CCQ_ERR_INVALID_ARG;
+  if (flags != 0) return CCQ_ERR_UNSUPPORTED;
+  if (d_k != d_v || d_k != 128) return CCQ_ERR_UNSUPPORTED;
+  if ((long long)N * H > 0x7fffffffLL) return CCQ_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !log_alpha || !w_lambda || !b_lambda || !S || !C || !ksum || !n || !d_o || !dS || !dC ||
+      !dksum || !dq || !dk || !dv || !dlog_alpha || !dw_lambda || !db_lambda)
+    return CCQ_ERR_INVALID_ARG;
+  if ((rule == CCQ_RULE_GDN) != (beta != nullptr) || (rule == CCQ_RULE_GDN) != (dbeta != nullptr))
+    return CCQ_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, d_o, dS, dC,
+                        dksum, dq, dk, dv, dlog_alpha, dbeta, dw_lambda, db_lambda};
+  for (const void* pp : ptrs)
+    if (misaligned(pp)) return CCQ_ERR_MISALIGNED;
+  ccq::StepBackArgs a{rule, dtype, N, H, d_k, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, d_o,
+                      dS, dC, dksum, dq, dk, dv, dlog_alpha, dbeta, dw_lambda, db_lambda};
+  const hipError_t e = ccq::launch_step_backward(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }
 

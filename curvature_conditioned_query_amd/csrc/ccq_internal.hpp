@@ -60,6 +60,19 @@ struct SubspaceArgs {
 };
 hipError_t launch_subspace(const SubspaceArgs& a, hipStream_t stream);
 
+// Backward of one recurrence step (one call after validation).
+struct StepBackArgs {
+  int rule, dtype, N, H, d;
+  const void *q, *k, *v, *log_alpha, *beta;
+  const float *w_lambda, *b_lambda;
+  const float *S, *C, *ksum;
+  const int64_t* n;
+  const float* d_o;
+  float *dS, *dC, *dksum;
+  float *dq, *dk, *dv, *dlog_alpha, *dbeta, *dw, *db;
+};
+hipError_t launch_step_backward(const StepBackArgs& a, hipStream_t stream);
+
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).
 size_t fwd_slot_bytes(int d);

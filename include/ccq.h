@@ -177,10 +177,36 @@ int ccq_key_subspace(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d_k
                      const uint8_t *needle, float *eigvals, float *basis, float *align,
                      float *delta_mu, int32_t *sweeps, int32_t flags, void *hip_stream);
 
+/*
+ * Backward of one step of the recurrence (the adjoint of ccq_decode_step), for training: the
+ * pages train CCQ models from scratch (10100.com write-up, section "方法解析" point 3).  For N
+ * sequences x H heads, given the carry BEFORE the step (S, C, ksum, n: as ccq_decode_step reads
+ * them, full-matrix C), the token (q, k, v, log_alpha, beta), the gate parameters, the output
+ * gradient d_o [N, H, d_v] fp32 and the adjoint of the carry AFTER the step (dS [N, H, d_v, d_k],
+ * dC [N, H, d_k, d_k], dksum [N, H, d_k], fp32; zeros after the last token), it
+ *   - overwrites dS, dC, dksum in place with the adjoint of the carry BEFORE the step (dC is
+ *     the adjoint of C as a general matrix; only its symmetric part acts on keys),
+ *   - writes the fp32 gradients dq, dk [N, H, d_k], dv [N, H, d_v], dlog_alpha (GLA [N, H, d_k],
+ *     GDN [N, H]), dbeta (GDN [N, H]; GLA: NULL), and per-sequence gate-parameter gradients
+ *     dw_lambda [N, H, d_k] and db_lambda [N, H] (the gradient of the shared [H, d_k] / [H]
+ *     parameters is their sum over sequences and steps).
+ * Running it over the tokens of a sequence in reverse order, each time from that token's carry
+ * before the step, gives the gradients of the whole recurrence (backpropagation through time).
+ * Inputs are used as given (flags must be 0: no in-kernel key normalisation, full C).
+ * d_k == d_v == 128; dtype is that of q, k, v, log_alpha, beta.  Returns a ccq_status.
+ */
+int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                      const void *q, const void *k, const void *v, const void *log_alpha,
+                      const void *beta, const float *w_lambda, const float *b_lambda,
+                      const float *S, const float *C, const float *ksum, const int64_t *n,
+                      const float *d_o, float *dS, float *dC, float *dksum, float *dq, float *dk,
+                      float *dv, float *dlog_alpha, float *dbeta, float *dw_lambda,
+                      float *db_lambda, int32_t flags, void *hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int32_t ccq_abi_version(void);
 
 #ifdef __cplusplus

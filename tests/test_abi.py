@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 5
+    assert lib.ccq_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -124,3 +124,27 @@ def _sub(lib, dtype=1, B=2, H=2, T=100, dk=128, r=16, flags=0, **ptrs):
 ])
 def test_subspace_argument_errors(lib, kw, code):
     assert _sub(lib, **kw) == code
+
+
+def _sb(lib, rule=0, dtype=1, N=2, H=2, dk=128, dv=128, flags=0, **ptrs):
+    names = ["q", "k", "v", "log_alpha", "beta", "w_lambda", "b_lambda", "S", "C", "ksum", "n", "d_o", "dS", "dC",
+             "dksum", "dq", "dk", "dv", "dlog_alpha", "dbeta", "dw_lambda", "db_lambda"]
+    vals = {n: FAKE for n in names}
+    if rule == 0:
+        vals["beta"] = vals["dbeta"] = None
+    vals.update(ptrs)
+    return lib.ccq_step_backward(rule, dtype, N, H, dk, dv, *[vals[n] for n in names], flags, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rule=2), INVALID), (dict(dtype=9), INVALID), (dict(N=0), INVALID), (dict(dk=64, dv=64), UNSUPPORTED),
+    (dict(dk=128, dv=64), UNSUPPORTED), (dict(flags=1), UNSUPPORTED), (dict(flags=2), UNSUPPORTED),
+    (dict(flags=4), INVALID), (dict(q=None), INVALID), (dict(d_o=None), INVALID), (dict(dS=None), INVALID),
+    (dict(dw_lambda=None), INVALID), (dict(beta=FAKE), INVALID), (dict(dbeta=FAKE), INVALID),
+    (dict(rule=1, beta=None, dbeta=FAKE), INVALID), (dict(rule=1, beta=FAKE, dbeta=None), INVALID),
+    (dict(dC=FAKE + 4), MISALIGNED),
+])
+def test_step_backward_argument_errors(lib, kw, code):
+    # every case must fail validation: a call that passed it would launch on the fake pointers
+    assert code != OK
+    assert _sb(lib, **kw) == code
