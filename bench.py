@@ -139,18 +139,27 @@ def time_prefill(wl, steps, warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    # the throughput: K back-to-back passes with nothing else on the stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = e0.elapsed_time(e1)
+    # per-kernel launch durations: K more passes with the events the library records on its
+    # stream around its kernels (each record adds a few microseconds between the kernels,
+    # so these passes are not the ones the throughput comes from)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
         step(i)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    total_ms = ev[0].elapsed_time(ev[steps])
-    # per-kernel launch durations from the events the library records on its stream
     phases = {name: float(np.mean([hip.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(steps)]))
               for a, name in enumerate(("summary", "scan", "main"))}
     hip.destroy()
