@@ -67,8 +67,10 @@ def trace_summary(paths, command, title):
     return "\n".join(out)
 
 
-def counter_per_dispatch(db_path, counter, kernel_regex):
-    """Average per-dispatch value of `counter` over the dispatches whose kernel name matches."""
+def counter_per_dispatch(db_path, counter, kernel_regex, largest_only=False):
+    """Average per-dispatch value of `counter` over the dispatches whose kernel name matches
+    (with largest_only, over those within 5 % of the largest: the calibration copies, not the
+    small launches of the same torch kernel that building the inputs may make)."""
     db = sqlite3.connect(db_path)
     cur = db.cursor()
     rows = cur.execute("select kernel_name, dispatch_id, counter_name, value, duration from counters_collection").fetchall()
@@ -84,6 +86,10 @@ def counter_per_dispatch(db_path, counter, kernel_regex):
         names.add(_short(k))
     if not per:
         raise SystemExit(f"{db_path}: no {counter} rows for kernels matching {kernel_regex!r}")
+    if largest_only:
+        top = max(per.values())
+        per = {d: v for d, v in per.items() if v >= 0.95 * top}
+        dur = {d: dur[d] for d in per}
     n = len(per)
     return sum(per.values()) / n, n, sum(dur.values()) / n / 1e3, sorted(names)
 
@@ -91,8 +97,8 @@ def counter_per_dispatch(db_path, counter, kernel_regex):
 def traffic_summary(a):
     f_k, n_f, us_f, names = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
     w_k, n_w, us_w, _ = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
-    cf_k, _, _, _ = counter_per_dispatch(a.fetch, "FETCH_SIZE", CALIB_KERNEL)
-    cw_k, _, _, _ = counter_per_dispatch(a.write, "WRITE_SIZE", CALIB_KERNEL)
+    cf_k, _, _, _ = counter_per_dispatch(a.fetch, "FETCH_SIZE", CALIB_KERNEL, largest_only=True)
+    cw_k, _, _, _ = counter_per_dispatch(a.write, "WRITE_SIZE", CALIB_KERNEL, largest_only=True)
     calib_bytes = a.calib_mib * (1 << 20)
     s_fetch = calib_bytes / (cf_k * 1024.0)
     s_write = calib_bytes / (cw_k * 1024.0)
