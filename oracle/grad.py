@@ -88,10 +88,14 @@ def ccq_step_backward(q, k, v, g, beta, w_lam, b_lam, rule: str, S, C, m, n, do,
     return out
 
 
-def ccq_sequence_backward(q, k, v, g, beta, w_lam, b_lam, rule: str, do, carry=None):
-    """Gradients of L = <do, o> through the whole recurrence over T tokens (inputs [B,H,T,...],
-    numpy, fp64): dq, dk, dv, dg, dbeta (GDN), dw [H,d], db [H], and the adjoint of the carry
-    in (dS, dC, dm) when one is given.  The reference for chaining the step backward in reverse."""
+def ccq_sequence_backward(q, k, v, g, beta, w_lam, b_lam, rule: str, do, carry=None, dS_T=None, dC_T=None,
+                          dm_T=None):
+    """Gradients of L = <do, o> + <dS_T, S_T> + <dC_T, C_T> + <dm_T, m_T> through the whole
+    recurrence over T tokens (inputs [B,H,T,...], numpy, fp64; the last three terms are present
+    when the adjoint of the carry after the last token is given, [B,H,...] each): dq, dk, dv, dg,
+    dbeta (GDN), dw [H,d], db [H], and the adjoint of the carry in (dS, dC, dm; of the zero carry
+    when none is given).  The reference for chaining the step backward in reverse and for the
+    chunked backward."""
     q, k, v, g, do = (_t(x) for x in (q, k, v, g, do))
     beta = _t(beta)
     w = _t(w_lam)
@@ -117,6 +121,9 @@ def ccq_sequence_backward(q, k, v, g, beta, w_lam, b_lam, rule: str, do, carry=N
         o, St, Ct, mt = ccq_step_torch(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t], bt, w, b, rule, St, Ct, mt, nt)
         nt = nt + 1.0
         L = L + (o * do[:, :, t]).sum()
+    for adj, state in ((dS_T, St), (dC_T, Ct), (dm_T, mt)):
+        if adj is not None:
+            L = L + (state * _t(adj)).sum()
     keys = [kk for kk, t in leaves.items() if t is not None]
     grads = torch.autograd.grad(L, [leaves[kk] for kk in keys], allow_unused=True)
     return {"d" + kk: (np.zeros(leaves[kk].shape) if gr is None else gr.detach().numpy())

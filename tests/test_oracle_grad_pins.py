@@ -145,6 +145,61 @@ def test_sequence_backward_finite_differences_and_step_chain(rule):
     assert np.allclose(dw, seq["dw"], atol=1e-10)
 
 
+@pytest.mark.parametrize("rule", ["gla", "gdn"])
+def test_sequence_backward_carry_adjoints(rule):
+    """With a carry in and the adjoint of the carry out given: the gradients against central
+    finite differences of the numpy recurrence with the terms <dS_T, S_T> + <dC_T, C_T> +
+    <dm_T, m_T> in the loss (inputs and carry in), and the whole sequence against its two
+    halves chained (the second half's carry-in adjoint is the first half's carry-out adjoint)."""
+    gen = gla_inputs if rule == "gla" else gdn_inputs
+    B, H, T, d = 1, 2, 6, 4
+    x = gen(B, H, T, d, 51, "f32", b_lam=0.4)
+    pre = gen(B, H, 5, d, 52, "f32", b_lam=0.4)
+    _, carry = ccq_recurrent(pre.q, pre.k, pre.v, pre.g, pre.beta, x.w_lam, x.b_lam, rule)
+    rng = np.random.default_rng(53)
+    do = rng.standard_normal((B, H, T, d))
+    adj = dict(dS_T=rng.standard_normal((B, H, d, d)), dC_T=rng.standard_normal((B, H, d, d)),
+               dm_T=rng.standard_normal((B, H, d)))
+    seq = ccq_sequence_backward(x.q, x.k, x.v, x.g, x.beta, x.w_lam, x.b_lam, rule, do, carry=carry, **adj)
+
+    def loss(xx, c):
+        o, c1 = ccq_recurrent(xx.q, xx.k, xx.v, xx.g, xx.beta, xx.w_lam, xx.b_lam, rule, carry=c.copy())
+        return (np.sum(o * do) + np.sum(c1.S * adj["dS_T"]) + np.sum(c1.C * adj["dC_T"])
+                + np.sum(c1.m * adj["dm_T"]))
+
+    h = 1e-6
+    for nm in ["q", "k", "v", "g", "w_lam", "b_lam"] + (["beta"] if rule == "gdn" else []):
+        e = rng.standard_normal(np.shape(getattr(x, nm)))
+        xp, xm = gen(B, H, T, d, 51, "f32", b_lam=0.4), gen(B, H, T, d, 51, "f32", b_lam=0.4)
+        setattr(xp, nm, getattr(x, nm).astype(np.float64) + h * e)
+        setattr(xm, nm, getattr(x, nm).astype(np.float64) - h * e)
+        num = (loss(xp, carry) - loss(xm, carry)) / (2 * h)
+        key = {"w_lam": "dw", "b_lam": "db"}.get(nm, "d" + nm)
+        assert np.isclose(np.sum(seq[key] * e), num, rtol=1e-6, atol=1e-8), (nm,)
+    for nm, key in (("S", "dS"), ("C", "dC"), ("m", "dm")):
+        e = rng.standard_normal(np.shape(getattr(carry, nm)))
+        cp, cm = carry.copy(), carry.copy()
+        setattr(cp, nm, getattr(carry, nm) + h * e)
+        setattr(cm, nm, getattr(carry, nm) - h * e)
+        num = (loss(x, cp) - loss(x, cm)) / (2 * h)
+        assert np.isclose(np.sum(seq[key] * e), num, rtol=1e-6, atol=1e-8), (nm,)
+    # two halves chained: tokens 3..5 from the carry after tokens 0..2, then tokens 0..2
+    sl = lambda a, lo, hi: None if a is None else a[:, :, lo:hi]  # noqa: E731
+    _, mid = ccq_recurrent(sl(x.q, 0, 3), sl(x.k, 0, 3), sl(x.v, 0, 3), sl(x.g, 0, 3), sl(x.beta, 0, 3),
+                           x.w_lam, x.b_lam, rule, carry=carry.copy())
+    second = ccq_sequence_backward(sl(x.q, 3, 6), sl(x.k, 3, 6), sl(x.v, 3, 6), sl(x.g, 3, 6), sl(x.beta, 3, 6),
+                                   x.w_lam, x.b_lam, rule, do[:, :, 3:], carry=mid, **adj)
+    first = ccq_sequence_backward(sl(x.q, 0, 3), sl(x.k, 0, 3), sl(x.v, 0, 3), sl(x.g, 0, 3), sl(x.beta, 0, 3),
+                                  x.w_lam, x.b_lam, rule, do[:, :, :3], carry=carry, dS_T=second["dS"],
+                                  dC_T=second["dC"], dm_T=second["dm"])
+    for key in ("dq", "dk", "dv", "dg") + (("dbeta",) if rule == "gdn" else ()):
+        assert np.allclose(np.concatenate([first[key], second[key]], axis=2), seq[key], atol=1e-10), key
+    for key in ("dw", "db"):
+        assert np.allclose(first[key] + second[key], seq[key], atol=1e-10), key
+    for key in ("dS", "dC", "dm"):
+        assert np.allclose(first[key], seq[key], atol=1e-10), key
+
+
 MUTATIONS = {
     "gla_decay_inverted": ("S1 = S * torch.exp(g)[..., None, :]", "S1 = S * torch.exp(-g)[..., None, :]"),
     "no_count_normalisation": ("u = Cq / n1[..., None]", "u = Cq"),
