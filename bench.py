@@ -33,6 +33,7 @@ CHUNK = 64
 PREFILL_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill.hip")
 DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode.hip")
 BACKWARD_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_step_backward.hip")
+BWD_CHUNKED_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_backward.hip")
 GDN_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill_gdn.hip")
 
 
@@ -368,6 +369,78 @@ def time_step_backward(steps, warmup, rule="gla"):
     return dict(name=f"ccq-{rule}-step-backward-N{N}H{H}d{d}", ms=ms, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
 
 
+def bwd_chunk_work(d, elem_bytes, L=CHUNK):
+    """Per 64-token chunk of the chunked backward: algorithmic flops of pass A and pass B (every
+    matrix product of the chunk algebra counted dense, 2 m n k; pass A: Q K^T, Q C_c, tril(P) K,
+    dO V^T, dO^T (qc e^B), dO S_c, tril(D) (k e^-B), dR K^T, dR C_c, tril(M) K, P^T dR, M^T Q,
+    dR^T Q; pass B: (qc e^B)(k e^-B)^T, dO V^T, A^T dO, D^T (qc e^B), (k e^-B) dS^T, V dS,
+    K (G + G^T)) and pass A's algorithmic HBM bytes (q, k, v, log alpha, d_o read; S_c, C_c,
+    ksum_c, w read; qc, qc * dqc, dq and the partial dk written, fp32; R_c, dG_c and the chunk
+    sums written)."""
+    flops_a = 2 * (5 * L * d * d + 8 * L * L * d)
+    flops_b = 2 * (3 * L * d * d + 4 * L * L * d)
+    bytes_a = 5 * L * d * elem_bytes + 2 * d * d * 4 + 2 * d * 4 + 4 * L * d * 4 + 2 * d * d * 4 + 4 * d * 4
+    return flops_a, flops_b, bytes_a
+
+
+def time_bwd_chunked(steps, warmup):
+    """Chunked backward over the prefill benchmark's inputs (B = 4, H = 16, T = 4096, d = 128, bf16,
+    zero carry) with a seeded bf16 output gradient; the carry-out adjoint is zero."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_bwd_chunked, load_library
+    from curvature_conditioned_query_amd.inputs import WORKLOADS, workload_inputs
+    load_library()
+    spec = WORKLOADS[1]
+    x = workload_inputs(1)
+    B, H, T, dk, dv = x.shape
+    bf = torch.bfloat16
+    q, k, v, g = (to_dev(a, bf) for a in (x.q, x.k, x.v, x.g))
+    w = torch.from_numpy(x.w_lam).cuda()
+    b = torch.from_numpy(x.b_lam).cuda()
+    del x
+    gen = torch.Generator(device="cuda").manual_seed(1007)
+    do = torch.randn((B, H, T, dv), generator=gen, device="cuda").to(bf)
+    out = ccq_bwd_chunked("gla", q, k, v, g, w, b, do)  # allocates the outputs and sizes the workspace
+    ws = torch.empty(int(_ws_bytes_bwd(B, H, T, dk)), dtype=torch.uint8, device="cuda")
+    hip = HipEvents(5 * steps)
+
+    def step(i=None):
+        pe = None if i is None else hip.slice(5 * i, 5)
+        return ccq_bwd_chunked("gla", q, k, v, g, w, b, do, workspace=ws, phase_events=pe)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    phases = {name: float(np.mean([hip.elapsed_ms(5 * i + a, 5 * i + a + 1) for i in range(steps)]))
+              for a, name in enumerate(("carries", "pass_a", "scan", "pass_b"))}
+    hip.destroy()
+    del out
+    return dict(name=f"ccq-gla-bwd-chunked-B{B}H{H}T{T}d{dk}-bf16", shape=(B, H, T, dk, dv), ms=ms, phase_ms=phases,
+                chunks=B * H * ((T + CHUNK - 1) // CHUNK))
+
+
+def _ws_bytes_bwd(B, H, T, d):
+    import ctypes
+    from curvature_conditioned_query_amd.binding import BwdParams, load_library
+    p = BwdParams()
+    p.rule, p.dtype, p.B, p.H, p.T, p.d_k, p.d_v, p.chunk = 0, 1, B, H, T, d, d, CHUNK
+    for n in ("q", "k", "v", "log_alpha", "w_lambda", "b_lambda", "d_o", "dq", "dk", "dv", "dlog_alpha",
+              "dw_lambda", "db_lambda"):
+        setattr(p, n, 1 << 20)  # aligned placeholders: only the size query reads this struct
+    return load_library().ccq_bwd_workspace_bytes(ctypes.byref(p))
+
+
 def jacobi_sweep_flops(d):
     """Algorithmic fp32 flops of one sweep of the parallel Jacobi method on a d x d symmetric
     matrix with eigenvectors: d - 1 steps, each rotating the d/2 (d/2 - 1)/2 off-diagonal
@@ -439,6 +512,8 @@ def main(argv=None):
     ap.add_argument("--no-backward", action="store_true", help="skip the step-backward leg")
     ap.add_argument("--backward-only", action="store_true", help="run the step-backward leg alone")
     ap.add_argument("--subspace-only", action="store_true", help="run the key-subspace diagnostic leg alone")
+    ap.add_argument("--no-bwd-chunked", action="store_true", help="skip the chunked-backward leg")
+    ap.add_argument("--bwd-chunked-only", action="store_true", help="run the chunked-backward leg alone")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -468,6 +543,11 @@ def main(argv=None):
             bres = time_step_backward(args.decode_steps, 3, rule)
             print(f"# {bres['name']}: {bres['ms'] * 1e3:.1f} us/step, {bres['gbs']:.1f} GB/s", file=sys.stderr,
                   flush=True)
+        return 0
+    if args.bwd_chunked_only:
+        cres = time_bwd_chunked(args.steps, args.warmup)
+        print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass; passes (ms) "
+              + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items()), file=sys.stderr, flush=True)
         return 0
     if args.subspace_only:
         sres = time_subspace(5, 1)
@@ -587,6 +667,33 @@ def main(argv=None):
                 "algorithmic_bytes_per_step": bres["bytes"]}
             print(f"# {bres['name']}: {bres['ms'] * 1e3:.1f} us/step, {bres['gbs']:.1f} GB/s", file=sys.stderr,
                   flush=True)
+    if not args.no_bwd_chunked:
+        cres = time_bwd_chunked(args.steps, args.warmup)
+        cB, cH, cT, cd, _ = cres["shape"]
+        fa, fb, ba = bwd_chunk_work(cd, 2)
+        pa = cres["phase_ms"]["pass_a"]
+        a_tf = fa * cres["chunks"] / (pa * 1e-3) / 1e12
+        a_gbs = ba * cres["chunks"] / (pa * 1e-3) / 1e9
+        pb = cres["phase_ms"]["pass_b"]
+        b_tf = fb * cres["chunks"] / (pb * 1e-3) / 1e12
+        out["bwd_chunked"] = {
+            "workload": cres["name"], "ms_per_step": round(cres["ms"], 4),
+            "tokens_per_s": round(cB * cT / (cres["ms"] * 1e-3), 1),
+            "pass_ms": {k: round(v, 4) for k, v in cres["phase_ms"].items()},
+            "roofline": dict(bound="mfma", achieved=round(a_tf, 2), peak=FP32_PEAK_TFLOPS, unit="TFLOP/s",
+                             frac=round(a_tf / FP32_PEAK_TFLOPS, 4),
+                             traffic=measured_traffic(f"traffic_{cres['name']}.json", file_sha(BWD_CHUNKED_SRC)),
+                             kernel=f"bwd_chunk_a_kernel<{cd},bf16> (fp32 MFMA operands)",
+                             avg_launch_ms=round(pa, 4), algorithmic_flops_per_launch=fa * cres["chunks"],
+                             algorithmic_bytes_per_launch=ba * cres["chunks"],
+                             hbm=dict(achieved=round(a_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                                      frac=round(a_gbs / HBM_PEAK_GBS, 4)),
+                             pass_b=dict(achieved=round(b_tf, 2), unit="TFLOP/s",
+                                         frac=round(b_tf / FP32_PEAK_TFLOPS, 4))),
+        }
+        print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass, {cB * cT / (cres['ms'] * 1e-3):.4g} tokens/s; "
+              "passes (ms) " + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items())
+              + f"; pass A {a_tf:.1f} TFLOP/s fp32 MFMA, pass B {b_tf:.1f}", file=sys.stderr, flush=True)
     if not args.no_subspace:
         sres = time_subspace(5, 1)
         s_tf = sres["flops"] / (sres["ms"] * 1e-3) / 1e12

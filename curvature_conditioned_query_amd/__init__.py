@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     ccq_fwd_chunked,
     ccq_fwd_workspace_bytes,
     ccq_key_subspace,
+    ccq_bwd_chunked,
     ccq_step_backward,
     library_path,
     load_library,

@@ -27,6 +27,8 @@ EXPORTED_SYMBOLS = (
     "ccq_decode_step",
     "ccq_key_subspace",
     "ccq_step_backward",
+    "ccq_bwd_chunked",
+    "ccq_bwd_workspace_bytes",
     "ccq_status_string",
     "ccq_abi_version",
 )
@@ -60,6 +62,27 @@ class FwdParams(ctypes.Structure):
     ]
 
 
+class BwdParams(ctypes.Structure):
+    """Mirror of ``ccq_bwd_params``."""
+
+    _fields_ = [
+        ("rule", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("log_alpha", ctypes.c_void_p),
+        ("w_lambda", ctypes.c_void_p), ("b_lambda", ctypes.c_void_p),
+        ("S0", ctypes.c_void_p), ("C0", ctypes.c_void_p), ("ksum0", ctypes.c_void_p), ("n0", ctypes.c_void_p),
+        ("d_o", ctypes.c_void_p),
+        ("dS_T", ctypes.c_void_p), ("dC_T", ctypes.c_void_p), ("dksum_T", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p), ("dlog_alpha", ctypes.c_void_p),
+        ("dw_lambda", ctypes.c_void_p), ("db_lambda", ctypes.c_void_p),
+        ("dS0", ctypes.c_void_p), ("dC0", ctypes.c_void_p), ("dksum0", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("phase_events", ctypes.c_void_p),
+        ("flags", ctypes.c_int32),
+    ]
+
+
 def library_path() -> str:
     return os.environ.get("CCQ_LIBRARY", os.path.join(_HERE, "libccq.so"))
 
@@ -87,6 +110,10 @@ def load_library():
     lib.ccq_key_subspace.restype = ctypes.c_int
     lib.ccq_step_backward.argtypes = [i32] * 6 + [vp] * 22 + [i32, vp]
     lib.ccq_step_backward.restype = ctypes.c_int
+    lib.ccq_bwd_chunked.argtypes = [ctypes.POINTER(BwdParams), vp]
+    lib.ccq_bwd_chunked.restype = ctypes.c_int
+    lib.ccq_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BwdParams)]
+    lib.ccq_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ccq_status_string.argtypes = [i32]
     lib.ccq_status_string.restype = ctypes.c_char_p
     lib.ccq_abi_version.argtypes = []
@@ -345,4 +372,66 @@ def ccq_step_backward(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, 
                                _ptr(out["db_lambda"]), 0, _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_step_backward")
+    return out
+
+
+def ccq_bwd_chunked(rule, q, k, v, log_alpha, w_lambda, b_lambda, d_o, carry_in=None, carry_out_adjoint=None,
+                    want_carry_in_adjoint: bool = False, workspace=None, stream=None, phase_events=None):
+    """Chunked backward of the prefill through the C ABI (see ``ccq_bwd_chunked`` in ccq.h).
+    q, k, v, log_alpha, d_o: [B, H, T, d] of one dtype; carry_in: (S0, C0, ksum0, n0) or None;
+    carry_out_adjoint: (dS_T, dC_T, dksum_T) fp32 or None.  Returns a dict of fp32 tensors dq, dk,
+    dv, dlog_alpha [B, H, T, d], dw_lambda [B, H, d], db_lambda [B, H] and, with
+    want_carry_in_adjoint, dS0, dC0, dksum0.  ``phase_events``: optional ctypes array of 5
+    hipEvent_t handles recorded around the passes."""
+    import torch
+    lib = load_library()
+    B, H, T, d_k = q.shape
+    d_v = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("d_o", d_o)):
+        _check_dev(name, t, q.dtype)
+        _check_numel(name, t, B * H * T * (d_v if name in ("v", "d_o") else d_k))
+    _check_dev("w_lambda", w_lambda, torch.float32)
+    _check_dev("b_lambda", b_lambda, torch.float32)
+    p = BwdParams()
+    p.rule = _rule_code(rule)
+    p.dtype = _dtype_code(q)
+    p.B, p.H, p.T, p.d_k, p.d_v, p.chunk = B, H, T, d_k, d_v, 64
+    p.q, p.k, p.v, p.log_alpha, p.d_o = (_ptr(x) for x in (q, k, v, log_alpha, d_o))
+    p.w_lambda, p.b_lambda = _ptr(w_lambda), _ptr(b_lambda)
+    if carry_in is not None:
+        S0, C0, m0, n0 = carry_in
+        for name, t, dt, cnt in (("S0", S0, torch.float32, B * H * d_v * d_k), ("C0", C0, torch.float32, B * H * d_k * d_k),
+                                 ("ksum0", m0, torch.float32, B * H * d_k), ("n0", n0, torch.int64, B * H)):
+            _check_dev(name, t, dt)
+            _check_numel(name, t, cnt)
+        p.S0, p.C0, p.ksum0, p.n0 = _ptr(S0), _ptr(C0), _ptr(m0), _ptr(n0)
+    if carry_out_adjoint is not None:
+        dS_T, dC_T, dm_T = carry_out_adjoint
+        for name, t, cnt in (("dS_T", dS_T, B * H * d_v * d_k), ("dC_T", dC_T, B * H * d_k * d_k),
+                             ("dksum_T", dm_T, B * H * d_k)):
+            _check_dev(name, t, torch.float32)
+            _check_numel(name, t, cnt)
+        p.dS_T, p.dC_T, p.dksum_T = _ptr(dS_T), _ptr(dC_T), _ptr(dm_T)
+    f = dict(dtype=torch.float32, device=q.device)
+    out = dict(dq=torch.empty((B, H, T, d_k), **f), dk=torch.empty((B, H, T, d_k), **f),
+               dv=torch.empty((B, H, T, d_v), **f), dlog_alpha=torch.empty((B, H, T, d_k), **f),
+               dw_lambda=torch.empty((B, H, d_k), **f), db_lambda=torch.empty((B, H), **f))
+    if want_carry_in_adjoint:
+        out.update(dS0=torch.empty((B, H, d_v, d_k), **f), dC0=torch.empty((B, H, d_k, d_k), **f),
+                   dksum0=torch.empty((B, H, d_k), **f))
+        p.dS0, p.dC0, p.dksum0 = _ptr(out["dS0"]), _ptr(out["dC0"]), _ptr(out["dksum0"])
+    p.dq, p.dk, p.dv, p.dlog_alpha = _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"])
+    p.dw_lambda, p.db_lambda = _ptr(out["dw_lambda"]), _ptr(out["db_lambda"])
+    nbytes = int(lib.ccq_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _check_dev("workspace", workspace)
+        p.workspace = workspace.data_ptr()
+        p.workspace_bytes = workspace.numel() * workspace.element_size()
+    if phase_events is not None:
+        p.phase_events = ctypes.cast(phase_events, ctypes.c_void_p)
+    st = lib.ccq_bwd_chunked(ctypes.byref(p), _stream_handle(stream))
+    if st != 0:
+        raise CcqError(st, "ccq_bwd_chunked")
     return out

@@ -69,11 +69,37 @@ size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
   return (size_t)p->B * p->H * seg * slot;
 }
 
+int validate_bwd(const ccq_bwd_params* p) {
+  if (!p) return CCQ_ERR_INVALID_ARG;
+  if (p->rule != CCQ_RULE_GLA && p->rule != CCQ_RULE_GDN) return CCQ_ERR_INVALID_ARG;
+  if (p->dtype != CCQ_DTYPE_F32 && p->dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
+  if (p->B <= 0 || p->H <= 0 || p->T <= 0 || p->d_k <= 0 || p->d_v <= 0 || p->chunk < 0) return CCQ_ERR_INVALID_ARG;
+  if (p->flags & ~(CCQ_FLAG_NORMALIZE_KEYS | CCQ_FLAG_PACKED_COV)) return CCQ_ERR_INVALID_ARG;
+  if (p->rule != CCQ_RULE_GLA || p->flags != 0) return CCQ_ERR_UNSUPPORTED;
+  if (p->chunk != 0 && p->chunk != kChunk) return CCQ_ERR_UNSUPPORTED;
+  if (p->d_k != p->d_v || !supported_d(p->dtype, p->d_k)) return CCQ_ERR_UNSUPPORTED;
+  const long long groups = (long long)p->B * p->H * ((p->T + kChunk - 1) / kChunk);
+  if (groups >= (1LL << 31) || (long long)p->B * p->H > 65535LL) return CCQ_ERR_UNSUPPORTED;
+  if (!p->q || !p->k || !p->v || !p->log_alpha || !p->w_lambda || !p->b_lambda || !p->d_o || !p->dq || !p->dk ||
+      !p->dv || !p->dlog_alpha || !p->dw_lambda || !p->db_lambda)
+    return CCQ_ERR_INVALID_ARG;
+  const int nin = (p->S0 != nullptr) + (p->C0 != nullptr) + (p->ksum0 != nullptr) + (p->n0 != nullptr);
+  const int nadj = (p->dS_T != nullptr) + (p->dC_T != nullptr) + (p->dksum_T != nullptr);
+  const int nout = (p->dS0 != nullptr) + (p->dC0 != nullptr) + (p->dksum0 != nullptr);
+  if ((nin != 0 && nin != 4) || (nadj != 0 && nadj != 3) || (nout != 0 && nout != 3)) return CCQ_ERR_INVALID_ARG;
+  const void* ptrs[] = {p->q, p->k, p->v, p->log_alpha, p->w_lambda, p->b_lambda, p->S0, p->C0, p->ksum0, p->n0,
+                        p->d_o, p->dS_T, p->dC_T, p->dksum_T, p->dq, p->dk, p->dv, p->dlog_alpha, p->dw_lambda,
+                        p->db_lambda, p->dS0, p->dC0, p->dksum0, p->workspace};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return CCQ_ERR_MISALIGNED;
+  return CCQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 6; }
+int32_t ccq_abi_version(void) { return 7; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -198,6 +224,52 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
   ccq::StepBackArgs a{rule, dtype, N, H, d_k, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ksum, n, d_o,
                       dS, dC, dksum, dq, dk, dv, dlog_alpha, dbeta, dw_lambda, db_lambda};
   const hipError_t e = ccq::launch_step_backward(a, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
+}
+
+size_t ccq_bwd_workspace_bytes(const ccq_bwd_params* p) {
+  if (validate_bwd(p) != CCQ_OK) return 0;
+  return ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k);
+}
+
+int ccq_bwd_chunked(const ccq_bwd_params* p, void* hip_stream) {
+  const int st = validate_bwd(p);
+  if (st != CCQ_OK) return st;
+  const size_t need = ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k);
+  if (p->workspace == nullptr || p->workspace_bytes < need) return CCQ_ERR_WORKSPACE;
+  ccq::BwdArgs a{};
+  a.dtype = p->dtype;
+  a.B = p->B;
+  a.H = p->H;
+  a.T = p->T;
+  a.d = p->d_k;
+  a.nchunks = (p->T + kChunk - 1) / kChunk;
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.log_alpha = p->log_alpha;
+  a.w_lambda = p->w_lambda;
+  a.b_lambda = p->b_lambda;
+  a.S0 = p->S0;
+  a.C0 = p->C0;
+  a.ksum0 = p->ksum0;
+  a.n0 = p->n0;
+  a.d_o = p->d_o;
+  a.dS_T = p->dS_T;
+  a.dC_T = p->dC_T;
+  a.dksum_T = p->dksum_T;
+  a.dq = p->dq;
+  a.dk = p->dk;
+  a.dv = p->dv;
+  a.dlog_alpha = p->dlog_alpha;
+  a.dw = p->dw_lambda;
+  a.db = p->db_lambda;
+  a.dS0 = p->dS0;
+  a.dC0 = p->dC0;
+  a.dksum0 = p->dksum0;
+  a.workspace = p->workspace;
+  a.events = p->phase_events;
+  const hipError_t e = ccq::launch_bwd(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }
 

@@ -1,0 +1,814 @@
+// Chunked backward of the CCQ read step on a GLA backbone (gfx950): the gradients of a loss
+// L(o, final carry) with respect to q, k, v, log alpha, the gate parameters and the carry in,
+// with the forward carry recomputed per chunk.
+//
+// The pages train CCQ models from scratch (10100.com write-up, section "方法解析" point 3),
+// which needs this pass; the forward it differentiates is the one of the chunked prefill
+// (gist.science summary of arXiv 2606.01294, §2 "理论推导", "机制", "集成"; GLA write rule
+// S_t = S_{t-1} diag(alpha_t) + v_t k_t^T).
+//
+// Per token (sums C_i, m_i, count n_i include token i):
+//   u_i = C_i q_i / n_i - m_i sq_i / n_i^2,  sq_i = m_i . q_i,  lambda_i = sigmoid(w . q_i + b)
+//   qc_i = q_i - lambda_i u_i,  o_i = S_i qc_i
+// Adjoint of the read, with dqc_i the gradient of L with respect to qc_i:
+//   dlogit_i = -(u_i . dqc_i) lambda_i (1 - lambda_i),  dr_i = -lambda_i dqc_i / n_i
+//   ds_i = -(m_i . dr_i) / n_i,  dm_i = ds_i q_i - (sq_i / n_i) dr_i
+//   dq_i = dqc_i + dlogit_i w + C_i dr_i + ds_i m_i
+//   and C_i = C_c + sum_{j<=i} k_j k_j^T, m_i = m_c + sum_{j<=i} k_j give every earlier key
+//   dk_j += sum_{i>=j} [dr_i (q_i . k_j) + q_i (dr_i . k_j) + dm_i].
+// Chunk algebra (chunk c of 64 tokens, carry at its start S_c, C_c, m_c, n_c; B_i the
+// chunk-local inclusive cumulative log decay per key channel, B_L its value at the last token;
+// P = Q K^T, M = dR K^T, D = dO V^T, A = (Qc e^B)(K e^-B)^T, all lower-triangular incl.):
+//   dQc = e^B * (dO S_c + tril(D) (K e^-B))
+//   dq  = dQc + dlogit w^T + dR C_c + ds * (m_c + cumsum K) + tril(M) K
+//   dk  = tril(P)^T dR + tril(M)^T Q + revcumsum(dm)                (statistics, this chunk)
+//       + K (G + G^T) + dm_after                                  (statistics, later tokens)
+//       + e^-B * (tril(D)^T (Qc e^B)) + e^{B_L - B} * (V dS_end)   (write rule)
+//   dv  = tril(A)^T dO + (K e^{B_L - B}) dS_end^T
+//   dlog alpha_i = sum_{s>=i in chunk} (qc_s * dqc_s - k_s * dk^{rule}_s)
+//                + e^{B_L} * colsum(S_c * dS_end) + sum_j k_j * (e^{B_L - B_j} * (V dS_end)_j)
+// where dS_end is the adjoint of the state at the chunk's end carried back from later chunks,
+// G = dC_T + sum over later tokens of dr_i q_i^T, dm_after = dksum_T + sum over later tokens of
+// dm_i.  The last line is the standard gate identity for a diagonal decay (the gradient of a
+// token's log decay is the suffix sum of qc * dqc - k * dk plus the final column sums of
+// S * dS), with the tokens after the chunk folded into S_end * dS_end and S_end written in terms
+// of S_c and the chunk's own terms.
+//
+// Passes (one stream, in order):
+//   1. chunk carries: the prefill's segment summary and scan with one chunk per segment give
+//      S_c, C_c, m_c for every chunk (workspace);
+//   2. pass A, one workgroup per (chain, chunk): the forward read recomputed, dQc, the read
+//      adjoint, dq (final), the chunk's own statistics part of dk (partial, into dk), and the
+//      chunk's contributions R_c = dO^T (Qc e^B), dG_c = dR^T Q, sum dm, sum dlogit q, sum dlogit;
+//   3. reverse scan over chunks, elementwise: dS_end(c), G(c), dm_after(c), and the carry-in
+//      adjoints dS0 = dS_start(0), dC0, dksum0; dw, db summed over chunks;
+//   4. pass B, one workgroup per (chain, chunk): dv, the rest of dk, dlog alpha.
+// Every contraction is an MFMA with fp32 operands (v_mfma_f32_16x16x4_f32) and fp32
+// accumulation; wave w of a workgroup owns the 16 channels [16w, 16w + 16) of d: a "strip"
+// holds, in accumulator layout, a [64 tokens] x [16 channels] block (element r of lane
+// (g = lane / 16, l = lane % 16) of tile ti is token 16 ti + 4 g + r, channel 16 w + l).
+#include "ccq_internal.hpp"
+#include "ccq_prefill_common.hpp"
+
+namespace ccq {
+
+namespace {
+
+using OpT = float;  // MFMA operand type of every contraction here
+
+template <int KO>
+__device__ __forceinline__ int kidx(int g, int e) {
+  if constexpr (KO == KORD_CONTIG) {
+    return 8 * g + e;
+  } else {
+    return 16 * (e >> 2) + 4 * g + (e & 3);
+  }
+}
+
+// Lane (g, l) receives X[row0 + l][k0 + kidx(g, e)]: as an A operand, rows of X; as a B
+// operand, X^T.  X row-major with the given pitch (LDS or global, any storage type).
+template <int KO, typename TS>
+__device__ __forceinline__ Frag<OpT> frag_rows(const TS* X, int pitch, int row0, int k0, int lane) {
+  Frag<OpT> f;
+  const int g = lane >> 4;
+  const TS* p = X + (size_t)(row0 + (lane & 15)) * pitch + k0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = cvt<OpT>(to_f32(p[kidx<KO>(g, e)]));
+  return f;
+}
+
+// Lane (g, l) receives X[k0 + kidx(g, e)][n0 + l]: as a B operand, X itself; as an A operand,
+// X^T.
+template <int KO, typename TS>
+__device__ __forceinline__ Frag<OpT> frag_cols(const TS* X, int pitch, int k0, int n0, int lane) {
+  Frag<OpT> f;
+  const int g = lane >> 4;
+  const TS* p = X + (size_t)k0 * pitch + n0 + (lane & 15);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = cvt<OpT>(to_f32(p[(size_t)kidx<KO>(g, e) * pitch]));
+  return f;
+}
+
+// Upper-triangular ones U[t][t'] = (t' >= t), t = 16 ti + (lane % 16), t' over K-step kk in
+// KORD_ACC order: as an A operand against a strip it forms reverse cumulative sums over tokens.
+__device__ __forceinline__ Frag<OpT> utri_frag(int ti, int kk, int lane) {
+  Frag<OpT> f;
+  const int t = 16 * ti + (lane & 15), g = lane >> 4;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (32 * kk + kidx<KORD_ACC>(g, e) >= t) ? 1.f : 0.f;
+  return f;
+}
+
+// out[ti] = sum_{j <= i} x_j (inclusive cumulative sum over the tokens of a strip).
+__device__ __forceinline__ void strip_cumsum(const f32x4 (&x)[4], f32x4 (&out)[4], int lane) {
+  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
+    out[ti] = zero4();
+    mma(out[ti], ltri_frag<OpT>(ti, 0, lane), b0);
+    if (ti >= 2) mma(out[ti], ltri_frag<OpT>(ti, 1, lane), b1);
+  }
+}
+
+// out[ti] (+)= sum_{j >= i} x_j (reverse cumulative sum over the tokens of a strip).
+__device__ __forceinline__ void strip_revcumsum_add(const f32x4 (&x)[4], f32x4 (&out)[4], int lane) {
+  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
+    if (ti < 2) mma(out[ti], utri_frag(ti, 0, lane), b0);
+    mma(out[ti], utri_frag(ti, 1, lane), b1);
+  }
+}
+
+// Strip of a row-major LDS tile: token 16 ti + 4 g + r, channel cw + l.
+template <typename TS>
+__device__ __forceinline__ void read_strip(const TS* X, int pitch, int cw, int lane, f32x4 (&out)[4]) {
+  const int g = lane >> 4, l = lane & 15;
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[ti][r] = to_f32(X[(16 * ti + 4 * g + r) * pitch + cw + l]);
+}
+
+template <typename TS>
+__device__ __forceinline__ void write_strip(TS* X, int pitch, int cw, int lane, const f32x4 (&v)[4]) {
+  const int g = lane >> 4, l = lane & 15;
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[(16 * ti + 4 * g + r) * pitch + cw + l] = (TS)v[ti][r];
+}
+
+// Strip rows 0 .. rows-1 to a global [token][D] array (row 0 at p).
+template <int D>
+__device__ __forceinline__ void store_strip_rows(float* p, int rows, int cw, int lane, const f32x4 (&v)[4]) {
+  const int g = lane >> 4, l = lane & 15;
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * g + r;
+      if (i < rows) p[(size_t)i * D + cw + l] = v[ti][r];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void load_strip_rows(const float* p, int rows, int cw, int lane, f32x4 (&v)[4]) {
+  const int g = lane >> 4, l = lane & 15;
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * g + r;
+      v[ti][r] = (i < rows) ? p[(size_t)i * D + cw + l] : 0.f;
+    }
+}
+
+// Rows 0 .. Lc-1 of a chunk of a [token][D] tensor into an LDS tile of pitch PQ, 16 bytes per
+// thread and step; rows Lc .. 63 are zeroed.
+template <int D, typename T, int PQ>
+__device__ __forceinline__ void load_tile(T (*dst)[PQ], const T* src, int Lc, int tid, int nthreads) {
+  constexpr int EPU = 16 / (int)sizeof(T), U = D / EPU;
+  for (int u = tid; u < kL * U; u += nthreads) {
+    const int row = u / U, col = (u % U) * EPU;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (row < Lc) x = *reinterpret_cast<const uint4*>(src + (size_t)row * D + col);
+    *reinterpret_cast<uint4*>(&dst[row][col]) = x;
+  }
+}
+
+// Tile (ti, tj) of tril_incl(X Y^T) for row-major tiles X, Y (contraction over D channels):
+// acc[r] = sum_c X[16 ti + 4 g + r][c] Y[16 tj + l][c], zero where column > row.
+template <int D, typename TX, typename TY>
+__device__ __forceinline__ f32x4 tril_tile(const TX* X, int px, const TY* Y, int py, int ti, int tj, int lane) {
+  f32x4 acc = zero4();
+  if (tj > ti) return acc;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+    mma(acc, frag_rows<KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), frag_rows<KORD_CONTIG>(Y, py, 16 * tj, 32 * kk, lane));
+  const int g = lane >> 4, l = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (16 * tj + l > 16 * ti + 4 * g + r) acc[r] = 0.f;
+  return acc;
+}
+
+// strip[ti] += X (rows 16 ti.., all D channels of a row-major LDS tile) times the D x 16 block
+// M[:, cw .. cw + 15] of a global fp32 matrix (M[a][cw + n], K running over a).
+template <int D, typename TX>
+__device__ __forceinline__ void strip_times_mat(const TX* X, int px, const float* M, int cw, int lane, f32x4 (&out)[4]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const Frag<OpT> b = frag_cols<KORD_CONTIG>(M, D, 32 * kk, cw, lane);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) mma(out[ti], frag_rows<KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
+  }
+}
+
+// strip[ti] += tril(Mt) x, Mt a 64 x 64 fp32 LDS tile (lower-triangular incl.), x a strip.
+template <int PT>
+__device__ __forceinline__ void tril_times_strip(const float* Mt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
+  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
+    mma(out[ti], frag_rows<KORD_ACC>(Mt, PT, 16 * ti, 0, lane), b0);
+    if (ti >= 2) mma(out[ti], frag_rows<KORD_ACC>(Mt, PT, 16 * ti, 32, lane), b1);
+  }
+}
+
+// strip[tj] += tril(Mt)^T x.
+template <int PT>
+__device__ __forceinline__ void trilT_times_strip(const float* Mt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
+  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj) {
+    if (tj < 2) mma(out[tj], frag_cols<KORD_ACC>(Mt, PT, 0, 16 * tj, lane), b0);
+    mma(out[tj], frag_cols<KORD_ACC>(Mt, PT, 32, 16 * tj, lane), b1);
+  }
+}
+
+// Rows [16 ta, 16 ta + 16) x strip columns of X^T y (contraction over the 64 tokens): X a
+// row-major LDS tile (token rows), y a strip.  acc[r] = out[16 ta + 4 g + r][cw + l].
+template <typename TX>
+__device__ __forceinline__ f32x4 tileT_times_strip(const TX* X, int px, int ta, const f32x4 (&y)[4], int lane) {
+  f32x4 acc = zero4();
+  mma(acc, frag_cols<KORD_ACC>(X, px, 0, 16 * ta, lane), acc_frag<OpT>(y[0], y[1]));
+  mma(acc, frag_cols<KORD_ACC>(X, px, 32, 16 * ta, lane), acc_frag<OpT>(y[2], y[3]));
+  return acc;
+}
+
+// Sum over the 16 channels of the lane group: every lane of group g gets the total for its
+// (ti, r) token.
+__device__ __forceinline__ float chan_sum(float x) { return group_sum<16>(x); }
+
+// Sum over the 64 tokens of a strip for the lane's channel (every lane gets it).
+__device__ __forceinline__ float token_sum(const f32x4 (&x)[4]) {
+  float s = 0.f;
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) s += x[ti][0] + x[ti][1] + x[ti][2] + x[ti][3];
+  s += __shfl_xor(s, 16, 64);
+  s += __shfl_xor(s, 32, 64);
+  return s;
+}
+
+constexpr int PT = kL + 4;  // pitch of the fp32 64 x 64 token tiles
+
+template <int D>
+constexpr int pf() { return D + 4; }  // pitch of fp32 [64][D] tiles
+
+// Workspace of one backward call (floats):
+//   forward carries   chains x NC x (2 D^2 + 2 D)   S | C | ksum | log decay (prefill layout)
+//   backward slots    chains x NC x (2 D^2 + 4 D)   dS | G | dm | dw | db (D, [0] used) | B_L
+//   qc, qc * dqc      2 x chains x NC x 64 x D
+template <int D>
+constexpr size_t bslot_floats() { return 2 * (size_t)D * D + 4 * D; }
+
+struct BwdLayout {
+  float *fwd, *bwd, *qc, *qdq;
+};
+
+__device__ __forceinline__ BwdLayout layout(const BwdArgs& a) {
+  const size_t chains = (size_t)a.B * a.H, NC = (size_t)a.nchunks, d = (size_t)a.d;
+  BwdLayout L;
+  L.fwd = static_cast<float*>(a.workspace);
+  L.bwd = L.fwd + chains * NC * (2 * d * d + 2 * d);
+  L.qc = L.bwd + chains * NC * (2 * d * d + 4 * d);
+  L.qdq = L.qc + chains * NC * kL * d;
+  return L;
+}
+
+template <int D, typename T>
+struct SmemA {
+  static constexpr int PQ = Cfg<D, T>::PQ, PF = pf<D>(), NW = D / 16;
+  union {
+    struct {
+      T V[kL][PQ];
+      T dO[kL][PQ];
+    } in;
+    float dR[kL][PF];  // once V and dO are no longer read
+  } u1;
+  T Q[kL][PQ];
+  T K[kL][PQ];
+  float P[kL][PT];
+  union {
+    T G[kL][PQ];
+    float Dm[kL][PT];  // tril(dO V^T), then tril(dR K^T)
+  } u2;
+  float red[NW][kL][2];
+  f32x4 tok[kL];     // lambda, 1/n, sq/n, -
+  float tok2[kL][2]; // dlogit, m_c . dr then ds
+};
+
+}  // namespace
+
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
+  using SM = SmemA<D, T>;
+  constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PF = SM::PF, NA = D / 16;
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
+  const int NC = a.nchunks;
+  const int chain = blockIdx.x / NC, c = blockIdx.x % NC, h = chain % a.H;
+  const int t0 = c * kL, Lc = min(kL, a.T - t0);
+  const size_t row0 = (size_t)chain * a.T + t0;
+  const BwdLayout L = layout(a);
+  const float* fslot = L.fwd + ((size_t)chain * NC + c) * (2 * (size_t)D * D + 2 * D);
+  const float* Sc = fslot;
+  const float* Cc = fslot + (size_t)D * D;
+  const float* mc = fslot + 2 * (size_t)D * D;
+  float* bslot = L.bwd + ((size_t)chain * NC + c) * bslot_floats<D>();
+  float* qcbuf = L.qc + ((size_t)chain * NC + c) * kL * D;
+  float* qdqbuf = L.qdq + ((size_t)chain * NC + c) * kL * D;
+  const int64_t nc = (a.n0 != nullptr ? a.n0[chain] : 0) + t0;
+
+  load_tile<D, T, PQ>(sm.Q, static_cast<const T*>(a.q) + row0 * D, Lc, tid, NT);
+  load_tile<D, T, PQ>(sm.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
+  load_tile<D, T, PQ>(sm.u2.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, tid, NT);
+  load_tile<D, T, PQ>(sm.u1.in.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
+  load_tile<D, T, PQ>(sm.u1.in.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
+  const float wv = a.w_lambda[(size_t)h * D + cw + l16];
+  const float mv = mc[cw + l16];
+  const float b_lam = a.b_lambda[h];
+  __syncthreads();
+
+  f32x4 qs[4], ks[4], bs[4], ck[4];
+  {
+    f32x4 gs[4];
+    read_strip(&sm.Q[0][0], PQ, cw, lane, qs);
+    read_strip(&sm.K[0][0], PQ, cw, lane, ks);
+    read_strip(&sm.u2.G[0][0], PQ, cw, lane, gs);
+    strip_cumsum(gs, bs, lane);
+    strip_cumsum(ks, ck, lane);
+  }
+  // per-token w . q and m_c . q: this wave's channels
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = chan_sum(qs[ti][r] * wv), x1 = chan_sum(qs[ti][r] * mv);
+      if (l16 == 0) {
+        sm.red[w][16 * ti + 4 * g + r][0] = x0;
+        sm.red[w][16 * ti + 4 * g + r][1] = x1;
+      }
+    }
+  // P = tril(Q K^T)
+  for (int idx = w; idx < 16; idx += NW) {
+    const int ti = idx >> 2, tj = idx & 3;
+    const f32x4 acc = tril_tile<D>(&sm.Q[0][0], PQ, &sm.K[0][0], PQ, ti, tj, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.P[16 * ti + 4 * g + r][16 * tj + l16] = acc[r];
+  }
+  __syncthreads();
+  // token scalars: 8 threads per token
+  for (int i = tid >> 3; i < kL; i += NT / 8) {
+    const int part = tid & 7;
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rs += sm.P[i][8 * part + j];
+    rs = group_sum<8>(rs);
+    if (part == 0) {
+      float logit = b_lam, mq = 0.f;
+      for (int v = 0; v < NW; ++v) {
+        logit += sm.red[v][i][0];
+        mq += sm.red[v][i][1];
+      }
+      const float sq = mq + rs;
+      const float inv_n = 1.0f / (float)(nc + i + 1);
+      sm.tok[i] = f32x4{sigmoidf(logit), inv_n, sq * inv_n, 0.f};
+    }
+  }
+  __syncthreads();
+
+  // u = (Q C_c + tril(P) K - (m_c + cumsum K) sq / n) / n,  qc = q - lambda u
+  f32x4 us[4], qc[4];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) us[ti] = zero4();
+  strip_times_mat<D>(&sm.Q[0][0], PQ, Cc, cw, lane, us);
+  tril_times_strip<PT>(&sm.P[0][0], ks, lane, us);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 ts = sm.tok[16 * ti + 4 * g + r];
+      const float u = (us[ti][r] - (mv + ck[ti][r]) * ts[2]) * ts[1];
+      us[ti][r] = u;
+      qc[ti][r] = qs[ti][r] - ts[0] * u;
+    }
+  store_strip_rows<D>(qcbuf, kL, cw, lane, qc);
+
+  // D = tril(dO V^T) (into the log-decay tile: every wave has read its strip of it)
+  for (int idx = w; idx < 16; idx += NW) {
+    const int ti = idx >> 2, tj = idx & 3;
+    const f32x4 acc = tril_tile<D>(&sm.u1.in.dO[0][0], PQ, &sm.u1.in.V[0][0], PQ, ti, tj, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.u2.Dm[16 * ti + 4 * g + r][16 * tj + l16] = acc[r];
+  }
+  // R_c = dO^T (qc e^B): the read's contribution to the adjoint of S_c
+  {
+    f32x4 qh[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qh[ti][r] = qc[ti][r] * __expf(bs[ti][r]);
+#pragma unroll 2
+    for (int ta = 0; ta < NA; ++ta) {
+      const f32x4 acc = tileT_times_strip(&sm.u1.in.dO[0][0], PQ, ta, qh, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bslot[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = acc[r];
+    }
+  }
+  __syncthreads();
+
+  // dQc = e^B * (dO S_c + tril(D) (K e^-B))
+  f32x4 dqc[4];
+  {
+    f32x4 kh[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      dqc[ti] = zero4();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kh[ti][r] = ks[ti][r] * __expf(-bs[ti][r]);
+    }
+    strip_times_mat<D>(&sm.u1.in.dO[0][0], PQ, Sc, cw, lane, dqc);
+    tril_times_strip<PT>(&sm.u2.Dm[0][0], kh, lane, dqc);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dqc[ti][r] *= __expf(bs[ti][r]);
+  }
+  {
+    f32x4 qdq[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) qdq[ti] = qc[ti] * dqc[ti];
+    store_strip_rows<D>(qdqbuf, kL, cw, lane, qdq);
+  }
+  // per-token u . dqc and m_c . dqc
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = chan_sum(us[ti][r] * dqc[ti][r]), x1 = chan_sum(mv * dqc[ti][r]);
+      if (l16 == 0) {
+        sm.red[w][16 * ti + 4 * g + r][0] = x0;
+        sm.red[w][16 * ti + 4 * g + r][1] = x1;
+      }
+    }
+  // dR = -lambda dqc / n
+  f32x4 dr[4];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 ts = sm.tok[16 * ti + 4 * g + r];
+      dr[ti][r] = -ts[0] * ts[1] * dqc[ti][r];
+    }
+  __syncthreads();  // V, dO and D are no longer read; red is complete
+  write_strip(&sm.u1.dR[0][0], PF, cw, lane, dr);
+  for (int i = tid; i < kL; i += NT) {
+    float udq = 0.f, mdq = 0.f;
+    for (int v = 0; v < NW; ++v) {
+      udq += sm.red[v][i][0];
+      mdq += sm.red[v][i][1];
+    }
+    const f32x4 ts = sm.tok[i];
+    sm.tok2[i][0] = -udq * ts[0] * (1.f - ts[0]);  // dlogit
+    sm.tok2[i][1] = -ts[0] * ts[1] * mdq;          // m_c . dr
+  }
+  __syncthreads();
+  // M = tril(dR K^T)
+  for (int idx = w; idx < 16; idx += NW) {
+    const int ti = idx >> 2, tj = idx & 3;
+    const f32x4 acc = tril_tile<D>(&sm.u1.dR[0][0], PF, &sm.K[0][0], PQ, ti, tj, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.u2.Dm[16 * ti + 4 * g + r][16 * tj + l16] = acc[r];
+  }
+  __syncthreads();
+  // ds_i = -(m_c . dr_i + sum_{j<=i} M_ij) / n_i
+  for (int i = tid >> 3; i < kL; i += NT / 8) {
+    const int part = tid & 7;
+    float rs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rs += sm.u2.Dm[i][8 * part + j];
+    rs = group_sum<8>(rs);
+    if (part == 0) sm.tok2[i][1] = -(sm.tok2[i][1] + rs) * sm.tok[i][1];
+  }
+  __syncthreads();
+
+  // dq = dqc + dlogit w + dR C_c + ds (m_c + cumsum K) + tril(M) K
+  {
+    f32x4 z[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
+    strip_times_mat<D>(&sm.u1.dR[0][0], PF, Cc, cw, lane, z);
+    tril_times_strip<PT>(&sm.u2.Dm[0][0], ks, lane, z);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * g + r;
+        z[ti][r] += dqc[ti][r] + sm.tok2[i][0] * wv + sm.tok2[i][1] * (mv + ck[ti][r]);
+      }
+    store_strip_rows<D>(a.dq + row0 * D, Lc, cw, lane, z);
+  }
+  // dm_i = ds_i q_i - (sq_i / n_i) dr_i;  this chunk's statistics part of dk:
+  // tril(P)^T dR + tril(M)^T Q + revcumsum(dm)
+  f32x4 dm[4];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ti + 4 * g + r;
+      dm[ti][r] = sm.tok2[i][1] * qs[ti][r] - sm.tok[i][2] * dr[ti][r];
+    }
+  {
+    f32x4 z[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
+    trilT_times_strip<PT>(&sm.P[0][0], dr, lane, z);
+    trilT_times_strip<PT>(&sm.u2.Dm[0][0], qs, lane, z);
+    strip_revcumsum_add(dm, z, lane);
+    store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, z);
+  }
+  // dG_c = dR^T Q
+  float* Gs = bslot + (size_t)D * D;
+#pragma unroll 2
+  for (int ta = 0; ta < NA; ++ta) {
+    const f32x4 acc = tileT_times_strip(&sm.u1.dR[0][0], PF, ta, qs, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Gs[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = acc[r];
+  }
+  // sum dm, sum dlogit q, sum dlogit, B_L
+  {
+    f32x4 dq_w[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dq_w[ti][r] = sm.tok2[16 * ti + 4 * g + r][0] * qs[ti][r];
+    const float sdm = token_sum(dm), sdw = token_sum(dq_w);
+    float* tail = bslot + 2 * (size_t)D * D;
+    if (g == 0) {
+      tail[cw + l16] = sdm;
+      tail[D + cw + l16] = sdw;
+    }
+    if (g == 3) tail[3 * D + cw + l16] = bs[3][3];
+    if (w == 0) {
+      const float db = group_sum<64>(sm.tok2[lane][0]);
+      if (lane == 0) tail[2 * D] = db;
+    }
+  }
+}
+
+// Reverse scan over the chunks of a chain, in place, one thread per 4 floats of dS | G | dm |
+// dw | db:  slot c receives dS_end(c), G(c), dm_after(c) (the adjoints carried back from the
+// chunks after c and the caller's carry-out adjoint); dS_end(c-1) = dS_end(c) diag(e^{B_L(c)}) + R_c.
+// What is left after chunk 0 is the carry-in adjoint.  dw and db are summed over chunks.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
+  const int chain = blockIdx.y;
+  const int NC = a.nchunks;
+  const int nf4 = (2 * D * D + 3 * D) / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nf4) return;
+  const size_t f = (size_t)idx * 4;
+  const BwdLayout L = layout(a);
+  float* base = L.bwd + (size_t)chain * NC * bslot_floats<D>();
+  const size_t DD = (size_t)D * D;
+  const int part = f < DD ? 0 : f < 2 * DD ? 1 : f < 2 * DD + D ? 2 : f < 2 * DD + 2 * D ? 3 : 4;
+  const size_t off = part == 0 ? f : part == 1 ? f - DD : f - 2 * DD - (size_t)D * (part - 2);
+  const int col = (int)(f % D);
+  f32x4 run = zero4();
+  if (part == 0 && a.dS_T) run = *reinterpret_cast<const f32x4*>(a.dS_T + (size_t)chain * DD + off);
+  if (part == 1 && a.dC_T) run = *reinterpret_cast<const f32x4*>(a.dC_T + (size_t)chain * DD + off);
+  if (part == 2 && a.dksum_T) run = *reinterpret_cast<const f32x4*>(a.dksum_T + (size_t)chain * D + off);
+  for (int cc = NC - 1; cc >= 0; --cc) {
+    float* slot = base + (size_t)cc * bslot_floats<D>();
+    const f32x4 x = *reinterpret_cast<const f32x4*>(slot + f);
+    if (part <= 2) *reinterpret_cast<f32x4*>(slot + f) = run;
+    if (part == 0) {
+      const f32x4 bl = *reinterpret_cast<const f32x4*>(slot + 2 * DD + 3 * D + col);
+      run = run * f32x4{__expf(bl[0]), __expf(bl[1]), __expf(bl[2]), __expf(bl[3])};
+    }
+    run += x;
+  }
+  if (part == 0 && a.dS0) *reinterpret_cast<f32x4*>(a.dS0 + (size_t)chain * DD + off) = run;
+  if (part == 1 && a.dC0) *reinterpret_cast<f32x4*>(a.dC0 + (size_t)chain * DD + off) = run;
+  if (part == 2 && a.dksum0) *reinterpret_cast<f32x4*>(a.dksum0 + (size_t)chain * D + off) = run;
+  if (part == 3) *reinterpret_cast<f32x4*>(a.dw + (size_t)chain * D + off) = run;
+  if (part == 4 && off == 0) a.db[chain] = run[0];
+}
+
+namespace {
+template <int D, typename T>
+struct SmemB {
+  static constexpr int PQ = Cfg<D, T>::PQ, PF = pf<D>();
+  union {
+    struct {
+      T K[kL][PQ];
+      T G[kL][PQ];
+    } in;
+    float Kh[kL][PF];  // k e^-B, once the key and log-decay strips are read
+  } u1;
+  T V[kL][PQ];
+  T dO[kL][PQ];
+  float Qh[kL][PF];  // qc e^B
+  float A[kL][PT];   // tril((qc e^B)(k e^-B)^T)
+  float Dm[kL][PT];  // tril(dO V^T)
+  float eBL[D];
+};
+}  // namespace
+
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
+  using SM = SmemB<D, T>;
+  constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PF = SM::PF;
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
+  const int NC = a.nchunks;
+  const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
+  const int t0 = c * kL, Lc = min(kL, a.T - t0);
+  const size_t row0 = (size_t)chain * a.T + t0;
+  const BwdLayout L = layout(a);
+  const float* Sc = L.fwd + ((size_t)chain * NC + c) * (2 * (size_t)D * D + 2 * D);
+  const float* bslot = L.bwd + ((size_t)chain * NC + c) * bslot_floats<D>();
+  const float* dSe = bslot;
+  const float* Ga = bslot + (size_t)D * D;
+  const float dma = bslot[2 * (size_t)D * D + cw + l16];
+  const float* qcbuf = L.qc + ((size_t)chain * NC + c) * kL * D;
+  const float* qdqbuf = L.qdq + ((size_t)chain * NC + c) * kL * D;
+
+  load_tile<D, T, PQ>(sm.u1.in.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
+  load_tile<D, T, PQ>(sm.u1.in.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, tid, NT);
+  load_tile<D, T, PQ>(sm.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
+  load_tile<D, T, PQ>(sm.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
+  f32x4 qc[4];
+  load_strip_rows<D>(qcbuf, kL, cw, lane, qc);
+  __syncthreads();
+
+  f32x4 ks[4], bs[4], dos[4], kg[4];
+  {
+    f32x4 gs[4];
+    read_strip(&sm.u1.in.K[0][0], PQ, cw, lane, ks);
+    read_strip(&sm.u1.in.G[0][0], PQ, cw, lane, gs);
+    strip_cumsum(gs, bs, lane);
+  }
+  read_strip(&sm.dO[0][0], PQ, cw, lane, dos);
+  const float bL = __shfl(bs[3][3], 48 + l16, 64);  // token 63
+  const float eBLv = __expf(bL);
+  if (g == 0) sm.eBL[cw + l16] = eBLv;
+  // K (G + G^T): the statistics part of dk from later tokens
+  {
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) kg[ti] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      Frag<OpT> b = frag_cols<KORD_CONTIG>(Ga, D, 32 * kk, cw, lane);
+      const Frag<OpT> bt = frag_rows<KORD_CONTIG>(Ga, D, cw, 32 * kk, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b.v[e] += bt.v[e];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) mma(kg[ti], frag_rows<KORD_CONTIG>(&sm.u1.in.K[0][0], PQ, 16 * ti, 32 * kk, lane), b);
+    }
+  }
+  f32x4 qh[4], ebn[4];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      qh[ti][r] = qc[ti][r] * __expf(bs[ti][r]);
+      ebn[ti][r] = __expf(-bs[ti][r]);
+    }
+  __syncthreads();  // key and log-decay tiles fully read
+  {
+    f32x4 kh[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) kh[ti] = ks[ti] * ebn[ti];
+    write_strip(&sm.u1.Kh[0][0], PF, cw, lane, kh);
+    write_strip(&sm.Qh[0][0], PF, cw, lane, qh);
+  }
+  __syncthreads();
+  for (int idx = w; idx < 16; idx += NW) {
+    const int ti = idx >> 2, tj = idx & 3;
+    const f32x4 x = tril_tile<D>(&sm.Qh[0][0], PF, &sm.u1.Kh[0][0], PF, ti, tj, lane);
+    const f32x4 y = tril_tile<D>(&sm.dO[0][0], PQ, &sm.V[0][0], PQ, ti, tj, lane);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sm.A[16 * ti + 4 * g + r][16 * tj + l16] = x[r];
+      sm.Dm[16 * ti + 4 * g + r][16 * tj + l16] = y[r];
+    }
+  }
+  __syncthreads();
+
+  // dv = tril(A)^T dO + (k e^-B) (dS_end diag(e^{B_L}))^T
+  {
+    f32x4 z[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
+    trilT_times_strip<PT>(&sm.A[0][0], dos, lane, z);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      Frag<OpT> b = frag_rows<KORD_CONTIG>(dSe, D, cw, 32 * kk, lane);  // dS_end[cw + l][kappa]
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b.v[e] *= sm.eBL[32 * kk + kidx<KORD_CONTIG>(g, e)];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) mma(z[ti], frag_rows<KORD_CONTIG>(&sm.u1.Kh[0][0], PF, 16 * ti, 32 * kk, lane), b);
+    }
+    store_strip_rows<D>(a.dv + row0 * D, Lc, cw, lane, z);
+  }
+  // write-rule part of dk: e^-B (tril(D)^T (qc e^B)) + e^{B_L - B} (V dS_end)
+  f32x4 dkr[4], dks[4];
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) dkr[ti] = dks[ti] = zero4();
+  trilT_times_strip<PT>(&sm.Dm[0][0], qh, lane, dkr);
+  strip_times_mat<D>(&sm.V[0][0], PQ, dSe, cw, lane, dks);
+#pragma unroll
+  for (int ti = 0; ti < 4; ++ti) {
+    dks[ti] = dks[ti] * ebn[ti] * eBLv;
+    dkr[ti] = dkr[ti] * ebn[ti] + dks[ti];
+  }
+  {
+    f32x4 part[4], dk[4];
+    load_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, part);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) dk[ti] = dkr[ti] + kg[ti] + part[ti] + dma;
+    store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, dk);
+  }
+  // dlog alpha = revcumsum(qc dqc - k dk_rule) + e^{B_L} colsum(S_c dS_end) + sum_j k_j dk_state_j
+  {
+    f32x4 z[4], out[4];
+    load_strip_rows<D>(qdqbuf, kL, cw, lane, z);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      z[ti] -= ks[ti] * dkr[ti];
+      out[ti] = zero4();
+      dks[ti] *= ks[ti];
+    }
+    strip_revcumsum_add(z, out, lane);
+    float cs = 0.f;
+    for (int row = g; row < D; row += 4) cs += Sc[(size_t)row * D + cw + l16] * dSe[(size_t)row * D + cw + l16];
+    cs += __shfl_xor(cs, 16, 64);
+    cs += __shfl_xor(cs, 32, 64);
+    const float after = eBLv * cs + token_sum(dks);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) out[ti] += after;
+    store_strip_rows<D>(a.dlog_alpha + row0 * D, Lc, cw, lane, out);
+  }
+}
+
+size_t bwd_workspace_bytes(int B, int H, int T, int d) {
+  const size_t chains = (size_t)B * H, NC = (size_t)((T + kL - 1) / kL), dd = (size_t)d;
+  return chains * NC * ((2 * dd * dd + 2 * dd) + (2 * dd * dd + 4 * dd) + 2 * kL * dd) * sizeof(float);
+}
+
+static hipError_t record_bwd_event(const BwdArgs& a, int i, hipStream_t s) {
+  if (a.events == nullptr) return hipSuccess;
+  return hipEventRecord(static_cast<hipEvent_t>(a.events[i]), s);
+}
+
+template <int D, typename T>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  const int chains = a.B * a.H, NC = a.nchunks;
+  // 1. carries at every chunk start: the prefill's summary and scan, one chunk per segment
+  FwdArgs f{};
+  f.rule = 0;
+  f.dtype = a.dtype;
+  f.B = a.B;
+  f.H = a.H;
+  f.T = a.T;
+  f.d = D;
+  f.segments = NC;
+  f.chunks_per_segment = 1;
+  f.k = a.k;
+  f.v = a.v;
+  f.log_alpha = a.log_alpha;
+  f.S0 = a.S0;
+  f.C0 = a.C0;
+  f.ksum0 = a.ksum0;
+  f.n0 = a.n0;
+  f.workspace = a.workspace;
+  f.flags = 0;
+  if (record_bwd_event(a, 0, s) != hipSuccess) return hipErrorLaunchFailure;
+  hipError_t e = launch_gla_chunk_carries(f, s);
+  if (e != hipSuccess) return e;
+  if (record_bwd_event(a, 1, s) != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL((bwd_chunk_a_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
+  if (record_bwd_event(a, 2, s) != hipSuccess) return hipErrorLaunchFailure;
+  const int nf4 = (2 * D * D + 3 * D) / 4;
+  hipLaunchKernelGGL((bwd_scan_kernel<D>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
+  if (record_bwd_event(a, 3, s) != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL((bwd_chunk_b_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return record_bwd_event(a, 4, s);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s) {
+  if (a.dtype == 1) {
+    if (a.d == 128) return launch_bwd_t<128, __bf16>(a, s);
+    if (a.d == 64) return launch_bwd_t<64, __bf16>(a, s);
+  } else if (a.d == 64) {
+    return launch_bwd_t<64, float>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace ccq

@@ -73,6 +73,27 @@ struct StepBackArgs {
 };
 hipError_t launch_step_backward(const StepBackArgs& a, hipStream_t stream);
 
+// Chunked backward of the GLA prefill (one call after validation).  nchunks = ceil(T / 64).
+struct BwdArgs {
+  int dtype, B, H, T, d, nchunks;
+  const void *q, *k, *v, *log_alpha;
+  const float *w_lambda, *b_lambda;
+  const float *S0, *C0, *ksum0;
+  const int64_t* n0;
+  const void* d_o;
+  const float *dS_T, *dC_T, *dksum_T;
+  float *dq, *dk, *dv, *dlog_alpha, *dw, *db;
+  float *dS0, *dC0, *dksum0;
+  void* workspace;
+  void* const* events;  // optional: 5 hipEvent_t around the passes
+};
+size_t bwd_workspace_bytes(int B, int H, int T, int d);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+// Summary and scan of the GLA prefill only: the carry at the start of every segment in the
+// workspace slots (the chunked backward runs it with one chunk per segment).
+hipError_t launch_gla_chunk_carries(const FwdArgs& a, hipStream_t stream);
+
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).
 size_t fwd_slot_bytes(int d);

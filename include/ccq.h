@@ -206,8 +206,64 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 6. */
+/* ABI version of this header: 7. */
 int32_t ccq_abi_version(void);
+
+/* Arguments of ccq_bwd_chunked.  Zero-initialise, then fill in. */
+typedef struct {
+  int32_t rule;   /* CCQ_RULE_GLA (the only rule with a chunked backward)                        */
+  int32_t dtype;  /* ccq_dtype of q, k, v, log_alpha and d_o                                       */
+  int32_t B, H, T;
+  int32_t d_k, d_v;
+  int32_t chunk;  /* 64, or 0 for the default (64)                                                 */
+
+  /* The forward's inputs, exactly as given to ccq_fwd_chunked (unit keys, no flags). */
+  const void *q, *k, *v, *log_alpha; /* [B, H, T, d] dtype                                         */
+  const float *w_lambda;             /* [H, d_k]                                                    */
+  const float *b_lambda;             /* [H]                                                         */
+  const float *S0, *C0, *ksum0;      /* carry in: all four NULL (zeros) or all four set (full C)    */
+  const int64_t *n0;
+
+  const void *d_o;                   /* [B, H, T, d_v] dtype: gradient of the loss w.r.t. o          */
+  /* Adjoint of the carry out (gradient of the loss w.r.t. S_T, C_T, ksum_T): all NULL (zero) or
+   * all set; [B, H, d_v, d_k], [B, H, d_k, d_k] (as a general matrix), [B, H, d_k] fp32. */
+  const float *dS_T, *dC_T, *dksum_T;
+
+  /* Gradients, fp32, written: */
+  float *dq, *dk;        /* [B, H, T, d_k]                                                          */
+  float *dv;             /* [B, H, T, d_v]                                                          */
+  float *dlog_alpha;     /* [B, H, T, d_k]                                                          */
+  float *dw_lambda;      /* [B, H, d_k] per sequence: the [H, d_k] parameter's gradient is their sum */
+  float *db_lambda;      /* [B, H]      per sequence                                                */
+  float *dS0, *dC0, *dksum0; /* adjoint of the carry in: all NULL (not wanted) or all set          */
+
+  void *workspace;        /* at least ccq_bwd_workspace_bytes(p) bytes of device memory             */
+  size_t workspace_bytes;
+  /* Optional per-pass timing: NULL, or 5 caller-created hipEvent_t recorded before the chunk
+   * carries, after them, after pass A, after the reverse scan and after pass B. */
+  void *const *phase_events;
+  int32_t flags;          /* must be 0                                                               */
+} ccq_bwd_params;
+
+/*
+ * Chunked backward of ccq_fwd_chunked on the GLA rule (training; the pages train CCQ models
+ * from scratch, 10100.com write-up, section "方法解析" point 3): for the loss
+ *   L = <d_o, o> + <dS_T, S_T> + <dC_T, C_T> + <dksum_T, ksum_T>
+ * of the forward with the same inputs and carry in, it writes dL/dq, dL/dk, dL/dv,
+ * dL/dlog_alpha, the per-sequence gate-parameter gradients and, when asked for, the adjoint of
+ * the carry in.  The forward carry at every 64-token chunk start is recomputed (not read from
+ * the forward), and each chunk's gradients follow from it and the adjoint carried back from
+ * later chunks.  Results equal backpropagation through the per-token recurrence up to
+ * rounding; the forward's precondition on the log decay applies.
+ * Supported: rule GLA, d_k == d_v, d in {64, 128} for CCQ_DTYPE_BF16, d == 64 for
+ * CCQ_DTYPE_F32, flags == 0; B * H * ceil(T / 64) < 2^31.  Returns a ccq_status.
+ */
+int ccq_bwd_chunked(const ccq_bwd_params *p, void *hip_stream);
+
+/* Bytes of device workspace ccq_bwd_chunked needs (0 for invalid p).  Depends only on B, H, T
+ * and d_k: per (b, h) and 64-token chunk, the carry, the carried-back adjoints and two fp32
+ * [64, d_k] tiles, about 4.2 d_k^2 floats per chunk (0.27 MB at d_k = 128). */
+size_t ccq_bwd_workspace_bytes(const ccq_bwd_params *p);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,7 @@ import re
 import pytest
 
 from curvature_conditioned_query_amd import binding
-from curvature_conditioned_query_amd.binding import FwdParams, load_library
+from curvature_conditioned_query_amd.binding import BwdParams, FwdParams, load_library
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ccq.h")
@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 6
+    assert lib.ccq_abi_version() == 7
 
 
 def test_status_strings(lib):
@@ -148,3 +148,45 @@ def test_step_backward_argument_errors(lib, kw, code):
     # every case must fail validation: a call that passed it would launch on the fake pointers
     assert code != OK
     assert _sb(lib, **kw) == code
+
+
+def _bparams(**kw):
+    p = BwdParams()
+    p.rule, p.dtype, p.B, p.H, p.T, p.d_k, p.d_v, p.chunk = 0, 1, 2, 2, 200, 128, 128, 64
+    for n in ("q", "k", "v", "log_alpha", "w_lambda", "b_lambda", "d_o", "dq", "dk", "dv", "dlog_alpha",
+              "dw_lambda", "db_lambda"):
+        setattr(p, n, FAKE)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rule=5), INVALID), (dict(rule=1), UNSUPPORTED), (dict(dtype=3), INVALID), (dict(T=0), INVALID),
+    (dict(B=-1), INVALID), (dict(chunk=-1), INVALID), (dict(chunk=128), UNSUPPORTED), (dict(flags=1), UNSUPPORTED),
+    (dict(flags=2), UNSUPPORTED), (dict(flags=8), INVALID), (dict(d_k=64, d_v=128), UNSUPPORTED),
+    (dict(dtype=0), UNSUPPORTED), (dict(d_k=256, d_v=256), UNSUPPORTED), (dict(B=300, H=300), UNSUPPORTED),
+    (dict(q=None), INVALID), (dict(d_o=None), INVALID), (dict(dlog_alpha=None), INVALID),
+    (dict(db_lambda=None), INVALID), (dict(S0=FAKE), INVALID), (dict(dS_T=FAKE, dC_T=FAKE), INVALID),
+    (dict(dS0=FAKE), INVALID), (dict(dv=FAKE + 8), MISALIGNED), (dict(n0=FAKE + 4, S0=FAKE, C0=FAKE, ksum0=FAKE), MISALIGNED),
+])
+def test_bwd_argument_errors(lib, kw, code):
+    # every case must fail validation: a call that passed it would launch on the fake pointers
+    assert code != OK
+    p = _bparams(**kw)
+    assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == code
+    assert lib.ccq_bwd_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_bwd_workspace_sizing_and_check(lib):
+    assert lib.ccq_bwd_chunked(None, None) == INVALID
+    assert lib.ccq_bwd_workspace_bytes(None) == 0
+    p = _bparams(B=4, H=16, T=4096)
+    need = lib.ccq_bwd_workspace_bytes(ctypes.byref(p))
+    # per chain and chunk: carry (2 d^2 + 2 d), adjoints (2 d^2 + 4 d), two fp32 [64, d] tiles
+    assert need == 4 * 16 * 64 * (4 * 128 * 128 + 6 * 128 + 2 * 64 * 128) * 4
+    p.workspace, p.workspace_bytes = FAKE, need - 16
+    assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == WORKSPACE
+    p.workspace = None
+    assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == WORKSPACE
+

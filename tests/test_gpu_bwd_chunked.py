@@ -1,0 +1,119 @@
+"""Chunked backward parity: ccq_bwd_chunked through the C ABI vs the fp64 oracle (autograd
+through the per-token recurrence, ``oracle.ccq_sequence_backward``) on the same inputs."""
+
+import numpy as np
+import pytest
+
+from curvature_conditioned_query_amd.inputs import bf16_round, gla_inputs
+from oracle import ccq_recurrent, ccq_sequence_backward, normwise_error
+
+from gpu_util import down, up, up_carry
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+GRADS = ("dq", "dk", "dv", "dg")
+
+
+def _cotangent(shape, seed, dtype):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    return bf16_round(x) if dtype == "bf16" else x
+
+
+def _run(dtype, B, H, T, d, seed, carry=False, adjoint=False, b_lam=-2.0, check_tol=None):
+    import torch
+    from curvature_conditioned_query_amd import ccq_bwd_chunked
+    x = gla_inputs(B, H, T, d, seed, dtype, b_lam=b_lam)
+    do = _cotangent((B, H, T, d), seed + 1, dtype)
+    dev_carry = ref_carry = None
+    if carry:  # the carry after a 70-token prefix of other inputs
+        pre = gla_inputs(B, H, 70, d, seed + 2, "f32", b_lam=b_lam)
+        _, c = ccq_recurrent(pre.q, pre.k, pre.v, pre.g, None, x.w_lam, x.b_lam, "gla")
+        dev_carry, (S64, C64, m64, n64) = up_carry(c)
+        from oracle import Carry
+        ref_carry = Carry(S64, C64, m64, n64)
+    adj = None
+    adj_np = {}
+    if adjoint:
+        rng = np.random.default_rng(seed + 3)
+        adj_np = dict(dS_T=rng.standard_normal((B, H, d, d)).astype(np.float32),
+                      dC_T=rng.standard_normal((B, H, d, d)).astype(np.float32) * np.float32(1e-2),
+                      dm_T=rng.standard_normal((B, H, d)).astype(np.float32) * np.float32(1e-1))
+        adj = tuple(torch.from_numpy(adj_np[k]).cuda() for k in ("dS_T", "dC_T", "dm_T"))
+    out = ccq_bwd_chunked("gla", up(x.q, dtype), up(x.k, dtype), up(x.v, dtype), up(x.g, dtype),
+                          torch.from_numpy(x.w_lam).cuda(), torch.from_numpy(x.b_lam).cuda(), up(do, dtype),
+                          carry_in=dev_carry, carry_out_adjoint=adj, want_carry_in_adjoint=True)
+    torch.cuda.synchronize()
+    ref = ccq_sequence_backward(x.q, x.k, x.v, x.g, None, x.w_lam, x.b_lam, "gla", do, carry=ref_carry,
+                                **{k: v.astype(np.float64) for k, v in adj_np.items()})
+    tol = TOL[dtype] if check_tol is None else check_tol
+    got = dict(dq=out["dq"], dk=out["dk"], dv=out["dv"], dg=out["dlog_alpha"], dS=out["dS0"], dC=out["dC0"],
+               dm=out["dksum0"])
+    errs = {}
+    for key in GRADS + ("dS", "dC", "dm"):
+        errs[key] = normwise_error(down(got[key]), ref[key])
+    errs["dw"] = normwise_error(down(out["dw_lambda"]).sum(axis=0), ref["dw"])
+    errs["db"] = normwise_error(down(out["db_lambda"]).sum(axis=0)[:, None], np.asarray(ref["db"])[:, None])
+    print(f"bwd {dtype} B={B} H={H} T={T} d={d} carry={carry} adjoint={adjoint}: "
+          + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for key, e in errs.items():
+        assert e <= tol, (key, e)
+    return out, ref
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_bwd_matches_oracle(gpu_lib, dtype, d):
+    """Three full chunks and a ragged one, from a zero carry."""
+    _run(dtype, B=1, H=2, T=200, d=d, seed=1100 + d)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_bwd_carry_and_final_adjoint(gpu_lib, dtype, d):
+    """From a carry in, with the adjoint of the carry out given: every gradient and the carry-in
+    adjoint."""
+    _run(dtype, B=2, H=1, T=150, d=d, seed=1200 + d, carry=True, adjoint=True)
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 65, 128])
+def test_bwd_short_and_boundary_lengths(gpu_lib, T):
+    """One token, a single ragged chunk, exactly one chunk, one chunk plus a token, two chunks."""
+    _run("f32", B=1, H=2, T=T, d=64, seed=1300 + T, carry=(T % 2 == 1), adjoint=True)
+
+
+def test_bwd_gate_off(gpu_lib):
+    """b = -inf: the cleaning is off, so dw and db are exactly zero and the rest is the plain GLA
+    backward (the oracle with lambda = 0)."""
+    out, _ = _run("f32", B=1, H=2, T=130, d=64, seed=1400, b_lam=-np.inf)
+    assert np.all(down(out["dw_lambda"]) == 0.0) and np.all(down(out["db_lambda"]) == 0.0)
+
+
+def test_bwd_strong_gate(gpu_lib):
+    """b = +4 (lambda near 1 everywhere): the statistics' share of dq and dk is large."""
+    _run("f32", B=1, H=1, T=140, d=64, seed=1500, b_lam=4.0, carry=True)
+
+
+def test_bwd_full_size_sampled(gpu_lib):
+    """The prefill benchmark shape (B = 4, H = 16, T = 4096, d = 128, bf16, zero carry) in one
+    launch; one sampled (b, h) chain against the oracle over all 4096 tokens."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_bwd_chunked
+    B, H, T, d, seed = 4, 16, 4096, 128, 1001
+    x = gla_inputs(B, H, T, d, seed, "bf16")
+    do = _cotangent((B, H, T, d), seed + 7, "bf16")
+    out = ccq_bwd_chunked("gla", up(x.q, "bf16"), up(x.k, "bf16"), up(x.v, "bf16"), up(x.g, "bf16"),
+                          torch.from_numpy(x.w_lam).cuda(), torch.from_numpy(x.b_lam).cuda(), up(do, "bf16"))
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "dlog_alpha", "dw_lambda", "db_lambda"):
+        assert bool(torch.isfinite(out[key]).all()), key
+    b, h = 3, 9
+    sl = lambda a: a[b:b + 1, h:h + 1]  # noqa: E731
+    ref = ccq_sequence_backward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), None, x.w_lam[h:h + 1], x.b_lam[h:h + 1], "gla",
+                                sl(do))
+    got = dict(dq=out["dq"], dk=out["dk"], dv=out["dv"], dg=out["dlog_alpha"])
+    for key in GRADS:
+        e = normwise_error(down(got[key][b:b + 1, h:h + 1]), ref[key])
+        print(f"bwd full-size chain ({b},{h}) {key} err {e:.2e}", flush=True)
+        assert e <= TOL["bf16"], key
+    e = normwise_error(down(out["dw_lambda"][b, h])[None], ref["dw"])
+    assert e <= TOL["bf16"]
+    assert abs(float(out["db_lambda"][b, h]) - float(ref["db"][0])) <= TOL["bf16"] * (abs(float(ref["db"][0])) + 1e-6)
