@@ -43,9 +43,9 @@
 //   3. reverse scan over chunks, elementwise: dS_end(c), G(c), dm_after(c), and the carry-in
 //      adjoints dS0 = dS_start(0), dC0, dksum0; dw, db summed over chunks;
 //   4. pass B, one workgroup per (chain, chunk): dv, the rest of dk, dlog alpha.
-// Every contraction is an MFMA with fp32 operands (v_mfma_f32_16x16x4_f32) and fp32
-// accumulation; wave w of a workgroup owns the 16 channels [16w, 16w + 16) of d: a "strip"
-// holds, in accumulator layout, a [64 tokens] x [16 channels] block (element r of lane
+// Every contraction is an MFMA with fp32 accumulation and operands of the input dtype
+// (v_mfma_f32_16x16x32_bf16 for bf16 inputs, v_mfma_f32_16x16x4_f32 for fp32 inputs); wave w
+// of a workgroup owns the 16 channels [16w, 16w + 16) of d: a "strip" holds, in accumulator layout, a [64 tokens] x [16 channels] block (element r of lane
 // (g = lane / 16, l = lane % 16) of tile ti is token 16 ti + 4 g + r, channel 16 w + l).
 #include "ccq_internal.hpp"
 #include "ccq_prefill_common.hpp"
@@ -54,7 +54,8 @@ namespace ccq {
 
 namespace {
 
-using OpT = float;  // MFMA operand type of every contraction here
+// MFMA operand type O: the input dtype (bf16 operands for bf16 inputs, fp32 for fp32 inputs);
+// the cumulative sums over tokens always take fp32 operands (exact for any input dtype).
 
 template <int KO>
 __device__ __forceinline__ int kidx(int g, int e) {
@@ -67,32 +68,32 @@ __device__ __forceinline__ int kidx(int g, int e) {
 
 // Lane (g, l) receives X[row0 + l][k0 + kidx(g, e)]: as an A operand, rows of X; as a B
 // operand, X^T.  X row-major with the given pitch (LDS or global, any storage type).
-template <int KO, typename TS>
-__device__ __forceinline__ Frag<OpT> frag_rows(const TS* X, int pitch, int row0, int k0, int lane) {
-  Frag<OpT> f;
+template <typename O, int KO, typename TS>
+__device__ __forceinline__ Frag<O> frag_rows(const TS* X, int pitch, int row0, int k0, int lane) {
+  Frag<O> f;
   const int g = lane >> 4;
   const TS* p = X + (size_t)(row0 + (lane & 15)) * pitch + k0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = cvt<OpT>(to_f32(p[kidx<KO>(g, e)]));
+  for (int e = 0; e < 8; ++e) f.v[e] = cvt<O>(to_f32(p[kidx<KO>(g, e)]));
   return f;
 }
 
 // Lane (g, l) receives X[k0 + kidx(g, e)][n0 + l]: as a B operand, X itself; as an A operand,
 // X^T.
-template <int KO, typename TS>
-__device__ __forceinline__ Frag<OpT> frag_cols(const TS* X, int pitch, int k0, int n0, int lane) {
-  Frag<OpT> f;
+template <typename O, int KO, typename TS>
+__device__ __forceinline__ Frag<O> frag_cols(const TS* X, int pitch, int k0, int n0, int lane) {
+  Frag<O> f;
   const int g = lane >> 4;
   const TS* p = X + (size_t)k0 * pitch + n0 + (lane & 15);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = cvt<OpT>(to_f32(p[(size_t)kidx<KO>(g, e) * pitch]));
+  for (int e = 0; e < 8; ++e) f.v[e] = cvt<O>(to_f32(p[(size_t)kidx<KO>(g, e) * pitch]));
   return f;
 }
 
 // Upper-triangular ones U[t][t'] = (t' >= t), t = 16 ti + (lane % 16), t' over K-step kk in
 // KORD_ACC order: as an A operand against a strip it forms reverse cumulative sums over tokens.
-__device__ __forceinline__ Frag<OpT> utri_frag(int ti, int kk, int lane) {
-  Frag<OpT> f;
+__device__ __forceinline__ Frag<float> utri_frag(int ti, int kk, int lane) {
+  Frag<float> f;
   const int t = 16 * ti + (lane & 15), g = lane >> 4;
 #pragma unroll
   for (int e = 0; e < 8; ++e) f.v[e] = (32 * kk + kidx<KORD_ACC>(g, e) >= t) ? 1.f : 0.f;
@@ -101,18 +102,18 @@ __device__ __forceinline__ Frag<OpT> utri_frag(int ti, int kk, int lane) {
 
 // out[ti] = sum_{j <= i} x_j (inclusive cumulative sum over the tokens of a strip).
 __device__ __forceinline__ void strip_cumsum(const f32x4 (&x)[4], f32x4 (&out)[4], int lane) {
-  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+  const Frag<float> b0 = acc_frag<float>(x[0], x[1]), b1 = acc_frag<float>(x[2], x[3]);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
     out[ti] = zero4();
-    mma(out[ti], ltri_frag<OpT>(ti, 0, lane), b0);
-    if (ti >= 2) mma(out[ti], ltri_frag<OpT>(ti, 1, lane), b1);
+    mma(out[ti], ltri_frag<float>(ti, 0, lane), b0);
+    if (ti >= 2) mma(out[ti], ltri_frag<float>(ti, 1, lane), b1);
   }
 }
 
 // out[ti] (+)= sum_{j >= i} x_j (reverse cumulative sum over the tokens of a strip).
 __device__ __forceinline__ void strip_revcumsum_add(const f32x4 (&x)[4], f32x4 (&out)[4], int lane) {
-  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+  const Frag<float> b0 = acc_frag<float>(x[0], x[1]), b1 = acc_frag<float>(x[2], x[3]);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
     if (ti < 2) mma(out[ti], utri_frag(ti, 0, lane), b0);
@@ -179,13 +180,13 @@ __device__ __forceinline__ void load_tile(T (*dst)[PQ], const T* src, int Lc, in
 
 // Tile (ti, tj) of tril_incl(X Y^T) for row-major tiles X, Y (contraction over D channels):
 // acc[r] = sum_c X[16 ti + 4 g + r][c] Y[16 tj + l][c], zero where column > row.
-template <int D, typename TX, typename TY>
+template <int D, typename O, typename TX, typename TY>
 __device__ __forceinline__ f32x4 tril_tile(const TX* X, int px, const TY* Y, int py, int ti, int tj, int lane) {
   f32x4 acc = zero4();
   if (tj > ti) return acc;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
-    mma(acc, frag_rows<KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), frag_rows<KORD_CONTIG>(Y, py, 16 * tj, 32 * kk, lane));
+    mma(acc, frag_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), frag_rows<O, KORD_CONTIG>(Y, py, 16 * tj, 32 * kk, lane));
   const int g = lane >> 4, l = lane & 15;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -195,45 +196,45 @@ __device__ __forceinline__ f32x4 tril_tile(const TX* X, int px, const TY* Y, int
 
 // strip[ti] += X (rows 16 ti.., all D channels of a row-major LDS tile) times the D x 16 block
 // M[:, cw .. cw + 15] of a global fp32 matrix (M[a][cw + n], K running over a).
-template <int D, typename TX>
+template <int D, typename O, typename TX>
 __device__ __forceinline__ void strip_times_mat(const TX* X, int px, const float* M, int cw, int lane, f32x4 (&out)[4]) {
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
-    const Frag<OpT> b = frag_cols<KORD_CONTIG>(M, D, 32 * kk, cw, lane);
+    const Frag<O> b = frag_cols<O, KORD_CONTIG>(M, D, 32 * kk, cw, lane);
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) mma(out[ti], frag_rows<KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
+    for (int ti = 0; ti < 4; ++ti) mma(out[ti], frag_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
   }
 }
 
 // strip[ti] += tril(Mt) x, Mt a 64 x 64 fp32 LDS tile (lower-triangular incl.), x a strip.
-template <int PT>
+template <int PT, typename O>
 __device__ __forceinline__ void tril_times_strip(const float* Mt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
-  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+  const Frag<O> b0 = acc_frag<O>(x[0], x[1]), b1 = acc_frag<O>(x[2], x[3]);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
-    mma(out[ti], frag_rows<KORD_ACC>(Mt, PT, 16 * ti, 0, lane), b0);
-    if (ti >= 2) mma(out[ti], frag_rows<KORD_ACC>(Mt, PT, 16 * ti, 32, lane), b1);
+    mma(out[ti], frag_rows<O, KORD_ACC>(Mt, PT, 16 * ti, 0, lane), b0);
+    if (ti >= 2) mma(out[ti], frag_rows<O, KORD_ACC>(Mt, PT, 16 * ti, 32, lane), b1);
   }
 }
 
 // strip[tj] += tril(Mt)^T x.
-template <int PT>
+template <int PT, typename O>
 __device__ __forceinline__ void trilT_times_strip(const float* Mt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
-  const Frag<OpT> b0 = acc_frag<OpT>(x[0], x[1]), b1 = acc_frag<OpT>(x[2], x[3]);
+  const Frag<O> b0 = acc_frag<O>(x[0], x[1]), b1 = acc_frag<O>(x[2], x[3]);
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
-    if (tj < 2) mma(out[tj], frag_cols<KORD_ACC>(Mt, PT, 0, 16 * tj, lane), b0);
-    mma(out[tj], frag_cols<KORD_ACC>(Mt, PT, 32, 16 * tj, lane), b1);
+    if (tj < 2) mma(out[tj], frag_cols<O, KORD_ACC>(Mt, PT, 0, 16 * tj, lane), b0);
+    mma(out[tj], frag_cols<O, KORD_ACC>(Mt, PT, 32, 16 * tj, lane), b1);
   }
 }
 
 // Rows [16 ta, 16 ta + 16) x strip columns of X^T y (contraction over the 64 tokens): X a
 // row-major LDS tile (token rows), y a strip.  acc[r] = out[16 ta + 4 g + r][cw + l].
-template <typename TX>
+template <typename O, typename TX>
 __device__ __forceinline__ f32x4 tileT_times_strip(const TX* X, int px, int ta, const f32x4 (&y)[4], int lane) {
   f32x4 acc = zero4();
-  mma(acc, frag_cols<KORD_ACC>(X, px, 0, 16 * ta, lane), acc_frag<OpT>(y[0], y[1]));
-  mma(acc, frag_cols<KORD_ACC>(X, px, 32, 16 * ta, lane), acc_frag<OpT>(y[2], y[3]));
+  mma(acc, frag_cols<O, KORD_ACC>(X, px, 0, 16 * ta, lane), acc_frag<O>(y[0], y[1]));
+  mma(acc, frag_cols<O, KORD_ACC>(X, px, 32, 16 * ta, lane), acc_frag<O>(y[2], y[3]));
   return acc;
 }
 
@@ -304,6 +305,7 @@ struct SmemA {
 template <int D, typename T>
 __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   using SM = SmemA<D, T>;
+  using O = T;
   constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PF = SM::PF, NA = D / 16;
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   // P = tril(Q K^T)
   for (int idx = w; idx < 16; idx += NW) {
     const int ti = idx >> 2, tj = idx & 3;
-    const f32x4 acc = tril_tile<D>(&sm.Q[0][0], PQ, &sm.K[0][0], PQ, ti, tj, lane);
+    const f32x4 acc = tril_tile<D, O>(&sm.Q[0][0], PQ, &sm.K[0][0], PQ, ti, tj, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.P[16 * ti + 4 * g + r][16 * tj + l16] = acc[r];
   }
@@ -383,8 +385,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   f32x4 us[4], qc[4];
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) us[ti] = zero4();
-  strip_times_mat<D>(&sm.Q[0][0], PQ, Cc, cw, lane, us);
-  tril_times_strip<PT>(&sm.P[0][0], ks, lane, us);
+  strip_times_mat<D, O>(&sm.Q[0][0], PQ, Cc, cw, lane, us);
+  tril_times_strip<PT, O>(&sm.P[0][0], ks, lane, us);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -399,7 +401,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   // D = tril(dO V^T) (into the log-decay tile: every wave has read its strip of it)
   for (int idx = w; idx < 16; idx += NW) {
     const int ti = idx >> 2, tj = idx & 3;
-    const f32x4 acc = tril_tile<D>(&sm.u1.in.dO[0][0], PQ, &sm.u1.in.V[0][0], PQ, ti, tj, lane);
+    const f32x4 acc = tril_tile<D, O>(&sm.u1.in.dO[0][0], PQ, &sm.u1.in.V[0][0], PQ, ti, tj, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.u2.Dm[16 * ti + 4 * g + r][16 * tj + l16] = acc[r];
   }
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) qh[ti][r] = qc[ti][r] * __expf(bs[ti][r]);
 #pragma unroll 2
     for (int ta = 0; ta < NA; ++ta) {
-      const f32x4 acc = tileT_times_strip(&sm.u1.in.dO[0][0], PQ, ta, qh, lane);
+      const f32x4 acc = tileT_times_strip<O>(&sm.u1.in.dO[0][0], PQ, ta, qh, lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) bslot[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = acc[r];
     }
@@ -429,8 +431,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) kh[ti][r] = ks[ti][r] * __expf(-bs[ti][r]);
     }
-    strip_times_mat<D>(&sm.u1.in.dO[0][0], PQ, Sc, cw, lane, dqc);
-    tril_times_strip<PT>(&sm.u2.Dm[0][0], kh, lane, dqc);
+    strip_times_mat<D, O>(&sm.u1.in.dO[0][0], PQ, Sc, cw, lane, dqc);
+    tril_times_strip<PT, O>(&sm.u2.Dm[0][0], kh, lane, dqc);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   // M = tril(dR K^T)
   for (int idx = w; idx < 16; idx += NW) {
     const int ti = idx >> 2, tj = idx & 3;
-    const f32x4 acc = tril_tile<D>(&sm.u1.dR[0][0], PF, &sm.K[0][0], PQ, ti, tj, lane);
+    const f32x4 acc = tril_tile<D, O>(&sm.u1.dR[0][0], PF, &sm.K[0][0], PQ, ti, tj, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) sm.u2.Dm[16 * ti + 4 * g + r][16 * tj + l16] = acc[r];
   }
@@ -499,8 +501,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    strip_times_mat<D>(&sm.u1.dR[0][0], PF, Cc, cw, lane, z);
-    tril_times_strip<PT>(&sm.u2.Dm[0][0], ks, lane, z);
+    strip_times_mat<D, O>(&sm.u1.dR[0][0], PF, Cc, cw, lane, z);
+    tril_times_strip<PT, O>(&sm.u2.Dm[0][0], ks, lane, z);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -524,8 +526,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    trilT_times_strip<PT>(&sm.P[0][0], dr, lane, z);
-    trilT_times_strip<PT>(&sm.u2.Dm[0][0], qs, lane, z);
+    trilT_times_strip<PT, O>(&sm.P[0][0], dr, lane, z);
+    trilT_times_strip<PT, O>(&sm.u2.Dm[0][0], qs, lane, z);
     strip_revcumsum_add(dm, z, lane);
     store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, z);
   }
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   float* Gs = bslot + (size_t)D * D;
 #pragma unroll 2
   for (int ta = 0; ta < NA; ++ta) {
-    const f32x4 acc = tileT_times_strip(&sm.u1.dR[0][0], PF, ta, qs, lane);
+    const f32x4 acc = tileT_times_strip<O>(&sm.u1.dR[0][0], PF, ta, qs, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) Gs[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = acc[r];
   }
@@ -620,6 +622,7 @@ struct SmemB {
 template <int D, typename T>
 __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   using SM = SmemB<D, T>;
+  using O = T;
   constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PF = SM::PF;
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
@@ -661,12 +664,13 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     for (int ti = 0; ti < 4; ++ti) kg[ti] = zero4();
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      Frag<OpT> b = frag_cols<KORD_CONTIG>(Ga, D, 32 * kk, cw, lane);
-      const Frag<OpT> bt = frag_rows<KORD_CONTIG>(Ga, D, cw, 32 * kk, lane);
+      const Frag<float> b0 = frag_cols<float, KORD_CONTIG>(Ga, D, 32 * kk, cw, lane);
+      const Frag<float> bt = frag_rows<float, KORD_CONTIG>(Ga, D, cw, 32 * kk, lane);
+      Frag<O> b;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) b.v[e] += bt.v[e];
+      for (int e = 0; e < 8; ++e) b.v[e] = cvt<O>(b0.v[e] + bt.v[e]);
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) mma(kg[ti], frag_rows<KORD_CONTIG>(&sm.u1.in.K[0][0], PQ, 16 * ti, 32 * kk, lane), b);
+      for (int ti = 0; ti < 4; ++ti) mma(kg[ti], frag_rows<O, KORD_CONTIG>(&sm.u1.in.K[0][0], PQ, 16 * ti, 32 * kk, lane), b);
     }
   }
   f32x4 qh[4], ebn[4];
@@ -688,8 +692,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   __syncthreads();
   for (int idx = w; idx < 16; idx += NW) {
     const int ti = idx >> 2, tj = idx & 3;
-    const f32x4 x = tril_tile<D>(&sm.Qh[0][0], PF, &sm.u1.Kh[0][0], PF, ti, tj, lane);
-    const f32x4 y = tril_tile<D>(&sm.dO[0][0], PQ, &sm.V[0][0], PQ, ti, tj, lane);
+    const f32x4 x = tril_tile<D, O>(&sm.Qh[0][0], PF, &sm.u1.Kh[0][0], PF, ti, tj, lane);
+    const f32x4 y = tril_tile<D, O>(&sm.dO[0][0], PQ, &sm.V[0][0], PQ, ti, tj, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       sm.A[16 * ti + 4 * g + r][16 * tj + l16] = x[r];
@@ -703,14 +707,15 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    trilT_times_strip<PT>(&sm.A[0][0], dos, lane, z);
+    trilT_times_strip<PT, O>(&sm.A[0][0], dos, lane, z);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      Frag<OpT> b = frag_rows<KORD_CONTIG>(dSe, D, cw, 32 * kk, lane);  // dS_end[cw + l][kappa]
+      const Frag<float> bf = frag_rows<float, KORD_CONTIG>(dSe, D, cw, 32 * kk, lane);  // dS_end[cw + l][kappa]
+      Frag<O> b;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) b.v[e] *= sm.eBL[32 * kk + kidx<KORD_CONTIG>(g, e)];
+      for (int e = 0; e < 8; ++e) b.v[e] = cvt<O>(bf.v[e] * sm.eBL[32 * kk + kidx<KORD_CONTIG>(g, e)]);
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) mma(z[ti], frag_rows<KORD_CONTIG>(&sm.u1.Kh[0][0], PF, 16 * ti, 32 * kk, lane), b);
+      for (int ti = 0; ti < 4; ++ti) mma(z[ti], frag_rows<O, KORD_CONTIG>(&sm.u1.Kh[0][0], PF, 16 * ti, 32 * kk, lane), b);
     }
     store_strip_rows<D>(a.dv + row0 * D, Lc, cw, lane, z);
   }
@@ -718,8 +723,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   f32x4 dkr[4], dks[4];
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) dkr[ti] = dks[ti] = zero4();
-  trilT_times_strip<PT>(&sm.Dm[0][0], qh, lane, dkr);
-  strip_times_mat<D>(&sm.V[0][0], PQ, dSe, cw, lane, dks);
+  trilT_times_strip<PT, O>(&sm.Dm[0][0], qh, lane, dkr);
+  strip_times_mat<D, O>(&sm.V[0][0], PQ, dSe, cw, lane, dks);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
     dks[ti] = dks[ti] * ebn[ti] * eBLv;
