@@ -55,7 +55,7 @@ namespace ccq {
 namespace {
 
 // MFMA operand type O: the input dtype (bf16 operands for bf16 inputs, fp32 for fp32 inputs);
-// the cumulative sums over tokens always take fp32 operands (exact for any input dtype).
+// the cumulative sums over tokens are exact for bf16 inputs and split hi + lo for computed values.
 
 template <int KO>
 __device__ __forceinline__ int kidx(int g, int e) {
@@ -92,32 +92,60 @@ __device__ __forceinline__ Frag<O> frag_cols(const TS* X, int pitch, int k0, int
 
 // Upper-triangular ones U[t][t'] = (t' >= t), t = 16 ti + (lane % 16), t' over K-step kk in
 // KORD_ACC order: as an A operand against a strip it forms reverse cumulative sums over tokens.
-__device__ __forceinline__ Frag<float> utri_frag(int ti, int kk, int lane) {
-  Frag<float> f;
+template <typename O>
+__device__ __forceinline__ Frag<O> utri_frag(int ti, int kk, int lane) {
+  Frag<O> f;
   const int t = 16 * ti + (lane & 15), g = lane >> 4;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = (32 * kk + kidx<KORD_ACC>(g, e) >= t) ? 1.f : 0.f;
+  for (int e = 0; e < 8; ++e) f.v[e] = cvt<O>((32 * kk + kidx<KORD_ACC>(g, e) >= t) ? 1.f : 0.f);
   return f;
 }
 
+// B operands of a strip's two K-steps of 32 tokens.  EXACT: the strip's values are exactly
+// representable in O (bf16 inputs read from a tile); otherwise, for bf16 operands, a second
+// pair holds the low parts x - bf16(x), so a sum against 0/1 weights keeps ~16 more bits.
+template <typename O, bool EXACT>
+struct StripOps {
+  Frag<O> hi0, hi1, lo0, lo1;
+  __device__ __forceinline__ explicit StripOps(const f32x4 (&x)[4]) {
+    hi0 = acc_frag<O>(x[0], x[1]);
+    hi1 = acc_frag<O>(x[2], x[3]);
+    if constexpr (!EXACT && sizeof(O) == 2) {
+      f32x4 r[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[t][e] = x[t][e] - (float)(O)x[t][e];
+      lo0 = acc_frag<O>(r[0], r[1]);
+      lo1 = acc_frag<O>(r[2], r[3]);
+    }
+  }
+  __device__ __forceinline__ void mma_k(f32x4& acc, const Frag<O>& a, int kk) const {
+    mma(acc, a, kk == 0 ? hi0 : hi1);
+    if constexpr (!EXACT && sizeof(O) == 2) mma(acc, a, kk == 0 ? lo0 : lo1);
+  }
+};
+
 // out[ti] = sum_{j <= i} x_j (inclusive cumulative sum over the tokens of a strip).
+template <typename O, bool EXACT>
 __device__ __forceinline__ void strip_cumsum(const f32x4 (&x)[4], f32x4 (&out)[4], int lane) {
-  const Frag<float> b0 = acc_frag<float>(x[0], x[1]), b1 = acc_frag<float>(x[2], x[3]);
+  const StripOps<O, EXACT> b(x);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
     out[ti] = zero4();
-    mma(out[ti], ltri_frag<float>(ti, 0, lane), b0);
-    if (ti >= 2) mma(out[ti], ltri_frag<float>(ti, 1, lane), b1);
+    b.mma_k(out[ti], ltri_frag<O>(ti, 0, lane), 0);
+    if (ti >= 2) b.mma_k(out[ti], ltri_frag<O>(ti, 1, lane), 1);
   }
 }
 
-// out[ti] (+)= sum_{j >= i} x_j (reverse cumulative sum over the tokens of a strip).
+// out[ti] += sum_{j >= i} x_j (reverse cumulative sum over the tokens of a strip).
+template <typename O, bool EXACT>
 __device__ __forceinline__ void strip_revcumsum_add(const f32x4 (&x)[4], f32x4 (&out)[4], int lane) {
-  const Frag<float> b0 = acc_frag<float>(x[0], x[1]), b1 = acc_frag<float>(x[2], x[3]);
+  const StripOps<O, EXACT> b(x);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
-    if (ti < 2) mma(out[ti], utri_frag(ti, 0, lane), b0);
-    mma(out[ti], utri_frag(ti, 1, lane), b1);
+    if (ti < 2) b.mma_k(out[ti], utri_frag<O>(ti, 0, lane), 0);
+    b.mma_k(out[ti], utri_frag<O>(ti, 1, lane), 1);
   }
 }
 
@@ -238,9 +266,29 @@ __device__ __forceinline__ f32x4 tileT_times_strip(const TX* X, int px, int ta, 
   return acc;
 }
 
-// Sum over the 16 channels of the lane group: every lane of group g gets the total for its
-// (ti, r) token.
-__device__ __forceinline__ float chan_sum(float x) { return group_sum<16>(x); }
+// One DPP exchange within rows of 16 lanes: the value of the lane the pattern pairs with.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Reduce-scatter over the 16 channels of a lane group: v[4 ti + r] is this lane's value for
+// token 16 ti + 4 g + r; lane l of the group returns the group's total for index l (token
+// 16 (l / 4) + 4 g + l % 4).  Four butterfly steps pair lane l with 15 - l (row mirror),
+// l ^ 7 within eight (half mirror), l ^ 3 and l ^ 1 within four (quad permutations); at each
+// step a lane keeps the half of its values its partner sends the other half of, so it moves
+// 8 + 4 + 2 + 1 values instead of 16 x 4.
+__device__ __forceinline__ float chan_reduce16(const float (&v)[16], int l) {
+  float a[8], b[4], c[2];
+  const bool up8 = (l & 8) != 0, up4 = (l & 4) != 0, up2 = (l & 2) != 0, up1 = (l & 1) != 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (up8 ? v[8 + j] : v[j]) + dpp<0x140>(up8 ? v[j] : v[8 + j]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = (up4 ? a[4 + j] : a[j]) + dpp<0x141>(up4 ? a[j] : a[4 + j]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) c[j] = (up2 ? b[2 + j] : b[j]) + dpp<0x1B>(up2 ? b[j] : b[2 + j]);
+  return (up1 ? c[1] : c[0]) + dpp<0xB1>(up1 ? c[0] : c[1]);
+}
 
 // Sum over the 64 tokens of a strip for the lane's channel (every lane gets it).
 __device__ __forceinline__ float token_sum(const f32x4 (&x)[4]) {
@@ -333,26 +381,28 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   const float b_lam = a.b_lambda[h];
   __syncthreads();
 
-  f32x4 qs[4], ks[4], bs[4], ck[4];
+  f32x4 qs[4], ks[4], bs[4];
   {
     f32x4 gs[4];
     read_strip(&sm.Q[0][0], PQ, cw, lane, qs);
     read_strip(&sm.K[0][0], PQ, cw, lane, ks);
     read_strip(&sm.u2.G[0][0], PQ, cw, lane, gs);
-    strip_cumsum(gs, bs, lane);
-    strip_cumsum(ks, ck, lane);
+    strip_cumsum<O, true>(gs, bs, lane);
   }
   // per-token w . q and m_c . q: this wave's channels
+  const int rtok = 16 * (l16 >> 2) + 4 * g + (l16 & 3);  // the token chan_reduce16 leaves here
+  {
+    float v0[16], v1[16];
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
+    for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x0 = chan_sum(qs[ti][r] * wv), x1 = chan_sum(qs[ti][r] * mv);
-      if (l16 == 0) {
-        sm.red[w][16 * ti + 4 * g + r][0] = x0;
-        sm.red[w][16 * ti + 4 * g + r][1] = x1;
+      for (int r = 0; r < 4; ++r) {
+        v0[4 * ti + r] = qs[ti][r] * wv;
+        v1[4 * ti + r] = qs[ti][r] * mv;
       }
-    }
+    sm.red[w][rtok][0] = chan_reduce16(v0, l16);
+    sm.red[w][rtok][1] = chan_reduce16(v1, l16);
+  }
   // P = tril(Q K^T)
   for (int idx = w; idx < 16; idx += NW) {
     const int ti = idx >> 2, tj = idx & 3;
@@ -387,12 +437,14 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   for (int ti = 0; ti < 4; ++ti) us[ti] = zero4();
   strip_times_mat<D, O>(&sm.Q[0][0], PQ, Cc, cw, lane, us);
   tril_times_strip<PT, O>(&sm.P[0][0], ks, lane, us);
+  f32x4 ck[4];  // cumulative key sum (recomputed where it is needed again: registers are short)
+  strip_cumsum<O, true>(ks, ck, lane);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const f32x4 ts = sm.tok[16 * ti + 4 * g + r];
-      const float u = (us[ti][r] - (mv + ck[ti][r]) * ts[2]) * ts[1];
+      const float u = (us[ti][r] - (mv + ck[ti][r]) * ts[2]) * ts[1];  // m_i = m_c + cumsum k
       us[ti][r] = u;
       qc[ti][r] = qs[ti][r] - ts[0] * u;
     }
@@ -445,16 +497,18 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     store_strip_rows<D>(qdqbuf, kL, cw, lane, qdq);
   }
   // per-token u . dqc and m_c . dqc
+  {
+    float v0[16], v1[16];
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
+    for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x0 = chan_sum(us[ti][r] * dqc[ti][r]), x1 = chan_sum(mv * dqc[ti][r]);
-      if (l16 == 0) {
-        sm.red[w][16 * ti + 4 * g + r][0] = x0;
-        sm.red[w][16 * ti + 4 * g + r][1] = x1;
+      for (int r = 0; r < 4; ++r) {
+        v0[4 * ti + r] = us[ti][r] * dqc[ti][r];
+        v1[4 * ti + r] = mv * dqc[ti][r];
       }
-    }
+    sm.red[w][rtok][0] = chan_reduce16(v0, l16);
+    sm.red[w][rtok][1] = chan_reduce16(v1, l16);
+  }
   // dR = -lambda dqc / n
   f32x4 dr[4];
 #pragma unroll
@@ -503,12 +557,14 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
     strip_times_mat<D, O>(&sm.u1.dR[0][0], PF, Cc, cw, lane, z);
     tril_times_strip<PT, O>(&sm.u2.Dm[0][0], ks, lane, z);
+    f32x4 ck2[4];
+    strip_cumsum<O, true>(ks, ck2, lane);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ti + 4 * g + r;
-        z[ti][r] += dqc[ti][r] + sm.tok2[i][0] * wv + sm.tok2[i][1] * (mv + ck[ti][r]);
+        z[ti][r] += dqc[ti][r] + sm.tok2[i][0] * wv + sm.tok2[i][1] * (mv + ck2[ti][r]);
       }
     store_strip_rows<D>(a.dq + row0 * D, Lc, cw, lane, z);
   }
@@ -528,7 +584,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
     trilT_times_strip<PT, O>(&sm.P[0][0], dr, lane, z);
     trilT_times_strip<PT, O>(&sm.u2.Dm[0][0], qs, lane, z);
-    strip_revcumsum_add(dm, z, lane);
+    strip_revcumsum_add<O, false>(dm, z, lane);
     store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, z);
   }
   // dG_c = dR^T Q
@@ -652,7 +708,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     f32x4 gs[4];
     read_strip(&sm.u1.in.K[0][0], PQ, cw, lane, ks);
     read_strip(&sm.u1.in.G[0][0], PQ, cw, lane, gs);
-    strip_cumsum(gs, bs, lane);
+    strip_cumsum<O, true>(gs, bs, lane);
   }
   read_strip(&sm.dO[0][0], PQ, cw, lane, dos);
   const float bL = __shfl(bs[3][3], 48 + l16, 64);  // token 63
@@ -747,7 +803,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
       out[ti] = zero4();
       dks[ti] *= ks[ti];
     }
-    strip_revcumsum_add(z, out, lane);
+    strip_revcumsum_add<O, false>(z, out, lane);
     float cs = 0.f;
     for (int row = g; row < D; row += 4) cs += Sc[(size_t)row * D + cw + l16] * dSe[(size_t)row * D + cw + l16];
     cs += __shfl_xor(cs, 16, 64);
