@@ -229,13 +229,13 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
 
 size_t ccq_bwd_workspace_bytes(const ccq_bwd_params* p) {
   if (validate_bwd(p) != CCQ_OK) return 0;
-  return ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k);
+  return ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k, p->dtype);
 }
 
 int ccq_bwd_chunked(const ccq_bwd_params* p, void* hip_stream) {
   const int st = validate_bwd(p);
   if (st != CCQ_OK) return st;
-  const size_t need = ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k);
+  const size_t need = ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k, p->dtype);
   if (p->workspace == nullptr || p->workspace_bytes < need) return CCQ_ERR_WORKSPACE;
   ccq::BwdArgs a{};
   a.dtype = p->dtype;

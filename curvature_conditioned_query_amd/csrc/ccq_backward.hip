@@ -35,8 +35,8 @@
 // of S_c and the chunk's own terms.
 //
 // Passes (one stream, in order):
-//   1. chunk carries: the prefill's segment summary and scan with one chunk per segment give
-//      S_c, C_c, m_c for every chunk (workspace);
+//   1. chunk carries: the prefill's segment summary with one chunk per segment, then a scan
+//      that writes S_c, C_c (input dtype) and m_c for every chunk (workspace);
 //   2. pass A, one workgroup per (chain, chunk): the forward read recomputed, dQc, the read
 //      adjoint, dq (final), the chunk's own statistics part of dk (partial, into dk), and the
 //      chunk's contributions R_c = dO^T (Qc e^B), dG_c = dR^T Q, sum dm, sum dlogit q, sum dlogit;
@@ -223,9 +223,9 @@ __device__ __forceinline__ f32x4 tril_tile(const TX* X, int px, const TY* Y, int
 }
 
 // strip[ti] += X (rows 16 ti.., all D channels of a row-major LDS tile) times the D x 16 block
-// M[:, cw .. cw + 15] of a global fp32 matrix (M[a][cw + n], K running over a).
-template <int D, typename O, typename TX>
-__device__ __forceinline__ void strip_times_mat(const TX* X, int px, const float* M, int cw, int lane, f32x4 (&out)[4]) {
+// M[:, cw .. cw + 15] of a global matrix (M[a][cw + n], K running over a).
+template <int D, typename O, typename TX, typename TM>
+__device__ __forceinline__ void strip_times_mat(const TX* X, int px, const TM* M, int cw, int lane, f32x4 (&out)[4]) {
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const Frag<O> b = frag_cols<O, KORD_CONTIG>(M, D, 32 * kk, cw, lane);
@@ -305,26 +305,64 @@ constexpr int PT = kL + 4;  // pitch of the fp32 64 x 64 token tiles
 template <int D>
 constexpr int pf() { return D + 4; }  // pitch of fp32 [64][D] tiles
 
-// Workspace of one backward call (floats):
-//   forward carries   chains x NC x (2 D^2 + 2 D)   S | C | ksum | log decay (prefill layout)
-//   backward slots    chains x NC x (2 D^2 + 4 D)   dS | G | dm | dw | db (D, [0] used) | B_L
-//   qc, qc * dqc      2 x chains x NC x 64 x D
-template <int D>
-constexpr size_t bslot_floats() { return 2 * (size_t)D * D + 4 * D; }
-
-struct BwdLayout {
-  float *fwd, *bwd, *qc, *qdq;
+// Workspace of one backward call, in this order (E = the input dtype; fp32 where noted):
+//   segment summaries  fp32 chains x NC x (2 D^2 + 2 D)  S | C | ksum | log decay (prefill layout)
+//   chunk carries      E    chains x NC x 2 D^2          S_c | C_c
+//   chunk key sums     fp32 chains x NC x D              m_c
+//   adjoint matrices   E    chains x NC x 2 D^2          R_c | dG_c, then dS_end | G
+//   adjoint tails      fp32 chains x NC x 4 D            dm | dw | db (D, [0] used) | B_L
+//   qc, qc * dqc       fp32 2 x chains x NC x 64 x D
+// The carries and the adjoint matrices are MFMA operands of the input dtype anyway, so they
+// are stored in it; every running sum is fp32 (in the scans' registers).
+struct BwdLayoutBytes {
+  size_t sum, car, carm, mat, tail, qc, qdq, total;
 };
 
-__device__ __forceinline__ BwdLayout layout(const BwdArgs& a) {
-  const size_t chains = (size_t)a.B * a.H, NC = (size_t)a.nchunks, d = (size_t)a.d;
-  BwdLayout L;
-  L.fwd = static_cast<float*>(a.workspace);
-  L.bwd = L.fwd + chains * NC * (2 * d * d + 2 * d);
-  L.qc = L.bwd + chains * NC * (2 * d * d + 4 * d);
-  L.qdq = L.qc + chains * NC * kL * d;
+__host__ __device__ inline BwdLayoutBytes bwd_layout_bytes(size_t chains, size_t NC, size_t d, size_t E) {
+  BwdLayoutBytes L;
+  size_t off = 0;
+  L.sum = off;
+  off += chains * NC * (2 * d * d + 2 * d) * 4;
+  L.car = off;
+  off += chains * NC * 2 * d * d * E;
+  L.carm = off;
+  off += chains * NC * d * 4;
+  L.mat = off;
+  off += chains * NC * 2 * d * d * E;
+  L.tail = off;
+  off += chains * NC * 4 * d * 4;
+  L.qc = off;
+  off += chains * NC * kL * d * 4;
+  L.qdq = off;
+  off += chains * NC * kL * d * 4;
+  L.total = off;
   return L;
 }
+
+template <typename T>
+struct BwdLayout {
+  float* sum;   // segment summaries
+  T* car;       // S_c | C_c per chunk
+  float* carm;  // m_c per chunk
+  T* mat;       // R_c | dG_c, then dS_end | G, per chunk
+  float* tail;  // dm | dw | db | B_L per chunk
+  float *qc, *qdq;
+};
+
+template <typename T>
+__device__ __forceinline__ BwdLayout<T> layout(const BwdArgs& a) {
+  const BwdLayoutBytes b = bwd_layout_bytes((size_t)a.B * a.H, (size_t)a.nchunks, (size_t)a.d, sizeof(T));
+  char* w = static_cast<char*>(a.workspace);
+  return BwdLayout<T>{reinterpret_cast<float*>(w + b.sum), reinterpret_cast<T*>(w + b.car),
+                      reinterpret_cast<float*>(w + b.carm), reinterpret_cast<T*>(w + b.mat),
+                      reinterpret_cast<float*>(w + b.tail), reinterpret_cast<float*>(w + b.qc),
+                      reinterpret_cast<float*>(w + b.qdq)};
+}
+
+template <typename T>
+__device__ __forceinline__ void st4t(T* p, const f32x4& v) { st4<T>(p, v); }
+template <typename T>
+__device__ __forceinline__ f32x4 ld4t(const T* p) { return ld4<T>(p); }
 
 template <int D, typename T>
 struct SmemA {
@@ -361,14 +399,15 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   const int chain = blockIdx.x / NC, c = blockIdx.x % NC, h = chain % a.H;
   const int t0 = c * kL, Lc = min(kL, a.T - t0);
   const size_t row0 = (size_t)chain * a.T + t0;
-  const BwdLayout L = layout(a);
-  const float* fslot = L.fwd + ((size_t)chain * NC + c) * (2 * (size_t)D * D + 2 * D);
-  const float* Sc = fslot;
-  const float* Cc = fslot + (size_t)D * D;
-  const float* mc = fslot + 2 * (size_t)D * D;
-  float* bslot = L.bwd + ((size_t)chain * NC + c) * bslot_floats<D>();
-  float* qcbuf = L.qc + ((size_t)chain * NC + c) * kL * D;
-  float* qdqbuf = L.qdq + ((size_t)chain * NC + c) * kL * D;
+  const BwdLayout<T> L = layout<T>(a);
+  const size_t slot = (size_t)chain * NC + c;
+  const T* Sc = L.car + slot * 2 * D * D;
+  const T* Cc = Sc + (size_t)D * D;
+  const float* mc = L.carm + slot * D;
+  T* bmat = L.mat + slot * 2 * D * D;
+  float* tail = L.tail + slot * 4 * D;
+  float* qcbuf = L.qc + slot * kL * D;
+  float* qdqbuf = L.qdq + slot * kL * D;
   const int64_t nc = (a.n0 != nullptr ? a.n0[chain] : 0) + t0;
 
   load_tile<D, T, PQ>(sm.Q, static_cast<const T*>(a.q) + row0 * D, Lc, tid, NT);
@@ -468,7 +507,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     for (int ta = 0; ta < NA; ++ta) {
       const f32x4 acc = tileT_times_strip<O>(&sm.u1.in.dO[0][0], PQ, ta, qh, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bslot[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = acc[r];
+      for (int r = 0; r < 4; ++r) bmat[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = (T)acc[r];
     }
   }
   __syncthreads();
@@ -588,12 +627,12 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, z);
   }
   // dG_c = dR^T Q
-  float* Gs = bslot + (size_t)D * D;
+  T* Gs = bmat + (size_t)D * D;
 #pragma unroll 2
   for (int ta = 0; ta < NA; ++ta) {
     const f32x4 acc = tileT_times_strip<O>(&sm.u1.dR[0][0], PF, ta, qs, lane);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Gs[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = acc[r];
+    for (int r = 0; r < 4; ++r) Gs[(size_t)(16 * ta + 4 * g + r) * D + cw + l16] = (T)acc[r];
   }
   // sum dm, sum dlogit q, sum dlogit, B_L
   {
@@ -603,7 +642,6 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dq_w[ti][r] = sm.tok2[16 * ti + 4 * g + r][0] * qs[ti][r];
     const float sdm = token_sum(dm), sdw = token_sum(dq_w);
-    float* tail = bslot + 2 * (size_t)D * D;
     if (g == 0) {
       tail[cw + l16] = sdm;
       tail[D + cw + l16] = sdw;
@@ -616,11 +654,62 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   }
 }
 
-// Reverse scan over the chunks of a chain, in place, one thread per 4 floats of dS | G | dm |
-// dw | db:  slot c receives dS_end(c), G(c), dm_after(c) (the adjoints carried back from the
-// chunks after c and the caller's carry-out adjoint); dS_end(c-1) = dS_end(c) diag(e^{B_L(c)}) + R_c.
-// What is left after chunk 0 is the carry-in adjoint.  dw and db are summed over chunks.
-template <int D>
+// Carry at every chunk start, from the segment summaries (one chunk per segment) of the
+// prefill's summary kernel: S_c, C_c (stored in the input dtype) and m_c (fp32), with
+//   carry[0] = carry in (or zero);  carry[c+1] = (S_c diag(e^{ldec_c}) + dS_c, C_c + dC_c, m_c + dm_c).
+// One thread per 4 consecutive floats of S | C | ksum; running sums in fp32; chunks in batches
+// of 8 whose summaries are loaded together before the dependent updates.
+template <int D, typename T>
+__global__ __launch_bounds__(256) void bwd_carry_scan_kernel(BwdArgs a) {
+  const int chain = blockIdx.y;
+  const int NC = a.nchunks;
+  const int nf4 = (2 * D * D + D) / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nf4) return;
+  const size_t f = (size_t)idx * 4, DD = (size_t)D * D;
+  const BwdLayout<T> L = layout<T>(a);
+  const size_t sstride = 2 * DD + 2 * D;
+  const float* sums = L.sum + (size_t)chain * NC * sstride;
+  const bool isS = f < DD, isM = f >= 2 * DD;
+  const int col = (int)(f % D);
+  f32x4 run = zero4();
+  if (a.S0 != nullptr) {
+    const float* src = isS ? a.S0 + (size_t)chain * DD + f
+                     : !isM ? a.C0 + (size_t)chain * DD + (f - DD)
+                            : a.ksum0 + (size_t)chain * D + (f - 2 * DD);
+    run = *reinterpret_cast<const f32x4*>(src);
+  }
+  constexpr int kBatch = 8;
+  for (int p0 = 0; p0 < NC; p0 += kBatch) {
+    f32x4 sum[kBatch], ld[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = p0 + j;
+      const float* slot = sums + (size_t)(p < NC - 1 ? p : 0) * sstride;
+      sum[j] = (p < NC - 1) ? *reinterpret_cast<const f32x4*>(slot + f) : zero4();
+      ld[j] = (isS && p < NC - 1) ? *reinterpret_cast<const f32x4*>(slot + 2 * DD + D + col) : zero4();
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = p0 + j;
+      if (p >= NC) break;
+      const size_t cslot = (size_t)chain * NC + p;
+      if (isM)
+        *reinterpret_cast<f32x4*>(L.carm + cslot * D + (f - 2 * DD)) = run;
+      else
+        st4t<T>(L.car + cslot * 2 * DD + f, run);
+      if (isS) run = run * f32x4{__expf(ld[j][0]), __expf(ld[j][1]), __expf(ld[j][2]), __expf(ld[j][3])};
+      run += sum[j];
+    }
+  }
+}
+
+// Reverse scan over the chunks of a chain, in place, one thread per 4 floats of dS | G (the
+// adjoint matrices, input dtype) and dm | dw | db (fp32 tails): chunk c receives dS_end(c), G(c),
+// dm_after(c) (the adjoints carried back from the chunks after c and the caller's carry-out
+// adjoint); dS_end(c-1) = dS_end(c) diag(e^{B_L(c)}) + R_c.  What is left after chunk 0 is the
+// carry-in adjoint.  dw and db are summed over chunks.  Running sums in fp32.
+template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
   const int chain = blockIdx.y;
   const int NC = a.nchunks;
@@ -628,25 +717,37 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= nf4) return;
   const size_t f = (size_t)idx * 4;
-  const BwdLayout L = layout(a);
-  float* base = L.bwd + (size_t)chain * NC * bslot_floats<D>();
+  const BwdLayout<T> L = layout<T>(a);
   const size_t DD = (size_t)D * D;
   const int part = f < DD ? 0 : f < 2 * DD ? 1 : f < 2 * DD + D ? 2 : f < 2 * DD + 2 * D ? 3 : 4;
   const size_t off = part == 0 ? f : part == 1 ? f - DD : f - 2 * DD - (size_t)D * (part - 2);
   const int col = (int)(f % D);
+  // this thread's 4 values in chunk c: matrices (parts 0, 1) or tails (parts 2..4)
+  auto mat_at = [&](int c) { return L.mat + ((size_t)chain * NC + c) * 2 * DD + f; };
+  auto tail_at = [&](int c) { return L.tail + ((size_t)chain * NC + c) * 4 * D; };
   f32x4 run = zero4();
   if (part == 0 && a.dS_T) run = *reinterpret_cast<const f32x4*>(a.dS_T + (size_t)chain * DD + off);
   if (part == 1 && a.dC_T) run = *reinterpret_cast<const f32x4*>(a.dC_T + (size_t)chain * DD + off);
   if (part == 2 && a.dksum_T) run = *reinterpret_cast<const f32x4*>(a.dksum_T + (size_t)chain * D + off);
-  for (int cc = NC - 1; cc >= 0; --cc) {
-    float* slot = base + (size_t)cc * bslot_floats<D>();
-    const f32x4 x = *reinterpret_cast<const f32x4*>(slot + f);
-    if (part <= 2) *reinterpret_cast<f32x4*>(slot + f) = run;
-    if (part == 0) {
-      const f32x4 bl = *reinterpret_cast<const f32x4*>(slot + 2 * DD + 3 * D + col);
-      run = run * f32x4{__expf(bl[0]), __expf(bl[1]), __expf(bl[2]), __expf(bl[3])};
+  constexpr int kBatch = 8;
+  for (int c0 = NC - 1; c0 >= 0; c0 -= kBatch) {
+    f32x4 x[kBatch], bl[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int cc = c0 - j < 0 ? 0 : c0 - j;
+      const bool ok = c0 - j >= 0;
+      x[j] = !ok ? zero4() : part <= 1 ? ld4t<T>(mat_at(cc)) : *reinterpret_cast<const f32x4*>(tail_at(cc) + (f - 2 * DD));
+      bl[j] = (ok && part == 0) ? *reinterpret_cast<const f32x4*>(tail_at(cc) + 3 * D + col) : zero4();
     }
-    run += x;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int cc = c0 - j;
+      if (cc < 0) break;
+      if (part <= 1) st4t<T>(mat_at(cc), run);
+      if (part == 2) *reinterpret_cast<f32x4*>(tail_at(cc) + (f - 2 * DD)) = run;
+      if (part == 0) run = run * f32x4{__expf(bl[j][0]), __expf(bl[j][1]), __expf(bl[j][2]), __expf(bl[j][3])};
+      run += x[j];
+    }
   }
   if (part == 0 && a.dS0) *reinterpret_cast<f32x4*>(a.dS0 + (size_t)chain * DD + off) = run;
   if (part == 1 && a.dC0) *reinterpret_cast<f32x4*>(a.dC0 + (size_t)chain * DD + off) = run;
@@ -686,14 +787,14 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
   const int t0 = c * kL, Lc = min(kL, a.T - t0);
   const size_t row0 = (size_t)chain * a.T + t0;
-  const BwdLayout L = layout(a);
-  const float* Sc = L.fwd + ((size_t)chain * NC + c) * (2 * (size_t)D * D + 2 * D);
-  const float* bslot = L.bwd + ((size_t)chain * NC + c) * bslot_floats<D>();
-  const float* dSe = bslot;
-  const float* Ga = bslot + (size_t)D * D;
-  const float dma = bslot[2 * (size_t)D * D + cw + l16];
-  const float* qcbuf = L.qc + ((size_t)chain * NC + c) * kL * D;
-  const float* qdqbuf = L.qdq + ((size_t)chain * NC + c) * kL * D;
+  const BwdLayout<T> L = layout<T>(a);
+  const size_t slot = (size_t)chain * NC + c;
+  const T* Sc = L.car + slot * 2 * D * D;
+  const T* dSe = L.mat + slot * 2 * D * D;
+  const T* Ga = dSe + (size_t)D * D;
+  const float dma = L.tail[slot * 4 * D + cw + l16];
+  const float* qcbuf = L.qc + slot * kL * D;
+  const float* qdqbuf = L.qdq + slot * kL * D;
 
   load_tile<D, T, PQ>(sm.u1.in.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
   load_tile<D, T, PQ>(sm.u1.in.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, tid, NT);
@@ -805,7 +906,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     }
     strip_revcumsum_add<O, false>(z, out, lane);
     float cs = 0.f;
-    for (int row = g; row < D; row += 4) cs += Sc[(size_t)row * D + cw + l16] * dSe[(size_t)row * D + cw + l16];
+    for (int row = g; row < D; row += 4) cs += to_f32(Sc[(size_t)row * D + cw + l16]) * to_f32(dSe[(size_t)row * D + cw + l16]);
     cs += __shfl_xor(cs, 16, 64);
     cs += __shfl_xor(cs, 32, 64);
     const float after = eBLv * cs + token_sum(dks);
@@ -815,9 +916,9 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   }
 }
 
-size_t bwd_workspace_bytes(int B, int H, int T, int d) {
-  const size_t chains = (size_t)B * H, NC = (size_t)((T + kL - 1) / kL), dd = (size_t)d;
-  return chains * NC * ((2 * dd * dd + 2 * dd) + (2 * dd * dd + 4 * dd) + 2 * kL * dd) * sizeof(float);
+size_t bwd_workspace_bytes(int B, int H, int T, int d, int dtype) {
+  const size_t chains = (size_t)B * H, NC = (size_t)((T + kL - 1) / kL);
+  return bwd_layout_bytes(chains, NC, (size_t)d, dtype == 1 ? 2 : 4).total;
 }
 
 static hipError_t record_bwd_event(const BwdArgs& a, int i, hipStream_t s) {
@@ -845,16 +946,19 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   f.C0 = a.C0;
   f.ksum0 = a.ksum0;
   f.n0 = a.n0;
-  f.workspace = a.workspace;
+  f.workspace = a.workspace;  // the segment summaries come first in the workspace
   f.flags = 0;
   if (record_bwd_event(a, 0, s) != hipSuccess) return hipErrorLaunchFailure;
-  hipError_t e = launch_gla_chunk_carries(f, s);
+  hipError_t e = launch_gla_chunk_summaries(f, s);
   if (e != hipSuccess) return e;
+  const int cf4 = (2 * D * D + D) / 4;
+  hipLaunchKernelGGL((bwd_carry_scan_kernel<D, T>), dim3((unsigned)((cf4 + 255) / 256), (unsigned)chains), dim3(256), 0,
+                     s, a);
   if (record_bwd_event(a, 1, s) != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_chunk_a_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
   if (record_bwd_event(a, 2, s) != hipSuccess) return hipErrorLaunchFailure;
   const int nf4 = (2 * D * D + 3 * D) / 4;
-  hipLaunchKernelGGL((bwd_scan_kernel<D>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_scan_kernel<D, T>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
   if (record_bwd_event(a, 3, s) != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_chunk_b_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
   e = hipGetLastError();

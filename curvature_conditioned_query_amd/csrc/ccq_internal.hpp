@@ -87,12 +87,12 @@ struct BwdArgs {
   void* workspace;
   void* const* events;  // optional: 5 hipEvent_t around the passes
 };
-size_t bwd_workspace_bytes(int B, int H, int T, int d);
+size_t bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
-// Summary and scan of the GLA prefill only: the carry at the start of every segment in the
-// workspace slots (the chunked backward runs it with one chunk per segment).
-hipError_t launch_gla_chunk_carries(const FwdArgs& a, hipStream_t stream);
+// Segment summaries of the GLA prefill only, into the workspace slots (the chunked backward
+// runs it with one chunk per segment and scans the result itself).
+hipError_t launch_gla_chunk_summaries(const FwdArgs& a, hipStream_t stream);
 
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).

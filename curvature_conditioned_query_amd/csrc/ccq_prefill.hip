@@ -594,16 +594,27 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
       run = *reinterpret_cast<const f32x4*>(src);
     }
   }
-  for (int p = 0; p < P; ++p) {
-    float* slot = base + (size_t)p * slot_f;
-    const f32x4 sum = (p < P - 1) ? *reinterpret_cast<const f32x4*>(slot + f) : zero4();
-    *reinterpret_cast<f32x4*>(slot + f) = run;
-    if (p < P - 1) {
-      if (isS) {
-        const f32x4 ld = *reinterpret_cast<const f32x4*>(slot + 2 * (size_t)D * D + D + col);
-        run = run * f32x4{__expf(ld[0]), __expf(ld[1]), __expf(ld[2]), __expf(ld[3])};
+  // Slots in batches of 8: the batch's summaries (and log decays) are loaded together before
+  // the dependent updates, so a long chain waits for memory once per batch, not once per slot.
+  constexpr int kBatch = 8;
+  for (int p0 = 0; p0 < P; p0 += kBatch) {
+    f32x4 sum[kBatch], ld[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = p0 + j;
+      const float* slot = base + (size_t)p * slot_f;
+      sum[j] = (p < P - 1) ? *reinterpret_cast<const f32x4*>(slot + f) : zero4();
+      ld[j] = (isS && p < P - 1) ? *reinterpret_cast<const f32x4*>(slot + 2 * (size_t)D * D + D + col) : zero4();
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = p0 + j;
+      if (p >= P) break;
+      *reinterpret_cast<f32x4*>(base + (size_t)p * slot_f + f) = run;
+      if (p < P - 1) {
+        if (isS) run = run * f32x4{__expf(ld[j][0]), __expf(ld[j][1]), __expf(ld[j][2]), __expf(ld[j][3])};
+        run += sum[j];
       }
-      run += sum;
     }
   }
 }
@@ -635,26 +646,23 @@ static hipError_t launch_gla(const FwdArgs& a, hipStream_t s) {
   return record_event(a, 3, s);
 }
 
-// The carry at the start of every segment (summary and scan only), into the workspace slots:
-// with one chunk per segment these are the carries at every chunk start, which the chunked
-// backward recomputes instead of storing them in the forward.
+// The segment summaries only (segments 0 .. P-2), into the workspace slots: with one chunk
+// per segment, the per-chunk carry updates the chunked backward scans into chunk carries.
 template <int D, typename T>
-static hipError_t launch_gla_carries_t(const FwdArgs& a, hipStream_t s) {
+static hipError_t launch_gla_summaries_t(const FwdArgs& a, hipStream_t s) {
   const int chains = a.B * a.H;
   const int P = a.segments;
   if (P > 1)
     hipLaunchKernelGGL((gla_summary_kernel<D, T>), dim3((unsigned)(chains * (P - 1))), dim3(4 * D), 0, s, a);
-  const int nf4 = (2 * D * D + D) / 4;
-  hipLaunchKernelGGL((gla_scan_kernel<D>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gla_chunk_carries(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_gla_chunk_summaries(const FwdArgs& a, hipStream_t s) {
   if (a.dtype == 1) {
-    if (a.d == 128) return launch_gla_carries_t<128, __bf16>(a, s);
-    if (a.d == 64) return launch_gla_carries_t<64, __bf16>(a, s);
+    if (a.d == 128) return launch_gla_summaries_t<128, __bf16>(a, s);
+    if (a.d == 64) return launch_gla_summaries_t<64, __bf16>(a, s);
   } else if (a.d == 64) {
-    return launch_gla_carries_t<64, float>(a, s);
+    return launch_gla_summaries_t<64, float>(a, s);
   }
   return hipErrorInvalidValue;
 }
