@@ -47,6 +47,8 @@
 // (v_mfma_f32_16x16x32_bf16 for bf16 inputs, v_mfma_f32_16x16x4_f32 for fp32 inputs); wave w
 // of a workgroup owns the 16 channels [16w, 16w + 16) of d: a "strip" holds, in accumulator layout, a [64 tokens] x [16 channels] block (element r of lane
 // (g = lane / 16, l = lane % 16) of tile ti is token 16 ti + 4 g + r, channel 16 w + l).
+#include <type_traits>
+
 #include "ccq_internal.hpp"
 #include "ccq_prefill_common.hpp"
 
@@ -181,28 +183,59 @@ __device__ __forceinline__ void store_strip_rows(float* p, int rows, int cw, int
     }
 }
 
-template <int D>
-__device__ __forceinline__ void load_strip_rows(const float* p, int rows, int cw, int lane, f32x4 (&v)[4]) {
-  const int g = lane >> 4, l = lane & 15;
+// A strip in the workspace's strip-major order: the 16 values of a lane are contiguous (lane
+// order within the wave, waves in order within the chunk), so each lane moves 4 x 16 bytes.
+__device__ __forceinline__ void store_strip_vec(float* p, int lane, const f32x4 (&v)[4]) {
+  f32x4* q = reinterpret_cast<f32x4*>(p + (size_t)lane * 16);
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
+  for (int ti = 0; ti < 4; ++ti) q[ti] = v[ti];
+}
+__device__ __forceinline__ void load_strip_vec(const float* p, int lane, f32x4 (&v)[4]) {
+  const f32x4* q = reinterpret_cast<const f32x4*>(p + (size_t)lane * 16);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * ti + 4 * g + r;
-      v[ti][r] = (i < rows) ? p[(size_t)i * D + cw + l] : 0.f;
-    }
+  for (int ti = 0; ti < 4; ++ti) v[ti] = q[ti];
 }
 
-// Rows 0 .. Lc-1 of a chunk of a [token][D] tensor into an LDS tile of pitch PQ, 16 bytes per
-// thread and step; rows Lc .. 63 are zeroed.
-template <int D, typename T, int PQ>
-__device__ __forceinline__ void load_tile(T (*dst)[PQ], const T* src, int Lc, int tid, int nthreads) {
+// Rows 0 .. Lc-1 of a [ROWS][D] block (row stride D) into an LDS tile of pitch PQ, 16 bytes per
+// thread and step; rows Lc .. ROWS-1 are zeroed.
+template <int D, int ROWS, typename T, int PQ>
+__device__ __forceinline__ void load_rows(T (*dst)[PQ], const T* src, int Lc, int tid, int nthreads) {
   constexpr int EPU = 16 / (int)sizeof(T), U = D / EPU;
-  for (int u = tid; u < kL * U; u += nthreads) {
+  for (int u = tid; u < ROWS * U; u += nthreads) {
     const int row = u / U, col = (u % U) * EPU;
     uint4 x = make_uint4(0u, 0u, 0u, 0u);
     if (row < Lc) x = *reinterpret_cast<const uint4*>(src + (size_t)row * D + col);
     *reinterpret_cast<uint4*>(&dst[row][col]) = x;
+  }
+}
+
+// Rows 0 .. Lc-1 of a chunk of a [token][D] tensor (64-row tile).
+template <int D, typename T, int PQ>
+__device__ __forceinline__ void load_tile(T (*dst)[PQ], const T* src, int Lc, int tid, int nthreads) {
+  load_rows<D, kL, T, PQ>(dst, src, Lc, tid, nthreads);
+}
+
+// Fragments of LDS tiles: wide reads when the tile already holds operands of type O (16- or
+// 8-byte row reads; gfx950 transposing reads for the column forms of bf16 tiles), otherwise
+// element reads converted to O.
+template <typename O, int KO, typename TS>
+__device__ __forceinline__ Frag<O> tile_rows(const TS* X, int pitch, int row0, int k0, int lane) {
+  if constexpr (std::is_same<TS, O>::value) {
+    return lds_frag<O, KO>(X, pitch, row0, k0, lane);
+  } else {
+    return frag_rows<O, KO>(X, pitch, row0, k0, lane);
+  }
+}
+template <typename O, int KO, typename TS>
+__device__ __forceinline__ Frag<O> tile_cols(const TS* X, int pitch, int k0, int n0, int lane) {
+  if constexpr (std::is_same<TS, O>::value && sizeof(O) == 2) {
+    if constexpr (KO == KORD_CONTIG) {
+      return tr_frag<O>(X, pitch, k0, n0, lane);
+    } else {
+      return tr_frag_acc<O>(X, pitch, k0, n0, lane);
+    }
+  } else {
+    return frag_cols<O, KO>(X, pitch, k0, n0, lane);
   }
 }
 
@@ -214,7 +247,7 @@ __device__ __forceinline__ f32x4 tril_tile(const TX* X, int px, const TY* Y, int
   if (tj > ti) return acc;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk)
-    mma(acc, frag_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), frag_rows<O, KORD_CONTIG>(Y, py, 16 * tj, 32 * kk, lane));
+    mma(acc, tile_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), tile_rows<O, KORD_CONTIG>(Y, py, 16 * tj, 32 * kk, lane));
   const int g = lane >> 4, l = lane & 15;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
@@ -230,29 +263,53 @@ __device__ __forceinline__ void strip_times_mat(const TX* X, int px, const TM* M
   for (int kk = 0; kk < D / 32; ++kk) {
     const Frag<O> b = frag_cols<O, KORD_CONTIG>(M, D, 32 * kk, cw, lane);
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) mma(out[ti], frag_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
+    for (int ti = 0; ti < 4; ++ti) mma(out[ti], tile_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
   }
 }
 
-// strip[ti] += tril(Mt) x, Mt a 64 x 64 fp32 LDS tile (lower-triangular incl.), x a strip.
-template <int PT, typename O>
-__device__ __forceinline__ void tril_times_strip(const float* Mt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
+// As strip_times_mat for a symmetric global matrix M: the block is read as rows
+// M[cw + n][a] (contiguous, 16 bytes per lane and K-step for bf16).
+template <int D, typename O, typename TX, typename TM>
+__device__ __forceinline__ void strip_times_sym(const TX* X, int px, const TM* M, int cw, int lane, f32x4 (&out)[4]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const Frag<O> b = frag_rows<O, KORD_CONTIG>(M, D, cw, 32 * kk, lane);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) mma(out[ti], tile_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
+  }
+}
+
+// As strip_times_mat for a D x D matrix staged in LDS (pitch pm).
+template <int D, typename O, typename TX, typename TM>
+__device__ __forceinline__ void strip_times_tile(const TX* X, int px, const TM* M, int pm, int cw, int lane,
+                                                 f32x4 (&out)[4]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const Frag<O> b = tile_cols<O, KORD_CONTIG>(M, pm, 32 * kk, cw, lane);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) mma(out[ti], tile_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
+  }
+}
+
+// strip[ti] += tril(Mt) x, Mt a 64 x 64 LDS tile (lower-triangular incl., pitch pt), x a strip.
+template <typename O, typename TS>
+__device__ __forceinline__ void tril_times_strip(const TS* Mt, int pt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
   const Frag<O> b0 = acc_frag<O>(x[0], x[1]), b1 = acc_frag<O>(x[2], x[3]);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
-    mma(out[ti], frag_rows<O, KORD_ACC>(Mt, PT, 16 * ti, 0, lane), b0);
-    if (ti >= 2) mma(out[ti], frag_rows<O, KORD_ACC>(Mt, PT, 16 * ti, 32, lane), b1);
+    mma(out[ti], tile_rows<O, KORD_ACC>(Mt, pt, 16 * ti, 0, lane), b0);
+    if (ti >= 2) mma(out[ti], tile_rows<O, KORD_ACC>(Mt, pt, 16 * ti, 32, lane), b1);
   }
 }
 
 // strip[tj] += tril(Mt)^T x.
-template <int PT, typename O>
-__device__ __forceinline__ void trilT_times_strip(const float* Mt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
+template <typename O, typename TS>
+__device__ __forceinline__ void trilT_times_strip(const TS* Mt, int pt, const f32x4 (&x)[4], int lane, f32x4 (&out)[4]) {
   const Frag<O> b0 = acc_frag<O>(x[0], x[1]), b1 = acc_frag<O>(x[2], x[3]);
 #pragma unroll
   for (int tj = 0; tj < 4; ++tj) {
-    if (tj < 2) mma(out[tj], frag_cols<O, KORD_ACC>(Mt, PT, 0, 16 * tj, lane), b0);
-    mma(out[tj], frag_cols<O, KORD_ACC>(Mt, PT, 32, 16 * tj, lane), b1);
+    if (tj < 2) mma(out[tj], tile_cols<O, KORD_ACC>(Mt, pt, 0, 16 * tj, lane), b0);
+    mma(out[tj], tile_cols<O, KORD_ACC>(Mt, pt, 32, 16 * tj, lane), b1);
   }
 }
 
@@ -261,8 +318,8 @@ __device__ __forceinline__ void trilT_times_strip(const float* Mt, const f32x4 (
 template <typename O, typename TX>
 __device__ __forceinline__ f32x4 tileT_times_strip(const TX* X, int px, int ta, const f32x4 (&y)[4], int lane) {
   f32x4 acc = zero4();
-  mma(acc, frag_cols<O, KORD_ACC>(X, px, 0, 16 * ta, lane), acc_frag<O>(y[0], y[1]));
-  mma(acc, frag_cols<O, KORD_ACC>(X, px, 32, 16 * ta, lane), acc_frag<O>(y[2], y[3]));
+  mma(acc, tile_cols<O, KORD_ACC>(X, px, 0, 16 * ta, lane), acc_frag<O>(y[0], y[1]));
+  mma(acc, tile_cols<O, KORD_ACC>(X, px, 32, 16 * ta, lane), acc_frag<O>(y[2], y[3]));
   return acc;
 }
 
@@ -311,11 +368,11 @@ constexpr int pf() { return D + 4; }  // pitch of fp32 [64][D] tiles
 //   chunk key sums     fp32 chains x NC x D              m_c
 //   adjoint matrices   E    chains x NC x 2 D^2          R_c | dG_c, then dS_end | G
 //   adjoint tails      fp32 chains x NC x 4 D            dm | dw | db (D, [0] used) | B_L
-//   qc, qc * dqc       fp32 2 x chains x NC x 64 x D
+//   qc, qc * dqc, dk   fp32 3 x chains x NC x 64 x D  (strip-major: a lane's 16 values contiguous)
 // The carries and the adjoint matrices are MFMA operands of the input dtype anyway, so they
 // are stored in it; every running sum is fp32 (in the scans' registers).
 struct BwdLayoutBytes {
-  size_t sum, car, carm, mat, tail, qc, qdq, total;
+  size_t sum, car, carm, mat, tail, qc, qdq, dkp, total;
 };
 
 __host__ __device__ inline BwdLayoutBytes bwd_layout_bytes(size_t chains, size_t NC, size_t d, size_t E) {
@@ -335,6 +392,8 @@ __host__ __device__ inline BwdLayoutBytes bwd_layout_bytes(size_t chains, size_t
   off += chains * NC * kL * d * 4;
   L.qdq = off;
   off += chains * NC * kL * d * 4;
+  L.dkp = off;
+  off += chains * NC * kL * d * 4;
   L.total = off;
   return L;
 }
@@ -346,7 +405,7 @@ struct BwdLayout {
   float* carm;  // m_c per chunk
   T* mat;       // R_c | dG_c, then dS_end | G, per chunk
   float* tail;  // dm | dw | db | B_L per chunk
-  float *qc, *qdq;
+  float *qc, *qdq, *dkp;  // cleaned query, qc * dqc, pass A's part of dk (strip-major)
 };
 
 template <typename T>
@@ -356,7 +415,7 @@ __device__ __forceinline__ BwdLayout<T> layout(const BwdArgs& a) {
   return BwdLayout<T>{reinterpret_cast<float*>(w + b.sum), reinterpret_cast<T*>(w + b.car),
                       reinterpret_cast<float*>(w + b.carm), reinterpret_cast<T*>(w + b.mat),
                       reinterpret_cast<float*>(w + b.tail), reinterpret_cast<float*>(w + b.qc),
-                      reinterpret_cast<float*>(w + b.qdq)};
+                      reinterpret_cast<float*>(w + b.qdq), reinterpret_cast<float*>(w + b.dkp)};
 }
 
 template <typename T>
@@ -381,6 +440,7 @@ struct SmemA {
     T G[kL][PQ];
     float Dm[kL][PT];  // tril(dO V^T), then tril(dR K^T)
   } u2;
+  T Sst[D][PQ];      // S_c, staged with 16-byte loads
   float red[NW][kL][2];
   f32x4 tok[kL];     // lambda, 1/n, sq/n, -
   float tok2[kL][2]; // dlogit, m_c . dr then ds
@@ -406,8 +466,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   const float* mc = L.carm + slot * D;
   T* bmat = L.mat + slot * 2 * D * D;
   float* tail = L.tail + slot * 4 * D;
-  float* qcbuf = L.qc + slot * kL * D;
-  float* qdqbuf = L.qdq + slot * kL * D;
+  const size_t sv = (slot * NW + w) * kL * 16;  // this wave's strip in the strip-major buffers
   const int64_t nc = (a.n0 != nullptr ? a.n0[chain] : 0) + t0;
 
   load_tile<D, T, PQ>(sm.Q, static_cast<const T*>(a.q) + row0 * D, Lc, tid, NT);
@@ -415,6 +474,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   load_tile<D, T, PQ>(sm.u2.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, tid, NT);
   load_tile<D, T, PQ>(sm.u1.in.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
   load_tile<D, T, PQ>(sm.u1.in.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
+  load_rows<D, D, T, PQ>(sm.Sst, Sc, D, tid, NT);
   const float wv = a.w_lambda[(size_t)h * D + cw + l16];
   const float mv = mc[cw + l16];
   const float b_lam = a.b_lambda[h];
@@ -474,8 +534,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   f32x4 us[4], qc[4];
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) us[ti] = zero4();
-  strip_times_mat<D, O>(&sm.Q[0][0], PQ, Cc, cw, lane, us);
-  tril_times_strip<PT, O>(&sm.P[0][0], ks, lane, us);
+  strip_times_sym<D, O>(&sm.Q[0][0], PQ, Cc, cw, lane, us);
+  tril_times_strip<O>(&sm.P[0][0], PT, ks, lane, us);
   f32x4 ck[4];  // cumulative key sum (recomputed where it is needed again: registers are short)
   strip_cumsum<O, true>(ks, ck, lane);
 #pragma unroll
@@ -487,7 +547,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
       us[ti][r] = u;
       qc[ti][r] = qs[ti][r] - ts[0] * u;
     }
-  store_strip_rows<D>(qcbuf, kL, cw, lane, qc);
+  store_strip_vec(L.qc + sv, lane, qc);
 
   // D = tril(dO V^T) (into the log-decay tile: every wave has read its strip of it)
   for (int idx = w; idx < 16; idx += NW) {
@@ -522,8 +582,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) kh[ti][r] = ks[ti][r] * __expf(-bs[ti][r]);
     }
-    strip_times_mat<D, O>(&sm.u1.in.dO[0][0], PQ, Sc, cw, lane, dqc);
-    tril_times_strip<PT, O>(&sm.u2.Dm[0][0], kh, lane, dqc);
+    strip_times_tile<D, O>(&sm.u1.in.dO[0][0], PQ, &sm.Sst[0][0], PQ, cw, lane, dqc);
+    tril_times_strip<O>(&sm.u2.Dm[0][0], PT, kh, lane, dqc);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -533,7 +593,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     f32x4 qdq[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) qdq[ti] = qc[ti] * dqc[ti];
-    store_strip_rows<D>(qdqbuf, kL, cw, lane, qdq);
+    store_strip_vec(L.qdq + sv, lane, qdq);
   }
   // per-token u . dqc and m_c . dqc
   {
@@ -594,8 +654,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    strip_times_mat<D, O>(&sm.u1.dR[0][0], PF, Cc, cw, lane, z);
-    tril_times_strip<PT, O>(&sm.u2.Dm[0][0], ks, lane, z);
+    strip_times_sym<D, O>(&sm.u1.dR[0][0], PF, Cc, cw, lane, z);
+    tril_times_strip<O>(&sm.u2.Dm[0][0], PT, ks, lane, z);
     f32x4 ck2[4];
     strip_cumsum<O, true>(ks, ck2, lane);
 #pragma unroll
@@ -621,10 +681,10 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    trilT_times_strip<PT, O>(&sm.P[0][0], dr, lane, z);
-    trilT_times_strip<PT, O>(&sm.u2.Dm[0][0], qs, lane, z);
+    trilT_times_strip<O>(&sm.P[0][0], PT, dr, lane, z);
+    trilT_times_strip<O>(&sm.u2.Dm[0][0], PT, qs, lane, z);
     strip_revcumsum_add<O, false>(dm, z, lane);
-    store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, z);
+    store_strip_vec(L.dkp + sv, lane, z);
   }
   // dG_c = dR^T Q
   T* Gs = bmat + (size_t)D * D;
@@ -759,19 +819,20 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
 namespace {
 template <int D, typename T>
 struct SmemB {
-  static constexpr int PQ = Cfg<D, T>::PQ, PF = pf<D>();
+  static constexpr int PQ = Cfg<D, T>::PQ, PTO = kL + 16 / (int)sizeof(T);
   union {
     struct {
       T K[kL][PQ];
       T G[kL][PQ];
     } in;
-    float Kh[kL][PF];  // k e^-B, once the key and log-decay strips are read
+    T Kh[kL][PQ];  // k e^-B, once the key and log-decay strips are read
   } u1;
   T V[kL][PQ];
   T dO[kL][PQ];
-  float Qh[kL][PF];  // qc e^B
-  float A[kL][PT];   // tril((qc e^B)(k e^-B)^T)
-  float Dm[kL][PT];  // tril(dO V^T)
+  T Qh[kL][PQ];    // qc e^B
+  T A[kL][PTO];    // tril((qc e^B)(k e^-B)^T)
+  T Dm[kL][PTO];   // tril(dO V^T)
+  T Mst[D][PQ];    // G, then dS_end (staged with 16-byte loads)
   float eBL[D];
 };
 }  // namespace
@@ -780,7 +841,7 @@ template <int D, typename T>
 __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   using SM = SmemB<D, T>;
   using O = T;
-  constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PF = SM::PF;
+  constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PTO = SM::PTO;
   __shared__ SM sm;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
   const int NC = a.nchunks;
@@ -793,15 +854,15 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   const T* dSe = L.mat + slot * 2 * D * D;
   const T* Ga = dSe + (size_t)D * D;
   const float dma = L.tail[slot * 4 * D + cw + l16];
-  const float* qcbuf = L.qc + slot * kL * D;
-  const float* qdqbuf = L.qdq + slot * kL * D;
+  const size_t sv = (slot * NW + w) * kL * 16;  // this wave's strip in the strip-major buffers
 
   load_tile<D, T, PQ>(sm.u1.in.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
   load_tile<D, T, PQ>(sm.u1.in.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, tid, NT);
   load_tile<D, T, PQ>(sm.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
   load_tile<D, T, PQ>(sm.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
+  load_rows<D, D, T, PQ>(sm.Mst, Ga, D, tid, NT);
   f32x4 qc[4];
-  load_strip_rows<D>(qcbuf, kL, cw, lane, qc);
+  load_strip_vec(L.qc + sv, lane, qc);
   __syncthreads();
 
   f32x4 ks[4], bs[4], dos[4], kg[4];
@@ -821,13 +882,13 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     for (int ti = 0; ti < 4; ++ti) kg[ti] = zero4();
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const Frag<float> b0 = frag_cols<float, KORD_CONTIG>(Ga, D, 32 * kk, cw, lane);
-      const Frag<float> bt = frag_rows<float, KORD_CONTIG>(Ga, D, cw, 32 * kk, lane);
+      const Frag<O> gc = tile_cols<O, KORD_CONTIG>(&sm.Mst[0][0], PQ, 32 * kk, cw, lane);  // G[c][kappa]
+      const Frag<O> gr = tile_rows<O, KORD_CONTIG>(&sm.Mst[0][0], PQ, cw, 32 * kk, lane);  // G[kappa][c]
       Frag<O> b;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) b.v[e] = cvt<O>(b0.v[e] + bt.v[e]);
+      for (int e = 0; e < 8; ++e) b.v[e] = cvt<O>(to_f32(gc.v[e]) + to_f32(gr.v[e]));
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) mma(kg[ti], frag_rows<O, KORD_CONTIG>(&sm.u1.in.K[0][0], PQ, 16 * ti, 32 * kk, lane), b);
+      for (int ti = 0; ti < 4; ++ti) mma(kg[ti], tile_rows<O, KORD_CONTIG>(&sm.u1.in.K[0][0], PQ, 16 * ti, 32 * kk, lane), b);
     }
   }
   f32x4 qh[4], ebn[4];
@@ -838,23 +899,24 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
       qh[ti][r] = qc[ti][r] * __expf(bs[ti][r]);
       ebn[ti][r] = __expf(-bs[ti][r]);
     }
-  __syncthreads();  // key and log-decay tiles fully read
+  __syncthreads();  // key, log-decay and G tiles fully read
+  load_rows<D, D, T, PQ>(sm.Mst, dSe, D, tid, NT);
   {
     f32x4 kh[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) kh[ti] = ks[ti] * ebn[ti];
-    write_strip(&sm.u1.Kh[0][0], PF, cw, lane, kh);
-    write_strip(&sm.Qh[0][0], PF, cw, lane, qh);
+    write_strip(&sm.u1.Kh[0][0], PQ, cw, lane, kh);
+    write_strip(&sm.Qh[0][0], PQ, cw, lane, qh);
   }
   __syncthreads();
   for (int idx = w; idx < 16; idx += NW) {
     const int ti = idx >> 2, tj = idx & 3;
-    const f32x4 x = tril_tile<D, O>(&sm.Qh[0][0], PF, &sm.u1.Kh[0][0], PF, ti, tj, lane);
+    const f32x4 x = tril_tile<D, O>(&sm.Qh[0][0], PQ, &sm.u1.Kh[0][0], PQ, ti, tj, lane);
     const f32x4 y = tril_tile<D, O>(&sm.dO[0][0], PQ, &sm.V[0][0], PQ, ti, tj, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sm.A[16 * ti + 4 * g + r][16 * tj + l16] = x[r];
-      sm.Dm[16 * ti + 4 * g + r][16 * tj + l16] = y[r];
+      sm.A[16 * ti + 4 * g + r][16 * tj + l16] = (T)x[r];
+      sm.Dm[16 * ti + 4 * g + r][16 * tj + l16] = (T)y[r];
     }
   }
   __syncthreads();
@@ -864,15 +926,15 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    trilT_times_strip<PT, O>(&sm.A[0][0], dos, lane, z);
+    trilT_times_strip<O>(&sm.A[0][0], PTO, dos, lane, z);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const Frag<float> bf = frag_rows<float, KORD_CONTIG>(dSe, D, cw, 32 * kk, lane);  // dS_end[cw + l][kappa]
+      const Frag<O> br = tile_rows<O, KORD_CONTIG>(&sm.Mst[0][0], PQ, cw, 32 * kk, lane);  // dS_end[cw + l][kappa]
       Frag<O> b;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) b.v[e] = cvt<O>(bf.v[e] * sm.eBL[32 * kk + kidx<KORD_CONTIG>(g, e)]);
+      for (int e = 0; e < 8; ++e) b.v[e] = cvt<O>(to_f32(br.v[e]) * sm.eBL[32 * kk + kidx<KORD_CONTIG>(g, e)]);
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) mma(z[ti], frag_rows<O, KORD_CONTIG>(&sm.u1.Kh[0][0], PF, 16 * ti, 32 * kk, lane), b);
+      for (int ti = 0; ti < 4; ++ti) mma(z[ti], tile_rows<O, KORD_CONTIG>(&sm.u1.Kh[0][0], PQ, 16 * ti, 32 * kk, lane), b);
     }
     store_strip_rows<D>(a.dv + row0 * D, Lc, cw, lane, z);
   }
@@ -880,8 +942,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   f32x4 dkr[4], dks[4];
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) dkr[ti] = dks[ti] = zero4();
-  trilT_times_strip<PT, O>(&sm.Dm[0][0], qh, lane, dkr);
-  strip_times_mat<D, O>(&sm.V[0][0], PQ, dSe, cw, lane, dks);
+  trilT_times_strip<O>(&sm.Dm[0][0], PTO, qh, lane, dkr);
+  strip_times_tile<D, O>(&sm.V[0][0], PQ, &sm.Mst[0][0], PQ, cw, lane, dks);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
     dks[ti] = dks[ti] * ebn[ti] * eBLv;
@@ -889,7 +951,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   }
   {
     f32x4 part[4], dk[4];
-    load_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, part);
+    load_strip_vec(L.dkp + sv, lane, part);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) dk[ti] = dkr[ti] + kg[ti] + part[ti] + dma;
     store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, dk);
@@ -897,7 +959,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   // dlog alpha = revcumsum(qc dqc - k dk_rule) + e^{B_L} colsum(S_c dS_end) + sum_j k_j dk_state_j
   {
     f32x4 z[4], out[4];
-    load_strip_rows<D>(qdqbuf, kL, cw, lane, z);
+    load_strip_vec(L.qdq + sv, lane, z);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       z[ti] -= ks[ti] * dkr[ti];
@@ -906,7 +968,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     }
     strip_revcumsum_add<O, false>(z, out, lane);
     float cs = 0.f;
-    for (int row = g; row < D; row += 4) cs += to_f32(Sc[(size_t)row * D + cw + l16]) * to_f32(dSe[(size_t)row * D + cw + l16]);
+    for (int row = g; row < D; row += 4) cs += to_f32(Sc[(size_t)row * D + cw + l16]) * to_f32(sm.Mst[row][cw + l16]);
     cs += __shfl_xor(cs, 16, 64);
     cs += __shfl_xor(cs, 32, 64);
     const float after = eBLv * cs + token_sum(dks);

@@ -262,7 +262,7 @@ int ccq_bwd_chunked(const ccq_bwd_params *p, void *hip_stream);
 
 /* Bytes of device workspace ccq_bwd_chunked needs (0 for invalid p).  Depends only on dtype, B,
  * H, T and d_k: per (b, h) and 64-token chunk, the forward carry update, the carry and the
- * carried-back adjoints, and two fp32 [64, d_k] tiles (0.33 MB per chunk at d_k = 128, bf16). */
+ * carried-back adjoints, and three fp32 [64, d_k] tiles (0.36 MB per chunk at d_k = 128, bf16). */
 size_t ccq_bwd_workspace_bytes(const ccq_bwd_params *p);
 
 #ifdef __cplusplus

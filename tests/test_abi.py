@@ -184,9 +184,9 @@ def test_bwd_workspace_sizing_and_check(lib):
     p = _bparams(B=4, H=16, T=4096)
     need = lib.ccq_bwd_workspace_bytes(ctypes.byref(p))
     # per chain and chunk (bf16): the fp32 carry update (2 d^2 + 2 d), the bf16 carry and adjoint
-    # matrices (2 d^2 each), the fp32 key sum (d) and adjoint tails (4 d), two fp32 [64, d] tiles
+    # matrices (2 d^2 each), the fp32 key sum (d) and adjoint tails (4 d), three fp32 [64, d] tiles
     d = 128
-    per = (2 * d * d + 2 * d) * 4 + 2 * d * d * 2 + d * 4 + 2 * d * d * 2 + 4 * d * 4 + 2 * 64 * d * 4
+    per = (2 * d * d + 2 * d) * 4 + 2 * d * d * 2 + d * 4 + 2 * d * d * 2 + 4 * d * 4 + 3 * 64 * d * 4
     assert need == 4 * 16 * 64 * per
     p.workspace, p.workspace_bytes = FAKE, need - 16
     assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == WORKSPACE
