@@ -35,8 +35,8 @@
 // of S_c and the chunk's own terms.
 //
 // Passes (one stream, in order):
-//   1. chunk carries: the prefill's segment summary with one chunk per segment, then a scan
-//      that writes S_c, C_c (input dtype) and m_c for every chunk (workspace);
+//   1. chunk carries: the prefill's segment summary and scan, then a walk over each segment's
+//      chunks that writes S_c, C_c (input dtype) and m_c for every chunk (workspace);
 //   2. pass A, one workgroup per (chain, chunk): the forward read recomputed, dQc, the read
 //      adjoint, dq (final), the chunk's own statistics part of dk (partial, into dk), and the
 //      chunk's contributions R_c = dO^T (Qc e^B), dG_c = dR^T Q, sum dm, sum dlogit q, sum dlogit;
@@ -363,7 +363,8 @@ template <int D>
 constexpr int pf() { return D + 4; }  // pitch of fp32 [64][D] tiles
 
 // Workspace of one backward call, in this order (E = the input dtype; fp32 where noted):
-//   segment summaries  fp32 chains x NC x (2 D^2 + 2 D)  S | C | ksum | log decay (prefill layout)
+//   segment slots      fp32 chains x NC x (2 D^2 + 2 D)  S | C | ksum | log decay (prefill layout;
+//                                                       the first chains x P of them used)
 //   chunk carries      E    chains x NC x 2 D^2          S_c | C_c
 //   chunk key sums     fp32 chains x NC x D              m_c
 //   adjoint matrices   E    chains x NC x 2 D^2          R_c | dG_c, then dS_end | G
@@ -714,53 +715,117 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   }
 }
 
-// Carry at every chunk start, from the segment summaries (one chunk per segment) of the
-// prefill's summary kernel: S_c, C_c (stored in the input dtype) and m_c (fp32), with
-//   carry[0] = carry in (or zero);  carry[c+1] = (S_c diag(e^{ldec_c}) + dS_c, C_c + dC_c, m_c + dm_c).
-// One thread per 4 consecutive floats of S | C | ksum; running sums in fp32; chunks in batches
-// of 8 whose summaries are loaded together before the dependent updates.
+namespace {
 template <int D, typename T>
-__global__ __launch_bounds__(256) void bwd_carry_scan_kernel(BwdArgs a) {
-  const int chain = blockIdx.y;
+struct SmemW {
+  static constexpr int PQ = Cfg<D, T>::PQ;
+  T K[2][kL][PQ];
+  T V[2][kL][PQ];
+  T G[2][kL][PQ];  // log decay; each wave then overwrites its own channels with k e^-B
+  float eBL[D];
+};
+}  // namespace
+
+// Carry at every chunk start, walking the chunks of a segment from the segment's carry-in (the
+// prefill's segment summary and scan; for one segment, the carry in): before chunk c it writes
+// the carry (S_c, C_c in the input dtype, m_c fp32), then applies the chunk's update
+//   C += K^T K,  m += sum k,  S = (S + V^T (K e^-B)) diag(e^{B_63})
+// (the prefill's carry update).  One workgroup per (chain, segment); wave w keeps rows
+// [16w, 16w + 16) of S (value rows) and the matching columns of C in MFMA accumulators, as the
+// prefill does; the next chunk's tiles stream into the other LDS buffer (gfx950 direct
+// HBM -> LDS loads) while the current chunk is applied.
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void bwd_carry_walk_kernel(BwdArgs a, int P, int cps) {
+  using SM = SmemW<D, T>;
+  using O = T;
+  constexpr int NW = D / 16, NA = D / 16, PQ = SM::PQ;
+  __shared__ SM sm;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
   const int NC = a.nchunks;
-  const int nf4 = (2 * D * D + D) / 4;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= nf4) return;
-  const size_t f = (size_t)idx * 4, DD = (size_t)D * D;
+  const int chain = blockIdx.x / P, seg = blockIdx.x % P;
+  const int c0 = seg * cps, c1 = min(NC, c0 + cps);
+  const size_t DD = (size_t)D * D;
   const BwdLayout<T> L = layout<T>(a);
-  const size_t sstride = 2 * DD + 2 * D;
-  const float* sums = L.sum + (size_t)chain * NC * sstride;
-  const bool isS = f < DD, isM = f >= 2 * DD;
-  const int col = (int)(f % D);
-  f32x4 run = zero4();
-  if (a.S0 != nullptr) {
-    const float* src = isS ? a.S0 + (size_t)chain * DD + f
-                     : !isM ? a.C0 + (size_t)chain * DD + (f - DD)
-                            : a.ksum0 + (size_t)chain * D + (f - 2 * DD);
-    run = *reinterpret_cast<const f32x4*>(src);
+  const float *S_in = nullptr, *C_in = nullptr, *m_in = nullptr;
+  if (P > 1) {  // the prefill's scan left every segment's carry-in in its slot
+    const float* slot = L.sum + ((size_t)chain * P + seg) * (2 * DD + 2 * D);
+    S_in = slot;
+    C_in = slot + DD;
+    m_in = slot + 2 * DD;
+  } else if (a.S0 != nullptr) {
+    S_in = a.S0 + (size_t)chain * DD;
+    C_in = a.C0 + (size_t)chain * DD;
+    m_in = a.ksum0 + (size_t)chain * D;
   }
-  constexpr int kBatch = 8;
-  for (int p0 = 0; p0 < NC; p0 += kBatch) {
-    f32x4 sum[kBatch], ld[kBatch];
+  // Sacc[t][r] = S[cw + l16][16 t + 4 g + r] (= S^T tile), Cacc[t][r] = C[16 t + 4 g + r][cw + l16]
+  f32x4 Sacc[NA], Cacc[NA];
+  float mv = 0.f;  // m[cw + l16]
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int p = p0 + j;
-      const float* slot = sums + (size_t)(p < NC - 1 ? p : 0) * sstride;
-      sum[j] = (p < NC - 1) ? *reinterpret_cast<const f32x4*>(slot + f) : zero4();
-      ld[j] = (isS && p < NC - 1) ? *reinterpret_cast<const f32x4*>(slot + 2 * DD + D + col) : zero4();
+  for (int t = 0; t < NA; ++t) {
+    Sacc[t] = S_in ? *reinterpret_cast<const f32x4*>(S_in + (size_t)(cw + l16) * D + 16 * t + 4 * g) : zero4();
+    Cacc[t] = C_in ? *reinterpret_cast<const f32x4*>(C_in + (size_t)(cw + l16) * D + 16 * t + 4 * g) : zero4();
+  }
+  if (m_in) mv = m_in[cw + l16];
+  // chunks whose update is needed: all but the segment's last (the carry after it is the next
+  // segment's carry-in, or unused after the chain's last chunk)
+  const int cu = c1 - 1;
+  const T* kg_ = static_cast<const T*>(a.k);
+  const T* vg_ = static_cast<const T*>(a.v);
+  const T* gg_ = static_cast<const T*>(a.log_alpha);
+  auto issue = [&](int c, int b) {
+    const size_t row0 = (size_t)chain * a.T + (size_t)c * kL;
+    dma_tile<D, T, PQ>(sm.K[b], kg_ + row0 * D, kL, w, NW, lane);
+    dma_tile<D, T, PQ>(sm.V[b], vg_ + row0 * D, kL, w, NW, lane);
+    dma_tile<D, T, PQ>(sm.G[b], gg_ + row0 * D, kL, w, NW, lane);
+  };
+  if (c0 < cu) issue(c0, 0);
+  for (int c = c0; c < c1; ++c) {
+    const size_t cs = (size_t)chain * NC + c;
+    T* Sd = L.car + cs * 2 * DD;
+    T* Cd = Sd + DD;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      st4t<T>(Sd + (size_t)(cw + l16) * D + 16 * t + 4 * g, Sacc[t]);
+      st4t<T>(Cd + (size_t)(cw + l16) * D + 16 * t + 4 * g, Cacc[t]);  // C symmetric: row cw + l16
+    }
+    if (g == 0) L.carm[cs * D + cw + l16] = mv;
+    if (c >= cu) break;
+    const int b = (c - c0) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // chunk c's tiles have landed; the other buffer is free
+    if (c + 1 < cu) issue(c + 1, b ^ 1);
+    f32x4 ks[4], bs[4];
+    {
+      f32x4 gs[4];
+      read_strip(&sm.K[b][0][0], PQ, cw, lane, ks);
+      read_strip(&sm.G[b][0][0], PQ, cw, lane, gs);
+      strip_cumsum<O, true>(gs, bs, lane);
+    }
+    mv += token_sum(ks);
+    {
+      f32x4 kp[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kp[ti][r] = ks[ti][r] * __expf(-bs[ti][r]);
+      write_strip(&sm.G[b][0][0], PQ, cw, lane, kp);  // own channels only: no other wave reads them before the barrier
+    }
+    const float eBLv = __expf(__shfl(bs[3][3], 48 + l16, 64));  // token 63
+    if (g == 0) sm.eBL[cw + l16] = eBLv;
+    lds_barrier();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const Frag<O> Bk = tile_cols<O, KORD_CONTIG>(&sm.K[b][0][0], PQ, 32 * kk, cw, lane);
+      const Frag<O> Bv = tile_cols<O, KORD_CONTIG>(&sm.V[b][0][0], PQ, 32 * kk, cw, lane);
+#pragma unroll
+      for (int t = 0; t < NA; ++t) {
+        mma(Cacc[t], tile_cols<O, KORD_CONTIG>(&sm.K[b][0][0], PQ, 32 * kk, 16 * t, lane), Bk);
+        mma(Sacc[t], tile_cols<O, KORD_CONTIG>(&sm.G[b][0][0], PQ, 32 * kk, 16 * t, lane), Bv);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int p = p0 + j;
-      if (p >= NC) break;
-      const size_t cslot = (size_t)chain * NC + p;
-      if (isM)
-        *reinterpret_cast<f32x4*>(L.carm + cslot * D + (f - 2 * DD)) = run;
-      else
-        st4t<T>(L.car + cslot * 2 * DD + f, run);
-      if (isS) run = run * f32x4{__expf(ld[j][0]), __expf(ld[j][1]), __expf(ld[j][2]), __expf(ld[j][3])};
-      run += sum[j];
-    }
+    for (int t = 0; t < NA; ++t) Sacc[t] *= *reinterpret_cast<const f32x4*>(&sm.eBL[16 * t + 4 * g]);
+    lds_barrier();  // eBL and the k e^-B columns are read before the next chunk rewrites them
   }
 }
 
@@ -999,8 +1064,6 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   f.H = a.H;
   f.T = a.T;
   f.d = D;
-  f.segments = NC;
-  f.chunks_per_segment = 1;
   f.k = a.k;
   f.v = a.v;
   f.log_alpha = a.log_alpha;
@@ -1010,12 +1073,18 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   f.n0 = a.n0;
   f.workspace = a.workspace;  // the segment summaries come first in the workspace
   f.flags = 0;
+  // segments: about one (chain, segment) workgroup per compute unit, as the prefill chooses
+  int P = (256 + chains - 1) / chains;
+  if (P > NC) P = NC;
+  if (P < 1) P = 1;
+  const int cps = (NC + P - 1) / P;
+  P = (NC + cps - 1) / cps;
+  f.segments = P;
+  f.chunks_per_segment = cps;
   if (record_bwd_event(a, 0, s) != hipSuccess) return hipErrorLaunchFailure;
-  hipError_t e = launch_gla_chunk_summaries(f, s);
+  hipError_t e = P > 1 ? launch_gla_segment_carries(f, s) : hipSuccess;
   if (e != hipSuccess) return e;
-  const int cf4 = (2 * D * D + D) / 4;
-  hipLaunchKernelGGL((bwd_carry_scan_kernel<D, T>), dim3((unsigned)((cf4 + 255) / 256), (unsigned)chains), dim3(256), 0,
-                     s, a);
+  hipLaunchKernelGGL((bwd_carry_walk_kernel<D, T>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a, P, cps);
   if (record_bwd_event(a, 1, s) != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_chunk_a_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
   if (record_bwd_event(a, 2, s) != hipSuccess) return hipErrorLaunchFailure;

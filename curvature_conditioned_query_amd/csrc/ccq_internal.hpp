@@ -90,9 +90,9 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
-// Segment summaries of the GLA prefill only, into the workspace slots (the chunked backward
-// runs it with one chunk per segment and scans the result itself).
-hipError_t launch_gla_chunk_summaries(const FwdArgs& a, hipStream_t stream);
+// Segment summary and scan of the GLA prefill only: every segment's carry-in in its workspace
+// slot (the chunked backward walks each segment's chunks from there).
+hipError_t launch_gla_segment_carries(const FwdArgs& a, hipStream_t stream);
 
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).

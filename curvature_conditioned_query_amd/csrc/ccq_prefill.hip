@@ -646,23 +646,25 @@ static hipError_t launch_gla(const FwdArgs& a, hipStream_t s) {
   return record_event(a, 3, s);
 }
 
-// The segment summaries only (segments 0 .. P-2), into the workspace slots: with one chunk
-// per segment, the per-chunk carry updates the chunked backward scans into chunk carries.
+// Summary and scan only: every segment's carry-in in its workspace slot (the chunked backward
+// walks each segment's chunks from there).
 template <int D, typename T>
-static hipError_t launch_gla_summaries_t(const FwdArgs& a, hipStream_t s) {
+static hipError_t launch_gla_carries_t(const FwdArgs& a, hipStream_t s) {
   const int chains = a.B * a.H;
   const int P = a.segments;
   if (P > 1)
     hipLaunchKernelGGL((gla_summary_kernel<D, T>), dim3((unsigned)(chains * (P - 1))), dim3(4 * D), 0, s, a);
+  const int nf4 = (2 * D * D + D) / 4;
+  hipLaunchKernelGGL((gla_scan_kernel<D>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gla_chunk_summaries(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_gla_segment_carries(const FwdArgs& a, hipStream_t s) {
   if (a.dtype == 1) {
-    if (a.d == 128) return launch_gla_summaries_t<128, __bf16>(a, s);
-    if (a.d == 64) return launch_gla_summaries_t<64, __bf16>(a, s);
+    if (a.d == 128) return launch_gla_carries_t<128, __bf16>(a, s);
+    if (a.d == 64) return launch_gla_carries_t<64, __bf16>(a, s);
   } else if (a.d == 64) {
-    return launch_gla_summaries_t<64, float>(a, s);
+    return launch_gla_carries_t<64, float>(a, s);
   }
   return hipErrorInvalidValue;
 }

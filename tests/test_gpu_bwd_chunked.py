@@ -20,6 +20,11 @@ def _cotangent(shape, seed, dtype):
     return bf16_round(x) if dtype == "bf16" else x
 
 
+def _gate_grad(dw, db):
+    """[H, d + 1]: dw_lambda and db_lambda of each head side by side."""
+    return np.concatenate([np.asarray(dw, np.float64), np.asarray(db, np.float64).reshape(-1, 1)], axis=1)
+
+
 def _run(dtype, B, H, T, d, seed, carry=False, adjoint=False, b_lam=-2.0, check_tol=None):
     import torch
     from curvature_conditioned_query_amd import ccq_bwd_chunked
@@ -52,8 +57,11 @@ def _run(dtype, B, H, T, d, seed, carry=False, adjoint=False, b_lam=-2.0, check_
     errs = {}
     for key in GRADS + ("dS", "dC", "dm"):
         errs[key] = normwise_error(down(got[key]), ref[key])
-    errs["dw"] = normwise_error(down(out["dw_lambda"]).sum(axis=0), ref["dw"])
-    errs["db"] = normwise_error(down(out["db_lambda"]).sum(axis=0)[:, None], np.asarray(ref["db"])[:, None])
+    # the gate's parameter gradient of one head, (dw_lambda, db_lambda), is one normwise slab: db
+    # alone is a sum over B*T tokens whose terms cancel, so its own relative error measures the
+    # cancellation, not the kernel
+    errs["dwdb"] = normwise_error(_gate_grad(down(out["dw_lambda"]).sum(axis=0), down(out["db_lambda"]).sum(axis=0)),
+                                  _gate_grad(ref["dw"], ref["db"]))
     print(f"bwd {dtype} B={B} H={H} T={T} d={d} carry={carry} adjoint={adjoint}: "
           + " ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
     for key, e in errs.items():
@@ -78,6 +86,14 @@ def test_bwd_carry_and_final_adjoint(gpu_lib, dtype, d):
 def test_bwd_short_and_boundary_lengths(gpu_lib, T):
     """One token, a single ragged chunk, exactly one chunk, one chunk plus a token, two chunks."""
     _run("f32", B=1, H=2, T=T, d=64, seed=1300 + T, carry=(T % 2 == 1), adjoint=True)
+
+
+@pytest.mark.parametrize("B,H,T", [(8, 16, 320), (16, 16, 130)])
+def test_bwd_multi_chunk_segments(gpu_lib, B, H, T):
+    """The carry walk over segments of several chunks (the segment count follows the number of
+    chains): 128 chains give two segments of three and two chunks, 256 chains one segment of
+    three chunks that starts from the carry in itself; with a carry-out adjoint."""
+    _run("bf16", B=B, H=H, T=T, d=64, seed=1600 + T, carry=True, adjoint=True)
 
 
 def test_bwd_gate_off(gpu_lib):
@@ -114,6 +130,7 @@ def test_bwd_full_size_sampled(gpu_lib):
         e = normwise_error(down(got[key][b:b + 1, h:h + 1]), ref[key])
         print(f"bwd full-size chain ({b},{h}) {key} err {e:.2e}", flush=True)
         assert e <= TOL["bf16"], key
-    e = normwise_error(down(out["dw_lambda"][b, h])[None], ref["dw"])
+    e = normwise_error(_gate_grad(down(out["dw_lambda"][b, h])[None], down(out["db_lambda"][b, h]).reshape(1)),
+                       _gate_grad(ref["dw"], ref["db"]))
+    print(f"bwd full-size chain ({b},{h}) dw, db err {e:.2e}", flush=True)
     assert e <= TOL["bf16"]
-    assert abs(float(out["db_lambda"][b, h]) - float(ref["db"][0])) <= TOL["bf16"] * (abs(float(ref["db"][0])) + 1e-6)
