@@ -41,6 +41,8 @@
 #include "ccq_internal.hpp"
 #include "ccq_prefill_common.hpp"
 
+#include <type_traits>
+
 namespace ccq {
 
 // Workspace slot of one (chain, segment): S [D][D] | C [D][D] | ksum [D] | log decay [D], fp32.
@@ -162,14 +164,20 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
 
   const Frag<T> Ih = ident_frag<T>(hb, lane);
 
-  for (int ch = cbeg; ch < cend; ++ch) {
+  // One chunk.  bf16: the intra-chunk attention takes hi + lo operands in the first chunk of a
+  // sequence read from an empty state, where an output is one or a few possibly cancelling
+  // products and nothing else; in every later chunk single bf16 operands, like every other
+  // product here, so the next chunk's k and v stream in from the start of the chunk.  That
+  // first chunk runs its own copy of the body, so the loop carries no registers for the split.
+  auto chunk = [&](const int ch, auto split_tag) {
+    constexpr bool split = kSplit && decltype(split_tag)::value;
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
 
     T (*Ks)[PQ] = sm.X[ch & 1];
     T (*Vs)[PQ] = sm.Y[ch & 1];
-    T (*Klo)[PQ] = sm.X[(ch + 1) & 1];   // bf16 only
-    T (*Qalo)[PQ] = sm.Y[(ch + 1) & 1];  // bf16 only
+    T (*Klo)[PQ] = sm.X[(ch + 1) & 1];   // split chunks only
+    T (*Qalo)[PQ] = sm.Y[(ch + 1) & 1];  // split chunks only
 
     // ---- this chunk's tiles have landed (own loads, then everyone's); rows past the end of
     // the sequence are zeroed
@@ -186,11 +194,9 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
       normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
       lds_barrier();
     }
-    if constexpr (!kSplit) {
-      if (ch + 1 < cend) {
-        dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
-        dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
-      }
+    if (!split && ch + 1 < cend) {
+      dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
+      dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
     }
 
     // ---- own channels: cumulative decay (4 consecutive channels per lane), k e^-B, key sum,
@@ -221,10 +227,12 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
         if constexpr (kSplit) {
           const bf16x4 kh = to_bf16x4(kp);
           *reinterpret_cast<bf16x4*>(&sm.Kp[t][cw + 4 * g]) = kh;
-          f32x4 kl;
+          if (split) {
+            f32x4 kl;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) kl[r] = kp[r] - (float)kh[r];
-          st4<T>(&Klo[t][cw + 4 * g], kl);
+            for (int r = 0; r < 4; ++r) kl[r] = kp[r] - (float)kh[r];
+            st4<T>(&Klo[t][cw + 4 * g], kl);
+          }
         } else {
           st4<T>(&sm.Kp[t][cw + 4 * g], kp);
         }
@@ -250,48 +258,28 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
     lds_barrier();
     if (ch + 1 < cend) dma_rows(sm.Gs, gg, ch + 1);
 
-    ccq_clean_query<D, T, 1, kSplit>(sm, Ks, Qalo, R, cw, lane,
-                                     [&](int, int ti, int r) { return __expf(BT[ti][r]); });
+    ccq_clean_query<D, T, 1, split>(sm, Ks, Qalo, R, cw, lane,
+                                    [&](int, int ti, int r) { return __expf(BT[ti][r]); });
+    // C += K^T K for the wave's channels: Q C0 is formed, so the statistic carry moves on here,
+    // beside the cleaned query, rather than in the output phase
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
+#pragma unroll
+      for (int t0_ = 0; t0_ < NA; t0_ += 4) {
+        Frag<T> Ak[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Ak[u] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mma(Cacc[t0_ + u], Ak[u], Bk);
+      }
+    }
     lds_barrier();
     if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);
 
-    // ---- intra-chunk attention (Qc e^B)(K e^-B)^T on the lower tiles -> Pm (masked)
-    for (int idx = w; idx < 10; idx += NW) {
-      const int ti = tri_row(idx), tj = tri_col(idx);
-      f32x4 acc = zero4();
-      Frag<T> Af[NK], Bf[NK], Alf[NK], Blf[NK];
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        Af[kk] = lds_frag<T, KORD_CONTIG>(&sm.Kp[0][0], PQ, 16 * tj, 32 * kk, lane);
-        Bf[kk] = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
-        if constexpr (kSplit) {
-          Alf[kk] = lds_frag<T, KORD_CONTIG>(&Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
-          Blf[kk] = lds_frag<T, KORD_CONTIG>(&Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        mma(acc, Af[kk], Bf[kk]);
-        if constexpr (kSplit) {
-          mma(acc, Af[kk], Blf[kk]);
-          mma(acc, Alf[kk], Bf[kk]);
-        }
-      }
-      const int i = 16 * ti + l16;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = (16 * tj + 4 * g + r <= i) ? acc[r] : 0.f;
-      st4<T>(&sm.Pm[i][16 * tj + 4 * g], acc);
-    }
-    lds_barrier();
-    if constexpr (kSplit) {  // the low parts are consumed: their buffers take the next k, v
-      if (ch + 1 < cend) {
-        dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
-        dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
-      }
-    }
-
-    // ---- O^T for the wave's 16 value rows: S0 (Qc e^B)^T + V^T A^T
+    // ---- O^T for the wave's 16 value rows, first part: S0 (Qc e^B)^T (needs only the cleaned
+    // query, so it runs beside the intra-chunk attention)
     f32x4 O[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
@@ -305,6 +293,45 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) mma(O[ti], A, Bq[ti]);
     }
+
+    // ---- intra-chunk attention (Qc e^B)(K e^-B)^T on the lower tiles -> Pm (masked)
+    {
+      constexpr bool kLo = split;
+      for (int idx = w; idx < 10; idx += NW) {
+        const int ti = tri_row(idx), tj = tri_col(idx);
+        f32x4 acc = zero4();
+        Frag<T> Af[NK], Bf[NK], Alf[NK], Blf[NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          Af[kk] = lds_frag<T, KORD_CONTIG>(&sm.Kp[0][0], PQ, 16 * tj, 32 * kk, lane);
+          Bf[kk] = lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane);
+          if constexpr (kLo) {
+            Alf[kk] = lds_frag<T, KORD_CONTIG>(&Klo[0][0], PQ, 16 * tj, 32 * kk, lane);
+            Blf[kk] = lds_frag<T, KORD_CONTIG>(&Qalo[0][0], PQ, 16 * ti, 32 * kk, lane);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+          mma(acc, Af[kk], Bf[kk]);
+          if constexpr (kLo) {
+            mma(acc, Af[kk], Blf[kk]);
+            mma(acc, Alf[kk], Bf[kk]);
+          }
+        }
+        const int i = 16 * ti + l16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = (16 * tj + 4 * g + r <= i) ? acc[r] : 0.f;
+        st4<T>(&sm.Pm[i][16 * tj + 4 * g], acc);
+      }
+    }
+    lds_barrier();
+    if (split && ch + 1 < cend) {  // the low parts are consumed: their buffers take the next k, v
+      dma_rows(sm.X[(ch + 1) & 1], kg, ch + 1);
+      dma_rows(sm.Y[(ch + 1) & 1], vg, ch + 1);
+    }
+
+    // ---- O^T, second part: + V^T A^T
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const Frag<T> A = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);  // V^T, own rows
@@ -322,25 +349,18 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
       if (i < Lc) st4<T>(og + (tok0 + t0 + i) * D + cw + 4 * g, O[ti]);
     }
 
-    // ---- carry update: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
+    // ---- carry update: S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
       const Frag<T> Bv = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);  // V[t][own channel]
 #pragma unroll
       for (int t0_ = 0; t0_ < NA; t0_ += 4) {
-        Frag<T> Ak[4], Ap[4];
+        Frag<T> Ap[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          Ak[u] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
-          Ap[u] = tr_frag<T>(&sm.Kp[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
-        }
+        for (int u = 0; u < 4; ++u) Ap[u] = tr_frag<T>(&sm.Kp[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          mma(Cacc[t0_ + u], Ak[u], Bk);
-          mma(Sacc[t0_ + u], Ap[u], Bv);
-        }
+        for (int u = 0; u < 4; ++u) mma(Sacc[t0_ + u], Ap[u], Bv);
       }
     }
 #pragma unroll
@@ -354,7 +374,10 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
     }
     nb += Lc;
     lds_barrier();
-  }
+  };
+  int ch = cbeg;
+  if (kSplit && ch < cend && nb == 0) chunk(ch++, std::true_type{});
+  for (; ch < cend; ++ch) chunk(ch, std::false_type{});
 
   // ---- carry out (last segment of the chain)
   if (seg == P - 1 && a.S_out != nullptr) {
