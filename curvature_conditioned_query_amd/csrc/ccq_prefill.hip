@@ -152,8 +152,9 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
   // Gram rows, q after the cleaned query, k and v after the intra-chunk attention (bf16) or at
   // the start of the previous chunk (fp32).
   auto chunk_len = [&](int ch) { return min(kL, a.T - ch * kL); };
+  const DmaPlan<D, T, PQ, NW> plan(w, lane);
   auto dma_rows = [&](T (*dst)[PQ], const T* g, int ch) {
-    dma_tile<D, T, PQ>(dst, g + (tok0 + (size_t)ch * kL) * D, chunk_len(ch), w, NW, lane);
+    plan.load(dst, g + (tok0 + (size_t)ch * kL) * D, chunk_len(ch), w);
   };
   if (cbeg < cend) {
     dma_rows(sm.Qs, qg, cbeg);
@@ -435,14 +436,15 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
   const T* vg = static_cast<const T*>(a.v);
   const T* gg = static_cast<const T*>(a.log_alpha);
   const bool norm = (a.flags & kFlagNormalizeKeys) != 0;
+  const DmaPlan<D, T, PQ, NW> plan(w, lane);
   auto dma = [&](T (*dst)[PQ], const T* src, int i) {
-    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w, NW, lane);
+    plan.load(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w);
   };
   // the m-th load instruction this wave issues for a tile (waves w, w + NW, ... share a tile)
   auto dma_part = [&](T (*dst)[PQ], const T* src, int i, int m) {
-    dma_unit<D, T, PQ>(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w + NW * m, lane);
+    plan.load_one(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w, m);
   };
-  constexpr int kParts = (PQ * (int)sizeof(T) / 16 + NW - 1) / NW;  // instructions per wave and tile
+  constexpr int kParts = DmaPlan<D, T, PQ, NW>::M;  // instructions per wave and tile
   // Loads of an interval in the order they are issued, one instruction at a time between
   // compute steps: values of chunk i+1, then keys and log decay of chunk i+2.
   auto issue = [&](int i, int q) {

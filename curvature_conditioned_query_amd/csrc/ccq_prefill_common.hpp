@@ -167,6 +167,40 @@ __device__ __forceinline__ void dma_tile(T (*dst)[PQ], const T* src, int Lc, int
   for (int j = w; j < U; j += nw) dma_unit<D, T, PQ>(dst, src, Lc, j, lane);
 }
 
+// The same tile loads with the lane's part of every instruction worked out once: instruction
+// j = w + NWAVES m of wave w reads row[m] (kL for a padding unit, so it always falls back to
+// row 0) at element offset off[m] of the chunk.  A tile load then costs a compare, a select
+// and an address add per instruction instead of the division by the row's unit count.
+template <int D, typename T, int PQ, int NWAVES>
+struct DmaPlan {
+  static constexpr int U = PQ * (int)sizeof(T) / 16, DU = D * (int)sizeof(T) / 16, EPU = 16 / (int)sizeof(T);
+  static constexpr int M = (U + NWAVES - 1) / NWAVES;  // instructions per wave and tile (at most)
+  int row[M];
+  int off[M];
+  __device__ __forceinline__ DmaPlan(int w, int lane) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int u = 64 * (w + NWAVES * m) + lane;
+      const int r = u / U, slot = u - r * U;
+      row[m] = slot < DU ? r : kL;
+      off[m] = slot < DU ? r * D + slot * EPU : 0;
+    }
+  }
+  // the wave's m-th instruction of the tile (nothing when there is none)
+  __device__ __forceinline__ void load_one(T (*dst)[PQ], const T* src, int Lc, int w, int m) const {
+    const int j = w + NWAVES * m;
+    if (j >= U) return;
+    const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) T*)&dst[0][0];
+    const T* p = src + (row[m] < Lc ? off[m] : 0);
+    const unsigned m0 = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)j);
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p) : "memory", "m0");
+  }
+  __device__ __forceinline__ void load(T (*dst)[PQ], const T* src, int Lc, int w) const {
+#pragma unroll
+    for (int m = 0; m < M; ++m) load_one(dst, src, Lc, w, m);
+  }
+};
+
 // C[row][col .. col + 3] of a symmetric D x D matrix held as its packed upper triangle (the
 // caller's carry with the packed-statistics flag).
 template <int D>
