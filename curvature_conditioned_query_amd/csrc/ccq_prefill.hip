@@ -53,9 +53,9 @@ struct Smem {
   using C_ = Cfg<D, T>;
   T Qs[kL][C_::PQ];     // q rows
   T Gs[kL][C_::PQ];     // log decay rows
-  // Chunk c keeps its k rows in X[c % 2] and v rows in Y[c % 2]; the other halves hold the
-  // bf16 low parts of k e^-B and q_clean e^B while the intra-chunk attention is formed, and
-  // then receive the next chunk's k and v.
+  // Chunk c keeps its k rows in X[c % 2] and v rows in Y[c % 2]; the other halves receive the
+  // next chunk's k and v (in the first chunk of a sequence they hold the bf16 low parts of
+  // k e^-B and q_clean e^B until the intra-chunk attention is formed).
   T X[2][kL][C_::PQ];
   T Y[2][kL][C_::PQ];
   T Kp[kL][C_::PQ];     // k * e^-B rows (hi part for bf16)
@@ -149,8 +149,8 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
 
   // ---- chunk tiles go straight from HBM to LDS (no registers involved), each as soon as the
   // previous chunk has finished reading the buffer it lands in: log decay after the gate and
-  // Gram rows, q after the cleaned query, k and v after the intra-chunk attention (bf16) or at
-  // the start of the previous chunk (fp32).
+  // Gram rows, q after the cleaned query, k and v at the start of the previous chunk (after its
+  // intra-chunk attention when that chunk splits its operands into hi + lo).
   auto chunk_len = [&](int ch) { return min(kL, a.T - ch * kL); };
   const DmaPlan<D, T, PQ, NW> plan(w, lane);
   auto dma_rows = [&](T (*dst)[PQ], const T* g, int ch) {

@@ -16,6 +16,11 @@ and writes the few figures the benchmark and the design notes use:
         of known size (torch.neg over MIB MiB of fp32: MIB MiB read and MIB MiB written).  The
         source file's sha256 is stored so that the benchmark only reports the figure while the
         kernel source is unchanged.
+
+    python profile_summary.py counters RUN.db [RUN.db ...] --kernel REGEX --out profiles/NAME.txt
+        --command "..." [--command "..."]
+        every counter the runs collected for the kernels matching REGEX, averaged per dispatch
+        (each counter summed over the rows of a dispatch), with the dispatches' average duration.
 """
 
 from __future__ import annotations
@@ -125,6 +130,31 @@ def traffic_summary(a):
     }
 
 
+def counters_summary(paths, kernel_regex, commands, title):
+    pat = re.compile(kernel_regex)
+    out = [f"# {title}", f"# kernels matching: {kernel_regex}"]
+    out += [f"# command: {c}" for c in commands]
+    out.append("")
+    out.append(f"{'counter':<32} {'per dispatch':>16} {'dispatches':>10} {'avg_us':>9}  run")
+    for path in paths:
+        db = sqlite3.connect(path)
+        rows = db.cursor().execute(
+            "select kernel_name, dispatch_id, counter_name, value, duration from counters_collection").fetchall()
+        per = collections.defaultdict(lambda: collections.defaultdict(float))
+        dur = collections.defaultdict(dict)
+        for k, d, c, v, du in rows:
+            if pat.search(k):
+                per[c][d] += v
+                dur[c][d] = du
+        for c in sorted(per):
+            vals = per[c]
+            n = len(vals)
+            us = sum(dur[c].values()) / n / 1e3
+            out.append(f"{c:<32} {sum(vals.values()) / n:>16.5g} {n:>10} {us:>9.2f}  {path.split('/')[-1]}")
+    out.append("")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -133,6 +163,12 @@ def main(argv=None):
     t.add_argument("--out", required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="rocprofv3 --kernel-trace --stats")
+    q = sub.add_parser("counters")
+    q.add_argument("dbs", nargs="+")
+    q.add_argument("--kernel", required=True)
+    q.add_argument("--out", required=True)
+    q.add_argument("--command", action="append", required=True)
+    q.add_argument("--title", default="rocprofv3 --pmc counters")
     c = sub.add_parser("traffic")
     c.add_argument("--fetch", required=True)
     c.add_argument("--write", required=True)
@@ -146,6 +182,11 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.mode == "trace":
         text = trace_summary(a.dbs, a.command, a.title)
+        with open(a.out, "w") as fh:
+            fh.write(text + "\n")
+        print(text)
+    elif a.mode == "counters":
+        text = counters_summary(a.dbs, a.kernel, a.command, a.title)
         with open(a.out, "w") as fh:
             fh.write(text + "\n")
         print(text)
