@@ -7,8 +7,9 @@ A step is one chunked-prefill pass of a CCQ-GLA layer over one batch of syntheti
 input (B=4, H=16, T=4096, d_k=d_v=128, bf16 q/k/v/log-decay, fp32 carry out), with
 the inputs resident in HBM.  ``value`` is prefill tokens/s (B*T per second).  The
 same run times the decode step (256 sequences x 16 heads, d=128, a carry pre-filled
-from an 8K-token prefix) and reports its HBM bandwidth, and times the fp64 CPU
-oracle on a bounded sample of the prefill workload.  Prints one JSON line.
+from an 8K-token prefix) and reports its HBM bandwidth, times the same GLA layer on 5x
+longer sequences (B=1, H=16, T=20480: per-token time against T=4096), and times the fp64
+CPU oracle on a bounded sample of the prefill workload.  Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -508,6 +509,7 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gdn", action="store_true", help="skip the Gated DeltaNet prefill leg")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context (T=20480) prefill leg")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill leg (profiling the decode kernel alone)")
     ap.add_argument("--no-subspace", action="store_true", help="skip the key-subspace diagnostic leg")
@@ -617,6 +619,22 @@ def main(argv=None):
     print(f"# prefill {spec['name']}: {ms:.3f} ms/step, {tok_s:.4g} tokens/s, {gbs:.1f} GB/s alg, "
           f"{tflops:.1f} TFLOP/s alg; kernels (ms) " +
           ", ".join(f"{k} {v:.4f}" for k, v in res["phase_ms"].items()), file=sys.stderr, flush=True)
+    if not args.no_long and args.workload == 1:
+        # the pages' systems claim is that CCQ's cost does not grow with sequence length: the same
+        # layer on 5x longer sequences (B=1, H=16, T=20480), per-token time against the line above
+        lres = time_prefill(3, args.steps, args.warmup)
+        lB, lH, lT = lres["shape"][:3]
+        l_ms = lres["total_ms"] / args.steps
+        ns_tok = l_ms * 1e6 / (lB * lH * lT)
+        ns_tok_1 = ms * 1e6 / (B * H * T)
+        out["long_context"] = {
+            "workload": lres["spec"]["name"], "ms_per_step": round(l_ms, 4),
+            "tokens_per_s": round(lB * lT / (l_ms * 1e-3), 1), "segments": lres["segments"],
+            "pass_ms": {k: round(v, 4) for k, v in lres["phase_ms"].items()},
+            "ns_per_token_head": round(ns_tok, 4), "ns_per_token_head_T4096": round(ns_tok_1, 4),
+            "ratio_to_T4096": round(ns_tok / ns_tok_1, 3)}
+        print(f"# prefill {lres['spec']['name']}: {l_ms:.3f} ms/step, {ns_tok:.4f} ns per (token, head) "
+              f"against {ns_tok_1:.4f} at T=4096", file=sys.stderr, flush=True)
     if not args.no_gdn:
         gres = time_prefill(2, args.steps, args.warmup)
         gB, gH, gT, gd, _ = gres["shape"]

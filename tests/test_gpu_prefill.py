@@ -104,6 +104,34 @@ def test_segment_counts_agree(segments):
     check(x, o, c, o_ref, c_ref, tag=f"segments={segments}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("segments", [1, 3, 5])
+def test_segment_counts_bf16(d, segments):
+    """bf16: only the first chunk of the sequence (segment 0, empty state) takes the hi + lo
+    attention operands; segments that start from a carry take single bf16 operands from their
+    first chunk on.  Every count stays within the bf16 bar."""
+    x = gla_inputs(1, 2, 520, d, 78 + d, "bf16")
+    o, c = gpu_prefill(x, segments=segments)
+    o_ref, c_ref = oracle(x)
+    check(x, o, c, o_ref, c_ref, tag=f"bf16 d={d} segments={segments}")
+
+
+@pytest.mark.parametrize("T2", [1, 5])
+def test_short_continuation_bf16(T2):
+    """bf16: a few tokens read from the carry of a 100-token prefix (the first chunk of this call
+    is not the sequence's first, so its attention operands are single bf16), against the oracle
+    continuation of the same fp32 carry."""
+    d = 128
+    x0 = gla_inputs(1, 3, 100, d, 93, "bf16")
+    _, c0 = gpu_prefill(x0)
+    carry = Carry(c0[0], c0[1], c0[2], c0[3])
+    x = gla_inputs(1, 3, T2, d, 94 + T2, "bf16")
+    c64 = Carry(*(np.asarray(a, np.float64) for a in (c0[0], c0[1], c0[2])), np.asarray(c0[3]))
+    o_ref, c_ref = oracle(x, c64)
+    o, c = gpu_prefill(x, carry=carry)
+    check(x, o, c, o_ref, c_ref, tag=f"continuation T2={T2}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_carry_resume_and_alias(dtype):
     """prefill(T1) -> carry -> prefill(T2) from it == prefill(T1 + T2); carry out may alias in."""
