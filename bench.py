@@ -108,7 +108,7 @@ def to_dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(dtype).contiguous()
 
 
-def time_prefill(wl, steps, warmup):
+def time_prefill(wl, steps, warmup, keep_outputs=False):
     import torch
     from curvature_conditioned_query_amd import ccq_fwd_chunked, load_library
     from curvature_conditioned_query_amd.inputs import WORKLOADS, workload_inputs
@@ -165,12 +165,16 @@ def time_prefill(wl, steps, warmup):
     phases = {name: float(np.mean([hip.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(steps)]))
               for a, name in enumerate(("summary", "scan", "main"))}
     hip.destroy()
+    outputs = None
+    if keep_outputs:  # the timed passes' o and final carry (every pass writes the same values)
+        outputs = {"o": o.float().cpu().numpy(), "S": cout[0].cpu().numpy(), "C": cout[1].cpu().numpy(),
+                   "ksum": cout[2].cpu().numpy(), "n": cout[3].cpu().numpy()}
     # segments the library resolved: its workspace holds one fp32 slot per (chain, segment)
     # when there is more than one segment (GLA: S, C, ksum, log decay; GDN: S, C, ksum, M)
     slot = (2 * dk * dk + 2 * dk) * 4 if spec["rule"] == "gla" else (3 * dk * dk + dk) * 4
     segs = int(p.segments) if p.segments else (ws_bytes // (B * H * slot) or 1)
     return dict(spec=spec, shape=(B, H, T, dk, dv), total_ms=total_ms, per_ms=per, wall_s=t_wall,
-                dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs, phase_ms=phases)
+                dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs, phase_ms=phases, outputs=outputs)
 
 
 class HipEvents:
@@ -455,16 +459,29 @@ def jacobi_sweep_flops(d):
 
 # ------------------------------------------------------------------ CPU oracle leg
 def _oracle_slab(args):
+    """Times the oracle on one chain; with the GPU's output for that chain (o, and the final
+    carry when the whole chain was run) also returns the normwise errors against it."""
     import oracle
-    q, k, v, g, beta, w, b, rule = args
+    q, k, v, g, beta, w, b, rule, gpu = args
     t = time.perf_counter()
-    oracle.ccq_recurrent(q, k, v, g, beta, w, b, rule)
-    return time.perf_counter() - t
+    o_ref, c_ref = oracle.ccq_recurrent(q, k, v, g, beta, w, b, rule)
+    dt = time.perf_counter() - t
+    if gpu is None:
+        return dt, None
+    errs = {"o": oracle.normwise_error(gpu["o"], o_ref)}
+    if "S" in gpu:
+        errs["S"] = oracle.normwise_error(gpu["S"], c_ref.S)
+        errs["C"] = oracle.normwise_error(gpu["C"], c_ref.C)
+        errs["ksum"] = oracle.normwise_error(gpu["ksum"][..., None], c_ref.m[..., None])
+        errs["n_exact"] = bool(np.array_equal(gpu["n"], c_ref.n))
+    return dt, errs
 
 
-def cpu_baseline(wl, tokens, max_workers):
+def cpu_baseline(wl, tokens, max_workers, gpu_out=None):
     """The fp64 recurrent oracle, as it is, on every (b, h) chain of the workload but only the
-    first `tokens` tokens of each; one chain slab per worker process, one BLAS thread each."""
+    first `tokens` tokens of each; one chain slab per worker process, one BLAS thread each.
+    With gpu_out (host copies of the timed passes' o and final carry) each worker also compares
+    the GPU's result for its chain with the oracle's."""
     import concurrent.futures as cf
     from curvature_conditioned_query_amd.inputs import workload_inputs
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
@@ -476,16 +493,29 @@ def cpu_baseline(wl, tokens, max_workers):
     for bb in range(B):
         for hh in range(H):
             sl = x.slab(bb, hh, 0, tokens)
-            jobs.append((sl.q, sl.k, sl.v, sl.g, sl.beta, sl.w_lam, sl.b_lam, x.rule))
+            gpu = None
+            if gpu_out is not None:
+                gpu = {"o": gpu_out["o"][bb:bb + 1, hh:hh + 1, :tokens]}
+                if tokens == T:
+                    for name in ("S", "C", "ksum", "n"):
+                        gpu[name] = gpu_out[name][bb:bb + 1, hh:hh + 1]
+            jobs.append((sl.q, sl.k, sl.v, sl.g, sl.beta, sl.w_lam, sl.b_lam, x.rule, gpu))
     workers = max(1, min(max_workers, len(jobs)))
     t0 = time.perf_counter()
     with cf.ProcessPoolExecutor(max_workers=workers) as ex:
-        cpu_s = sum(ex.map(_oracle_slab, jobs))
+        res = list(ex.map(_oracle_slab, jobs))
     wall = time.perf_counter() - t0
+    cpu_s = sum(r[0] for r in res)
+    errs = [r[1] for r in res if r[1] is not None]
+    parity = None
+    if errs:
+        parity = {key: (all(e[key] for e in errs) if key == "n_exact" else max(e[key] for e in errs))
+                  for key in errs[0]}
+        parity.update(chains=len(errs), tokens=tokens)
     return dict(value=B * tokens / wall, unit="tokens/s", cores=workers, kind="oracle",
                 sample=f"all {B * H} (b,h) chains of the workload, first {tokens} of {T} tokens each; "
                        f"fp64 per-token recurrence; {workers} worker processes; {cpu_s:.1f} CPU-s, {wall:.1f} s wall",
-                wall_s=wall, cpu_s=cpu_s)
+                wall_s=wall, cpu_s=cpu_s, parity=parity)
 
 
 def cpu_model():
@@ -564,7 +594,7 @@ def main(argv=None):
             print(f"# {dres['name']}: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s",
                   file=sys.stderr, flush=True)
         return 0
-    res = time_prefill(args.workload, args.steps, args.warmup)
+    res = time_prefill(args.workload, args.steps, args.warmup, keep_outputs=not args.no_cpu)
     B, H, T, dk, dv = res["shape"]
     spec = res["spec"]
     elem = 2 if res["dtype"] == "bf16" else 4
@@ -737,11 +767,21 @@ def main(argv=None):
             ncpu = len(os.sched_getaffinity(0))
         except AttributeError:
             ncpu = os.cpu_count() or 1
-        cb = cpu_baseline(args.workload, args.cpu_tokens, min(ncpu, 16))
+        cb = cpu_baseline(args.workload, args.cpu_tokens, min(ncpu, 16), gpu_out=res["outputs"])
         cb["cpu_model"] = cpu_model()
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample", "cpu_model")}
         print(f"# cpu oracle: {cb['value']:.4g} tokens/s on {cb['cores']} cores ({cb['wall_s']:.1f} s wall)",
               file=sys.stderr, flush=True)
+        if cb["parity"] is not None:
+            # the timed passes' own output against the oracle, normwise per (b, h) chain (max over
+            # chains), at the tolerance the inputs' precision sets
+            tol = 2e-2 if res["dtype"] == "bf16" else 1e-4
+            par = dict(cb["parity"], tolerance=tol, against="fp64 per-token recurrence (oracle)")
+            par["pass"] = bool(all(v <= tol for k, v in par.items() if k in ("o", "S", "C", "ksum"))
+                               and par.get("n_exact", True))
+            out["parity"] = {k: (round(v, 8) if isinstance(v, float) else v) for k, v in par.items()}
+            print(f"# parity of the timed passes' output: " + ", ".join(
+                f"{k} {v:.3e}" for k, v in cb["parity"].items() if isinstance(v, float)), file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
     return 0
 
