@@ -32,7 +32,7 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 CHUNK = 64
 PREFILL_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill.hip")
-DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode.hip")
+DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode_kernel.hpp")
 BACKWARD_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_step_backward.hip")
 BWD_CHUNKED_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_backward.hip")
 GDN_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill_gdn.hip")

@@ -17,6 +17,8 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// the packed-C variants (their own translation unit)
+hipError_t launch_decode_packed(const DecodeArgs& a, hipStream_t stream);
 
 // One prefill call after validation.  Segment scheme: the T tokens of every (b, h)
 // chain are cut into `segments` contiguous runs of whole chunks.  With more than one
