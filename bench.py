@@ -35,7 +35,7 @@ PREFILL_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq
 DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode_kernel.hpp")
 BACKWARD_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_step_backward.hip")
 BWD_CHUNKED_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_backward.hip")
-GDN_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill_gdn.hip")
+GDN_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill_gdn_kernels.hpp")
 
 
 # ------------------------------------------------------------------ algorithmic work

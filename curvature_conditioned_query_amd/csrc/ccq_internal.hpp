@@ -103,5 +103,7 @@ size_t gdn_slot_bytes(int d);
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Gated DeltaNet prefill.
 hipError_t launch_gdn(const FwdArgs& a, hipStream_t stream);
+// the Gated DeltaNet segment summary kernel (its own translation unit)
+hipError_t launch_gdn_summary(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace ccq

@@ -1,0 +1,671 @@
+// Chunked prefill of the CCQ read step on a Gated DeltaNet backbone (gfx950): the kernels.  Included
+// by ccq_prefill_gdn.hip (main kernel, scans, launch) and ccq_prefill_gdn_summary.hip (segment
+// summary), which the build compiles with different scheduler settings.
+//
+// Method (gist.science summary of arXiv 2606.01294, §2 "理论推导", §2 "机制", §2 "集成"):
+// the cleaned query qc_t = q_t - lambda_t Sigma_t q_t replaces q_t in the read o_t = S_t qc_t,
+// the write rule is left as it is.  The Gated DeltaNet write rule (standard definition) is
+//   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  alpha_t = exp(g_t), scalar.
+//
+// Chunk algebra (rows i = 0..63 of a chunk, carry S0; gamma_i = prod_{j<=i} alpha_j inside the
+// chunk, Gam_ij = gamma_i / gamma_j).  With delta_t = beta_t (v_t - alpha_t S_{t-1} k_t) the rule
+// reads S_t = alpha_t S_{t-1} + delta_t k_t^T, so S_i = gamma_i S0 + sum_{j<=i} Gam_ij delta_j k_j^T
+// and the deltas of a chunk solve a unit lower-triangular system:
+//   (I + A) Delta = X,   A_ij = beta_i Gam_ij k_i . k_j (j < i),   X = diag(beta) (V - diag(gamma) K S0^T)
+//   O   = diag(gamma) Qc S0^T + (tril_incl(Qc K^T) * Gam) Delta
+//   S_L = gamma_L S0 + Delta^T diag(gamma_L / gamma) K
+// The CCQ statistics part (gate, Q K^T, Q C0, cleaned query) is the rule-independent code in
+// ccq_prefill_common.hpp; C0 += K^T K, m0 += sum k, n0 += L as for every rule.
+//
+// Segments.  S_L is affine in S0: S_L = S0 M_c + b_c with M_c = gamma_L I - W^T diag(gamma_L /
+// gamma) K (W = (I + A)^{-1} diag(beta gamma) K) and b_c the S_L of a zero S0.  A run of chunks
+// therefore maps S_in to S_in M_seg + dS_seg, where dS_seg is the run's S from zero and M_seg
+// is the same recurrence applied to a d_k x d_k state that starts at I with v = 0 (then X and
+// b_c carry no v term).  With more than one segment per chain, gdn_summary_kernel computes
+// (dS, dC, dksum) and M for every segment but the last, gdn_scan_state_kernel chains
+// S_in[p+1] = S_in[p] M_p + dS_p in fp32, gdn_scan_sum_kernel adds up C and ksum, and the
+// main kernel runs every segment from its carry-in.
+//
+// Kernel layout.  One workgroup of D/16 waves per (chain, segment); wave w owns the 16 value
+// channels [16w, 16w + 16): its tiles of C and S^T live in MFMA accumulators (as in the GLA
+// kernel), and so do its columns of X and Delta, held as Delta[j][v] tiles (token rows).  The
+// triangular system is solved in fp32 by 16-token blocks: the inverses of the four diagonal
+// blocks (I + A_bb)^{-1} come from forward substitution (one lane per column), then every wave
+// runs Delta_b = (I + A_bb)^{-1} (X_b - sum_{b' < b} A_bb' Delta_b') on its own columns with
+// fp32 MFMAs, the off-diagonal blocks of A read from LDS.  Products on bf16 operands with fp32
+// accumulation: K S0^T, Qc S0^T, the intra term and the carry update; the intra matrix Qc K^T
+// takes qc as bf16 hi + lo.
+#pragma once
+
+#include "ccq_internal.hpp"
+#include "ccq_prefill_common.hpp"
+
+namespace ccq {
+
+// Workspace slot of one (chain, segment): S [D][D] | C [D][D] | ksum [D] | M [D][D], fp32.
+__host__ __device__ static inline size_t gdn_slot_floats(int d) { return 3 * (size_t)d * d + d; }
+
+template <int D, typename T>
+struct GdnSmem {
+  using C_ = Cfg<D, T>;
+  T Qs[kL][C_::PQ];        // q rows
+  T Ks[2][kL][C_::PQ];     // k rows of chunk c in Ks[c % 2]; the other half receives chunk c + 1
+  T Vs[kL][C_::PQ];        // v rows
+  T Qa[kL][C_::PQ];        // cleaned query (hi part for bf16)
+  T Qalo[C_::LO][C_::PQ];  // bf16 only: lo part of the cleaned query
+  T Pm[kL][C_::PT];        // tril(Q K^T - c 1^T), then M = tril(Qc K^T) * Gam
+  T Wt[4][C_::PQ];         // w_lambda hi, lo; key sum hi, lo
+  float As[kL][kL + 4];    // A_ij = beta_i Gam_ij k_i . k_j below the diagonal (lower tiles only)
+  float Tb[4][16][16 + 4]; // (I + A_bb)^{-1} of the four diagonal 16-token blocks
+  float m0[D], m1[D];
+  float lgam[kL], beta[kL];  // chunk-local log gamma_i, beta_i
+  f32x4 tok[kL];             // lambda, 1/n, sq/n^2, gate logit + b
+};
+
+// ---------------------------------------------------------------- steps shared by the kernels
+
+// Wave 1: chunk-local log gamma (inclusive scan over lanes = tokens) and beta into LDS.
+template <int D, typename T>
+__device__ __forceinline__ void gdn_gates(GdnSmem<D, T>& sm, float sg, float sb, int lane) {
+  float x = sg;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  sm.lgam[lane] = x;
+  sm.beta[lane] = sb;
+}
+
+// A = beta Gam (K K^T) below the diagonal, lower 16x16 tiles idx = i0, i0 + step, ... < 10.
+template <int D, typename T>
+__device__ __forceinline__ void gdn_build_A(GdnSmem<D, T>& sm, const T (*Ks)[Cfg<D, T>::PQ], int i0, int step,
+                                            int lane) {
+  using C_ = Cfg<D, T>;
+  constexpr int NK = C_::NK, PQ = C_::PQ;
+  const int g = lane >> 4, l16 = lane & 15;
+  for (int idx = i0; idx < 10; idx += step) {
+    const int ti = tri_row(idx), tj = tri_col(idx);
+    f32x4 acc = zero4();  // k_j . k_i at j = 16 tj + 4 g + r, i = 16 ti + l16
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const Frag<T> A = lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+      const Frag<T> B = lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * ti, 32 * kk, lane);
+      mma(acc, A, B);
+    }
+    const int i = 16 * ti + l16, j0 = 16 * tj + 4 * g;
+    const float lgi = sm.lgam[i], bi = sm.beta[i];
+    const f32x4 lgj = *reinterpret_cast<const f32x4*>(&sm.lgam[j0]);
+    f32x4 av;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) av[r] = (j0 + r < i) ? bi * __expf(lgi - lgj[r]) * acc[r] : 0.f;
+    *reinterpret_cast<f32x4*>(&sm.As[i][j0]) = av;
+  }
+}
+
+// Key sums m1 = m0 + sum_t k_t: 2D threads (rel = 0 .. 2D - 1), two per channel, 32 tokens each.
+template <int D, typename T>
+__device__ __forceinline__ void gdn_key_sums(GdnSmem<D, T>& sm, const T (*Ks)[Cfg<D, T>::PQ], int rel) {
+  const int c = rel >> 1, half = rel & 1;
+  float s = 0.f;
+#pragma unroll 8
+  for (int t = 32 * half; t < 32 * half + 32; ++t) s += to_f32(Ks[t][c]);
+  s += __shfl_xor(s, 1, 64);
+  if (half == 0) sm.m1[c] = sm.m0[c] + s;
+}
+
+// One wave: (I + A_bb)^{-1} for the four diagonal blocks in fp32.  Lane (block, i) holds row i
+// of A_bb and of the inverse T, starting from T_i = e_i; for each pivot k the 16 lanes of a
+// block receive row k of T (final by then) and the rows below it apply T_i -= A_ik T_k, which
+// is forward substitution of T (I + A_bb) = I row by row.  About 20 registers per lane.
+template <int D, typename T>
+__device__ __forceinline__ void gdn_diag_inverse(GdnSmem<D, T>& sm, int lane) {
+  const int blk = lane >> 4, i = lane & 15, base = 16 * blk;
+  float trow[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) trow[j] = (j == i) ? 1.f : 0.f;
+#pragma unroll
+  for (int k = 0; k < 15; ++k) {
+    const float coef = (i > k) ? sm.As[base + i][base + k] : 0.f;
+#pragma unroll
+    for (int j = 0; j <= k; ++j) {  // row k of T is zero right of column k
+      const float tk = __shfl(trow[j], k, 16);
+      trow[j] -= coef * tk;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<f32x4*>(&sm.Tb[blk][i][4 * q]) = f32x4{trow[4 * q], trow[4 * q + 1], trow[4 * q + 2], trow[4 * q + 3]};
+}
+
+// X = beta (V - gamma K S0^T) on the wave's 16 state rows (WITH_V false: V = 0).  X[b][r] at
+// token 16 b + 4 g + r, state row cw + l16; stile(t) is the tile S^T[16 t + 4 g + r][cw + l16].
+template <int D, typename T, bool WITH_V, typename STile>
+__device__ __forceinline__ void gdn_rhs(const GdnSmem<D, T>& sm, const T (*Ks)[Cfg<D, T>::PQ], STile stile, int cw,
+                                        int lane, f32x4 (&X)[4]) {
+  using C_ = Cfg<D, T>;
+  constexpr int NK = C_::NK, PQ = C_::PQ;
+  const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) X[b] = zero4();
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const Frag<T> Bs = acc_frag<T>(stile(2 * kk), stile(2 * kk + 1));  // S0^T, own columns
+#pragma unroll
+    for (int b = 0; b < 4; ++b) mma(X[b], lds_frag<T, KORD_ACC>(&Ks[0][0], PQ, 16 * b, 32 * kk, lane), Bs);
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int j0 = 16 * b + 4 * g;
+    const f32x4 lg = *reinterpret_cast<const f32x4*>(&sm.lgam[j0]);
+    const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[j0]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = WITH_V ? to_f32(sm.Vs[j0 + r][cw + l16]) : 0.f;
+      X[b][r] = bt[r] * (v - __expf(lg[r]) * X[b][r]);
+    }
+  }
+}
+
+// Delta = (I + A)^{-1} X by 16-token blocks (fp32 MFMAs), on the wave's columns.
+template <int D, typename T>
+__device__ __forceinline__ void gdn_solve(const GdnSmem<D, T>& sm, const f32x4 (&X)[4], int lane, f32x4 (&Dl)[4]) {
+  const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    f32x4 Z = X[b];
+#pragma unroll
+    for (int bp = 0; bp < b; ++bp) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.As[16 * b + l16][16 * bp + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Z = __builtin_amdgcn_mfma_f32_16x16x4f32(-a4[r], Dl[bp][r], Z, 0, 0, 0);
+    }
+    const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sm.Tb[b][l16][4 * g]);
+    Dl[b] = zero4();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Dl[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(t4[r], Z[r], Dl[b], 0, 0, 0);
+  }
+}
+
+// S^T = gamma_L S^T + K^T diag(gamma_L / gamma) Delta on the wave's state tiles.
+template <int D, typename T, typename STileM>
+__device__ __forceinline__ void gdn_state_update(const GdnSmem<D, T>& sm, const T (*Ks)[Cfg<D, T>::PQ],
+                                                 STileM stile, const f32x4 (&Dl)[4], int lane) {
+  using C_ = Cfg<D, T>;
+  constexpr int NA = C_::NA, PQ = C_::PQ;
+  const int g = lane >> 4;
+  const float lgL = sm.lgam[kL - 1];
+  const float gL = __expf(lgL);
+#pragma unroll
+  for (int t = 0; t < NA; ++t) stile(t) *= gL;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    f32x4 d0 = Dl[2 * kk], d1 = Dl[2 * kk + 1];
+    const f32x4 lg0 = *reinterpret_cast<const f32x4*>(&sm.lgam[32 * kk + 4 * g]);
+    const f32x4 lg1 = *reinterpret_cast<const f32x4*>(&sm.lgam[32 * kk + 16 + 4 * g]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      d0[r] *= __expf(lgL - lg0[r]);
+      d1[r] *= __expf(lgL - lg1[r]);
+    }
+    const Frag<T> Bd = acc_frag<T>(d0, d1);  // diag(gamma_L / gamma) Delta, own columns
+#pragma unroll
+    for (int t = 0; t < NA; ++t) mma(stile(t), tr_frag_acc<T>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane), Bd);
+  }
+}
+
+// C += K^T K on the wave's tiles.
+template <int D, typename T>
+__device__ __forceinline__ void gdn_cov_update(const T (*Ks)[Cfg<D, T>::PQ], f32x4 (&Cacc)[Cfg<D, T>::NA], int cw,
+                                               int lane) {
+  using C_ = Cfg<D, T>;
+  constexpr int NA = C_::NA, PQ = C_::PQ;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);  // K[t][own channel]
+#pragma unroll
+    for (int t = 0; t < NA; ++t) mma(Cacc[t], tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane), Bk);
+  }
+}
+
+// ---------------------------------------------------------------- main kernel
+
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
+  using C_ = Cfg<D, T>;
+  constexpr int NW = C_::NW, NA = C_::NA, NK = C_::NK;
+  constexpr int PQ = C_::PQ, PT = C_::PT;
+  constexpr bool kSplit = sizeof(T) == 2;
+  __shared__ GdnSmem<D, T> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int cw = 16 * w;  // this wave's 16 channels
+  const int P = a.segments, cps = a.chunks_per_segment;
+  const int chain = blockIdx.x / P, seg = blockIdx.x % P;
+  const int h = chain % a.H;
+  const int nchunks = (a.T + kL - 1) / kL;
+  const int cbeg = seg * cps;
+  const int cend = min(nchunks, cbeg + cps);
+  const size_t tok0 = (size_t)chain * (size_t)a.T;
+  const T* qg = static_cast<const T*>(a.q);
+  const T* kg = static_cast<const T*>(a.k);
+  const T* vg = static_cast<const T*>(a.v);
+  const T* gg = static_cast<const T*>(a.log_alpha);
+  const T* bg = static_cast<const T*>(a.beta);
+
+  // ---- carry in: the segment's slot when there are segments, else the caller's carry
+  // the caller's C0 / C_out may be the packed upper triangle (the workspace slots never are)
+  const bool cpacked = (a.flags & kFlagPackedCov) != 0;
+  constexpr size_t kTri = (size_t)D * (D + 1) / 2;
+  const float* Sin = nullptr;
+  const float* Cin = nullptr;
+  const float* min_ = nullptr;
+  bool cin_packed = false;
+  if (P > 1) {
+    const float* slot = static_cast<const float*>(a.workspace) + ((size_t)chain * P + seg) * gdn_slot_floats(D);
+    Sin = slot;
+    Cin = slot + (size_t)D * D;
+    min_ = slot + 2 * (size_t)D * D;
+  } else if (a.S0 != nullptr) {
+    Sin = a.S0 + (size_t)chain * D * D;
+    cin_packed = cpacked;
+    Cin = a.C0 + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
+    min_ = a.ksum0 + (size_t)chain * D;
+  }
+  f32x4 Cacc[NA], Sacc[NA];
+  {
+    const int row = cw + l16;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      const int col = 16 * t + 4 * g;
+      Sacc[t] = Sin ? *reinterpret_cast<const f32x4*>(Sin + (size_t)row * D + col) : zero4();
+      if (Cin == nullptr)
+        Cacc[t] = zero4();
+      else if (cin_packed)
+        Cacc[t] = ld_packed4<D>(Cin, row, col);
+      else
+        Cacc[t] = *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int64_t nb = (int64_t)cbeg * kL + ((a.n0 != nullptr) ? a.n0[chain] : 0);
+  const float b_lam = a.b_lambda[h];
+  if (tid < D) {
+    const int c = tid;
+    const float m = min_ ? min_[c] : 0.f;
+    sm.m0[c] = m;
+    const float wv = a.w_lambda[(size_t)h * D + c];
+    const T whi = (T)wv, mhi = (T)m;
+    sm.Wt[0][c] = whi;
+    sm.Wt[1][c] = (T)(wv - (float)whi);
+    sm.Wt[2][c] = mhi;
+    sm.Wt[3][c] = (T)(m - (float)mhi);
+  }
+  for (int e = tid; e < kL * PT; e += 64 * NW) (&sm.Pm[0][0])[e] = (T)0.f;
+
+  // ---- chunk tiles go straight from HBM to LDS (no registers involved): k of the next chunk
+  // at the start of a chunk (it has its own buffer), q and v once the cleaned query and X
+  // are formed.  Wave 1 keeps the per-token log alpha and beta of the next chunk in registers
+  // (lane = token).  Rows past the end of the sequence are zeroed (beta = 0 then makes their
+  // deltas zero).
+  auto chunk_len = [&](int c) { return min(kL, a.T - c * kL); };
+  auto dma_rows = [&](T (*dst)[PQ], const T* src, int c) {
+    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, lane);
+  };
+  float sg = 0.f, sb = 0.f;
+  auto load_gates = [&](int c) {
+    if (w == 1) {
+      const bool ok = lane < chunk_len(c);
+      const size_t i = tok0 + (size_t)c * kL + (ok ? lane : 0);
+      const float x = ldf(gg, i), y = ldf(bg, i);
+      sg = ok ? x : 0.f;
+      sb = ok ? y : 0.f;
+    }
+  };
+  if (cbeg < cend) {
+    dma_rows(sm.Qs, qg, cbeg);
+    dma_rows(sm.Ks[cbeg & 1], kg, cbeg);
+    dma_rows(sm.Vs, vg, cbeg);
+    load_gates(cbeg);
+  }
+
+  for (int ch = cbeg; ch < cend; ++ch) {
+    const int t0 = ch * kL;
+    const int Lc = min(kL, a.T - t0);
+    T (*Ks)[PQ] = sm.Ks[ch & 1];
+
+    // ---- this chunk's tiles have landed; gates; rows past the end of the sequence zeroed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (w == 1) gdn_gates<D, T>(sm, sg, sb, lane);
+    lds_barrier();
+    if (Lc < kL) {
+      zero_tail<D, T, PQ>(sm.Qs, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(Ks, Lc, tid, 64 * NW);
+      zero_tail<D, T, PQ>(sm.Vs, Lc, tid, 64 * NW);
+      lds_barrier();
+    }
+    if (a.flags & kFlagNormalizeKeys) {
+      normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
+      lds_barrier();
+    }
+    if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1);
+
+    // ---- gate and Gram rows (waves 0..3) and Q C0 (every wave); A = beta Gam (K K^T) below
+    // the diagonal and the key sums (the other waves at d = 128, all of them at d = 64)
+    ccq_gram_rows<D, T, NW>(sm, Ks, w, lane, nb, b_lam);
+    {
+      constexpr int kw0 = (NW >= 8) ? 4 : 0, kws = NW - kw0;
+      if (w >= kw0) gdn_build_A<D, T>(sm, Ks, w - kw0, kws, lane);
+      if (tid >= 2 * D) gdn_key_sums<D, T>(sm, Ks, tid - 2 * D);
+    }
+    f32x4 R[1][4];
+    ccq_query_carry<D, T, 1, false>(sm, [&](int, int t) -> const f32x4& { return Cacc[t]; }, lane, R);
+    lds_barrier();
+
+    // ---- inverses of the diagonal blocks (last wave), cleaned query
+    if (w == NW - 1) gdn_diag_inverse<D, T>(sm, lane);
+    ccq_clean_query<D, T, 1, kSplit>(sm, Ks, sm.Qalo, R, cw, lane, [](int, int, int) { return 1.0f; });
+    lds_barrier();
+    if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);  // q of this chunk is no longer read
+
+    // ---- X = beta (V - gamma K S0^T) and Delta on the wave's columns; M = tril(Qc K^T) * Gam
+    // on the lower tiles -> Pm
+    f32x4 X[4];
+    gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, X);
+
+    for (int idx = w; idx < 10; idx += NW) {
+      const int ti = tri_row(idx), tj = tri_col(idx);
+      f32x4 acc = zero4();  // qc_i . k_j at j = 16 tj + 4 g + r, i = 16 ti + l16
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const Frag<T> A = lds_frag<T, KORD_CONTIG>(&Ks[0][0], PQ, 16 * tj, 32 * kk, lane);
+        mma(acc, A, lds_frag<T, KORD_CONTIG>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane));
+        if constexpr (kSplit) mma(acc, A, lds_frag<T, KORD_CONTIG>(&sm.Qalo[0][0], PQ, 16 * ti, 32 * kk, lane));
+        __builtin_amdgcn_sched_barrier(0);  // one K step of operands live at a time
+      }
+      const int i = 16 * ti + l16, j0 = 16 * tj + 4 * g;
+      const float lgi = sm.lgam[i];
+      const f32x4 lgj = *reinterpret_cast<const f32x4*>(&sm.lgam[j0]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = (j0 + r <= i) ? acc[r] * __expf(lgi - lgj[r]) : 0.f;
+      st4<T>(&sm.Pm[i][j0], acc);
+    }
+    f32x4 Dl[4];  // Delta[b][r] at token 16 b + 4 g + r, value channel cw + l16 (fp32)
+    gdn_solve<D, T>(sm, X, lane, Dl);
+    lds_barrier();
+    if (ch + 1 < cend) {  // v of this chunk is no longer read
+      dma_rows(sm.Vs, vg, ch + 1);
+      load_gates(ch + 1);
+    }
+
+    // ---- O^T for the wave's 16 value rows: gamma * S0 Qc^T + Delta^T M^T
+    f32x4 O[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) O[ti] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const Frag<T> A = acc_frag<T>(Sacc[2 * kk], Sacc[2 * kk + 1]);
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) mma(O[ti], A, lds_frag<T, KORD_ACC>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane));
+    }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) O[ti] *= __expf(sm.lgam[16 * ti + l16]);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const Frag<T> A = acc_frag<T>(Dl[2 * kk], Dl[2 * kk + 1]);  // Delta^T, own rows
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        if (kk == 1 && ti < 2) continue;  // tokens 32..63 never precede tokens 0..31
+        mma(O[ti], A, lds_frag<T, KORD_ACC>(&sm.Pm[0][0], PT, 16 * ti, 32 * kk, lane));
+      }
+    }
+    T* og = static_cast<T*>(a.o);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+      const int i = 16 * ti + l16;
+      if (i < Lc) st4<T>(og + (tok0 + t0 + i) * D + cw + 4 * g, O[ti]);
+    }
+
+    // ---- carry update: C += K^T K;  S^T = gamma_L S0^T + K^T diag(gamma_L / gamma) Delta
+    gdn_cov_update<D, T>(Ks, Cacc, cw, lane);
+    gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Sacc[t]; }, Dl, lane);
+    if (tid < D) {
+      const float m = sm.m1[tid];
+      sm.m0[tid] = m;
+      const T mhi = (T)m;
+      sm.Wt[2][tid] = mhi;
+      sm.Wt[3][tid] = (T)(m - (float)mhi);
+    }
+    nb += Lc;
+    lds_barrier();
+  }
+
+  // ---- carry out (last segment)
+  if (seg == P - 1 && a.S_out != nullptr) {
+    float* Sout = a.S_out + (size_t)chain * D * D;
+    float* Cout = a.C_out + (size_t)chain * (cpacked ? kTri : (size_t)D * D);
+    const int row = cw + l16;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+      const int col = 16 * t + 4 * g;
+      *reinterpret_cast<f32x4*>(Sout + (size_t)row * D + col) = Sacc[t];
+      if (cpacked)
+        st_packed4<D>(Cout, row, col, Cacc[t]);
+      else
+        *reinterpret_cast<f32x4*>(Cout + (size_t)row * D + col) = Cacc[t];
+    }
+    if (tid < D) a.ksum_out[(size_t)chain * D + tid] = sm.m0[tid];
+    if (tid == 0) a.n_out[chain] = nb;
+  }
+}
+
+// ---------------------------------------------------------------- segment summaries
+
+// Workgroup (chain, segment p < P-1): runs the segment from a zero carry, (dS, dC, dksum), and
+// the transition recurrence (state starting at I, v = 0), M_p, side by side, sharing the
+// staged keys, A and the diagonal inverses; writes both to slot p.  Summary segments are
+// whole chunks.
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
+  using C_ = Cfg<D, T>;
+  constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
+  __shared__ GdnSmem<D, T> sm;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int cw = 16 * w;
+  const int P = a.segments, cps = a.chunks_per_segment;
+  const int chain = blockIdx.x / (P - 1), seg = blockIdx.x % (P - 1);
+  const int nchunks = (a.T + kL - 1) / kL;
+  const int cbeg = seg * cps;
+  const int cend = min(nchunks, cbeg + cps);
+  const size_t tok0 = (size_t)chain * (size_t)a.T;
+  const T* kg = static_cast<const T*>(a.k);
+  const T* vg = static_cast<const T*>(a.v);
+  const T* gg = static_cast<const T*>(a.log_alpha);
+  const T* bg = static_cast<const T*>(a.beta);
+
+  // states: S from zero, M from the identity; C from zero
+  f32x4 Sacc[NA], Macc[NA], Cacc[NA];
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    Sacc[t] = zero4();
+    Cacc[t] = zero4();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Macc[t][r] = (cw + l16 == 16 * t + 4 * g + r) ? 1.f : 0.f;
+  }
+  if (tid < D) sm.m0[tid] = 0.f;
+
+  auto chunk_len = [&](int c) { return min(kL, a.T - c * kL); };
+  auto dma_rows = [&](T (*dst)[PQ], const T* src, int c) {
+    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, lane);
+  };
+  float sg = 0.f, sb = 0.f;
+  auto load_gates = [&](int c) {
+    if (w == 1) {
+      const bool ok = lane < chunk_len(c);
+      const size_t i = tok0 + (size_t)c * kL + (ok ? lane : 0);
+      const float x = ldf(gg, i), y = ldf(bg, i);
+      sg = ok ? x : 0.f;
+      sb = ok ? y : 0.f;
+    }
+  };
+  if (cbeg < cend) {
+    dma_rows(sm.Ks[cbeg & 1], kg, cbeg);
+    dma_rows(sm.Vs, vg, cbeg);
+    load_gates(cbeg);
+  }
+
+  for (int ch = cbeg; ch < cend; ++ch) {
+    T (*Ks)[PQ] = sm.Ks[ch & 1];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (w == 1) gdn_gates<D, T>(sm, sg, sb, lane);
+    lds_barrier();
+    if (a.flags & kFlagNormalizeKeys) {
+      normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
+      lds_barrier();
+    }
+    if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1);
+
+    gdn_build_A<D, T>(sm, Ks, w, NW, lane);
+    if (tid >= 2 * D) gdn_key_sums<D, T>(sm, Ks, tid - 2 * D);
+    lds_barrier();
+
+    if (w == NW - 1) gdn_diag_inverse<D, T>(sm, lane);
+    f32x4 XS[4], XM[4];
+    gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, XS);
+    gdn_rhs<D, T, false>(sm, Ks, [&](int t) -> const f32x4& { return Macc[t]; }, cw, lane, XM);
+    lds_barrier();
+    if (ch + 1 < cend) {
+      dma_rows(sm.Vs, vg, ch + 1);
+      load_gates(ch + 1);
+    }
+
+    {
+      f32x4 Dl[4];
+      gdn_solve<D, T>(sm, XS, lane, Dl);
+      gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Sacc[t]; }, Dl, lane);
+    }
+    {
+      f32x4 Dl[4];
+      gdn_solve<D, T>(sm, XM, lane, Dl);
+      gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Macc[t]; }, Dl, lane);
+    }
+    gdn_cov_update<D, T>(Ks, Cacc, cw, lane);
+    if (tid < D) sm.m0[tid] = sm.m1[tid];
+    lds_barrier();
+  }
+
+  float* slot = static_cast<float*>(a.workspace) + ((size_t)chain * P + seg) * gdn_slot_floats(D);
+  const int row = cw + l16;
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    const size_t o = (size_t)row * D + 16 * t + 4 * g;
+    *reinterpret_cast<f32x4*>(slot + o) = Sacc[t];
+    *reinterpret_cast<f32x4*>(slot + (size_t)D * D + o) = Cacc[t];
+    *reinterpret_cast<f32x4*>(slot + 2 * (size_t)D * D + D + o) = Macc[t];
+  }
+  if (tid < D) slot[2 * (size_t)D * D + tid] = sm.m0[tid];
+}
+
+// ---------------------------------------------------------------- scans over segments
+
+// S part, in fp32: slot p holds dS_p and M_p (p < P-1) and receives S_in[p] (p <= P-1):
+//   S_in[0] = S0 (or 0),  S_in[p+1] = S_in[p] M_p + dS_p.
+// Workgroup (16-row block rb of S, chain), D/32 waves: wave w computes the two 16x16 output
+// tiles at columns 32 w .. 32 w + 31 with fp32 MFMAs (v_mfma_f32_16x16x4_f32, one K-slice of 4
+// per instruction), the A operand (rows of S_in[p]) and B operand (M_p) read from LDS, eight
+// K-slices of operands at a time.  The running rows live in the accumulators: lane (g, l)
+// holds rows 4 g + r, column n0 + 16 t + l.
+template <int D>
+__global__ __launch_bounds__(2 * D) void gdn_scan_state_kernel(FwdArgs a) {
+  constexpr int NT = 2 * D, KB = 8;
+  __shared__ float Ss[16][D + 4];
+  __shared__ float Ms[D][D + 4];
+  const int rb = blockIdx.x, chain = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int P = a.segments;
+  const size_t slot_f = gdn_slot_floats(D);
+  float* base = static_cast<float*>(a.workspace) + (size_t)chain * P * slot_f;
+  const int n0 = 32 * w;
+  auto elem = [&](int t, int r) { return (size_t)(16 * rb + 4 * g + r) * D + n0 + 16 * t + l16; };
+  f32x4 run[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) run[t][r] = (a.S0 != nullptr) ? a.S0[(size_t)chain * D * D + elem(t, r)] : 0.f;
+  for (int p = 0; p < P; ++p) {
+    float* slot = base + (size_t)p * slot_f;
+    f32x4 dS[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dS[t][r] = (p < P - 1) ? slot[elem(t, r)] : 0.f;
+        slot[elem(t, r)] = run[t][r];
+      }
+    if (p == P - 1) break;
+    // M_p: every load in flight before the first LDS store
+    constexpr int NV = D * D / 4 / NT;
+    const float* M = slot + 2 * (size_t)D * D + D;
+    f32x4 mv[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) mv[v] = *reinterpret_cast<const f32x4*>(M + 4 * (size_t)(tid + NT * v));
+    __syncthreads();  // the previous step's reads of Ss and Ms are done
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e = 4 * (tid + NT * v);
+      *reinterpret_cast<f32x4*>(&Ms[e / D][e % D]) = mv[v];
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ss[4 * g + r][n0 + 16 * t + l16] = run[t][r];
+    __syncthreads();
+    run[0] = dS[0];
+    run[1] = dS[1];
+    for (int k0 = 0; k0 < D / 4; k0 += KB) {
+      float av[KB], b0[KB], b1[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int kk = k0 + u;
+        av[u] = Ss[l16][4 * kk + g];
+        b0[u] = Ms[4 * kk + g][n0 + l16];
+        b1[u] = Ms[4 * kk + g][n0 + 16 + l16];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        run[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], b0[u], run[0], 0, 0, 0);
+        run[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], b1[u], run[1], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// C and ksum part: additive exclusive scan, one thread per float of the C | ksum region.
+template <int D>
+__global__ __launch_bounds__(256) void gdn_scan_sum_kernel(FwdArgs a) {
+  const int chain = blockIdx.y;
+  const int P = a.segments;
+  const size_t f = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= (size_t)D * D + D) return;
+  const size_t slot_f = gdn_slot_floats(D);
+  float* base = static_cast<float*>(a.workspace) + (size_t)chain * P * slot_f + (size_t)D * D;
+  float run = 0.f;
+  if (a.S0 != nullptr) {
+    if (f >= (size_t)D * D)
+      run = a.ksum0[(size_t)chain * D + (f - (size_t)D * D)];
+    else if (a.flags & kFlagPackedCov)
+      run = a.C0[(size_t)chain * D * (D + 1) / 2 + packed_index((int)f / D, (int)f % D, D)];
+    else
+      run = a.C0[(size_t)chain * D * D + f];
+  }
+  for (int p = 0; p < P; ++p) {
+    float* v = base + (size_t)p * slot_f + f;
+    const float d = (p < P - 1) ? *v : 0.f;
+    *v = run;
+    run += d;
+  }
+}
+
+}  // namespace ccq
