@@ -747,7 +747,7 @@ __global__ __launch_bounds__(4 * D) void bwd_carry_walk_kernel(BwdArgs a, int P,
   const size_t DD = (size_t)D * D;
   const BwdLayout<T> L = layout<T>(a);
   const float *S_in = nullptr, *C_in = nullptr, *m_in = nullptr;
-  if (P > 1) {  // the prefill's scan left every segment's carry-in in its slot
+  if (P > 1 && seg > 0) {  // the prefill's scan left the carry-in of segments 1.. in their slots
     const float* slot = L.sum + ((size_t)chain * P + seg) * (2 * DD + 2 * D);
     S_in = slot;
     C_in = slot + DD;

@@ -92,8 +92,9 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
-// Segment summary and scan of the GLA prefill only: every segment's carry-in in its workspace
-// slot (the chunked backward walks each segment's chunks from there).
+// Segment summary and scan of the GLA prefill only: the carry-in of every segment after the
+// first in its workspace slot (the chunked backward walks each segment's chunks from there, the
+// first from the caller's carry).
 hipError_t launch_gla_segment_carries(const FwdArgs& a, hipStream_t stream);
 
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
   const float* Cin = nullptr;
   const float* min_ = nullptr;
   bool cin_packed = false;
-  if (P > 1) {
+  if (P > 1 && seg > 0) {  // segment 0 starts from the caller's carry (or zeros) itself
     const float* slot = slots + ((size_t)chain * P + seg) * slot_f;
     Sin = slot;
     Cin = slot + (size_t)D * D;
@@ -588,8 +588,9 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
 }
 
 // Exclusive scan of segment summaries into carry-ins, in place.  Slot p holds the summary
-// of segment p (p < P-1) and receives the carry-in of segment p (p <= P-1):
-//   carry_in[0] = carry0;  carry_in[p+1] = (S_in[p] diag(e^{ldec[p]}) + dS[p], C + dC, m + dm).
+// of segment p (p < P-1) and receives the carry-in of segment p (1 <= p <= P-1):
+//   carry_in[0] = carry0 (not stored: segment 0 reads the caller's carry);
+//   carry_in[p+1] = (S_in[p] diag(e^{ldec[p]}) + dS[p], C + dC, m + dm).
 // One thread per 4 consecutive floats of the S | C | ksum part of a slot.
 template <int D>
 __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
     for (int j = 0; j < kBatch; ++j) {
       const int p = p0 + j;
       if (p >= P) break;
-      *reinterpret_cast<f32x4*>(base + (size_t)p * slot_f + f) = run;
+      if (p > 0) *reinterpret_cast<f32x4*>(base + (size_t)p * slot_f + f) = run;
       if (p < P - 1) {
         if (isS) run = run * f32x4{__expf(ld[j][0]), __expf(ld[j][1]), __expf(ld[j][2]), __expf(ld[j][3])};
         run += sum[j];
@@ -671,8 +672,8 @@ static hipError_t launch_gla(const FwdArgs& a, hipStream_t s) {
   return record_event(a, 3, s);
 }
 
-// Summary and scan only: every segment's carry-in in its workspace slot (the chunked backward
-// walks each segment's chunks from there).
+// Summary and scan only: the carry-in of every segment after the first in its workspace slot
+// (the chunked backward walks each segment's chunks from there, the first from the caller's carry).
 template <int D, typename T>
 static hipError_t launch_gla_carries_t(const FwdArgs& a, hipStream_t s) {
   const int chains = a.B * a.H;
