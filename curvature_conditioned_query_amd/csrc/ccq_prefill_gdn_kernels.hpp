@@ -253,7 +253,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   const T* gg = static_cast<const T*>(a.log_alpha);
   const T* bg = static_cast<const T*>(a.beta);
 
-  // ---- carry in: the segment's slot when there are segments, else the caller's carry
+  // ---- carry in: the segment's slot for segments 1.., else the caller's carry (or zeros)
   // the caller's C0 / C_out may be the packed upper triangle (the workspace slots never are)
   const bool cpacked = (a.flags & kFlagPackedCov) != 0;
   constexpr size_t kTri = (size_t)D * (D + 1) / 2;
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   const float* Cin = nullptr;
   const float* min_ = nullptr;
   bool cin_packed = false;
-  if (P > 1) {
+  if (P > 1 && seg > 0) {
     const float* slot = static_cast<const float*>(a.workspace) + ((size_t)chain * P + seg) * gdn_slot_floats(D);
     Sin = slot;
     Cin = slot + (size_t)D * D;
@@ -569,8 +569,9 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------- scans over segments
 
-// S part, in fp32: slot p holds dS_p and M_p (p < P-1) and receives S_in[p] (p <= P-1):
-//   S_in[0] = S0 (or 0),  S_in[p+1] = S_in[p] M_p + dS_p.
+// S part, in fp32: slot p holds dS_p and M_p (p < P-1) and receives S_in[p] (1 <= p <= P-1):
+//   S_in[0] = S0 (or 0),  S_in[p+1] = S_in[p] M_p + dS_p.  The main kernel's segment 0 reads the
+// caller's carry itself, so slot 0 keeps its summary.
 // Workgroup (16-row block rb of S, chain), D/32 waves: wave w computes the two 16x16 output
 // tiles at columns 32 w .. 32 w + 31 with fp32 MFMAs (v_mfma_f32_16x16x4_f32, one K-slice of 4
 // per instruction), the A operand (rows of S_in[p]) and B operand (M_p) read from LDS, eight
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(2 * D) void gdn_scan_state_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         dS[t][r] = (p < P - 1) ? slot[elem(t, r)] : 0.f;
-        slot[elem(t, r)] = run[t][r];
+        if (p > 0) slot[elem(t, r)] = run[t][r];  // segment 0 reads the caller's carry itself
       }
     if (p == P - 1) break;
     // M_p: every load in flight before the first LDS store
@@ -642,7 +643,8 @@ __global__ __launch_bounds__(2 * D) void gdn_scan_state_kernel(FwdArgs a) {
   }
 }
 
-// C and ksum part: additive exclusive scan, one thread per float of the C | ksum region.
+// C and ksum part: additive exclusive scan, one thread per float of the C | ksum region (slot 0
+// not written, as for S).
 template <int D>
 __global__ __launch_bounds__(256) void gdn_scan_sum_kernel(FwdArgs a) {
   const int chain = blockIdx.y;
@@ -663,7 +665,7 @@ __global__ __launch_bounds__(256) void gdn_scan_sum_kernel(FwdArgs a) {
   for (int p = 0; p < P; ++p) {
     float* v = base + (size_t)p * slot_f + f;
     const float d = (p < P - 1) ? *v : 0.f;
-    *v = run;
+    if (p > 0) *v = run;
     run += d;
   }
 }
