@@ -445,8 +445,8 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
     plan.load_one(dst, src + (tok0 + (size_t)(cbeg + i) * kL) * D, kL, w, m);
   };
   constexpr int kParts = DmaPlan<D, T, PQ, NW>::M;  // instructions per wave and tile
-  // Loads of an interval in the order they are issued, one instruction at a time between
-  // compute steps: values of chunk i+1, then keys and log decay of chunk i+2.
+  // Loads of an interval in the order they are issued: values of chunk i+1, then keys and log
+  // decay of chunk i+2.
   auto issue = [&](int i, int q) {
     if (q < kParts) {
       if (i + 1 < n) dma_part(sm.Vs[(i + 1) & 1], vg, i + 1, q);
@@ -525,13 +525,17 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
   lds_barrier();
 
   for (int i = 0; i < n; ++i) {
-    // Every buffer a load writes here was last read in the previous interval.  The loads are
-    // spread over the interval one instruction at a time: a burst of them stalls the issuing
-    // waves while the CU's vector-memory path drains it.
-    issue(i, 0);
+    // Every buffer a load writes here was last read in the previous interval.  One tile's
+    // instructions go out before the decay step, the next tile's after it and the last tile's
+    // one at a time between the first MFMA groups of the carry update, so none is left for the
+    // interval's end, where the closing wait would take its whole latency (the summary is 4 %
+    // faster than with three of them there, and than with all of them issued at once).
+#pragma unroll
+    for (int q = 0; q < kParts; ++q) issue(i, q);
     if (i + 1 < n) decay_keys(i + 1);
     __builtin_amdgcn_sched_barrier(0);
-    issue(i, 1);
+#pragma unroll
+    for (int q = kParts; q < 2 * kParts; ++q) issue(i, q);
 
     // carry update of chunk i: C += K^T K;  S^T = diag(e^{B_63}) (S^T + (K e^-B)^T V)
     T (*Ks)[PQ] = sm.Ks[i % 3];
@@ -555,11 +559,11 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
           mma(Cacc[t0_ + u], Ak[u], Bk);
           mma(Sacc[t0_ + u], Ap[u], Bv);
         }
-        issue(i, 2 + kk * (NA / 4) + t0_ / 4);
+        if (2 * kParts + kk * (NA / 4) + t0_ / 4 < 3 * kParts) issue(i, 2 * kParts + kk * (NA / 4) + t0_ / 4);
       }
     }
 #pragma unroll
-    for (int q = 2 + 2 * (NA / 4); q < 3 * kParts; ++q) issue(i, q);
+    for (int q = 2 * kParts + 2 * (NA / 4); q < 3 * kParts; ++q) issue(i, q);
 #pragma unroll
     for (int t = 0; t < NA; ++t) Sacc[t] *= *reinterpret_cast<const f32x4*>(&sm.eBL[i & 1][16 * t + 4 * g]);
 
