@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libccq.so")
-SOURCES = ["ccq_api.cpp", "ccq_decode.hip", "ccq_decode_packed.hip", "ccq_prefill.hip", "ccq_prefill_gdn.hip", "ccq_prefill_gdn_summary.hip", "ccq_subspace.hip",
+SOURCES = ["ccq_api.cpp", "ccq_decode.hip", "ccq_decode_packed.hip", "ccq_prefill.hip", "ccq_prefill_summary.hip", "ccq_prefill_gdn.hip", "ccq_prefill_gdn_summary.hip", "ccq_subspace.hip",
            "ccq_step_backward.hip", "ccq_backward.hip"]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code.
@@ -29,8 +29,9 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 # Per-source scheduler choice, measured on the GPU against the default: the GLA prefill's main
-# kernel is 2-3 % faster with the iterative ILP scheduler (its segment summary 1 % slower, the
-# pass 1-2 % faster); the Gated DeltaNet kernels spill far more under it, so they keep the
+# kernel is 2-3 % faster with the iterative ILP scheduler; its segment summary and carry scan are
+# 3 % faster under the max-ILP one (and 1-3 % slower under iterative ILP), so they sit in a file
+# of their own.  The Gated DeltaNet kernels spill far more under iterative ILP and keep the
 # default.
 # The full-C decode step moves its 1 GiB of state 5 % faster under the same scheduler (6.23 against
 # 5.91 TB/s); the packed-C variants are 8 % slower under it, so they sit in a file of their own.
@@ -38,6 +39,7 @@ _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 # The Gated DeltaNet segment summary is faster under the memory-clause scheduler, its main kernel
 # slower, so the summary is instantiated in a file of its own.
 EXTRA = {"ccq_prefill.hip": _ILP, "ccq_decode.hip": _ILP,
+         "ccq_prefill_summary.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
          "ccq_prefill_gdn_summary.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 

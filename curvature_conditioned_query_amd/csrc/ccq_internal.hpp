@@ -96,6 +96,10 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 // first in its workspace slot (the chunked backward walks each segment's chunks from there, the
 // first from the caller's carry).
 hipError_t launch_gla_segment_carries(const FwdArgs& a, hipStream_t stream);
+// the summary (segments > 1) and scan launches themselves (their own translation unit); launch
+// errors are left for the caller's hipGetLastError
+void launch_gla_summary(const FwdArgs& a, hipStream_t stream);
+void launch_gla_scan(const FwdArgs& a, hipStream_t stream);
 
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).
