@@ -31,11 +31,7 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA, TFLOP/s
 CHUNK = 64
-PREFILL_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill.hip")
-DECODE_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_decode_kernel.hpp")
-BACKWARD_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_step_backward.hip")
-BWD_CHUNKED_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_backward.hip")
-GDN_SRC = os.path.join(ROOT, "curvature_conditioned_query_amd", "csrc", "ccq_prefill_gdn_kernels.hpp")
+MALL_FLUSH_BYTES = 512 << 20  # written between the flushed passes: twice the MI355X's 256 MB MALL
 
 
 # ------------------------------------------------------------------ algorithmic work
@@ -87,8 +83,13 @@ def file_sha(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(name, src_sha):
-    """HBM traffic from committed rocprofv3 --pmc summaries, if taken on the current source."""
+def library_sha():
+    """Hash of every library source, header and compile flag (the one the profiles/ records store)."""
+    from curvature_conditioned_query_amd.build import library_sha256
+    return library_sha256()
+
+
+def _profile_record(name, lib_sha):
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
@@ -97,9 +98,22 @@ def measured_traffic(name, src_sha):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != src_sha:
+    if rec.get("library_sha256") != lib_sha:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def measured_traffic(name, lib_sha):
+    """HBM bytes per launch from a committed rocprofv3 --pmc record, if it was taken on the library
+    as it is now (every source, header and flag), else None."""
+    rec = _profile_record(name, lib_sha)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
+
+
+def measured_mfma(name, lib_sha):
+    """Counter-based MFMA-pipe utilisation from a committed record, if taken on the current library."""
+    rec = _profile_record(name, lib_sha)
+    return None if rec is None else rec.get("mfma_busy_frac")
 
 
 # ------------------------------------------------------------------ GPU legs
@@ -108,7 +122,7 @@ def to_dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda").to(dtype).contiguous()
 
 
-def time_prefill(wl, steps, warmup, keep_outputs=False):
+def time_prefill(wl, steps, warmup, keep_outputs=False, flushed=100):
     import torch
     from curvature_conditioned_query_amd import ccq_fwd_chunked, load_library
     from curvature_conditioned_query_amd.inputs import WORKLOADS, workload_inputs
@@ -165,6 +179,21 @@ def time_prefill(wl, steps, warmup, keep_outputs=False):
     phases = {name: float(np.mean([hip.elapsed_ms(4 * i + a, 4 * i + a + 1) for i in range(steps)]))
               for a, name in enumerate(("summary", "scan", "main"))}
     hip.destroy()
+    # `flushed` more passes, each after an untimed 512 MB write that evicts the MALL (so every pass
+    # reads its inputs from HBM), each timed alone with events on the launch stream; the median
+    # is reported beside the back-to-back rate
+    flushed_ms = []
+    if flushed > 0:
+        buf = torch.empty(MALL_FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(flushed)]
+        for i, (a0, a1) in enumerate(evs):
+            buf.fill_(float(i))
+            a0.record(stream)
+            step()
+            a1.record(stream)
+        torch.cuda.synchronize()
+        flushed_ms = [a0.elapsed_time(a1) for a0, a1 in evs]
+        del buf
     outputs = None
     if keep_outputs:  # the timed passes' o and final carry (every pass writes the same values)
         outputs = {"o": o.float().cpu().numpy(), "S": cout[0].cpu().numpy(), "C": cout[1].cpu().numpy(),
@@ -174,7 +203,48 @@ def time_prefill(wl, steps, warmup, keep_outputs=False):
     slot = (2 * dk * dk + 2 * dk) * 4 if spec["rule"] == "gla" else (3 * dk * dk + dk) * 4
     segs = int(p.segments) if p.segments else (ws_bytes // (B * H * slot) or 1)
     return dict(spec=spec, shape=(B, H, T, dk, dv), total_ms=total_ms, per_ms=per, wall_s=t_wall,
-                dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs, phase_ms=phases, outputs=outputs)
+                dtype=spec["dtype"], workspace_bytes=ws_bytes, segments=segs, phase_ms=phases, outputs=outputs,
+                flushed_ms=flushed_ms)
+
+
+def prefill_roofline(res, flops, nbytes, elem, lib_sha):
+    """Roofline of a prefill pass's dominant kernel, the main kernel (one launch per pass).
+
+    achieved = the pass's algorithmic bytes (q, k, v and the gates read once, o written once, the
+    final carry written: the work of the whole layer, none of it intermediate) over the main
+    kernel's average launch duration; frac = achieved / 8 TB/s.  The main kernel's own bytes
+    (those plus the segment carry-ins it reads from the workspace, an intermediate of the segment
+    split) are reported beside it, as is the method's flop rate over the same duration and the
+    counter-based MFMA-pipe utilisation of the kernel when a record of it matches the library."""
+    B, H, T, dk, _ = res["shape"]
+    spec = res["spec"]
+    main_ms = res["phase_ms"]["main"]
+    mfma_peak = BF16_PEAK_TFLOPS if elem == 2 else FP32_PEAK_TFLOPS
+    k_gbs = nbytes / (main_ms * 1e-3) / 1e9
+    k_tflops = flops / (main_ms * 1e-3) / 1e12
+    kname = "gla_main_kernel" if spec["rule"] == "gla" else "gdn_main_kernel"
+    return dict(bound="hbm", achieved=round(k_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(k_gbs / HBM_PEAK_GBS, 4),
+                traffic=measured_traffic(f"traffic_{spec['name']}.json", lib_sha),
+                kernel=f"{kname}<{dk},{'bf16' if elem == 2 else 'f32'}>", avg_launch_ms=round(main_ms, 4),
+                algorithmic_bytes_per_launch=nbytes, algorithmic_flops_per_launch=flops,
+                kernel_bytes_with_segment_carries=main_kernel_bytes(B, H, T, dk, elem, res["segments"] or 1,
+                                                                    spec["rule"]),
+                mfma=dict(achieved=round(k_tflops, 1), peak=mfma_peak, unit="TFLOP/s",
+                          frac=round(k_tflops / mfma_peak, 4),
+                          counter_busy_frac=measured_mfma(f"mfma_{spec['name']}.json", lib_sha)),
+                pass_ms={k: round(v, 4) for k, v in res["phase_ms"].items()})
+
+
+def flushed_summary(res, tokens):
+    """Median (and spread) of the MALL-flushed passes of a prefill leg."""
+    f = res["flushed_ms"]
+    if not f:
+        return None
+    med = float(np.median(f))
+    return dict(passes=len(f), median_ms=round(med, 4), min_ms=round(float(np.min(f)), 4),
+                max_ms=round(float(np.max(f)), 4), tokens_per_s=round(tokens / (med * 1e-3), 1),
+                flush_bytes=MALL_FLUSH_BYTES)
 
 
 class HipEvents:
@@ -210,10 +280,18 @@ class HipEvents:
             self.rt.hipEventDestroy(h)
 
 
-def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False):
+# (sequence, head) pairs of the decode workload whose prefix, carry and first step are kept on the
+# host for the oracle check in the CPU leg
+DECODE_SAMPLES = ((0, 0), (131, 7), (255, 15))
+
+
+def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False, keep_samples=False):
     """Decode workload: 256 sequences x 16 heads, d=128, carry from an 8192-token prefix
     built by the prefill kernel on device-generated seeded inputs.  packed_cov: the statistic
-    C is kept as its packed upper triangle (prefill writes it so, decode updates it so)."""
+    C is kept as its packed upper triangle (prefill writes it so, decode updates it so).
+    keep_samples: host copies, for the sampled heads, of the prefix, of the carry the prefill
+    built from it, and of the first decode step's token, output and carry after it (that step
+    runs before the warm-up; the timed steps follow from its state)."""
     import torch
     from curvature_conditioned_query_amd import ccq_decode_step, ccq_fwd_chunked
     from curvature_conditioned_query_amd.inputs import WORKLOADS
@@ -228,6 +306,7 @@ def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False):
     n = torch.empty((N, H), dtype=torch.int64, device="cuda")
     w = (torch.randn((H, d), generator=gen, device="cuda") / np.sqrt(d)).float().contiguous()
     b = torch.full((H,), -2.0, device="cuda")
+    samples = {}
     for s0 in range(0, N, seqs_per_batch):
         nb = min(seqs_per_batch, N - s0)
         shp = (nb, H, T, d)
@@ -236,6 +315,11 @@ def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False):
         kk = (kk / kk.norm(dim=-1, keepdim=True)).to(bf)
         vv = torch.randn(shp, generator=gen, device="cuda").to(bf)
         gg = (torch.nn.functional.logsigmoid(torch.randn(shp, generator=gen, device="cuda")) / 16).to(bf)
+        if keep_samples:
+            for (sq, hh) in DECODE_SAMPLES:
+                if s0 <= sq < s0 + nb:
+                    samples[(sq, hh)] = {name: t[sq - s0, hh].float().cpu().numpy()
+                                         for name, t in (("q", qq), ("k", kk), ("v", vv), ("g", gg))}
         ccq_fwd_chunked("gla", qq, kk, vv, gg, None, w, b,
                         carry_out=(S[s0:s0 + nb], C[s0:s0 + nb], m[s0:s0 + nb], n[s0:s0 + nb]),
                         packed_cov=packed_cov)
@@ -252,6 +336,22 @@ def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False):
     def step():
         ccq_decode_step("gla", tq, tk, tv, tg, None, w, b, S, C, m, n, o=o, packed_cov=packed_cov)
 
+    def carry_of(sq, hh):
+        return tuple(t[sq, hh].cpu().numpy().copy() for t in (S, C, m, n))
+
+    if keep_samples:
+        for (sq, hh), rec in samples.items():
+            rec["carry"] = carry_of(sq, hh)
+            rec["token"] = {name: t[sq, hh].float().cpu().numpy() for name, t in
+                            (("q", tq), ("k", tk), ("v", tv), ("g", tg))}
+        step()
+        torch.cuda.synchronize()
+        for (sq, hh), rec in samples.items():
+            rec["o"] = o[sq, hh].float().cpu().numpy()
+            rec["carry_after"] = carry_of(sq, hh)
+        wh, bh = w.cpu().numpy(), b.cpu().numpy()
+        for (sq, hh), rec in samples.items():
+            rec["w"], rec["b"] = wh[hh:hh + 1], bh[hh:hh + 1]
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -267,7 +367,7 @@ def time_decode(steps, warmup, seqs_per_batch=32, packed_cov=False):
     name = spec["name"].replace("decode-", "decode-packed-") if packed_cov else spec["name"]
     del S, C, m, n
     return dict(spec=spec, name=name, ms_per_step=ms, bytes_per_step=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9,
-                tokens_per_s=N / (ms * 1e-3))
+                tokens_per_s=N / (ms * 1e-3), samples=samples, packed_cov=packed_cov)
 
 
 def time_subspace(calls, warmup, r=16):
@@ -518,6 +618,53 @@ def cpu_baseline(wl, tokens, max_workers, gpu_out=None):
                 wall_s=wall, cpu_s=cpu_s, parity=parity)
 
 
+def decode_parity(samples, packed_cov, cache):
+    """The oracle on the sampled heads of the decode leg: the carry after the 8192-token prefix
+    (against the carry the prefill kernel built) and one decode step from the GPU's own carry
+    (against the GPU step's output and carry after it).  Normwise errors, max over the samples;
+    `cache` keeps the prefix runs, which both decode legs share."""
+    import oracle
+    errs = {}
+
+    def upd(key, e):
+        errs[key] = max(errs.get(key, 0.0), e)
+
+    n_exact = True
+    for key, rec in samples.items():
+        if key not in cache:
+            pre = {name: rec[name][None, None] for name in ("q", "k", "v", "g")}
+            cache[key] = oracle.ccq_recurrent(pre["q"], pre["k"], pre["v"], pre["g"], None, rec["w"], rec["b"],
+                                              "gla")[1]
+        ref = cache[key]
+        d = rec["carry"][0].shape[-1]
+
+        def full_c(c):
+            return oracle.unpack_upper(c, d) if packed_cov else c
+
+        S, C, m, n = rec["carry"]
+        upd("prefix_S", oracle.normwise_error(S[None, None], ref.S))
+        upd("prefix_C", oracle.normwise_error(full_c(C)[None, None], ref.C))
+        upd("prefix_ksum", oracle.normwise_error(m[None, None, :, None], ref.m[..., None]))
+        n_exact &= bool(np.array_equal(np.asarray(n).reshape(1, 1), ref.n))
+        gc = oracle.Carry(S[None, None].astype(np.float64), full_c(C)[None, None].astype(np.float64),
+                          m[None, None].astype(np.float64), np.asarray(n, np.int64).reshape(1, 1))
+        tok = {name: rec["token"][name][None, None] for name in ("q", "k", "v", "g")}
+        o_ref, c_ref = oracle.ccq_decode_step(tok["q"], tok["k"], tok["v"], tok["g"], None, rec["w"], rec["b"], "gla",
+                                              gc)
+        S1, C1, m1, n1 = rec["carry_after"]
+        upd("step_o", oracle.normwise_error(rec["o"][None, None, :, None], o_ref[..., None]))
+        upd("step_S", oracle.normwise_error(S1[None, None], c_ref.S))
+        upd("step_C", oracle.normwise_error(full_c(C1)[None, None], c_ref.C))
+        upd("step_ksum", oracle.normwise_error(m1[None, None, :, None], c_ref.m[..., None]))
+        n_exact &= bool(np.array_equal(np.asarray(n1).reshape(1, 1), c_ref.n))
+    tol = 2e-2
+    out = {k: round(v, 8) for k, v in errs.items()}
+    out.update(n_exact=n_exact, samples=[list(k) for k in samples], tolerance=tol,
+               against="fp64 per-token recurrence (oracle)",
+               **{"pass": bool(n_exact and all(v <= tol for v in errs.values()))})
+    return out
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -606,29 +753,12 @@ def main(argv=None):
     mfma_peak = BF16_PEAK_TFLOPS if res["dtype"] == "bf16" else FP32_PEAK_TFLOPS
     intensity = flops / nbytes
     ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
-    bound = "hbm" if intensity < ridge else "mfma"
-    src_sha = file_sha(PREFILL_SRC)
-    # Roofline of the dominant kernel, the main prefill kernel (one launch per pass): its
-    # algorithmic bytes and the method's flops over its own average launch duration.
-    main_ms = res["phase_ms"]["main"]
-    main_bytes = main_kernel_bytes(B, H, T, dk, elem, res["segments"] or 1, spec["rule"])
-    k_gbs = main_bytes / (main_ms * 1e-3) / 1e9
-    k_tflops = flops / (main_ms * 1e-3) / 1e12
-    traffic = measured_traffic(f"traffic_{spec['name']}.json", src_sha)
-    if bound == "hbm":
-        roof = dict(bound="hbm", achieved=round(k_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(k_gbs / HBM_PEAK_GBS, 4), traffic=traffic)
-    else:
-        roof = dict(bound="mfma", achieved=round(k_tflops, 1), peak=mfma_peak, unit="TFLOP/s",
-                    frac=round(k_tflops / mfma_peak, 4), traffic=traffic)
-    roof.update(kernel=f"gla_main_kernel<{dk},{'bf16' if elem == 2 else 'f32'}>",
-                avg_launch_ms=round(main_ms, 4), algorithmic_bytes_per_launch=main_bytes,
-                algorithmic_flops_per_launch=flops,
-                mfma=dict(achieved=round(k_tflops, 1), peak=mfma_peak, unit="TFLOP/s",
-                          frac=round(k_tflops / mfma_peak, 4)),
-                pass_ms={k: round(v, 4) for k, v in res["phase_ms"].items()},
-                whole_pass=dict(bytes=nbytes, gbs=round(gbs, 1), tflops=round(tflops, 1),
-                                hbm_frac=round(gbs / HBM_PEAK_GBS, 4)))
+    lib_sha = library_sha()
+    roof = prefill_roofline(res, flops, nbytes, elem, lib_sha)
+    roof.update(whole_pass=dict(bytes=nbytes, gbs=round(gbs, 1), tflops=round(tflops, 1),
+                                hbm_frac=round(gbs / HBM_PEAK_GBS, 4)),
+                bound_by_intensity="hbm" if intensity < ridge else "mfma",
+                flushed=flushed_summary(res, B * T))
     out = {
         "metric": "CCQ-GLA prefill tokens/s (H16,dk128,T4K) + MFMA util; decode HBM GB/s",
         "value": round(tok_s, 1),
@@ -652,7 +782,7 @@ def main(argv=None):
     if not args.no_long and args.workload == 1:
         # the pages' systems claim is that CCQ's cost does not grow with sequence length: the same
         # layer on 5x longer sequences (B=1, H=16, T=20480), per-token time against the line above
-        lres = time_prefill(3, args.steps, args.warmup)
+        lres = time_prefill(3, args.steps, args.warmup, flushed=0)
         lB, lH, lT = lres["shape"][:3]
         l_ms = lres["total_ms"] / args.steps
         ns_tok = l_ms * 1e6 / (lB * lH * lT)
@@ -671,41 +801,34 @@ def main(argv=None):
         g_ms = gres["total_ms"] / args.steps
         g_flops, g_bytes = prefill_work(gB, gH, gT, gd, 2, "gdn")
         g_main = gres["phase_ms"]["main"]
-        g_kbytes = main_kernel_bytes(gB, gH, gT, gd, 2, gres["segments"] or 1, "gdn")
-        g_gbs = g_kbytes / (g_main * 1e-3) / 1e9
-        g_tf = g_flops / (g_main * 1e-3) / 1e12
-        gsrc = file_sha(GDN_SRC)
+        groof = prefill_roofline(gres, g_flops, g_bytes, 2, lib_sha)
+        groof["flushed"] = flushed_summary(gres, gB * gT)
+        g_gbs, g_tf = groof["achieved"], groof["mfma"]["achieved"]
         out["gdn"] = {
             "workload": gres["spec"]["name"], "ms_per_step": round(g_ms, 4),
             "tokens_per_s": round(gB * gT / (g_ms * 1e-3), 1), "segments": gres["segments"],
             "pass_ms": {k: round(v, 4) for k, v in gres["phase_ms"].items()},
-            "roofline": dict(bound="hbm", achieved=round(g_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=round(g_gbs / HBM_PEAK_GBS, 4),
-                             traffic=measured_traffic(f"traffic_{gres['spec']['name']}.json", gsrc),
-                             kernel=f"gdn_main_kernel<{gd},bf16>", avg_launch_ms=round(g_main, 4),
-                             algorithmic_bytes_per_launch=g_kbytes, algorithmic_flops_per_launch=g_flops,
-                             mfma=dict(achieved=round(g_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                                       frac=round(g_tf / BF16_PEAK_TFLOPS, 4))),
+            "roofline": groof,
         }
         print(f"# prefill {gres['spec']['name']}: {g_ms:.3f} ms/step, {gB * gT / (g_ms * 1e-3):.4g} tokens/s, "
               f"main kernel {g_main:.4f} ms, {g_gbs:.1f} GB/s alg, {g_tf:.1f} TFLOP/s alg",
               file=sys.stderr, flush=True)
+    decode_samples = {}
     if not args.no_decode:
-        dsrc = file_sha(DECODE_SRC)
         for key, packed in (("decode", False), ("decode_packed", True)):
-            dres = time_decode(args.decode_steps, 3, packed_cov=packed)
+            dres = time_decode(args.decode_steps, 3, packed_cov=packed, keep_samples=not args.no_cpu)
+            decode_samples[key] = (dres["samples"], packed)
             out[key] = {
                 "workload": dres["name"], "ms_per_step": round(dres["ms_per_step"], 4),
                 "tokens_per_s": round(dres["tokens_per_s"], 1), "packed_cov": packed,
                 "roofline": dict(bound="hbm", achieved=round(dres["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                                  frac=round(dres["gbs"] / HBM_PEAK_GBS, 4),
-                                 traffic=measured_traffic(f"traffic_{dres['name']}.json", dsrc)),
+                                 traffic=measured_traffic(f"traffic_{dres['name']}.json", lib_sha)),
                 "algorithmic_bytes_per_step": dres["bytes_per_step"],
             }
             print(f"# {dres['name']}: {dres['ms_per_step']*1e3:.1f} us/step, {dres['gbs']:.1f} GB/s",
                   file=sys.stderr, flush=True)
     if not args.no_backward:
-        bsrc = file_sha(BACKWARD_SRC)
         out["step_backward"] = {}
         for rule in ("gla", "gdn"):
             bres = time_step_backward(args.decode_steps, 3, rule)
@@ -713,7 +836,7 @@ def main(argv=None):
                 "workload": bres["name"], "ms_per_step": round(bres["ms"], 4),
                 "roofline": dict(bound="hbm", achieved=round(bres["gbs"], 1), peak=HBM_PEAK_GBS, unit="GB/s",
                                  frac=round(bres["gbs"] / HBM_PEAK_GBS, 4),
-                                 traffic=measured_traffic(f"traffic_{bres['name']}.json", bsrc)),
+                                 traffic=measured_traffic(f"traffic_{bres['name']}.json", lib_sha)),
                 "algorithmic_bytes_per_step": bres["bytes"]}
             print(f"# {bres['name']}: {bres['ms'] * 1e3:.1f} us/step, {bres['gbs']:.1f} GB/s", file=sys.stderr,
                   flush=True)
@@ -732,7 +855,7 @@ def main(argv=None):
             "pass_ms": {k: round(v, 4) for k, v in cres["phase_ms"].items()},
             "roofline": dict(bound="hbm", achieved=round(a_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                              frac=round(a_gbs / HBM_PEAK_GBS, 4),
-                             traffic=measured_traffic(f"traffic_{cres['name']}.json", file_sha(BWD_CHUNKED_SRC)),
+                             traffic=measured_traffic(f"traffic_{cres['name']}.json", lib_sha),
                              kernel=f"bwd_chunk_a_kernel<{cd},bf16>",
                              avg_launch_ms=round(pa, 4), algorithmic_flops_per_launch=fa * cres["chunks"],
                              algorithmic_bytes_per_launch=ba * cres["chunks"],
@@ -772,6 +895,13 @@ def main(argv=None):
         out["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample", "cpu_model")}
         print(f"# cpu oracle: {cb['value']:.4g} tokens/s on {cb['cores']} cores ({cb['wall_s']:.1f} s wall)",
               file=sys.stderr, flush=True)
+        cache = {}
+        for key, (smp, packed) in decode_samples.items():
+            if smp:
+                out[key]["parity"] = decode_parity(smp, packed, cache)
+                print(f"# {key} parity on {len(smp)} sampled heads: " + ", ".join(
+                    f"{k} {v:.3e}" for k, v in out[key]["parity"].items() if isinstance(v, float)),
+                      file=sys.stderr, flush=True)
         if cb["parity"] is not None:
             # the timed passes' own output against the oracle, normwise per (b, h) chain (max over
             # chains), at the tolerance the inputs' precision sets

@@ -43,6 +43,25 @@ EXTRA = {"ccq_prefill.hip": _ILP, "ccq_decode.hip": _ILP,
          "ccq_prefill_gdn_summary.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
+def library_sha256() -> str:
+    """sha256 over everything that decides the built code: every file under csrc/ and include/
+    (name and contents, in sorted order) and the compile flags of every translation unit.
+    Counter records under profiles/ store it, so a record stops counting as soon as any
+    source, header or flag changes."""
+    import hashlib
+    h = hashlib.sha256()
+    for top in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(top)):
+            path = os.path.join(top, name)
+            if os.path.isfile(path):
+                h.update(os.path.relpath(path, ROOT).encode())
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    for src in SOURCES:
+        h.update(" ".join([src, *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, [])]).encode())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):

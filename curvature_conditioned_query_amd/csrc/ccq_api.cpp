@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ccq_internal.hpp"
+#include "ccq_overlap.hpp"
 
 static_assert(CCQ_FLAG_NORMALIZE_KEYS == ccq::kFlagNormalizeKeys && CCQ_FLAG_PACKED_COV == ccq::kFlagPackedCov,
               "flag bits of the header and the kernels agree");
@@ -63,10 +64,20 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
   return CCQ_OK;
 }
 
+size_t fwd_slot(const ccq_fwd_params* p) {
+  return (p->rule == CCQ_RULE_GDN) ? ccq::gdn_slot_bytes(p->d_k) : ccq::fwd_slot_bytes(p->d_k);
+}
+
 size_t fwd_ws_bytes(const ccq_fwd_params* p, int seg) {
   if (seg <= 1) return 0;
-  const size_t slot = (p->rule == CCQ_RULE_GDN) ? ccq::gdn_slot_bytes(p->d_k) : ccq::fwd_slot_bytes(p->d_k);
-  return (size_t)p->B * p->H * seg * slot;
+  const size_t chains = (size_t)p->B * p->H;
+  return ccq::fwd_count_offset(chains, seg, fwd_slot(p)) + chains * sizeof(int64_t);
+}
+
+// Whether any byte of the carry out is also a byte of the carry in.
+bool carry_overlaps(const ccq_fwd_params* p) {
+  const ccq::CarryRanges in{p->S0, p->C0, p->ksum0, p->n0}, out{p->S_out, p->C_out, p->ksum_out, p->n_out};
+  return ccq::carry_ranges_overlap(in, out, (size_t)p->B * p->H, (size_t)p->d_k, (p->flags & CCQ_FLAG_PACKED_COV) != 0);
 }
 
 int validate_bwd(const ccq_bwd_params* p) {
@@ -125,7 +136,7 @@ int ccq_fwd_chunked(const ccq_fwd_params* p, void* hip_stream) {
   if (st != CCQ_OK) return st;
   const size_t need = fwd_ws_bytes(p, seg);
   if (need > 0 && (p->workspace == nullptr || p->workspace_bytes < need)) return CCQ_ERR_WORKSPACE;
-  ccq::FwdArgs a;
+  ccq::FwdArgs a{};
   a.rule = p->rule;
   a.dtype = p->dtype;
   a.B = p->B;
@@ -153,6 +164,7 @@ int ccq_fwd_chunked(const ccq_fwd_params* p, void* hip_stream) {
   a.workspace = p->workspace;
   a.events = p->phase_events;
   a.flags = p->flags;
+  a.snapshot = (seg > 1 && carry_overlaps(p)) ? 1 : 0;
   const hipError_t e = ccq::launch_fwd(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }

@@ -37,7 +37,18 @@ struct FwdArgs {
   void* workspace;
   void* const* events;  // optional: 4 hipEvent_t around the kernels of the pass
   int flags;             // ccq_flag bits
+  // Set when segments > 1 and the carry out overlaps the carry in: the scan then copies the
+  // caller's carry into slot 0 and n0 into the workspace's count area, and every segment of
+  // the main kernel reads those copies, so no workgroup can read a carry another one has
+  // already overwritten.
+  int snapshot;
 };
+
+// The workspace of a prefill with more than one segment: chains x P slots, then one int64
+// token count per chain (the snapshot of n0, written only when `snapshot` is set).
+__host__ __device__ inline size_t fwd_count_offset(size_t chains, int P, size_t slot_bytes) {
+  return chains * (size_t)P * slot_bytes;
+}
 
 constexpr int kFlagNormalizeKeys = 1;
 constexpr int kFlagPackedCov = 2;  // C0 / C_out / decode C hold the packed upper triangle

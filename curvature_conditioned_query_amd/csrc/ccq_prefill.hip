@@ -103,7 +103,9 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
   const float* Cin = nullptr;
   const float* min_ = nullptr;
   bool cin_packed = false;
-  if (P > 1 && seg > 0) {  // segment 0 starts from the caller's carry (or zeros) itself
+  // segment 0 starts from the caller's carry (or zeros) itself, unless the carry out overlaps
+  // it: then the scan has copied it into slot 0
+  if (P > 1 && (seg > 0 || a.snapshot)) {
     const float* slot = slots + ((size_t)chain * P + seg) * slot_f;
     Sin = slot;
     Cin = slot + (size_t)D * D;
@@ -131,7 +133,10 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
   // the carry-in loads complete here, so nothing in the chunk loop waits on them
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int64_t nb = (int64_t)cbeg * kL;  // tokens before this chunk (count base)
-  if (a.n0 != nullptr) nb += a.n0[chain];
+  if (a.n0 != nullptr)
+    nb += a.snapshot ? reinterpret_cast<const int64_t*>(reinterpret_cast<const char*>(a.workspace) +
+                                                          fwd_count_offset((size_t)a.B * a.H, P, slot_f * sizeof(float)))[chain]
+                     : a.n0[chain];
   const float b_lam = a.b_lambda[h];
 
   if (tid < D) {

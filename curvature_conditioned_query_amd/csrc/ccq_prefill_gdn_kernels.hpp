@@ -261,7 +261,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   const float* Cin = nullptr;
   const float* min_ = nullptr;
   bool cin_packed = false;
-  if (P > 1 && seg > 0) {
+  if (P > 1 && (seg > 0 || a.snapshot)) {  // slot 0 holds a copy of the caller's carry when the carry out overlaps it
     const float* slot = static_cast<const float*>(a.workspace) + ((size_t)chain * P + seg) * gdn_slot_floats(D);
     Sin = slot;
     Cin = slot + (size_t)D * D;
@@ -288,7 +288,12 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  int64_t nb = (int64_t)cbeg * kL + ((a.n0 != nullptr) ? a.n0[chain] : 0);
+  int64_t nb = (int64_t)cbeg * kL;
+  if (a.n0 != nullptr)
+    nb += a.snapshot ? reinterpret_cast<const int64_t*>(static_cast<const char*>(a.workspace) +
+                                                         fwd_count_offset((size_t)a.B * a.H, P,
+                                                                          gdn_slot_floats(D) * sizeof(float)))[chain]
+                     : a.n0[chain];
   const float b_lam = a.b_lambda[h];
   if (tid < D) {
     const int c = tid;
@@ -571,7 +576,8 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
 
 // S part, in fp32: slot p holds dS_p and M_p (p < P-1) and receives S_in[p] (1 <= p <= P-1):
 //   S_in[0] = S0 (or 0),  S_in[p+1] = S_in[p] M_p + dS_p.  The main kernel's segment 0 reads the
-// caller's carry itself, so slot 0 keeps its summary.
+// caller's carry itself, so slot 0 keeps its summary -- unless the carry out overlaps the carry
+// in: then slot 0 receives S_in[0] as well.
 // Workgroup (16-row block rb of S, chain), D/32 waves: wave w computes the two 16x16 output
 // tiles at columns 32 w .. 32 w + 31 with fp32 MFMAs (v_mfma_f32_16x16x4_f32, one K-slice of 4
 // per instruction), the A operand (rows of S_in[p]) and B operand (M_p) read from LDS, eight
@@ -602,7 +608,8 @@ __global__ __launch_bounds__(2 * D) void gdn_scan_state_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         dS[t][r] = (p < P - 1) ? slot[elem(t, r)] : 0.f;
-        if (p > 0) slot[elem(t, r)] = run[t][r];  // segment 0 reads the caller's carry itself
+        // segment 0 reads the caller's carry itself unless the carry out overlaps it
+        if (p > 0 || a.snapshot) slot[elem(t, r)] = run[t][r];
       }
     if (p == P - 1) break;
     // M_p: every load in flight before the first LDS store
@@ -652,6 +659,11 @@ __global__ __launch_bounds__(256) void gdn_scan_sum_kernel(FwdArgs a) {
   const size_t f = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (f >= (size_t)D * D + D) return;
   const size_t slot_f = gdn_slot_floats(D);
+  if (a.snapshot && f == 0) {  // the caller's token count, for every segment of the main kernel
+    int64_t* counts = reinterpret_cast<int64_t*>(static_cast<char*>(a.workspace) +
+                                                 fwd_count_offset((size_t)a.B * a.H, P, slot_f * sizeof(float)));
+    counts[chain] = a.n0 != nullptr ? a.n0[chain] : 0;
+  }
   float* base = static_cast<float*>(a.workspace) + (size_t)chain * P * slot_f + (size_t)D * D;
   float run = 0.f;
   if (a.S0 != nullptr) {
@@ -665,7 +677,7 @@ __global__ __launch_bounds__(256) void gdn_scan_sum_kernel(FwdArgs a) {
   for (int p = 0; p < P; ++p) {
     float* v = base + (size_t)p * slot_f + f;
     const float d = (p < P - 1) ? *v : 0.f;
-    if (p > 0) *v = run;
+    if (p > 0 || a.snapshot) *v = run;
     run += d;
   }
 }

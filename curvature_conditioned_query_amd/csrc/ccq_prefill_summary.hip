@@ -203,7 +203,8 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
 
 // Exclusive scan of segment summaries into carry-ins, in place.  Slot p holds the summary
 // of segment p (p < P-1) and receives the carry-in of segment p (1 <= p <= P-1):
-//   carry_in[0] = carry0 (not stored: segment 0 reads the caller's carry);
+//   carry_in[0] = carry0 (stored in slot 0 only when the carry out overlaps the carry in;
+//                 otherwise segment 0 reads the caller's carry);
 //   carry_in[p+1] = (S_in[p] diag(e^{ldec[p]}) + dS[p], C + dC, m + dm).
 // One thread per 4 consecutive floats of the S | C | ksum part of a slot.
 template <int D>
@@ -216,6 +217,11 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
   if (idx >= nf4) return;
   const size_t f = (size_t)idx * 4;
   float* base = static_cast<float*>(a.workspace) + (size_t)chain * P * slot_f;
+  if (a.snapshot && idx == 0) {  // the caller's token count, for every segment of the main kernel
+    int64_t* counts = reinterpret_cast<int64_t*>(static_cast<char*>(a.workspace) +
+                                                 fwd_count_offset((size_t)a.B * a.H, P, slot_f * sizeof(float)));
+    counts[chain] = a.n0 != nullptr ? a.n0[chain] : 0;
+  }
   const bool isS = f < (size_t)D * D;
   const int col = (int)(f % D);
   f32x4 run = zero4();
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
     for (int j = 0; j < kBatch; ++j) {
       const int p = p0 + j;
       if (p >= P) break;
-      if (p > 0) *reinterpret_cast<f32x4*>(base + (size_t)p * slot_f + f) = run;
+      if (p > 0 || a.snapshot) *reinterpret_cast<f32x4*>(base + (size_t)p * slot_f + f) = run;
       if (p < P - 1) {
         if (isS) run = run * f32x4{__expf(ld[j][0]), __expf(ld[j][1]), __expf(ld[j][2]), __expf(ld[j][3])};
         run += sum[j];

@@ -99,7 +99,9 @@ typedef struct {
 
   void *o;               /* [B, H, T, d_v] dtype, written                                       */
 
-  /* Carry out: all four NULL (not wanted) or all four set.  May alias the carry in. */
+  /* Carry out: all four NULL (not wanted) or all four set.  May alias or overlap the carry in:
+   * with more than one segment the call then first copies the carry in (and n0) into the
+   * workspace, which ccq_fwd_workspace_bytes always leaves room for, and reads only the copy. */
   float *S_out;
   float *C_out;          /* same layout as C0                                                    */
   float *ksum_out;
@@ -123,9 +125,13 @@ typedef struct {
  * chunks of 64 tokens; the statistics are carried chunk by chunk exactly as the backbone's
  * state is (summary §2 "机制").  A call with a carry in continues the sequence
  * the carry came from.  T need not be a multiple of 64.
- * Precondition (GLA): within any 64-token chunk the cumulative log decay of each key channel
- * stays above -80 on either side of the chunk's midpoint (no fp32 overflow of e^{+-B}).
- * Returns a ccq_status.
+ * Precondition (GLA): the call cuts its T tokens into chunks of 64 counted from its own first
+ * token (tokens 64c .. 64c + 63).  Within every chunk the decay is factored with the chunk's
+ * start as reference, so for every key channel the sum of log_alpha over a whole chunk
+ * (equivalently, since log_alpha <= 0, from the chunk's first token to any later token of it)
+ * must stay above -80: an average log decay above -1.25 per token (alpha > 0.29).  Beyond it
+ * e^{-B} overflows in fp32 and o and the carry are not finite; nothing checks this.
+ * Gated DeltaNet has no such limit.  Returns a ccq_status.
  */
 int ccq_fwd_chunked(const ccq_fwd_params *p, void *hip_stream);
 

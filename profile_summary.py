@@ -21,19 +21,35 @@ and writes the few figures the benchmark and the design notes use:
         --command "..." [--command "..."]
         every counter the runs collected for the kernels matching REGEX, averaged per dispatch
         (each counter summed over the rows of a dispatch), with the dispatches' average duration.
+
+    python profile_summary.py mfma RUN.db --kernel REGEX --workload NAME --out profiles/mfma_NAME.json
+        --command "..."
+        counter-based MFMA-pipe utilisation of the kernels matching REGEX: SQ_VALU_MFMA_BUSY_CYCLES
+        (the MFMA unit's busy cycles summed over every SIMD) over 1024 SIMDs x the dispatch's
+        duration x the nominal 2.4 GHz clock.
+
+Records (traffic, mfma) store the library hash of ``curvature_conditioned_query_amd.build``
+(every source, header and compile flag), so the benchmark only reports a figure while the built
+code is the one it was measured on.
 """
 
 from __future__ import annotations
 
 import argparse
 import collections
-import hashlib
 import json
 import re
 import sqlite3
 import sys
 
 CALIB_KERNEL = r"neg_kernel"
+SIMDS = 1024            # MI355X: 256 compute units x 4 SIMDs
+NOMINAL_CLOCK_HZ = 2.4e9
+
+
+def library_sha256() -> str:
+    from curvature_conditioned_query_amd.build import library_sha256 as _sha
+    return _sha()
 
 
 def _short(name: str) -> str:
@@ -109,13 +125,11 @@ def traffic_summary(a):
     s_write = calib_bytes / (cw_k * 1024.0)
     fetch_b = f_k * 1024.0 * s_fetch
     write_b = w_k * 1024.0 * s_write
-    with open(a.source, "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
     return {
         "workload": a.workload,
         "kernel": names,
         "source": a.source,
-        "source_sha256": sha,
+        "library_sha256": library_sha256(),
         "dispatches": {"fetch_run": n_f, "write_run": n_w},
         "avg_duration_us_under_counters": {"fetch_run": round(us_f, 2), "write_run": round(us_w, 2)},
         "fetch_kib_per_dispatch": round(f_k, 1),
@@ -127,6 +141,22 @@ def traffic_summary(a):
         "hbm_write_bytes_per_launch": round(write_b),
         "hbm_bytes_per_launch": round(fetch_b + write_b),
         "commands": {"fetch": a.fetch_command, "write": a.write_command},
+    }
+
+
+def mfma_summary(a):
+    busy, n, us, names = counter_per_dispatch(a.db, "SQ_VALU_MFMA_BUSY_CYCLES", a.kernel)
+    frac = busy / (SIMDS * us * 1e-6 * NOMINAL_CLOCK_HZ)
+    return {
+        "workload": a.workload,
+        "kernel": names,
+        "library_sha256": library_sha256(),
+        "dispatches": n,
+        "avg_duration_us_under_counters": round(us, 2),
+        "mfma_busy_cycles_per_dispatch": round(busy, 1),
+        "mfma_busy_frac": round(frac, 4),
+        "definition": "SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x avg dispatch duration x 2.4 GHz)",
+        "command": a.command,
     }
 
 
@@ -179,8 +209,20 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     c.add_argument("--fetch-command", required=True)
     c.add_argument("--write-command", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("db")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--workload", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    if a.mode == "trace":
+    if a.mode == "mfma":
+        rec = mfma_summary(a)
+        with open(a.out, "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(rec, indent=1))
+    elif a.mode == "trace":
         text = trace_summary(a.dbs, a.command, a.title)
         with open(a.out, "w") as fh:
             fh.write(text + "\n")

@@ -44,6 +44,20 @@ def test_main_kernel_bytes_with_segments():
     assert bench.main_kernel_bytes(B, H, T, d, 2, 1) == 369_230_336 - 3 * 64 * (2 * d * d + d) * 4
 
 
+def test_prefill_roofline_uses_the_algorithmic_bytes():
+    """frac divides the pass's algorithmic bytes (343,966,208 at the headline shape), not the main
+    kernel's own reads of the segment carry-ins, by the main kernel's launch duration."""
+    res = dict(shape=(4, 16, 4096, 128, 128), spec=dict(rule="gla", name="w"), segments=4,
+               phase_ms=dict(summary=0.05, scan=0.01, main=0.1))
+    flops, nbytes = bench.prefill_work(4, 16, 4096, 128, 2)
+    roof = bench.prefill_roofline(res, flops, nbytes, 2, "0" * 64)
+    assert roof["algorithmic_bytes_per_launch"] == 343_966_208
+    assert roof["achieved"] == round(343_966_208 / 1e-4 / 1e9, 1)
+    assert roof["frac"] == round(343_966_208 / 1e-4 / 8e12, 4)
+    assert roof["kernel_bytes_with_segment_carries"] == 369_230_336
+    assert roof["traffic"] is None and roof["mfma"]["counter_busy_frac"] is None
+
+
 def test_gdn_prefill_counts():
     d = 128
     flops, nbytes = bench.prefill_work(1, 1, L, d, 2, "gdn")

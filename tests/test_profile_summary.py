@@ -2,7 +2,8 @@
 
 profile_summary.py turns two rocprofv3 --pmc databases (FETCH_SIZE, WRITE_SIZE) into bytes per
 launch by scaling each counter with its reading for a streaming copy of known size; bench.py
-reports the figure only while the kernel source still hashes to the recorded value.  Both are
+reports the figure only while the library (every source, header and compile flag) still hashes
+to the recorded value.  Both are
 checked here on a small synthetic counter database with known answers.
 """
 
@@ -14,6 +15,7 @@ import sqlite3
 
 import bench
 import profile_summary as ps
+from curvature_conditioned_query_amd import build
 
 KIB = 1024.0
 CALIB_MIB = 64
@@ -57,19 +59,60 @@ def test_traffic_scaling(tmp_path):
     assert rec["hbm_write_bytes_per_launch"] == round(400.0 * KIB)
     assert rec["hbm_bytes_per_launch"] == round(1100.0 * KIB * 2.0 + 400.0 * KIB)
     assert rec["avg_duration_us_under_counters"]["fetch_run"] == 6.0
-    assert rec["source_sha256"] == bench.file_sha(str(src))
+    assert rec["library_sha256"] == build.library_sha256()
 
 
-def test_committed_records_are_read_only_for_their_source_hash():
+def test_mfma_busy_fraction(tmp_path):
+    """SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) over 1024 SIMDs x duration x 2.4 GHz."""
+    main = "void ccq::gdn_main_kernel<128, __bf16>(ccq::FwdArgs)"
+    busy = 0.25 * 1024 * 100e-6 * 2.4e9  # a quarter of the SIMD cycles of a 100 us dispatch
+    _db(tmp_path / "m.db", "SQ_VALU_MFMA_BUSY_CYCLES", [(main, 1, busy, 100_000), (main, 2, busy, 100_000)])
+    a = argparse.Namespace(db=str(tmp_path / "m.db"), kernel="gdn_main_kernel", workload="w", command="c")
+    rec = ps.mfma_summary(a)
+    assert rec["mfma_busy_frac"] == 0.25
+    assert rec["dispatches"] == 2
+    assert rec["library_sha256"] == build.library_sha256()
+
+
+def test_library_hash_covers_sources_headers_and_flags(tmp_path, monkeypatch):
+    """Any change to a source, a header or a compile flag changes the hash the records are read by."""
+    base = build.library_sha256()
+    monkeypatch.setitem(build.EXTRA, "ccq_api.cpp", ["-DCCQ_SOME_FLAG"])
+    assert build.library_sha256() != base
+    monkeypatch.delitem(build.EXTRA, "ccq_api.cpp")
+    assert build.library_sha256() == base
+    csrc = tmp_path / "csrc"
+    inc = tmp_path / "include"
+    csrc.mkdir()
+    inc.mkdir()
+    (csrc / "a.hpp").write_text("int a;\n")
+    (inc / "ccq.h").write_text("int b;\n")
+    monkeypatch.setattr(build, "CSRC", str(csrc))
+    monkeypatch.setattr(build, "INCLUDE", str(inc))
+    h1 = build.library_sha256()
+    (csrc / "a.hpp").write_text("int a2;\n")
+    h2 = build.library_sha256()
+    (inc / "ccq.h").write_text("int b2;\n")
+    h3 = build.library_sha256()
+    assert len({h1, h2, h3}) == 3
+
+
+def test_committed_records_are_read_only_for_the_library_they_were_taken_on():
     names = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "traffic_*.json")))
-    assert names
     for path in names:
         with open(path) as f:
             rec = json.load(f)
         name = os.path.basename(path)
-        assert bench.measured_traffic(name, rec["source_sha256"]) == rec["hbm_bytes_per_launch"]
+        assert bench.measured_traffic(name, rec["library_sha256"]) == rec["hbm_bytes_per_launch"]
         assert bench.measured_traffic(name, "0" * 64) is None
         # every record names the kernel source it was taken on and both counter commands
         assert os.path.exists(os.path.join(bench.ROOT, rec["source"]))
         assert "FETCH_SIZE" in rec["commands"]["fetch"] and "WRITE_SIZE" in rec["commands"]["write"]
+    for path in sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "mfma_*.json"))):
+        with open(path) as f:
+            rec = json.load(f)
+        name = os.path.basename(path)
+        assert bench.measured_mfma(name, rec["library_sha256"]) == rec["mfma_busy_frac"]
+        assert bench.measured_mfma(name, "0" * 64) is None
+        assert "SQ_VALU_MFMA_BUSY_CYCLES" in rec["command"]
     assert bench.measured_traffic("traffic_no-such-workload.json", "0" * 64) is None
