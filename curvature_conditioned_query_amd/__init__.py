@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     CcqError,
     ccq_decode_step,
     ccq_fwd_chunked,
+    ccq_fwd_chunked_noalloc,
     ccq_fwd_workspace_bytes,
     ccq_key_subspace,
     ccq_bwd_chunked,

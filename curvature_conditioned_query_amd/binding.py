@@ -23,6 +23,7 @@ _LIB = None
 # Every symbol include/ccq.h declares (kept in one place for the export test).
 EXPORTED_SYMBOLS = (
     "ccq_fwd_chunked",
+    "ccq_fwd_chunked_noalloc",
     "ccq_fwd_workspace_bytes",
     "ccq_decode_step",
     "ccq_key_subspace",
@@ -102,6 +103,8 @@ def load_library():
     i32 = ctypes.c_int32
     lib.ccq_fwd_chunked.argtypes = [ctypes.POINTER(FwdParams), vp]
     lib.ccq_fwd_chunked.restype = ctypes.c_int
+    lib.ccq_fwd_chunked_noalloc.argtypes = [ctypes.POINTER(FwdParams), vp]
+    lib.ccq_fwd_chunked_noalloc.restype = ctypes.c_int
     lib.ccq_fwd_workspace_bytes.argtypes = [ctypes.POINTER(FwdParams)]
     lib.ccq_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ccq_decode_step.argtypes = [i32, i32, i32, i32, i32, i32] + [vp] * 12 + [i32, vp]
@@ -264,6 +267,24 @@ def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
     st = lib.ccq_fwd_chunked(ctypes.byref(p), _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_fwd_chunked")
+    return o
+
+
+def ccq_fwd_chunked_noalloc(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
+                            carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
+                            stream=None, normalize_keys: bool = False, packed_cov: bool = False):
+    """ccq_fwd_chunked_noalloc through the C ABI: the prefill with the library's own device array
+    as its workspace (nothing is allocated for it; o is allocated here only when not given).
+    Returns o."""
+    import torch
+    lib = load_library()
+    if o is None:
+        o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    p = make_fwd_params(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o,
+                        carry_in, carry_out, segments, chunk, None, normalize_keys, packed_cov)
+    st = lib.ccq_fwd_chunked_noalloc(ctypes.byref(p), _stream_handle(stream))
+    if st != 0:
+        raise CcqError(st, "ccq_fwd_chunked_noalloc")
     return o
 
 

@@ -80,6 +80,54 @@ bool carry_overlaps(const ccq_fwd_params* p) {
   return ccq::carry_ranges_overlap(in, out, (size_t)p->B * p->H, (size_t)p->d_k, (p->flags & CCQ_FLAG_PACKED_COV) != 0);
 }
 
+}  // namespace
+
+namespace ccq {
+
+int fwd_resolve(const ccq_fwd_params* p, int* segments, int* chunks_per_segment) {
+  return validate_fwd(p, segments, chunks_per_segment);
+}
+
+size_t fwd_workspace_for(const ccq_fwd_params* p, int segments) { return fwd_ws_bytes(p, segments); }
+
+int fwd_launch(const ccq_fwd_params* p, int seg, int cps, void* workspace, hipStream_t stream) {
+  ccq::FwdArgs a{};
+  a.rule = p->rule;
+  a.dtype = p->dtype;
+  a.B = p->B;
+  a.H = p->H;
+  a.T = p->T;
+  a.d = p->d_k;
+  a.segments = seg;
+  a.chunks_per_segment = cps;
+  a.q = p->q;
+  a.k = p->k;
+  a.v = p->v;
+  a.log_alpha = p->log_alpha;
+  a.beta = p->beta;
+  a.w_lambda = p->w_lambda;
+  a.b_lambda = p->b_lambda;
+  a.S0 = p->S0;
+  a.C0 = p->C0;
+  a.ksum0 = p->ksum0;
+  a.n0 = p->n0;
+  a.o = p->o;
+  a.S_out = p->S_out;
+  a.C_out = p->C_out;
+  a.ksum_out = p->ksum_out;
+  a.n_out = p->n_out;
+  a.workspace = workspace;
+  a.events = p->phase_events;
+  a.flags = p->flags;
+  a.snapshot = (seg > 1 && carry_overlaps(p)) ? 1 : 0;
+  const hipError_t e = ccq::launch_fwd(a, stream);
+  return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
+}
+
+}  // namespace ccq
+
+namespace {
+
 int validate_bwd(const ccq_bwd_params* p) {
   if (!p) return CCQ_ERR_INVALID_ARG;
   if (p->rule != CCQ_RULE_GLA && p->rule != CCQ_RULE_GDN) return CCQ_ERR_INVALID_ARG;
@@ -110,7 +158,7 @@ int validate_bwd(const ccq_bwd_params* p) {
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 7; }
+int32_t ccq_abi_version(void) { return 8; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -136,37 +184,7 @@ int ccq_fwd_chunked(const ccq_fwd_params* p, void* hip_stream) {
   if (st != CCQ_OK) return st;
   const size_t need = fwd_ws_bytes(p, seg);
   if (need > 0 && (p->workspace == nullptr || p->workspace_bytes < need)) return CCQ_ERR_WORKSPACE;
-  ccq::FwdArgs a{};
-  a.rule = p->rule;
-  a.dtype = p->dtype;
-  a.B = p->B;
-  a.H = p->H;
-  a.T = p->T;
-  a.d = p->d_k;
-  a.segments = seg;
-  a.chunks_per_segment = cps;
-  a.q = p->q;
-  a.k = p->k;
-  a.v = p->v;
-  a.log_alpha = p->log_alpha;
-  a.beta = p->beta;
-  a.w_lambda = p->w_lambda;
-  a.b_lambda = p->b_lambda;
-  a.S0 = p->S0;
-  a.C0 = p->C0;
-  a.ksum0 = p->ksum0;
-  a.n0 = p->n0;
-  a.o = p->o;
-  a.S_out = p->S_out;
-  a.C_out = p->C_out;
-  a.ksum_out = p->ksum_out;
-  a.n_out = p->n_out;
-  a.workspace = p->workspace;
-  a.events = p->phase_events;
-  a.flags = p->flags;
-  a.snapshot = (seg > 1 && carry_overlaps(p)) ? 1 : 0;
-  const hipError_t e = ccq::launch_fwd(a, static_cast<hipStream_t>(hip_stream));
-  return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
+  return ccq::fwd_launch(p, seg, cps, p->workspace, static_cast<hipStream_t>(hip_stream));
 }
 
 int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d_k, int32_t d_v, const void* q,

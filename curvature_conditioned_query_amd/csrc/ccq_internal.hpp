@@ -5,7 +5,15 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ccq.h"
+
 namespace ccq {
+
+// The prefill entry points' shared host steps (ccq_api.cpp): argument validation with the
+// resolved segment split, the workspace that split needs, and the launch on a given workspace.
+int fwd_resolve(const ccq_fwd_params* p, int* segments, int* chunks_per_segment);
+size_t fwd_workspace_for(const ccq_fwd_params* p, int segments);
+int fwd_launch(const ccq_fwd_params* p, int segments, int chunks_per_segment, void* workspace, hipStream_t stream);
 
 struct DecodeArgs {
   int rule, dtype, N, H, d, flags;

@@ -21,7 +21,8 @@
  * Conventions for every entry point
  *   - All pointers are DEVICE pointers owned by the caller; the library allocates no memory,
  *     keeps no pointer after it returns and holds no global mutable state.  Calls are
- *     reentrant.
+ *     reentrant.  The one exception is ccq_fwd_chunked_noalloc, whose workspace is a device
+ *     array the library holds (see there).
  *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default stream) without any
  *     host synchronisation.  The caller keeps buffers alive until the stream has passed the
  *     call.
@@ -139,6 +140,27 @@ int ccq_fwd_chunked(const ccq_fwd_params *p, void *hip_stream);
  * only on rule, dtype, B, H, T, d_k, d_v, chunk and segments.  Returns 0 for invalid p too. */
 size_t ccq_fwd_workspace_bytes(const ccq_fwd_params *p);
 
+/* Size of the device array ccq_fwd_chunked_noalloc takes its workspace from: 64 MiB. */
+#define CCQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * ccq_fwd_chunked for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It computes exactly what
+ * ccq_fwd_chunked computes, with the same kernels, but calls no allocating routine and takes no
+ * workspace: p->workspace and p->workspace_bytes are ignored, and the workspace is a
+ * CCQ_NOALLOC_SCRATCH_BYTES device array inside the library.  Each device the library runs on
+ * holds its own copy of that array from the first such call on it until the process ends.
+ * Segments: with p->segments == 0 the library's own choice, made longer (fewer per chain) until
+ * its workspace fits the array; a p->segments whose workspace (ccq_fwd_workspace_bytes) exceeds
+ * CCQ_NOALLOC_SCRATCH_BYTES returns CCQ_ERR_WORKSPACE before anything is enqueued.  Every call
+ * on a device shares that device's array and leaves its contents behind (no call needs it to
+ * start at zero): calls that can overlap on one device -- on different streams, or from
+ * different threads -- race on it and must be serialised by the caller.  The first call on a
+ * device looks the array up (hipGetSymbolAddress) with that device current; a failed lookup
+ * returns CCQ_ERR_LAUNCH.  Other arguments, errors and semantics as ccq_fwd_chunked.
+ */
+int ccq_fwd_chunked_noalloc(const ccq_fwd_params *p, void *hip_stream);
+
 /*
  * One decode step for N sequences x H heads, state updated in place:
  *   n += 1; C += k k^T; ksum += k; Sigma q = C q / n - ksum (ksum . q) / n^2;
@@ -212,7 +234,7 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 7. */
+/* ABI version of this header: 8. */
 int32_t ccq_abi_version(void);
 
 /* Arguments of ccq_bwd_chunked.  Zero-initialise, then fill in. */

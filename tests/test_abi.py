@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 7
+    assert lib.ccq_abi_version() == 8
 
 
 def test_status_strings(lib):
@@ -86,6 +86,28 @@ def test_fwd_workspace_sizing_and_check(lib):
     # one segment per chain needs none
     assert lib.ccq_fwd_workspace_bytes(ctypes.byref(_params(B=4, H=16, T=4096, segments=1))) == 0
     assert lib.ccq_fwd_workspace_bytes(ctypes.byref(_params(B=64, H=16, T=64))) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rule=7), INVALID), (dict(B=0), INVALID), (dict(chunk=32), UNSUPPORTED), (dict(q=None), INVALID),
+    (dict(k=FAKE + 4), MISALIGNED), (dict(flags=4), INVALID), (dict(S0=FAKE), INVALID),
+])
+def test_fwd_noalloc_argument_errors(lib, kw, code):
+    """The no-allocation variant validates exactly as ccq_fwd_chunked does, before any HIP call."""
+    assert lib.ccq_fwd_chunked_noalloc(ctypes.byref(_params(**kw)), None) == code
+    assert lib.ccq_fwd_chunked_noalloc(None, None) == INVALID
+
+
+def test_fwd_noalloc_rejects_segments_beyond_its_array(lib):
+    """An explicit segment count whose workspace exceeds the 64 MiB array is refused before any
+    launch; the workspace fields are ignored (no workspace is needed or read)."""
+    scratch = 64 << 20
+    # Gated DeltaNet slots are 3 d^2 + d floats: 256 chains x 4 segments x 197,120 B > 64 MiB
+    p = _params(rule=1, beta=FAKE, B=16, H=16, T=4096, segments=4)
+    assert lib.ccq_fwd_workspace_bytes(ctypes.byref(p)) > scratch
+    assert lib.ccq_fwd_chunked_noalloc(ctypes.byref(p), None) == WORKSPACE
+    p.workspace, p.workspace_bytes = FAKE, 1 << 40  # a caller workspace does not help: it is not used
+    assert lib.ccq_fwd_chunked_noalloc(ctypes.byref(p), None) == WORKSPACE
 
 
 def _dec(lib, rule=0, dtype=1, N=2, H=2, dk=128, dv=128, flags=0, **ptrs):
