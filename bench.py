@@ -490,30 +490,48 @@ def bwd_chunk_work(d, elem_bytes, L=CHUNK):
     return flops_a, flops_b, bytes_a
 
 
-def time_bwd_chunked(steps, warmup):
-    """Chunked backward over the prefill benchmark's inputs (B = 4, H = 16, T = 4096, d = 128, bf16,
-    zero carry) with a seeded bf16 output gradient; the carry-out adjoint is zero."""
+def gdn_bwd_chunk_work(d, elem_bytes, L=CHUNK):
+    """Per 64-token chunk of the Gated DeltaNet chunked backward: algorithmic flops of pass A and pass
+    B (every matrix product counted dense, 2 m n k; pass A: the read's Q K^T, Q C_c, tril(P) K,
+    dR C_c, dR K^T, M2 K, P^T dR, M2^T Q, dR^T Q, and the rule's K K^T, K S_c^T, T X, Qc K^T, M^T dO,
+    T^T Z, dO Delta^T, dO^T (gamma Qc), Z'^T (beta gamma K), dO S_c, (dM Gam) K; pass B: K (G + G^T),
+    K S_c^T, T X, Qc K^T, dO Delta^T, M^T dO, K dS_L^T, T^T dDelta, dX Delta^T, K K^T, (dM Gam)^T Qc,
+    W_A K, W_A^T K, dX S_c, Delta dS_L, Qc S_c^T) and pass A's algorithmic HBM bytes (q, k, v, d_o,
+    log alpha, beta read; S_c, C_c, m_c, w read; qc, dq and the partial dk written, fp32; the
+    64 x 64 inverse, R_c and dG_c written in the input dtype; the chunk sums written)."""
+    flops_a = 2 * (7 * L * d * d + 14 * L * L * d)
+    flops_b = 2 * (6 * L * d * d + 11 * L * L * d)
+    bytes_a = (4 * L * d * elem_bytes + 2 * L * elem_bytes + 2 * d * d * elem_bytes + 2 * d * 4
+               + 3 * L * d * 4 + L * L * elem_bytes + 2 * d * d * elem_bytes + 4 * d * 4)
+    return flops_a, flops_b, bytes_a
+
+
+def time_bwd_chunked(steps, warmup, rule="gla"):
+    """Chunked backward over a prefill benchmark's inputs (B = 4, H = 16, T = 4096, d = 128, bf16,
+    zero carry; GLA on the headline prefill's inputs, Gated DeltaNet on its own prefill's) with a
+    seeded bf16 output gradient; the carry-out adjoint is zero."""
     import torch
     from curvature_conditioned_query_amd import ccq_bwd_chunked, load_library
     from curvature_conditioned_query_amd.inputs import WORKLOADS, workload_inputs
     load_library()
-    spec = WORKLOADS[1]
-    x = workload_inputs(1)
+    wl = 1 if rule == "gla" else 2
+    x = workload_inputs(wl)
     B, H, T, dk, dv = x.shape
     bf = torch.bfloat16
     q, k, v, g = (to_dev(a, bf) for a in (x.q, x.k, x.v, x.g))
+    beta = None if x.beta is None else to_dev(x.beta, bf)
     w = torch.from_numpy(x.w_lam).cuda()
     b = torch.from_numpy(x.b_lam).cuda()
     del x
     gen = torch.Generator(device="cuda").manual_seed(1007)
     do = torch.randn((B, H, T, dv), generator=gen, device="cuda").to(bf)
-    out = ccq_bwd_chunked("gla", q, k, v, g, w, b, do)  # allocates the outputs and sizes the workspace
-    ws = torch.empty(int(_ws_bytes_bwd(B, H, T, dk)), dtype=torch.uint8, device="cuda")
+    out = ccq_bwd_chunked(rule, q, k, v, g, w, b, do, beta=beta)  # allocates the outputs
+    ws = torch.empty(int(_ws_bytes_bwd(B, H, T, dk, rule)), dtype=torch.uint8, device="cuda")
     hip = HipEvents(5 * steps)
 
     def step(i=None):
         pe = None if i is None else hip.slice(5 * i, 5)
-        return ccq_bwd_chunked("gla", q, k, v, g, w, b, do, workspace=ws, phase_events=pe)
+        return ccq_bwd_chunked(rule, q, k, v, g, w, b, do, workspace=ws, phase_events=pe, beta=beta)
 
     for _ in range(warmup):
         step()
@@ -533,19 +551,53 @@ def time_bwd_chunked(steps, warmup):
               for a, name in enumerate(("carries", "pass_a", "scan", "pass_b"))}
     hip.destroy()
     del out
-    return dict(name=f"ccq-gla-bwd-chunked-B{B}H{H}T{T}d{dk}-bf16", shape=(B, H, T, dk, dv), ms=ms, phase_ms=phases,
-                chunks=B * H * ((T + CHUNK - 1) // CHUNK))
+    return dict(name=f"ccq-{rule}-bwd-chunked-B{B}H{H}T{T}d{dk}-bf16", shape=(B, H, T, dk, dv), ms=ms,
+                phase_ms=phases, chunks=B * H * ((T + CHUNK - 1) // CHUNK), rule=rule)
 
 
-def _ws_bytes_bwd(B, H, T, d):
+def _ws_bytes_bwd(B, H, T, d, rule="gla"):
     import ctypes
     from curvature_conditioned_query_amd.binding import BwdParams, load_library
     p = BwdParams()
-    p.rule, p.dtype, p.B, p.H, p.T, p.d_k, p.d_v, p.chunk = 0, 1, B, H, T, d, d, CHUNK
-    for n in ("q", "k", "v", "log_alpha", "w_lambda", "b_lambda", "d_o", "dq", "dk", "dv", "dlog_alpha",
-              "dw_lambda", "db_lambda"):
+    p.rule, p.dtype, p.B, p.H, p.T, p.d_k, p.d_v, p.chunk = (0 if rule == "gla" else 1), 1, B, H, T, d, d, CHUNK
+    names = ["q", "k", "v", "log_alpha", "w_lambda", "b_lambda", "d_o", "dq", "dk", "dv", "dlog_alpha", "dw_lambda",
+             "db_lambda"] + ([] if rule == "gla" else ["beta", "dbeta"])
+    for n in names:
         setattr(p, n, 1 << 20)  # aligned placeholders: only the size query reads this struct
     return load_library().ccq_bwd_workspace_bytes(ctypes.byref(p))
+
+
+def bwd_chunked_entry(cres, lib_sha):
+    """The JSON entry of a chunked-backward leg: time per pass, per-pass times from the library's
+    events, and pass A's roofline (algorithmic bytes and flops per chunk x chunks, over its event-timed
+    launch duration; pass B's flop rate beside it)."""
+    cB, cH, cT, cd, _ = cres["shape"]
+    fa, fb, ba = bwd_chunk_work(cd, 2) if cres["rule"] == "gla" else gdn_bwd_chunk_work(cd, 2)
+    pa = cres["phase_ms"]["pass_a"]
+    a_tf = fa * cres["chunks"] / (pa * 1e-3) / 1e12
+    a_gbs = ba * cres["chunks"] / (pa * 1e-3) / 1e9
+    pb = cres["phase_ms"]["pass_b"]
+    b_tf = fb * cres["chunks"] / (pb * 1e-3) / 1e12
+    kern = "bwd_chunk_a_kernel" if cres["rule"] == "gla" else "gdn_bwd_a_kernel"
+    print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass, {cB * cT / (cres['ms'] * 1e-3):.4g} tokens/s; "
+          "passes (ms) " + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items())
+          + f"; pass A {a_gbs:.1f} GB/s alg, {a_tf:.1f} TFLOP/s, pass B {b_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    return {
+        "workload": cres["name"], "ms_per_step": round(cres["ms"], 4),
+        "tokens_per_s": round(cB * cT / (cres["ms"] * 1e-3), 1),
+        "pass_ms": {k: round(v, 4) for k, v in cres["phase_ms"].items()},
+        "roofline": dict(bound="hbm", achieved=round(a_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(a_gbs / HBM_PEAK_GBS, 4),
+                         traffic=measured_traffic(f"traffic_{cres['name']}.json", lib_sha),
+                         kernel=f"{kern}<{cd},bf16>", avg_launch_ms=round(pa, 4),
+                         algorithmic_flops_per_launch=fa * cres["chunks"],
+                         algorithmic_bytes_per_launch=ba * cres["chunks"],
+                         intensity_flop_per_byte=round(fa / ba, 1),
+                         ridge_flop_per_byte=round(BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9), 1),
+                         mfma=dict(achieved=round(a_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                                   frac=round(a_tf / BF16_PEAK_TFLOPS, 4)),
+                         pass_b=dict(achieved=round(b_tf, 1), unit="TFLOP/s", frac=round(b_tf / BF16_PEAK_TFLOPS, 4))),
+    }
 
 
 def jacobi_sweep_flops(d):
@@ -726,9 +778,10 @@ def main(argv=None):
                   flush=True)
         return 0
     if args.bwd_chunked_only:
-        cres = time_bwd_chunked(args.steps, args.warmup)
-        print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass; passes (ms) "
-              + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items()), file=sys.stderr, flush=True)
+        for rule in ("gla", "gdn"):
+            cres = time_bwd_chunked(args.steps, args.warmup, rule=rule)
+            print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass; passes (ms) "
+                  + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items()), file=sys.stderr, flush=True)
         return 0
     if args.subspace_only:
         sres = time_subspace(5, 1)
@@ -842,33 +895,9 @@ def main(argv=None):
                   flush=True)
     if not args.no_bwd_chunked:
         cres = time_bwd_chunked(args.steps, args.warmup)
-        cB, cH, cT, cd, _ = cres["shape"]
-        fa, fb, ba = bwd_chunk_work(cd, 2)
-        pa = cres["phase_ms"]["pass_a"]
-        a_tf = fa * cres["chunks"] / (pa * 1e-3) / 1e12
-        a_gbs = ba * cres["chunks"] / (pa * 1e-3) / 1e9
-        pb = cres["phase_ms"]["pass_b"]
-        b_tf = fb * cres["chunks"] / (pb * 1e-3) / 1e12
-        out["bwd_chunked"] = {
-            "workload": cres["name"], "ms_per_step": round(cres["ms"], 4),
-            "tokens_per_s": round(cB * cT / (cres["ms"] * 1e-3), 1),
-            "pass_ms": {k: round(v, 4) for k, v in cres["phase_ms"].items()},
-            "roofline": dict(bound="hbm", achieved=round(a_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=round(a_gbs / HBM_PEAK_GBS, 4),
-                             traffic=measured_traffic(f"traffic_{cres['name']}.json", lib_sha),
-                             kernel=f"bwd_chunk_a_kernel<{cd},bf16>",
-                             avg_launch_ms=round(pa, 4), algorithmic_flops_per_launch=fa * cres["chunks"],
-                             algorithmic_bytes_per_launch=ba * cres["chunks"],
-                             intensity_flop_per_byte=round(fa / ba, 1),
-                             ridge_flop_per_byte=round(BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9), 1),
-                             mfma=dict(achieved=round(a_tf, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                                       frac=round(a_tf / BF16_PEAK_TFLOPS, 4)),
-                             pass_b=dict(achieved=round(b_tf, 1), unit="TFLOP/s",
-                                         frac=round(b_tf / BF16_PEAK_TFLOPS, 4))),
-        }
-        print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass, {cB * cT / (cres['ms'] * 1e-3):.4g} tokens/s; "
-              "passes (ms) " + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items())
-              + f"; pass A {a_gbs:.1f} GB/s alg, {a_tf:.1f} TFLOP/s, pass B {b_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        out["bwd_chunked"] = bwd_chunked_entry(cres, lib_sha)
+        gcres = time_bwd_chunked(args.steps, args.warmup, rule="gdn")
+        out["bwd_chunked_gdn"] = bwd_chunked_entry(gcres, lib_sha)
     if not args.no_subspace:
         sres = time_subspace(5, 1)
         s_tf = sres["flops"] / (sres["ms"] * 1e-3) / 1e12

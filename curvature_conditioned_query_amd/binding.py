@@ -81,6 +81,7 @@ class BwdParams(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("phase_events", ctypes.c_void_p),
         ("flags", ctypes.c_int32),
+        ("beta", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
     ]
 
 
@@ -397,24 +398,30 @@ def ccq_step_backward(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, 
 
 
 def ccq_bwd_chunked(rule, q, k, v, log_alpha, w_lambda, b_lambda, d_o, carry_in=None, carry_out_adjoint=None,
-                    want_carry_in_adjoint: bool = False, workspace=None, stream=None, phase_events=None):
+                    want_carry_in_adjoint: bool = False, workspace=None, stream=None, phase_events=None, beta=None):
     """Chunked backward of the prefill through the C ABI (see ``ccq_bwd_chunked`` in ccq.h).
-    q, k, v, log_alpha, d_o: [B, H, T, d] of one dtype; carry_in: (S0, C0, ksum0, n0) or None;
-    carry_out_adjoint: (dS_T, dC_T, dksum_T) fp32 or None.  Returns a dict of fp32 tensors dq, dk,
-    dv, dlog_alpha [B, H, T, d], dw_lambda [B, H, d], db_lambda [B, H] and, with
+    q, k, v, d_o: [B, H, T, d] of one dtype; log_alpha: [B, H, T, d] (GLA) or [B, H, T] (Gated
+    DeltaNet, with beta [B, H, T]); carry_in: (S0, C0, ksum0, n0) or None; carry_out_adjoint:
+    (dS_T, dC_T, dksum_T) fp32 or None.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha (the
+    shape of log_alpha), dbeta (Gated DeltaNet), dw_lambda [B, H, d], db_lambda [B, H] and, with
     want_carry_in_adjoint, dS0, dC0, dksum0.  ``phase_events``: optional ctypes array of 5
     hipEvent_t handles recorded around the passes."""
     import torch
     lib = load_library()
     B, H, T, d_k = q.shape
     d_v = v.shape[-1]
-    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("d_o", d_o)):
+    rule_c = _rule_code(rule)
+    gdn = rule_c == CCQ_RULE_GDN
+    if gdn != (beta is not None):
+        raise ValueError("beta is given for Gated DeltaNet and only for it")
+    for name, t in (("q", q), ("k", k), ("v", v), ("log_alpha", log_alpha), ("d_o", d_o), ("beta", beta)):
         _check_dev(name, t, q.dtype)
-        _check_numel(name, t, B * H * T * (d_v if name in ("v", "d_o") else d_k))
+        per = d_v if name in ("v", "d_o") else (1 if name == "beta" or (gdn and name == "log_alpha") else d_k)
+        _check_numel(name, t, B * H * T * per)
     _check_dev("w_lambda", w_lambda, torch.float32)
     _check_dev("b_lambda", b_lambda, torch.float32)
     p = BwdParams()
-    p.rule = _rule_code(rule)
+    p.rule = rule_c
     p.dtype = _dtype_code(q)
     p.B, p.H, p.T, p.d_k, p.d_v, p.chunk = B, H, T, d_k, d_v, 64
     p.q, p.k, p.v, p.log_alpha, p.d_o = (_ptr(x) for x in (q, k, v, log_alpha, d_o))
@@ -435,8 +442,12 @@ def ccq_bwd_chunked(rule, q, k, v, log_alpha, w_lambda, b_lambda, d_o, carry_in=
         p.dS_T, p.dC_T, p.dksum_T = _ptr(dS_T), _ptr(dC_T), _ptr(dm_T)
     f = dict(dtype=torch.float32, device=q.device)
     out = dict(dq=torch.empty((B, H, T, d_k), **f), dk=torch.empty((B, H, T, d_k), **f),
-               dv=torch.empty((B, H, T, d_v), **f), dlog_alpha=torch.empty((B, H, T, d_k), **f),
+               dv=torch.empty((B, H, T, d_v), **f),
+               dlog_alpha=torch.empty((B, H, T) if gdn else (B, H, T, d_k), **f),
                dw_lambda=torch.empty((B, H, d_k), **f), db_lambda=torch.empty((B, H), **f))
+    if gdn:
+        out["dbeta"] = torch.empty((B, H, T), **f)
+        p.beta, p.dbeta = _ptr(beta), _ptr(out["dbeta"])
     if want_carry_in_adjoint:
         out.update(dS0=torch.empty((B, H, d_v, d_k), **f), dC0=torch.empty((B, H, d_k, d_k), **f),
                    dksum0=torch.empty((B, H, d_k), **f))

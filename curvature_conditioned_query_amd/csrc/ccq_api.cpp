@@ -134,7 +134,7 @@ int validate_bwd(const ccq_bwd_params* p) {
   if (p->dtype != CCQ_DTYPE_F32 && p->dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
   if (p->B <= 0 || p->H <= 0 || p->T <= 0 || p->d_k <= 0 || p->d_v <= 0 || p->chunk < 0) return CCQ_ERR_INVALID_ARG;
   if (p->flags & ~(CCQ_FLAG_NORMALIZE_KEYS | CCQ_FLAG_PACKED_COV)) return CCQ_ERR_INVALID_ARG;
-  if (p->rule != CCQ_RULE_GLA || p->flags != 0) return CCQ_ERR_UNSUPPORTED;
+  if (p->flags != 0) return CCQ_ERR_UNSUPPORTED;
   if (p->chunk != 0 && p->chunk != kChunk) return CCQ_ERR_UNSUPPORTED;
   if (p->d_k != p->d_v || !supported_d(p->dtype, p->d_k)) return CCQ_ERR_UNSUPPORTED;
   const long long groups = (long long)p->B * p->H * ((p->T + kChunk - 1) / kChunk);
@@ -142,23 +142,30 @@ int validate_bwd(const ccq_bwd_params* p) {
   if (!p->q || !p->k || !p->v || !p->log_alpha || !p->w_lambda || !p->b_lambda || !p->d_o || !p->dq || !p->dk ||
       !p->dv || !p->dlog_alpha || !p->dw_lambda || !p->db_lambda)
     return CCQ_ERR_INVALID_ARG;
+  const bool gdn = p->rule == CCQ_RULE_GDN;
+  if (gdn != (p->beta != nullptr) || gdn != (p->dbeta != nullptr)) return CCQ_ERR_INVALID_ARG;
   const int nin = (p->S0 != nullptr) + (p->C0 != nullptr) + (p->ksum0 != nullptr) + (p->n0 != nullptr);
   const int nadj = (p->dS_T != nullptr) + (p->dC_T != nullptr) + (p->dksum_T != nullptr);
   const int nout = (p->dS0 != nullptr) + (p->dC0 != nullptr) + (p->dksum0 != nullptr);
   if ((nin != 0 && nin != 4) || (nadj != 0 && nadj != 3) || (nout != 0 && nout != 3)) return CCQ_ERR_INVALID_ARG;
   const void* ptrs[] = {p->q, p->k, p->v, p->log_alpha, p->w_lambda, p->b_lambda, p->S0, p->C0, p->ksum0, p->n0,
                         p->d_o, p->dS_T, p->dC_T, p->dksum_T, p->dq, p->dk, p->dv, p->dlog_alpha, p->dw_lambda,
-                        p->db_lambda, p->dS0, p->dC0, p->dksum0, p->workspace};
+                        p->db_lambda, p->dS0, p->dC0, p->dksum0, p->workspace, p->beta, p->dbeta};
   for (const void* q : ptrs)
     if (misaligned(q)) return CCQ_ERR_MISALIGNED;
   return CCQ_OK;
+}
+
+size_t bwd_ws_bytes(const ccq_bwd_params* p) {
+  return p->rule == CCQ_RULE_GDN ? ccq::gdn_bwd_workspace_bytes(p->B, p->H, p->T, p->d_k, p->dtype)
+                                 : ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k, p->dtype);
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 8; }
+int32_t ccq_abi_version(void) { return 9; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -259,15 +266,18 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
 
 size_t ccq_bwd_workspace_bytes(const ccq_bwd_params* p) {
   if (validate_bwd(p) != CCQ_OK) return 0;
-  return ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k, p->dtype);
+  return bwd_ws_bytes(p);
 }
 
 int ccq_bwd_chunked(const ccq_bwd_params* p, void* hip_stream) {
   const int st = validate_bwd(p);
   if (st != CCQ_OK) return st;
-  const size_t need = ccq::bwd_workspace_bytes(p->B, p->H, p->T, p->d_k, p->dtype);
+  const size_t need = bwd_ws_bytes(p);
   if (p->workspace == nullptr || p->workspace_bytes < need) return CCQ_ERR_WORKSPACE;
   ccq::BwdArgs a{};
+  a.rule = p->rule;
+  a.beta = p->beta;
+  a.dbeta = p->dbeta;
   a.dtype = p->dtype;
   a.B = p->B;
   a.H = p->H;

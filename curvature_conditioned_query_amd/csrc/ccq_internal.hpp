@@ -97,7 +97,10 @@ hipError_t launch_step_backward(const StepBackArgs& a, hipStream_t stream);
 // Chunked backward of the GLA prefill (one call after validation).  nchunks = ceil(T / 64).
 struct BwdArgs {
   int dtype, B, H, T, d, nchunks;
+  int rule;              // 0 GLA, 1 Gated DeltaNet
   const void *q, *k, *v, *log_alpha;
+  const void* beta;      // Gated DeltaNet: [B, H, T]
+  float* dbeta;          // Gated DeltaNet: [B, H, T] fp32
   const float *w_lambda, *b_lambda;
   const float *S0, *C0, *ksum0;
   const int64_t* n0;
@@ -110,6 +113,9 @@ struct BwdArgs {
 };
 size_t bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// the Gated DeltaNet chunked backward (its own translation unit)
+size_t gdn_bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
+hipError_t launch_gdn_bwd(const BwdArgs& a, hipStream_t stream);
 
 // Segment summary and scan of the GLA prefill only: the carry-in of every segment after the
 // first in its workspace slot (the chunked backward walks each segment's chunks from there, the

@@ -13,6 +13,7 @@
 #pragma once
 
 #include "ccq_device.hpp"
+#include "ccq_internal.hpp"
 
 namespace ccq {
 

@@ -234,18 +234,19 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 8. */
+/* ABI version of this header: 9. */
 int32_t ccq_abi_version(void);
 
 /* Arguments of ccq_bwd_chunked.  Zero-initialise, then fill in. */
 typedef struct {
-  int32_t rule;   /* CCQ_RULE_GLA (the only rule with a chunked backward)                        */
+  int32_t rule;   /* ccq_rule: CCQ_RULE_GLA or CCQ_RULE_GDN                                      */
   int32_t dtype;  /* ccq_dtype of q, k, v, log_alpha and d_o                                       */
   int32_t B, H, T;
   int32_t d_k, d_v;
   int32_t chunk;  /* 64, or 0 for the default (64)                                                 */
 
-  /* The forward's inputs, exactly as given to ccq_fwd_chunked (unit keys, no flags). */
+  /* The forward's inputs, exactly as given to ccq_fwd_chunked (unit keys, no flags); log_alpha is
+   * [B, H, T, d_k] for GLA and [B, H, T] for Gated DeltaNet (whose beta comes at the end). */
   const void *q, *k, *v, *log_alpha; /* [B, H, T, d] dtype                                         */
   const float *w_lambda;             /* [H, d_k]                                                    */
   const float *b_lambda;             /* [H]                                                         */
@@ -260,7 +261,7 @@ typedef struct {
   /* Gradients, fp32, written: */
   float *dq, *dk;        /* [B, H, T, d_k]                                                          */
   float *dv;             /* [B, H, T, d_v]                                                          */
-  float *dlog_alpha;     /* [B, H, T, d_k]                                                          */
+  float *dlog_alpha;     /* [B, H, T, d_k] (GLA) or [B, H, T] (Gated DeltaNet)                      */
   float *dw_lambda;      /* [B, H, d_k] per sequence: the [H, d_k] parameter's gradient is their sum */
   float *db_lambda;      /* [B, H]      per sequence                                                */
   float *dS0, *dC0, *dksum0; /* adjoint of the carry in: all NULL (not wanted) or all set          */
@@ -271,26 +272,36 @@ typedef struct {
    * carries, after them, after pass A, after the reverse scan and after pass B. */
   void *const *phase_events;
   int32_t flags;          /* must be 0                                                               */
+  /* Gated DeltaNet only (both NULL for GLA): the forward's beta [B, H, T] (dtype) and its
+   * gradient dbeta [B, H, T] (fp32, written). */
+  const void *beta;
+  float *dbeta;
 } ccq_bwd_params;
 
 /*
- * Chunked backward of ccq_fwd_chunked on the GLA rule (training; the pages train CCQ models
- * from scratch, 10100.com write-up, section "方法解析" point 3): for the loss
+ * Chunked backward of ccq_fwd_chunked, on either write rule (training; the pages train CCQ models
+ * on both backbones from scratch, 10100.com write-up, section "方法解析" point 3, gist.science
+ * summary §4): for the loss
  *   L = <d_o, o> + <dS_T, S_T> + <dC_T, C_T> + <dksum_T, ksum_T>
  * of the forward with the same inputs and carry in, it writes dL/dq, dL/dk, dL/dv,
- * dL/dlog_alpha, the per-sequence gate-parameter gradients and, when asked for, the adjoint of
- * the carry in.  The forward carry at every 64-token chunk start is recomputed (not read from
- * the forward), and each chunk's gradients follow from it and the adjoint carried back from
- * later chunks.  Results equal backpropagation through the per-token recurrence up to
- * rounding; the forward's precondition on the log decay applies.
- * Supported: rule GLA, d_k == d_v, d in {64, 128} for CCQ_DTYPE_BF16, d == 64 for
- * CCQ_DTYPE_F32, flags == 0; B * H * ceil(T / 64) < 2^31.  Returns a ccq_status.
+ * dL/dlog_alpha (and dL/dbeta for Gated DeltaNet), the per-sequence gate-parameter gradients and,
+ * when asked for, the adjoint of the carry in.  The forward carry at every 64-token chunk start is
+ * recomputed (not read from the forward), and each chunk's gradients follow from it and the
+ * adjoint carried back from later chunks: for GLA through the diagonal decay, for Gated DeltaNet
+ * through the transpose of each chunk's d_k x d_k state transition.  Results equal
+ * backpropagation through the per-token recurrence up to rounding; the forward's precondition on
+ * the GLA log decay applies.
+ * Supported: d_k == d_v, d in {64, 128} for CCQ_DTYPE_BF16, d == 64 for CCQ_DTYPE_F32,
+ * flags == 0; B * H <= 65535; B * H * ceil(T / 64) < 2^31.  beta and dbeta are set for Gated
+ * DeltaNet and NULL for GLA (else CCQ_ERR_INVALID_ARG).  Returns a ccq_status.
  */
 int ccq_bwd_chunked(const ccq_bwd_params *p, void *hip_stream);
 
-/* Bytes of device workspace ccq_bwd_chunked needs (0 for invalid p).  Depends only on dtype, B,
- * H, T and d_k: per (b, h) and 64-token chunk, the forward carry update, the carry and the
- * carried-back adjoints, and three fp32 [64, d_k] tiles (0.36 MB per chunk at d_k = 128, bf16). */
+/* Bytes of device workspace ccq_bwd_chunked needs (0 for invalid p).  Depends only on rule,
+ * dtype, B, H, T and d_k: per (b, h) and 64-token chunk, the carry and the carried-back adjoints
+ * and fp32 [64, d_k] tiles (GLA: also the forward carry update, 0.36 MB per chunk at d_k = 128,
+ * bf16; Gated DeltaNet: also the chunk's 64 x 64 triangular inverse, 0.21 MB per chunk), plus for
+ * Gated DeltaNet the prefill's segment slots. */
 size_t ccq_bwd_workspace_bytes(const ccq_bwd_params *p);
 
 #ifdef __cplusplus

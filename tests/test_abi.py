@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 8
+    assert lib.ccq_abi_version() == 9
 
 
 def test_status_strings(lib):
@@ -184,7 +184,9 @@ def _bparams(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(rule=5), INVALID), (dict(rule=1), UNSUPPORTED), (dict(dtype=3), INVALID), (dict(T=0), INVALID),
+    (dict(rule=5), INVALID), (dict(rule=1), INVALID), (dict(rule=1, beta=FAKE), INVALID),
+    (dict(rule=1, dbeta=FAKE), INVALID), (dict(beta=FAKE, dbeta=FAKE), INVALID),
+    (dict(rule=1, beta=FAKE + 2, dbeta=FAKE), MISALIGNED), (dict(dtype=3), INVALID), (dict(T=0), INVALID),
     (dict(B=-1), INVALID), (dict(chunk=-1), INVALID), (dict(chunk=128), UNSUPPORTED), (dict(flags=1), UNSUPPORTED),
     (dict(flags=2), UNSUPPORTED), (dict(flags=8), INVALID), (dict(d_k=64, d_v=128), UNSUPPORTED),
     (dict(dtype=0), UNSUPPORTED), (dict(d_k=256, d_v=256), UNSUPPORTED), (dict(B=300, H=300), UNSUPPORTED),
@@ -213,5 +215,21 @@ def test_bwd_workspace_sizing_and_check(lib):
     p.workspace, p.workspace_bytes = FAKE, need - 16
     assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == WORKSPACE
     p.workspace = None
+    assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == WORKSPACE
+
+
+def test_gdn_bwd_workspace_sizing(lib):
+    """Gated DeltaNet: the prefill's segment slots for the carry pass (about one segment per compute
+    unit: 4 per chain at 64 chains), then per chain and chunk (bf16) the bf16 carry and adjoint
+    matrices (2 d^2 each), the fp32 key sum (d) and adjoint tails (4 d), the bf16 64 x 64 triangular
+    inverse and two fp32 [64, d] tiles."""
+    p = _bparams(rule=1, beta=FAKE, dbeta=FAKE, B=4, H=16, T=4096)
+    need = lib.ccq_bwd_workspace_bytes(ctypes.byref(p))
+    d, chains, P = 128, 64, 4
+    seg = chains * P * (3 * d * d + d) * 4 + chains * 8
+    seg = (seg + 255) // 256 * 256
+    per = 2 * d * d * 2 + d * 4 + 64 * 64 * 2 + 2 * d * d * 2 + 4 * d * 4 + 2 * 64 * d * 4
+    assert need == seg + chains * 64 * per
+    p.workspace, p.workspace_bytes = FAKE, need - 16
     assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == WORKSPACE
 

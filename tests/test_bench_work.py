@@ -93,6 +93,20 @@ def test_bwd_chunk_work():
     assert ba == reads + writes == 347_136
 
 
+def test_gdn_bwd_chunk_work():
+    """Gated DeltaNet chunked backward per chunk: pass A has 7 L x d x d products (Q C_c, dR C_c,
+    dR^T Q, K S_c^T, dO^T (gamma Qc), Z'^T (beta gamma K), dO S_c) and 14 L x L x d ones; pass B 6
+    and 11.  Pass A reads q, k, v, d_o (bf16), log alpha and beta, S_c and C_c (bf16), m_c and w;
+    writes qc, dq and the partial dk (fp32), the 64 x 64 inverse, R_c and dG_c (bf16), the tails."""
+    d = 128
+    fa, fb, ba = bench.gdn_bwd_chunk_work(d, 2)
+    assert fa == 2 * (7 * L * d * d + 14 * L * L * d) == 29_360_128
+    assert fb == 2 * (6 * L * d * d + 11 * L * L * d) == 24_117_248
+    reads = 4 * L * d * 2 + 2 * L * 2 + 2 * d * d * 2 + 2 * d * 4
+    writes = 3 * L * d * 4 + L * L * 2 + 2 * d * d * 2 + 4 * d * 4
+    assert ba == reads + writes
+
+
 def test_jacobi_sweep_flops():
     d = 128
     pairs = d // 2
