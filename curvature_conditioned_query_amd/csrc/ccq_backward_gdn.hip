@@ -290,7 +290,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_walk_kernel(BwdArgs a, int P, i
     gdn_build_A<D, T>(sm, sm.Ks[0], w, NW, lane);
     if (tid >= 2 * D) gdn_key_sums<D, T>(sm, sm.Ks[0], tid - 2 * D);
     __syncthreads();
-    if (w == NW - 1) gdn_diag_inverse<D, T>(sm, lane);
+    if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
     f32x4 X[4];
     gdn_rhs<D, T, true>(sm, sm.Ks[0], [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, X);
     __syncthreads();

@@ -138,6 +138,49 @@ __device__ __forceinline__ void gdn_diag_inverse(GdnSmem<D, T>& sm, int lane) {
     *reinterpret_cast<f32x4*>(&sm.Tb[blk][i][4 * q]) = f32x4{trow[4 * q], trow[4 * q + 1], trow[4 * q + 2], trow[4 * q + 3]};
 }
 
+// One wave: (I + A_bb)^{-1} of diagonal block blk in fp32 with MFMAs.  N = A_bb is strictly lower
+// triangular, so N^16 = 0 and (I + N)^{-1} = sum_k (-N)^k = (I - N)(I + N^2)(I + N^4)(I + N^8): three
+// squarings and three products, 24 v_mfma_f32_16x16x4_f32 in a chain four products deep, instead of a
+// 15-step forward substitution.  Every product takes its B operand straight from the accumulators of
+// the previous one (element r of lane (g, l) is X[4 g + r][l], the B layout of k-slice r) and its A
+// operand from LDS: the powers are written to Tb[blk] (which receives the inverse at the end) and to an
+// upper block of As, which the kernels never use (A is strictly lower triangular).  The LDS traffic
+// stays inside the wave, whose LDS instructions complete in order, so no barrier is needed.
+template <int D, typename T>
+__device__ __forceinline__ void gdn_diag_inverse_mfma(GdnSmem<D, T>& sm, int blk, int lane) {
+  const int g = lane >> 4, l = lane & 15, base = 16 * blk;
+  constexpr int PA = kL + 4;
+  const float* N = &sm.As[base][base];
+  float* s1 = &sm.Tb[blk][0][0];                                            // pitch 20
+  // upper blocks (0,1) (0,2) (0,3) (1,2) for blocks 0..3
+  float* s2 = &sm.As[blk == 3 ? 16 : 0][blk == 3 ? 32 : 16 * (blk + 1)];   // pitch PA
+  auto mm = [&](const float* X, int px, const f32x4& y, f32x4 acc) {        // acc + X Y
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[l * px + 4 * g + r], y[r], acc, 0, 0, 0);
+    return acc;
+  };
+  auto put = [&](float* X, int px, const f32x4& v) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[(4 * g + r) * px + l] = v[r];
+  };
+  f32x4 n1, e;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    n1[r] = N[(4 * g + r) * PA + l];
+    e[r] = (4 * g + r == l ? 1.f : 0.f) - n1[r];  // I - N
+  }
+  const f32x4 n2 = mm(N, PA, n1, zero4());
+  put(s1, 20, n2);
+  e = mm(s1, 20, e, e);                     // (I - N)(I + N^2)
+  const f32x4 n4 = mm(s1, 20, n2, zero4());
+  put(s2, PA, n4);
+  e = mm(s2, PA, e, e);                     // ... (I + N^4)
+  const f32x4 n8 = mm(s2, PA, n4, zero4());
+  put(s1, 20, n8);
+  e = mm(s1, 20, e, e);                     // ... (I + N^8)
+  put(s1, 20, e);
+}
+
 // X = beta (V - gamma K S0^T) on the wave's 16 state rows (WITH_V false: V = 0).  X[b][r] at
 // token 16 b + 4 g + r, state row cw + l16; stile(t) is the tile S^T[16 t + 4 g + r][cw + l16].
 template <int D, typename T, bool WITH_V, typename STile>
@@ -367,8 +410,8 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     ccq_query_carry<D, T, 1, false>(sm, [&](int, int t) -> const f32x4& { return Cacc[t]; }, lane, R);
     lds_barrier();
 
-    // ---- inverses of the diagonal blocks (last wave), cleaned query
-    if (w == NW - 1) gdn_diag_inverse<D, T>(sm, lane);
+    // ---- inverses of the diagonal blocks (the last four waves, one block each), cleaned query
+    if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
     ccq_clean_query<D, T, 1, kSplit>(sm, Ks, sm.Qalo, R, cw, lane, [](int, int, int) { return 1.0f; });
     lds_barrier();
     if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);  // q of this chunk is no longer read
@@ -535,7 +578,7 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
     if (tid >= 2 * D) gdn_key_sums<D, T>(sm, Ks, tid - 2 * D);
     lds_barrier();
 
-    if (w == NW - 1) gdn_diag_inverse<D, T>(sm, lane);
+    if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
     f32x4 XS[4], XM[4];
     gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, XS);
     gdn_rhs<D, T, false>(sm, Ks, [&](int t) -> const f32x4& { return Macc[t]; }, cw, lane, XM);
