@@ -406,12 +406,13 @@ def time_subspace(calls, warmup, r=16):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / calls
     dmu = out[3].float().cpu().numpy()
-    sweeps = torch.empty((B, H), dtype=torch.int32, device="cuda")
-    ccq_key_subspace(C, m, n, k, r=r, needle=needle, packed_cov=True, sweeps=sweeps)
+    iters = torch.empty((B, H), dtype=torch.int32, device="cuda")
+    ccq_key_subspace(C, m, n, k, r=r, needle=needle, packed_cov=True, iters=iters)
     torch.cuda.synchronize()
-    sw = sweeps.cpu().numpy()
+    it = iters.cpu().numpy()
     return dict(name=f"ccq-key-subspace-B{B}H{H}T{T}d{d}-r{r}", ms=ms, heads=B * H, tokens=B * T,
-                delta_mu_mean=float(np.nanmean(dmu)), sweeps=sw, flops=float(sw.sum()) * jacobi_sweep_flops(d))
+                delta_mu_mean=float(np.nanmean(dmu)), iters=it,
+                flops=sum(eigen_flops(d, r, int(x)) for x in it.ravel()))
 
 
 def step_backward_bytes_per_head(d, elem_bytes):
@@ -600,13 +601,22 @@ def bwd_chunked_entry(cres, lib_sha):
     }
 
 
-def jacobi_sweep_flops(d):
-    """Algorithmic fp32 flops of one sweep of the parallel Jacobi method on a d x d symmetric
-    matrix with eigenvectors: d - 1 steps, each rotating the d/2 (d/2 - 1)/2 off-diagonal
-    2 x 2 blocks on both sides (24 flops), the d/2 diagonal blocks (4) and two rows of the
-    eigenvector matrix per pair (6 per column)."""
-    npairs = d // 2
-    return (d - 1) * (npairs * (npairs - 1) // 2 * 24 + npairs * 4 + npairs * d * 6)
+EIG_THREADS = 512  # the eigen kernel's workgroup: 512 / d lanes per eigenvalue in the multisection
+
+
+def eigen_flops(d, r, rounds):
+    """Algorithmic fp32 flops of one head's eigen-decomposition (d x d, top-r vectors) with
+    ``rounds`` multisection rounds summed over its eigenvalues: the Householder tridiagonalisation
+    (4/3 d^3, the standard count), the Sturm counts (4 flops per term, 512 / d points per round),
+    three inverse-iteration solves per vector (12 flops per row), two Gram-Schmidt passes (a dot
+    and an update, 4d flops per pair) and the back-transformation (4 flops per entry of each
+    reflector, per vector)."""
+    tri = 4 * d ** 3 // 3
+    sturm = rounds * (EIG_THREADS // d) * 4 * d
+    inv = 3 * 12 * d * r
+    mgs = 2 * (r * (r - 1) // 2) * 4 * d
+    back = sum(4 * (d - k - 1) for k in range(d - 2)) * r
+    return tri + sturm + inv + mgs + back
 
 
 # ------------------------------------------------------------------ CPU oracle leg
@@ -785,7 +795,7 @@ def main(argv=None):
         return 0
     if args.subspace_only:
         sres = time_subspace(5, 1)
-        print(f"# {sres['name']}: {sres['ms']:.3f} ms/call, sweeps {sres['sweeps'].min()}..{sres['sweeps'].max()}, "
+        print(f"# {sres['name']}: {sres['ms']:.3f} ms/call, multisection rounds per head {sres['iters'].min()}..{sres['iters'].max()}, "
               f"{sres['flops'] / (sres['ms'] * 1e-3) / 1e12:.3f} TFLOP/s", file=sys.stderr, flush=True)
         return 0
     if args.no_prefill:
@@ -904,8 +914,8 @@ def main(argv=None):
         out["subspace"] = {"workload": sres["name"], "ms_per_call": round(sres["ms"], 4),
                            "heads_per_s": round(sres["heads"] / (sres["ms"] * 1e-3), 1),
                            "delta_mu_mean": round(sres["delta_mu_mean"], 4),
-                           "sweeps": {"min": int(sres["sweeps"].min()), "max": int(sres["sweeps"].max()),
-                                      "mean": round(float(sres["sweeps"].mean()), 2)},
+                           "multisection_rounds": {"min": int(sres["iters"].min()), "max": int(sres["iters"].max()),
+                                                   "mean": round(float(sres["iters"].mean()), 2)},
                            "roofline": dict(bound="alu", achieved=round(s_tf, 3), peak=FP32_PEAK_TFLOPS,
                                             unit="TFLOP/s", frac=round(s_tf / FP32_PEAK_TFLOPS, 5),
                                             traffic=None, kernel="subspace_eigen_kernel<128> (with the "

@@ -320,11 +320,12 @@ def ccq_decode_step(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, ks
 
 
 def ccq_key_subspace(C, ksum, n, k, r: int = 16, needle=None, packed_cov: bool = False, stream=None,
-                     sweeps=None):
+                     iters=None):
     """Key-covariance subspace diagnostic through the C ABI (see ``ccq_key_subspace`` in ccq.h).
     C [B, H, d, d] (or packed [B, H, d (d + 1) / 2]), ksum [B, H, d], n [B, H] int64: the
     statistics; k [B, H, T, d]: the keys to score; needle [B, H, T] bool / uint8 or None;
-    sweeps: optional int32 [B, H] tensor that receives the Jacobi sweep counts.
+    iters: optional int32 [B, H] tensor that receives the bisection work per head (multisection
+        rounds summed over the eigenvalues).
     Returns (eigvals [B, H, d], basis [B, H, r, d], align [B, H, T], delta_mu [B, H] or None),
     allocated with torch on k's device."""
     import torch
@@ -340,9 +341,9 @@ def ccq_key_subspace(C, ksum, n, k, r: int = 16, needle=None, packed_cov: bool =
     eig = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     basis = torch.empty((B, H, r, d), dtype=torch.float32, device=dev)
     align = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-    if sweeps is not None:
-        _check_dev("sweeps", sweeps, torch.int32)
-        _check_numel("sweeps", sweeps, B * H)
+    if iters is not None:
+        _check_dev("iters", iters, torch.int32)
+        _check_numel("iters", iters, B * H)
     dmu = None
     nd = None
     if needle is not None:
@@ -351,7 +352,7 @@ def ccq_key_subspace(C, ksum, n, k, r: int = 16, needle=None, packed_cov: bool =
         _check_numel("needle", nd, B * H * T)
         dmu = torch.empty((B, H), dtype=torch.float32, device=dev)
     st = lib.ccq_key_subspace(_dtype_code(k), B, H, T, d, r, _ptr(C), _ptr(ksum), _ptr(n), _ptr(k), _ptr(nd),
-                              _ptr(eig), _ptr(basis), _ptr(align), _ptr(dmu), _ptr(sweeps),
+                              _ptr(eig), _ptr(basis), _ptr(align), _ptr(dmu), _ptr(iters),
                               FLAG_PACKED_COV if packed_cov else 0, _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_key_subspace")

@@ -165,7 +165,7 @@ size_t bwd_ws_bytes(const ccq_bwd_params* p) {
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 9; }
+int32_t ccq_abi_version(void) { return 10; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -217,7 +217,7 @@ int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d
 
 int ccq_key_subspace(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d_k, int32_t r, const float* C,
                      const float* ksum, const int64_t* n, const void* k, const uint8_t* needle, float* eigvals,
-                     float* basis, float* align, float* delta_mu, int32_t* sweeps, int32_t flags,
+                     float* basis, float* align, float* delta_mu, int32_t* iters, int32_t flags,
                      void* hip_stream) {
   if (dtype != CCQ_DTYPE_F32 && dtype != CCQ_DTYPE_BF16) return CCQ_ERR_INVALID_ARG;
   if (B <= 0 || H <= 0 || T <= 0 || d_k <= 0 || r <= 0 || r > d_k) return CCQ_ERR_INVALID_ARG;
@@ -227,11 +227,11 @@ int ccq_key_subspace(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d_k
   if ((long long)B * H > 65535LL) return CCQ_ERR_UNSUPPORTED;  // heads index the grid's y dimension
   if (!C || !ksum || !n || !k || !eigvals || !basis || !align) return CCQ_ERR_INVALID_ARG;
   if ((needle == nullptr) != (delta_mu == nullptr)) return CCQ_ERR_INVALID_ARG;
-  const void* ptrs[] = {C, ksum, n, k, needle, eigvals, basis, align, delta_mu, sweeps};
+  const void* ptrs[] = {C, ksum, n, k, needle, eigvals, basis, align, delta_mu, iters};
   for (const void* pp : ptrs)
     if (misaligned(pp)) return CCQ_ERR_MISALIGNED;
   ccq::SubspaceArgs a{dtype, B, H, T, d_k, r, flags, C, ksum, n, k, needle, eigvals, basis, align, delta_mu,
-                      sweeps};
+                      iters};
   const hipError_t e = ccq::launch_subspace(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }

@@ -77,7 +77,7 @@ struct SubspaceArgs {
   const void* k;
   const uint8_t* needle;
   float *eigvals, *basis, *align, *delta_mu;
-  int32_t* sweeps;
+  int32_t* iters;
 };
 hipError_t launch_subspace(const SubspaceArgs& a, hipStream_t stream);
 

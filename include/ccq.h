@@ -191,19 +191,21 @@ int ccq_decode_step(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t d
  *                            ([B, H, T, d_k] dtype; a_t = 0 for a zero key),
  *   delta_mu [B, H]        : mean a_t over tokens with needle[b][h][t] != 0 minus the mean over
  *                            the others (NaN when either set is empty); needle [B, H, T] uint8,
- *   sweeps  [B, H] int32   : Jacobi sweeps the head took (optional, may be NULL).
- * needle and delta_mu are both NULL (no Δμ) or both set; sweeps may be NULL; every other
+ *   iters   [B, H] int32   : bisection work of the head: the multisection rounds of its d_k
+ *                            eigenvalues, summed (0 for Sigma = 0; optional, may be NULL).
+ * needle and delta_mu are both NULL (no Δμ) or both set; iters may be NULL; every other
  * pointer is required.
  * flags: CCQ_FLAG_PACKED_COV (C packed as for the other entry points); other bits are
  * CCQ_ERR_INVALID_ARG.  1 <= r <= min(32, d_k); d_k in {64, 128}; B * H <= 65535; dtype as for
- * the other entry points.  The eigenvectors come from the cyclic Jacobi method in fp32 (to about 1e-6 of the
- * largest eigenvalue); the subspace, and with it a_t, is well defined when eigenvalue r
+ * the other entry points.  The eigen-decomposition runs in fp32: Householder tridiagonalisation,
+ * bisection on Sturm counts for the eigenvalues (to about 1e-6 of the largest), inverse
+ * iteration with Gram-Schmidt for the eigenvectors (orthonormal to about 1e-6); the subspace, and with it a_t, is well defined when eigenvalue r
  * exceeds eigenvalue r + 1.  Returns a ccq_status.
  */
 int ccq_key_subspace(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d_k, int32_t r,
                      const float *C, const float *ksum, const int64_t *n, const void *k,
                      const uint8_t *needle, float *eigvals, float *basis, float *align,
-                     float *delta_mu, int32_t *sweeps, int32_t flags, void *hip_stream);
+                     float *delta_mu, int32_t *iters, int32_t flags, void *hip_stream);
 
 /*
  * Backward of one step of the recurrence (the adjoint of ccq_decode_step), for training: the
@@ -234,7 +236,7 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
 /* Static description of a status code (never NULL). */
 const char *ccq_status_string(int32_t status);
 
-/* ABI version of this header: 9. */
+/* ABI version of this header: 10. */
 int32_t ccq_abi_version(void);
 
 /* Arguments of ccq_bwd_chunked.  Zero-initialise, then fill in. */

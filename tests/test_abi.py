@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 9
+    assert lib.ccq_abi_version() == 10
 
 
 def test_status_strings(lib):
@@ -129,9 +129,9 @@ def test_decode_argument_errors(lib, kw, code):
 
 
 def _sub(lib, dtype=1, B=2, H=2, T=100, dk=128, r=16, flags=0, **ptrs):
-    names = ["C", "ksum", "n", "k", "needle", "eigvals", "basis", "align", "delta_mu", "sweeps"]
+    names = ["C", "ksum", "n", "k", "needle", "eigvals", "basis", "align", "delta_mu", "iters"]
     vals = {n: FAKE for n in names}
-    vals["sweeps"] = None
+    vals["iters"] = None
     vals.update(ptrs)
     return lib.ccq_key_subspace(dtype, B, H, T, dk, r, *[vals[n] for n in names], flags, None)
 
@@ -142,7 +142,7 @@ def _sub(lib, dtype=1, B=2, H=2, T=100, dk=128, r=16, flags=0, **ptrs):
     (dict(B=300, H=300), UNSUPPORTED), (dict(C=None), INVALID), (dict(k=None), INVALID),
     (dict(basis=None), INVALID), (dict(align=None), INVALID), (dict(needle=None), INVALID),
     (dict(delta_mu=None), INVALID), (dict(flags=1), INVALID), (dict(flags=4), INVALID),
-    (dict(ksum=FAKE + 4), MISALIGNED), (dict(needle=FAKE + 1), MISALIGNED), (dict(sweeps=FAKE + 4), MISALIGNED),
+    (dict(ksum=FAKE + 4), MISALIGNED), (dict(needle=FAKE + 1), MISALIGNED), (dict(iters=FAKE + 4), MISALIGNED),
 ])
 def test_subspace_argument_errors(lib, kw, code):
     assert _sub(lib, **kw) == code

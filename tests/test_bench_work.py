@@ -107,11 +107,14 @@ def test_gdn_bwd_chunk_work():
     assert ba == reads + writes
 
 
-def test_jacobi_sweep_flops():
-    d = 128
-    pairs = d // 2
-    per_step = 24 * pairs * (pairs - 1) // 2 + 4 * pairs + 6 * d * pairs
-    assert bench.jacobi_sweep_flops(d) == (d - 1) * per_step == 12_419_584
+def test_eigen_flops():
+    """d = 128, r = 16, 10 multisection rounds per eigenvalue: 4/3 d^3 for the tridiagonal form,
+    4 points x 4 flops x d per round, 36 d per vector of inverse iteration, 2 x 120 pairs x 4d of
+    Gram-Schmidt, 4 r sum_{m=2}^{d-1} m of back-transformation."""
+    d, r = 128, 16
+    back = 4 * r * (d * (d - 1) // 2 - 1)
+    assert bench.eigen_flops(d, r, 10 * d) == 2_796_202 + 2_621_440 + 73_728 + 122_880 + back
+    assert bench.eigen_flops(d, r, 0) == bench.eigen_flops(d, r, 10 * d) - 2_621_440
 
 
 def test_more_than_one_gpu_is_refused():

@@ -1,8 +1,9 @@
 """Key-covariance subspace diagnostic: HIP kernels through the C ABI vs the fp64 oracle.
 
-Tolerances, derived from the fp32 Jacobi method (every rotation is exact to a few fp32 ulps of
-the matrix norm, so the eigenvalues carry an absolute error of order d * 2^-24 * lambda_max and
-an eigenvector one of that over the gap to its neighbours): eigenvalues within 2e-5 of
+Tolerances, derived from the fp32 method (the Householder reduction is backward stable to a few
+d * 2^-24 of the matrix norm, bisection adds a few ulps, so the eigenvalues carry an absolute
+error of order d * 2^-24 * lambda_max and an eigenvector one of that over the gap to its
+neighbours; Gram-Schmidt twice keeps the basis orthonormal to a few ulps): eigenvalues within 2e-5 of
 lambda_max; the rows of the basis within 2e-3 (the closest pair of the 16 leading eigenvalues of
 these keys is about 1e-2 of lambda_max apart); per-key alignment and Δμ within 1e-4 (they depend
 on the subspace only, whose gap to the rest of the spectrum is about 0.25 lambda_max).  The keys
@@ -114,6 +115,63 @@ def test_subspace_edge_cases():
     _check((w[:, :1], U[:, :1], a[:, :1], dm[:, :1]), ref, "edge head 0")
 
 
+@pytest.mark.parametrize("T,r", [(40, 32), (10, 32)])
+def test_subspace_rank_deficient(T, r):
+    """Fewer keys than channels (Sigma has rank <= T - 1, so d - T + 1 eigenvalues are zero): the
+    eigenvalues match; the basis rows are orthonormal; for T = 10 the top 32 reach into the zero
+    cluster, where any orthonormal completion is correct, so the rows that are unique (the
+    leading ones, r <= 8 here) are compared, and the alignment stays in [0, 1]."""
+    k, _ = subspace_keys(1, 2, T, 128, 360 + T, "f32", rank=4)
+    C, m, n = _stats(k)
+    w, U, a, _ = _gpu(C, m, n, k, r, None, "f32")
+    wr, Ur, _, _ = _oracle(C, m, n, k, r, None)
+    lam = np.max(np.abs(wr), axis=-1, keepdims=True)
+    ew = np.max(np.abs(w - wr) / lam)
+    G = U @ np.swapaxes(U, -1, -2)
+    eo = np.max(np.abs(G - np.eye(r)))
+    print(f"rank-deficient T={T} r={r}: eig err {ew:.2e} orthonormality {eo:.2e}", flush=True)
+    assert ew <= EIG_TOL
+    assert eo <= 1e-5
+    assert np.all((a >= -1e-6) & (a <= 1 + 1e-5))
+    lead = 4  # the keys' four leading directions are well separated from the rest
+    assert np.max(np.abs(U[..., :lead, :] - Ur[..., :lead, :])) <= BASIS_TOL
+
+
+def test_subspace_repeated_eigenvalues():
+    """Sigma = diag(values) with exact repeats (5 x3, 3 x2, then distinct values and a zero block):
+    the eigenvalues are exact to rounding, the basis rows are orthonormal, and each group of equal
+    eigenvalues is spanned correctly: the projector onto the top 3 (and top 5) rows equals the
+    coordinate projector of those channels."""
+    import torch
+    from curvature_conditioned_query_amd import ccq_key_subspace
+    d, r = 64, 8
+    vals = np.zeros(d)
+    vals[[7, 20, 41]] = 5.0
+    vals[[3, 60]] = 3.0
+    vals[[11, 12, 13]] = [2.0, 1.5, 1.0]
+    vals[30:40] = 0.25
+    n = np.array([[1000]], dtype=np.int64)
+    C = (np.diag(vals) * 1000).astype(np.float32)[None, None]
+    m = np.zeros((1, 1, d), np.float32)
+    k = np.random.default_rng(370).standard_normal((1, 1, 70, d)).astype(np.float32)
+    out = ccq_key_subspace(torch.from_numpy(C).cuda(), torch.from_numpy(m).cuda(), torch.from_numpy(n).cuda(),
+                           torch.from_numpy(k).cuda(), r=r)
+    torch.cuda.synchronize()
+    w, U = down(out[0])[0, 0], down(out[1])[0, 0]
+    ref = np.sort(vals)[::-1]
+    assert np.max(np.abs(w - ref)) <= EIG_TOL * 5.0
+    assert np.max(np.abs(U @ U.T - np.eye(r))) <= 1e-5
+    for top, chans in ((3, [7, 20, 41]), (5, [7, 20, 41, 3, 60])):
+        P = U[:top].T @ U[:top]
+        Pr = np.zeros((d, d))
+        Pr[chans, chans] = 1.0
+        e = np.max(np.abs(P - Pr))
+        print(f"repeated eigenvalues: projector onto the top {top} off by {e:.2e}", flush=True)
+        assert e <= 1e-4
+    for j, ch in zip(range(5, 8), (11, 12, 13)):  # distinct values: the unit vector itself
+        assert np.max(np.abs(U[j] - np.eye(d)[ch])) <= 1e-5
+
+
 def test_subspace_from_prefill_carry():
     """The statistics as ccq_fwd_chunked carries them (C, ksum, n after a GLA prefill of the
     keys), full and packed, feed the diagnostic; the oracle reads the same carry values."""
@@ -155,19 +213,21 @@ def test_subspace_full_size_sampled():
         _check(tuple(t[sl] for t in got), ref, f"full size head ({b},{h})")
 
 
-def test_subspace_sweep_counts():
-    """The optional sweep counts: a zero statistic (n = 0) converges in one sweep (nothing to
-    rotate), a full covariance in a handful (quadratic convergence), never at the cap."""
+@pytest.mark.parametrize("d", [64, 128])
+def test_subspace_iteration_counts(d):
+    """The optional bisection work per head: a zero statistic (n = 0) needs none; a full
+    covariance needs about log_{G+1}(2^23) rounds per eigenvalue with G = 512 / d points per
+    round (8 at d = 64, 10 at d = 128), far below the cap of 40."""
     import torch
     from curvature_conditioned_query_amd import ccq_key_subspace
-    k, _ = subspace_keys(1, 2, 300, 128, 350, "bf16")
+    k, _ = subspace_keys(1, 2, 300, d, 350, "bf16")
     C, m, n = _stats(k)
     n[0, 0] = 0
-    sw = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    it = torch.full((1, 2), -1, dtype=torch.int32, device="cuda")
     ccq_key_subspace(torch.from_numpy(C).cuda(), torch.from_numpy(m).cuda(), torch.from_numpy(n).cuda(),
-                     up(k, "bf16"), r=16, sweeps=sw)
+                     up(k, "bf16"), r=16, iters=it)
     torch.cuda.synchronize()
-    s = sw.cpu().numpy()
-    print(f"sweeps {s}", flush=True)
-    assert s[0, 0] == 1
-    assert 3 <= s[0, 1] < 24
+    s = it.cpu().numpy()
+    print(f"d={d} multisection rounds per head {s}", flush=True)
+    assert s[0, 0] == 0
+    assert 6 * d <= s[0, 1] <= 14 * d
