@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libccq.so")
-SOURCES = ["ccq_api.cpp", "ccq_decode.hip", "ccq_decode_packed.hip", "ccq_prefill.hip", "ccq_prefill_summary.hip", "ccq_prefill_gdn.hip", "ccq_prefill_gdn_summary.hip", "ccq_subspace.hip",
+SOURCES = ["ccq_api.cpp", "ccq_decode.hip", "ccq_decode_packed.hip", "ccq_prefill.hip", "ccq_prefill_summary.hip", "ccq_prefill_gdn.hip", "ccq_prefill_gdn_summary.hip", "ccq_prefill_pipe.hip", "ccq_subspace.hip",
            "ccq_step_backward.hip", "ccq_backward.hip", "ccq_backward_gdn.hip", "ccq_noalloc.hip"]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for all device code.

@@ -125,6 +125,9 @@ hipError_t launch_gla_segment_carries(const FwdArgs& a, hipStream_t stream);
 // errors are left for the caller's hipGetLastError
 void launch_gla_summary(const FwdArgs& a, hipStream_t stream);
 void launch_gla_scan(const FwdArgs& a, hipStream_t stream);
+// The pipelined GLA main kernel (d = 128, bf16, keys as given): statistics and state on
+// separate waves a chunk apart.
+hipError_t launch_gla_pipe(const FwdArgs& a, hipStream_t stream);
 
 // Bytes of one segment slot of the workspace: GLA (S, C, ksum and the segment's log decay),
 // Gated DeltaNet (S, C, ksum and the segment's d x d transition matrix).

@@ -424,8 +424,13 @@ static hipError_t launch_gla(const FwdArgs& a, hipStream_t s) {
     return hipErrorLaunchFailure;
   }
   if (record_event(a, 2, s) != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((gla_main_kernel<D, T>), dim3((unsigned)(chains * P)), block, 0, s, a);
-  const hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (D == 128 && sizeof(T) == 2 && !(a.flags & kFlagNormalizeKeys)) {
+    e = launch_gla_pipe(a, s);
+  } else {
+    hipLaunchKernelGGL((gla_main_kernel<D, T>), dim3((unsigned)(chains * P)), block, 0, s, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   return record_event(a, 3, s);
 }
