@@ -281,7 +281,8 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   constexpr bool kSplit = sizeof(T) == 2;
   __shared__ GdnSmem<D, T> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, and known to be so
   const int cw = 16 * w;  // this wave's 16 channels
   const int P = a.segments, cps = a.chunks_per_segment;
   const int chain = blockIdx.x / P, seg = blockIdx.x % P;
@@ -357,27 +358,35 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   // (lane = token).  Rows past the end of the sequence are zeroed (beta = 0 then makes their
   // deltas zero).
   auto chunk_len = [&](int c) { return min(kL, a.T - c * kL); };
-  auto dma_rows = [&](T (*dst)[PQ], const T* src, int c) {
-    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, lane);
+  auto dma_rows = [&](T (*dst)[PQ], const T* src, int c, int ln) {
+    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, ln);
   };
   float sg = 0.f, sb = 0.f;
-  auto load_gates = [&](int c) {
+  auto load_gates = [&](int c, int ln) {
     if (w == 1) {
-      const bool ok = lane < chunk_len(c);
-      const size_t i = tok0 + (size_t)c * kL + (ok ? lane : 0);
+      const bool ok = ln < chunk_len(c);
+      const size_t i = tok0 + (size_t)c * kL + (ok ? ln : 0);
       const float x = ldf(gg, i), y = ldf(bg, i);
       sg = ok ? x : 0.f;
       sb = ok ? y : 0.f;
     }
   };
   if (cbeg < cend) {
-    dma_rows(sm.Qs, qg, cbeg);
-    dma_rows(sm.Ks[cbeg & 1], kg, cbeg);
-    dma_rows(sm.Vs, vg, cbeg);
-    load_gates(cbeg);
+    dma_rows(sm.Qs, qg, cbeg, lane);
+    dma_rows(sm.Ks[cbeg & 1], kg, cbeg, lane);
+    dma_rows(sm.Vs, vg, cbeg, lane);
+    load_gates(cbeg, lane);
   }
 
   for (int ch = cbeg; ch < cend; ++ch) {
+    // lane-derived values come from the lane index recomputed (and made opaque) every chunk, so
+    // the compiler recomputes LDS addresses per chunk instead of holding them in registers across
+    // the loop (where they spill, and every reload waits behind the in-flight tile loads)
+    int lane_opaque;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_opaque));
+    const int lane = lane_opaque, g = lane >> 4, l16 = lane & 15;
+    (void)g;
+    (void)l16;
     const int t0 = ch * kL;
     const int Lc = min(kL, a.T - t0);
     T (*Ks)[PQ] = sm.Ks[ch & 1];
@@ -396,7 +405,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
       normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
       lds_barrier();
     }
-    if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1);
+    if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1, lane);
 
     // ---- gate and Gram rows (waves 0..3) and Q C0 (every wave); A = beta Gam (K K^T) below
     // the diagonal and the key sums (the other waves at d = 128, all of them at d = 64)
@@ -414,7 +423,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
     ccq_clean_query<D, T, 1, kSplit>(sm, Ks, sm.Qalo, R, cw, lane, [](int, int, int) { return 1.0f; });
     lds_barrier();
-    if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1);  // q of this chunk is no longer read
+    if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1, lane);  // q of this chunk is no longer read
 
     // ---- X = beta (V - gamma K S0^T) and Delta on the wave's columns; M = tril(Qc K^T) * Gam
     // on the lower tiles -> Pm
@@ -442,8 +451,8 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     gdn_solve<D, T>(sm, X, lane, Dl);
     lds_barrier();
     if (ch + 1 < cend) {  // v of this chunk is no longer read
-      dma_rows(sm.Vs, vg, ch + 1);
-      load_gates(ch + 1);
+      dma_rows(sm.Vs, vg, ch + 1, lane);
+      load_gates(ch + 1, lane);
     }
 
     // ---- O^T for the wave's 16 value rows: gamma * S0 Qc^T + Delta^T M^T
@@ -519,7 +528,8 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
   constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
   __shared__ GdnSmem<D, T> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cw = 16 * w;
   const int P = a.segments, cps = a.chunks_per_segment;
   const int chain = blockIdx.x / (P - 1), seg = blockIdx.x % (P - 1);
@@ -544,26 +554,30 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
   if (tid < D) sm.m0[tid] = 0.f;
 
   auto chunk_len = [&](int c) { return min(kL, a.T - c * kL); };
-  auto dma_rows = [&](T (*dst)[PQ], const T* src, int c) {
-    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, lane);
+  auto dma_rows = [&](T (*dst)[PQ], const T* src, int c, int ln) {
+    dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, ln);
   };
   float sg = 0.f, sb = 0.f;
-  auto load_gates = [&](int c) {
+  auto load_gates = [&](int c, int ln) {
     if (w == 1) {
-      const bool ok = lane < chunk_len(c);
-      const size_t i = tok0 + (size_t)c * kL + (ok ? lane : 0);
+      const bool ok = ln < chunk_len(c);
+      const size_t i = tok0 + (size_t)c * kL + (ok ? ln : 0);
       const float x = ldf(gg, i), y = ldf(bg, i);
       sg = ok ? x : 0.f;
       sb = ok ? y : 0.f;
     }
   };
   if (cbeg < cend) {
-    dma_rows(sm.Ks[cbeg & 1], kg, cbeg);
-    dma_rows(sm.Vs, vg, cbeg);
-    load_gates(cbeg);
+    dma_rows(sm.Ks[cbeg & 1], kg, cbeg, lane);
+    dma_rows(sm.Vs, vg, cbeg, lane);
+    load_gates(cbeg, lane);
   }
 
   for (int ch = cbeg; ch < cend; ++ch) {
+    // the lane index recomputed, opaque to the compiler, every chunk (as in the main kernel)
+    int lane_opaque;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_opaque));
+    const int lane = lane_opaque;
     T (*Ks)[PQ] = sm.Ks[ch & 1];
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (w == 1) gdn_gates<D, T>(sm, sg, sb, lane);
@@ -572,7 +586,7 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
       normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
       lds_barrier();
     }
-    if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1);
+    if (ch + 1 < cend) dma_rows(sm.Ks[(ch + 1) & 1], kg, ch + 1, lane);
 
     gdn_build_A<D, T>(sm, Ks, w, NW, lane);
     if (tid >= 2 * D) gdn_key_sums<D, T>(sm, Ks, tid - 2 * D);
@@ -584,8 +598,8 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
     gdn_rhs<D, T, false>(sm, Ks, [&](int t) -> const f32x4& { return Macc[t]; }, cw, lane, XM);
     lds_barrier();
     if (ch + 1 < cend) {
-      dma_rows(sm.Vs, vg, ch + 1);
-      load_gates(ch + 1);
+      dma_rows(sm.Vs, vg, ch + 1, lane);
+      load_gates(ch + 1, lane);
     }
 
     {
