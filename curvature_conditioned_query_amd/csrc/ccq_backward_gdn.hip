@@ -124,12 +124,9 @@ __device__ __forceinline__ GdnBwdLayout<T> gdn_layout(const BwdArgs& a) {
 // The chunk's gates into LDS (one wave, lane = token): beta, the chunk-local cumulative log decay lg
 // (inclusive), gamma = e^lg, beta gamma and D = e^{lg_L - lg}; tokens at or past Lc count as
 // log alpha = 0, beta = 0.  Returns gamma_L (every lane).
-template <typename T>
-__device__ __forceinline__ float chunk_gates(const T* gg, const T* bg, size_t row0, int Lc, int lane, float* lg_,
-                                             float* gam, float* beta, float* bgam, float* dd) {
-  const bool ok = lane < Lc;
-  const float x = ok ? ldf(gg, row0 + lane) : 0.f;
-  const float b = ok ? ldf(bg, row0 + lane) : 0.f;
+// chunk_gates from the token's log alpha x and beta b, already loaded (0 past the end).
+__device__ __forceinline__ float chunk_gates_from(float x, float b, int lane, float* lg_, float* gam, float* beta,
+                                                  float* bgam, float* dd) {
   float lg = x;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -144,6 +141,15 @@ __device__ __forceinline__ float chunk_gates(const T* gg, const T* bg, size_t ro
   if (bgam) bgam[lane] = b * ga;
   if (dd) dd[lane] = __expf(lgL - lg);
   return __expf(lgL);
+}
+
+template <typename T>
+__device__ __forceinline__ float chunk_gates(const T* gg, const T* bg, size_t row0, int Lc, int lane, float* lg_,
+                                             float* gam, float* beta, float* bgam, float* dd) {
+  const bool ok = lane < Lc;
+  const float x = ok ? ldf(gg, row0 + lane) : 0.f;
+  const float b = ok ? ldf(bg, row0 + lane) : 0.f;
+  return chunk_gates_from(x, b, lane, lg_, gam, beta, bgam, dd);
 }
 
 // acc = X Y for 16 x 16 fp32 blocks in LDS (fp32 MFMA, K in slices of 4: lane (g, l) supplies
@@ -519,46 +525,96 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
 // chain), two waves of 16 rows each; a wave keeps its rows transposed in MFMA accumulators
 // (dSt[a][r] at lane (g, l) = dS[v0 + l][16 a + 4 g + r]), so the running adjoint never leaves the
 // registers.  dS_end(c) replaces R_c in the workspace (input dtype).
+// The walk is software-pipelined one chunk ahead: while chunk c is applied, chunk c-1's key tile
+// and inverse stream into the other half of two LDS buffers (direct HBM -> LDS loads), its R block
+// into registers, and wave 0 forms its gates after chunk c's products; one wait and one barrier
+// per chunk.
 template <int D, typename T>
 __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
   using O = T;
   constexpr int PQ = Cfg<D, T>::PQ, PE = kL + 16 / (int)sizeof(T), NA = D / 16;
-  __shared__ T Ks[kL][PQ];
-  __shared__ T Tm[kL][PE];
-  __shared__ float dd[kL], bgam[kL];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  __shared__ T Ks[2][kL][PQ];
+  __shared__ T Tm[2][kL][PE];
+  __shared__ __align__(16) float dd[2][kL];
+  __shared__ __align__(16) float bgam[2][kL];
+  __shared__ float gLs[2];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chain = blockIdx.y, v0 = 32 * blockIdx.x + 16 * w;
   const int NC = a.nchunks;
   const size_t DD = (size_t)D * D;
   const GdnBwdLayout<T> L = gdn_layout<T>(a);
-  f32x4 dSt[NA];
+  const T* kg = static_cast<const T*>(a.k);
+  const T* gg = static_cast<const T*>(a.log_alpha);
+  const T* bg = static_cast<const T*>(a.beta);
+  auto chunk_len = [&](int c) { return min(kL, a.T - c * kL); };
+  auto row0_of = [&](int c) { return (size_t)chain * a.T + (size_t)c * kL; };
+  auto rblock = [&](int c) { return L.mat + ((size_t)chain * NC + c) * 2 * DD + (size_t)(v0 + l16) * D + 4 * g; };
+  auto issue_tiles = [&](int c, int ln) {  // chunk c's key tile and inverse into buffer c & 1
+    dma_tile<D, T, PQ>(Ks[c & 1], kg + row0_of(c) * D, chunk_len(c), w, 2, ln);
+    dma_tile<kL, T, PE>(Tm[c & 1], L.tinv + ((size_t)chain * NC + c) * kTT, kL, w, 2, ln);
+  };
+  auto gates = [&](int c, int ln, float x, float b) {  // wave 0: chunk c's D and beta gamma, gamma_L
+    const float gl = chunk_gates_from(x, b, ln, nullptr, nullptr, nullptr, bgam[c & 1], dd[c & 1]);
+    if (ln == 0) gLs[c & 1] = gl;
+  };
+  auto gate_in = [&](int c, int ln, float& x, float& b) {  // wave 0: chunk c's log alpha, beta
+    const bool ok = ln < chunk_len(c);
+    const size_t i = row0_of(c) + (ok ? ln : 0);
+    const float x_ = ldf(gg, i), b_ = ldf(bg, i);
+    x = ok ? x_ : 0.f;
+    b = ok ? b_ : 0.f;
+  };
+
+  f32x4 dSt[NA], Rv[NA];
 #pragma unroll
   for (int t = 0; t < NA; ++t)
     dSt[t] = a.dS_T ? *reinterpret_cast<const f32x4*>(a.dS_T + (size_t)chain * DD + (size_t)(v0 + l16) * D + 16 * t + 4 * g)
                     : zero4();
-  __shared__ float gL_s;
-  for (int c = NC - 1; c >= 0; --c) {
-    const size_t slot = (size_t)chain * NC + c;
-    const int t0 = c * kL, Lc = min(kL, a.T - t0);
-    const size_t row0 = (size_t)chain * a.T + t0;
-    T* Rm = L.mat + slot * 2 * DD;
-    f32x4 Rv[NA];
+  if (NC > 0) {
+    const int c = NC - 1;
+    issue_tiles(c, lane);
+    const T* R = rblock(c);
 #pragma unroll
-    for (int t = 0; t < NA; ++t) {
-      T* p = Rm + (size_t)(v0 + l16) * D + 16 * t + 4 * g;
-      Rv[t] = ld4<T>(p);
-      st4<T>(p, dSt[t]);  // dS_end(c)
-    }
-    __syncthreads();  // the previous chunk's tiles are no longer read
-    load_tile<D, T, PQ>(Ks, static_cast<const T*>(a.k) + row0 * D, Lc, tid, 128);
-    load_rows<kL, kL, T, PE>(Tm, L.tinv + slot * kTT, kL, tid, 128);
+    for (int t = 0; t < NA; ++t) Rv[t] = ld4<T>(R + 16 * t);
     if (w == 0) {
-      const float gl = chunk_gates<T>(static_cast<const T*>(a.log_alpha), static_cast<const T*>(a.beta), row0, Lc, lane,
-                                      nullptr, nullptr, nullptr, bgam, dd);
-      if (lane == 0) gL_s = gl;
+      float x, b;
+      gate_in(c, lane, x, b);
+      gates(c, lane, x, b);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const float gL = gL_s;
+    const int Lc = chunk_len(c);
+    if (Lc < kL) {  // the ragged last chunk: rows past the end of the sequence read as zeros
+      zero_tail<D, T, PQ>(Ks[c & 1], Lc, tid, 128);
+      __syncthreads();
+    }
+  }
+  for (int c = NC - 1; c >= 0; --c) {
+    // lane index recomputed per chunk (opaque), so lane-derived addresses are not held across the loop
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int gq = ln >> 4, lq = ln & 15;
+    // chunk c - 1 streams in; its R block (read before dS_end(c - 1) is stored over it) too
+    f32x4 Rn[NA];
+    float gx = 0.f, gb = 0.f;
+    if (c > 0) {
+      if (w == 0) gate_in(c - 1, ln, gx, gb);
+      issue_tiles(c - 1, ln);
+      const T* R = L.mat + ((size_t)chain * NC + c - 1) * 2 * DD + (size_t)(v0 + lq) * D + 4 * gq;
+#pragma unroll
+      for (int t = 0; t < NA; ++t) Rn[t] = ld4<T>(R + 16 * t);
+    }
+    {
+      T* R = L.mat + ((size_t)chain * NC + c) * 2 * DD + (size_t)(v0 + lq) * D + 4 * gq;
+#pragma unroll
+      for (int t = 0; t < NA; ++t) st4<T>(R + 16 * t, dSt[t]);  // dS_end(c)
+    }
+    const T (*Kc)[PQ] = Ks[c & 1];
+    const T (*Tc)[PE] = Tm[c & 1];
+    const float* ddc = dd[c & 1];
+    const float* bgc = bgam[c & 1];
+    const float gL = gLs[c & 1];
     // Y^T = K dS^T (token rows), scaled by D
     f32x4 y[4];
 #pragma unroll
@@ -567,21 +623,23 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
     for (int kk = 0; kk < D / 32; ++kk) {
       const Frag<O> b = acc_frag<O>(dSt[2 * kk], dSt[2 * kk + 1]);
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) mma(y[ti], lds_frag<O, KORD_ACC>(&Ks[0][0], PQ, 16 * ti, 32 * kk, lane), b);
+      for (int ti = 0; ti < 4; ++ti) mma(y[ti], lds_frag<O, KORD_ACC>(&Kc[0][0], PQ, 16 * ti, 32 * kk, ln), b);
     }
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[ti][r] *= dd[16 * ti + 4 * g + r];
+    for (int ti = 0; ti < 4; ++ti) {
+      const f32x4 s = *reinterpret_cast<const f32x4*>(&ddc[16 * ti + 4 * gq]);
+      y[ti] *= s;
+    }
     // Y'^T = T^T (D Y^T), scaled by beta gamma
     f32x4 yp[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) yp[ti] = zero4();
-    trilT_times_strip<O>(&Tm[0][0], PE, y, lane, yp);
+    trilT_times_strip<O>(&Tc[0][0], PE, y, ln, yp);
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) yp[ti][r] *= bgam[16 * ti + 4 * g + r];
+    for (int ti = 0; ti < 4; ++ti) {
+      const f32x4 s = *reinterpret_cast<const f32x4*>(&bgc[16 * ti + 4 * gq]);
+      yp[ti] *= s;
+    }
     // dS^T = gamma_L dS^T - K^T Y'^T + R_c^T
 #pragma unroll
     for (int t = 0; t < NA; ++t) dSt[t] = gL * dSt[t] + Rv[t];
@@ -591,9 +649,16 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
         f32x4 acc = zero4();
-        mma(acc, tile_cols<O, KORD_ACC>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane), b);
+        mma(acc, tile_cols<O, KORD_ACC>(&Kc[0][0], PQ, 32 * kk, 16 * t, ln), b);
         dSt[t] -= acc;
       }
+    }
+    if (c > 0) {
+      if (w == 0) gates(c - 1, ln, gx, gb);
+#pragma unroll
+      for (int t = 0; t < NA; ++t) Rv[t] = Rn[t];
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // chunk c - 1 has landed; chunk c's buffers are free
     }
   }
   if (a.dS0 != nullptr) {
