@@ -361,56 +361,72 @@ __global__ __launch_bounds__(4 * D) void bwd_carry_walk_kernel(BwdArgs a, int P,
   }
 }
 
-// Reverse scan over the chunks of a chain, in place, one thread per 4 floats of dS | G (the
-// adjoint matrices, input dtype) and dm | dw | db (fp32 tails): chunk c receives dS_end(c), G(c),
-// dm_after(c) (the adjoints carried back from the chunks after c and the caller's carry-out
-// adjoint); dS_end(c-1) = dS_end(c) diag(e^{B_L(c)}) + R_c.  What is left after chunk 0 is the
-// carry-in adjoint.  dw and db are summed over chunks.  Running sums in fp32.
+// Reverse scan over the chunks of a chain, in place: chunk c receives dS_end(c), G(c), dm_after(c)
+// (the adjoints carried back from the chunks after c and the caller's carry-out adjoint);
+// dS_end(c-1) = dS_end(c) diag(e^{B_L(c)}) + R_c, G and dm_after by plain sums.  What is left after
+// chunk 0 is the carry-in adjoint.  dw and db are summed over chunks.  Running sums in fp32.
+// Blocks 0 .. nmb-1 take the adjoint matrices dS | G (input dtype), one 16-byte vector per thread;
+// the last block the fp32 tails dm | dw | db, 4 floats per thread.  Which part a thread scans is
+// uniform over its block.
 template <int D, typename T>
 __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
+  constexpr int EPV = 16 / (int)sizeof(T);          // matrix elements per thread
+  constexpr int NMV = 2 * D * D / EPV;              // matrix vectors per chunk
+  constexpr int NMB = (NMV + 255) / 256;            // matrix blocks
   const int chain = blockIdx.y;
   const int NC = a.nchunks;
-  const int nf4 = (2 * D * D + 3 * D) / 4;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= nf4) return;
-  const size_t f = (size_t)idx * 4;
   const BwdLayout<T> L = layout<T>(a);
   const size_t DD = (size_t)D * D;
-  const int part = f < DD ? 0 : f < 2 * DD ? 1 : f < 2 * DD + D ? 2 : f < 2 * DD + 2 * D ? 3 : 4;
-  const size_t off = part == 0 ? f : part == 1 ? f - DD : f - 2 * DD - (size_t)D * (part - 2);
-  const int col = (int)(f % D);
-  // this thread's 4 values in chunk c: matrices (parts 0, 1) or tails (parts 2..4)
-  auto mat_at = [&](int c) { return L.mat + ((size_t)chain * NC + c) * 2 * DD + f; };
-  auto tail_at = [&](int c) { return L.tail + ((size_t)chain * NC + c) * 4 * D; };
-  f32x4 run = zero4();
-  if (part == 0 && a.dS_T) run = *reinterpret_cast<const f32x4*>(a.dS_T + (size_t)chain * DD + off);
-  if (part == 1 && a.dC_T) run = *reinterpret_cast<const f32x4*>(a.dC_T + (size_t)chain * DD + off);
-  if (part == 2 && a.dksum_T) run = *reinterpret_cast<const f32x4*>(a.dksum_T + (size_t)chain * D + off);
-  constexpr int kBatch = 8;
-  for (int c0 = NC - 1; c0 >= 0; c0 -= kBatch) {
-    f32x4 x[kBatch], bl[kBatch];
+  if ((int)blockIdx.x < NMB) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= NMV) return;
+    const size_t f = (size_t)idx * EPV;
+    float run[EPV];
+    T* x0 = L.mat + (size_t)chain * NC * 2 * DD + f;
+    if (f < DD) {  // dS: decayed by the chunk's e^{B_L} per key channel (the matrix column)
+      const float* src = a.dS_T ? a.dS_T + (size_t)chain * DD + f : nullptr;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int cc = c0 - j < 0 ? 0 : c0 - j;
-      const bool ok = c0 - j >= 0;
-      x[j] = !ok ? zero4() : part <= 1 ? ld4t<T>(mat_at(cc)) : *reinterpret_cast<const f32x4*>(tail_at(cc) + (f - 2 * DD));
-      bl[j] = (ok && part == 0) ? *reinterpret_cast<const f32x4*>(tail_at(cc) + 3 * D + col) : zero4();
-    }
+      for (int e = 0; e < EPV; ++e) run[e] = src ? src[e] : 0.f;
+      rev_scan_vec<T, true>(x0, 2 * DD, NC, L.tail + (size_t)chain * NC * 4 * D + 3 * D + f % D, 4 * (size_t)D, run);
+      if (a.dS0) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int cc = c0 - j;
-      if (cc < 0) break;
-      if (part <= 1) st4t<T>(mat_at(cc), run);
-      if (part == 2) *reinterpret_cast<f32x4*>(tail_at(cc) + (f - 2 * DD)) = run;
-      if (part == 0) run = run * f32x4{__expf(bl[j][0]), __expf(bl[j][1]), __expf(bl[j][2]), __expf(bl[j][3])};
-      run += x[j];
+        for (int e = 0; e < EPV; ++e) a.dS0[(size_t)chain * DD + f + e] = run[e];
+      }
+    } else {       // G: plain sums
+      const size_t o = f - DD;
+      const float* src = a.dC_T ? a.dC_T + (size_t)chain * DD + o : nullptr;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) run[e] = src ? src[e] : 0.f;
+      rev_scan_vec<T, false>(x0, 2 * DD, NC, nullptr, 0, run);
+      if (a.dC0) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) a.dC0[(size_t)chain * DD + o + e] = run[e];
+      }
     }
+    return;
   }
-  if (part == 0 && a.dS0) *reinterpret_cast<f32x4*>(a.dS0 + (size_t)chain * DD + off) = run;
-  if (part == 1 && a.dC0) *reinterpret_cast<f32x4*>(a.dC0 + (size_t)chain * DD + off) = run;
-  if (part == 2 && a.dksum0) *reinterpret_cast<f32x4*>(a.dksum0 + (size_t)chain * D + off) = run;
-  if (part == 3) *reinterpret_cast<f32x4*>(a.dw + (size_t)chain * D + off) = run;
-  if (part == 4 && off == 0) a.db[chain] = run[0];
+  // tails dm | dw | db: dm scanned (what is left is dksum0), dw and db only summed
+  const int idx = threadIdx.x;
+  if (idx >= 3 * D / 4) return;
+  const size_t o = (size_t)idx * 4;
+  const int part = (int)(o / D);  // 0 dm, 1 dw, 2 db
+  float run[4];
+  const float* src = (part == 0 && a.dksum_T) ? a.dksum_T + (size_t)chain * D + o : nullptr;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) run[e] = src ? src[e] : 0.f;
+  float* x0 = L.tail + (size_t)chain * NC * 4 * D + o;
+  if (part == 0) {
+    rev_scan_vec<float, false>(x0, 4 * (size_t)D, NC, nullptr, 0, run);
+    if (a.dksum0) *reinterpret_cast<f32x4*>(a.dksum0 + (size_t)chain * D + o) = f32x4{run[0], run[1], run[2], run[3]};
+  } else {  // only summed: the per-chunk values stay (pass B does not read them)
+    for (int c = 0; c < NC; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(x0 + (size_t)c * 4 * D);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) run[e] += v[e];
+    }
+    if (part == 1) *reinterpret_cast<f32x4*>(a.dw + (size_t)chain * D + (o - D)) = f32x4{run[0], run[1], run[2], run[3]};
+    if (part == 2 && o == 2 * (size_t)D) a.db[chain] = run[0];
+  }
 }
 
 namespace {
@@ -620,8 +636,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   if (record_bwd_event(a, 1, s) != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_chunk_a_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
   if (record_bwd_event(a, 2, s) != hipSuccess) return hipErrorLaunchFailure;
-  const int nf4 = (2 * D * D + 3 * D) / 4;
-  hipLaunchKernelGGL((bwd_scan_kernel<D, T>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains), dim3(256), 0, s, a);
+  const int nmb = (2 * D * D / (16 / (int)sizeof(T)) + 255) / 256;  // matrix blocks, then one tail block
+  hipLaunchKernelGGL((bwd_scan_kernel<D, T>), dim3((unsigned)(nmb + 1), (unsigned)chains), dim3(256), 0, s, a);
   if (record_bwd_event(a, 3, s) != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_chunk_b_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
   e = hipGetLastError();

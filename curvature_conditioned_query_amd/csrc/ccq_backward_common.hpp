@@ -537,5 +537,86 @@ __device__ __forceinline__ void read_adjoint(const TK* Kt, int pq, const float (
   }
 }
 
+// ---- reverse scans over the chunks of a chain (the carried-back adjoints)
+
+// The 16 / sizeof(E) elements of a 16-byte vector of type E as fp32, and back (bf16 rounded to nearest
+// even).
+template <typename E>
+__device__ __forceinline__ void unpack16(const uint4& u, float (&f)[16 / sizeof(E)]) {
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+  }
+}
+template <typename E>
+__device__ __forceinline__ uint4 pack16(const float (&f)[16 / sizeof(E)]) {
+  if constexpr (sizeof(E) == 2) {
+    const bf16x8 v = {(__bf16)f[0], (__bf16)f[1], (__bf16)f[2], (__bf16)f[3],
+                      (__bf16)f[4], (__bf16)f[5], (__bf16)f[6], (__bf16)f[7]};
+    return __builtin_bit_cast(uint4, v);
+  } else {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+}
+
+// Reverse exclusive scan, over the NC chunks of a chain, of one 16-byte vector of a per-chunk array
+// (chunk c's vector at x0 + c * stride): chunk c's vector is replaced by run, the value carried back
+// from the chunks after it (on entry: the caller's adjoint of the carry out, or zeros), and then
+// run = run * e^{dec(c)} + x(c) with dec(c) the fp32 log decays at dec0 + c * dec_stride (DECAY), or
+// run + x(c).  On return run holds what is carried back past chunk 0.  Chunks go in batches of kB
+// whose loads are all issued before the first is used (no conditional loads inside a batch, so the
+// waits are counted exactly); a shorter first batch (NC not a multiple of kB) goes one chunk at a
+// time.  Every branch depends only on NC, so the path is uniform.
+template <typename E, bool DECAY>
+__device__ __forceinline__ void rev_scan_vec(E* x0, size_t stride, int NC, const float* dec0, size_t dec_stride,
+                                             float (&run)[16 / sizeof(E)]) {
+  constexpr int N = 16 / (int)sizeof(E), kB = 8;
+  auto step = [&](int cc, uint4 xv, const float (&dl)[N]) {  // xv by value: the store below overwrites its source
+    *reinterpret_cast<uint4*>(x0 + (size_t)cc * stride) = pack16<E>(run);
+    float x[N];
+    unpack16<E>(xv, x);
+#pragma unroll
+    for (int e = 0; e < N; ++e) run[e] = (DECAY ? run[e] * __expf(dl[e]) : run[e]) + x[e];
+  };
+  auto load_dec = [&](int cc, float (&dl)[N]) {
+    if constexpr (DECAY) {
+#pragma unroll
+      for (int q = 0; q < N / 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(dec0 + (size_t)cc * dec_stride + 4 * q);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dl[4 * q + r] = v[r];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < N; ++e) dl[e] = 0.f;
+    }
+  };
+  int c = NC - 1;
+  for (; c >= 0 && (c + 1) % kB != 0; --c) {  // the ragged batch at the end, one chunk at a time
+    float dl[N];
+    load_dec(c, dl);
+    const uint4 xv = *reinterpret_cast<const uint4*>(x0 + (size_t)c * stride);
+    step(c, xv, dl);
+  }
+  for (; c >= 0; c -= kB) {  // c + 1 is a multiple of kB: chunks c, c - 1, .., c - kB + 1
+    uint4 xv[kB];
+    float dl[kB][N];
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      xv[j] = *reinterpret_cast<const uint4*>(x0 + (size_t)(c - j) * stride);
+      load_dec(c - j, dl[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < kB; ++j) step(c - j, xv[j], dl[j]);
+  }
+}
+
 }  // namespace bk
 }  // namespace ccq

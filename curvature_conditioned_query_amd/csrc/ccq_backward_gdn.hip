@@ -668,48 +668,56 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
   }
 }
 
-// The additive adjoints, one thread per 4 floats of G (D x D, input dtype, the second half of each
-// chunk's adjoint matrices) and of the tails dm | dw | db: G(c) = dC_T + sum over later chunks of
-// dG, dm_after(c) = dksum_T + sum over later chunks of dm (each replacing the chunk's own), and dw, db
-// summed over every chunk.  What is left after chunk 0 is the adjoint of the carry in.
+// The additive adjoints: G(c) = dC_T + sum over later chunks of dG (input dtype, the second half of
+// each chunk's adjoint matrices), dm_after(c) = dksum_T + sum over later chunks of dm (each replacing
+// the chunk's own), and dw, db summed over every chunk.  What is left after chunk 0 is the adjoint of
+// the carry in.  Blocks 0 .. nmb-1 take G, one 16-byte vector per thread; the last block the fp32
+// tails dm | dw | db, 4 floats per thread (the part is uniform over a block).
 template <int D, typename T>
 __global__ __launch_bounds__(256) void gdn_bwd_scan_sums_kernel(BwdArgs a) {
+  constexpr int EPV = 16 / (int)sizeof(T);
+  constexpr int NMV = D * D / EPV;
+  constexpr int NMB = (NMV + 255) / 256;
   const int chain = blockIdx.y;
   const int NC = a.nchunks;
-  const int nf4 = (D * D + 3 * D) / 4;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= nf4) return;
-  const size_t f = (size_t)idx * 4;
   const GdnBwdLayout<T> L = gdn_layout<T>(a);
   const size_t DD = (size_t)D * D;
-  const int part = f < DD ? 0 : f < DD + D ? 1 : f < DD + 2 * D ? 2 : 3;  // G, dm, dw, db
-  const size_t toff = f - DD;  // offset into a tail (parts 1..3)
-  auto mat_at = [&](int c) { return L.mat + ((size_t)chain * NC + c) * 2 * DD + DD + f; };
-  auto tail_at = [&](int c) { return L.tail + ((size_t)chain * NC + c) * 4 * D + toff; };
-  f32x4 run = zero4();
-  if (part == 0 && a.dC_T) run = *reinterpret_cast<const f32x4*>(a.dC_T + (size_t)chain * DD + f);
-  if (part == 1 && a.dksum_T) run = *reinterpret_cast<const f32x4*>(a.dksum_T + (size_t)chain * D + toff);
-  constexpr int kBatch = 8;
-  for (int c0 = NC - 1; c0 >= 0; c0 -= kBatch) {
-    f32x4 x[kBatch];
+  if ((int)blockIdx.x < NMB) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= NMV) return;
+    const size_t f = (size_t)idx * EPV;
+    float run[EPV];
+    const float* src = a.dC_T ? a.dC_T + (size_t)chain * DD + f : nullptr;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int cc = c0 - j;
-      x[j] = cc < 0 ? zero4() : part == 0 ? ld4<T>(mat_at(cc)) : *reinterpret_cast<const f32x4*>(tail_at(cc));
-    }
+    for (int e = 0; e < EPV; ++e) run[e] = src ? src[e] : 0.f;
+    rev_scan_vec<T, false>(L.mat + (size_t)chain * NC * 2 * DD + DD + f, 2 * DD, NC, nullptr, 0, run);
+    if (a.dC0) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int cc = c0 - j;
-      if (cc < 0) break;
-      if (part == 0) st4<T>(mat_at(cc), run);
-      if (part == 1) *reinterpret_cast<f32x4*>(tail_at(cc)) = run;
-      run += x[j];
+      for (int e = 0; e < EPV; ++e) a.dC0[(size_t)chain * DD + f + e] = run[e];
     }
+    return;
   }
-  if (part == 0 && a.dC0) *reinterpret_cast<f32x4*>(a.dC0 + (size_t)chain * DD + f) = run;
-  if (part == 1 && a.dksum0) *reinterpret_cast<f32x4*>(a.dksum0 + (size_t)chain * D + toff) = run;
-  if (part == 2) *reinterpret_cast<f32x4*>(a.dw + (size_t)chain * D + (toff - D)) = run;
-  if (part == 3 && toff == 2 * (size_t)D) a.db[chain] = run[0];
+  const int idx = threadIdx.x;
+  if (idx >= 3 * D / 4) return;
+  const size_t o = (size_t)idx * 4;
+  const int part = (int)(o / D);  // 0 dm, 1 dw, 2 db
+  float run[4];
+  const float* src = (part == 0 && a.dksum_T) ? a.dksum_T + (size_t)chain * D + o : nullptr;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) run[e] = src ? src[e] : 0.f;
+  float* x0 = L.tail + (size_t)chain * NC * 4 * D + o;
+  if (part == 0) {
+    rev_scan_vec<float, false>(x0, 4 * (size_t)D, NC, nullptr, 0, run);
+    if (a.dksum0) *reinterpret_cast<f32x4*>(a.dksum0 + (size_t)chain * D + o) = f32x4{run[0], run[1], run[2], run[3]};
+  } else {
+    for (int c = 0; c < NC; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(x0 + (size_t)c * 4 * D);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) run[e] += v[e];
+    }
+    if (part == 1) *reinterpret_cast<f32x4*>(a.dw + (size_t)chain * D + (o - D)) = f32x4{run[0], run[1], run[2], run[3]};
+    if (part == 2 && o == 2 * (size_t)D) a.db[chain] = run[0];
+  }
 }
 
 // ---------------------------------------------------------------- 4. pass B
@@ -1020,9 +1028,9 @@ static hipError_t launch_gdn_bwd_t(const BwdArgs& a, hipStream_t s) {
   if (rec(2) != hipSuccess) return hipErrorLaunchFailure;
   // 3. reverse scans
   hipLaunchKernelGGL((gdn_bwd_scan_s_kernel<D, T>), dim3(D / 32, (unsigned)chains), dim3(128), 0, s, a);
-  const int nf4 = (D * D + 3 * D) / 4;
-  hipLaunchKernelGGL((gdn_bwd_scan_sums_kernel<D, T>), dim3((unsigned)((nf4 + 255) / 256), (unsigned)chains),
-                     dim3(256), 0, s, a);
+  const int nmb = (D * D / (16 / (int)sizeof(T)) + 255) / 256;  // G blocks, then one tail block
+  hipLaunchKernelGGL((gdn_bwd_scan_sums_kernel<D, T>), dim3((unsigned)(nmb + 1), (unsigned)chains), dim3(256), 0,
+                     s, a);
   if (rec(3) != hipSuccess) return hipErrorLaunchFailure;
   // 4. pass B
   hipLaunchKernelGGL((gdn_bwd_b_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
