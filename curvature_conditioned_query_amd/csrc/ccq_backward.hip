@@ -432,7 +432,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(BwdArgs a) {
 namespace {
 template <int D, typename T>
 struct SmemB {
-  static constexpr int PQ = Cfg<D, T>::PQ, PTO = kL + 16 / (int)sizeof(T);
+  static constexpr int PQ = Cfg<D, T>::PQ, PTO = kL + 16 / (int)sizeof(T), NW = D / 16;
   union {
     struct {
       T K[kL][PQ];
@@ -442,21 +442,35 @@ struct SmemB {
   } u1;
   T V[kL][PQ];
   T dO[kL][PQ];
-  T Qh[kL][PQ];    // qc e^B
-  T A[kL][PTO];    // tril((qc e^B)(k e^-B)^T)
-  T Dm[kL][PTO];   // tril(dO V^T)
-  T Mst[D][PQ];    // G, then dS_end (staged with 16-byte loads)
+  union {
+    T Gm[D][PQ];   // the carried-back statistics adjoint G (read only before the tiles below are formed)
+    struct {
+      T Qh[kL][PQ];  // qc e^B
+      T A[kL][PTO];  // tril((qc e^B)(k e^-B)^T)
+      T Dm[kL][PTO]; // tril(dO V^T)
+    } t;
+  } u3;
+  T Mst[D][PQ];    // dS_end
   float eBL[D];
+  float red[NW][D];  // per-wave column sums of S_c * dS_end
 };
 }  // namespace
 
+// Pass B.  Every global read of the chunk goes out at the workgroup's start, so the chunk waits for
+// memory once: the token tiles, G and dS_end straight from HBM into LDS (direct loads), the three
+// fp32 strips of pass A and this thread's 16-byte blocks of S_c (for colsum(S_c * dS_end)) into
+// registers.
 template <int D, typename T>
 __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   using SM = SmemB<D, T>;
   using O = T;
   constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PTO = SM::PTO;
+  constexpr int EPU = 16 / (int)sizeof(T), UR = D / EPU, NP = D * UR / NT;  // S_c blocks: per row, per thread
+  static_assert(sizeof(decltype(SM::u3.t)) >= sizeof(decltype(SM::u3.Gm)), "G overlays the formed tiles");
+  static_assert(NP * NT == D * UR && NT % UR == 0, "S_c rows split evenly over the workgroup");
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), cw = 16 * w;
   const int NC = a.nchunks;
   const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
   const int t0 = c * kL, Lc = min(kL, a.T - t0);
@@ -466,17 +480,36 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   const T* Sc = L.car + slot * 2 * D * D;
   const T* dSe = L.mat + slot * 2 * D * D;
   const T* Ga = dSe + (size_t)D * D;
-  const float dma = L.tail[slot * 4 * D + cw + l16];
   const size_t sv = (slot * NW + w) * kL * 16;  // this wave's strip in the strip-major buffers
 
-  load_tile<D, T, PQ>(sm.u1.in.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.u1.in.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
-  load_rows<D, D, T, PQ>(sm.Mst, Ga, D, tid, NT);
-  f32x4 qc[4];
+  // ---- every read of the chunk, issued at once
+  dma_tile<D, T, PQ>(sm.u1.in.K, static_cast<const T*>(a.k) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.u1.in.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.V, static_cast<const T*>(a.v) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, w, NW, lane);
+#pragma unroll
+  for (int h = 0; h < D / kL; ++h) {
+    dma_tile<D, T, PQ>(&sm.u3.Gm[kL * h], Ga + (size_t)kL * h * D, kL, w, NW, lane);
+    dma_tile<D, T, PQ>(&sm.Mst[kL * h], dSe + (size_t)kL * h * D, kL, w, NW, lane);
+  }
+  f32x4 qc[4], dkp[4], qdq[4];
   load_strip_vec(L.qc + sv, lane, qc);
+  load_strip_vec(L.dkp + sv, lane, dkp);
+  load_strip_vec(L.qdq + sv, lane, qdq);
+  uint4 scb[NP];  // S_c[tid / UR + (NT / UR) p][EPU (tid % UR) ..]
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+    scb[p] = *reinterpret_cast<const uint4*>(Sc + (size_t)(tid / UR + (NT / UR) * p) * D + EPU * (tid % UR));
+  const float dma = L.tail[slot * 4 * D + cw + l16];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
+    zero_tail<D, T, PQ>(sm.u1.in.K, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.u1.in.G, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.V, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.dO, Lc, tid, NT);
+    __syncthreads();
+  }
 
   f32x4 ks[4], bs[4], dos[4], kg[4];
   {
@@ -495,13 +528,36 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     for (int ti = 0; ti < 4; ++ti) kg[ti] = zero4();
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const Frag<O> gc = tile_cols<O, KORD_CONTIG>(&sm.Mst[0][0], PQ, 32 * kk, cw, lane);  // G[c][kappa]
-      const Frag<O> gr = tile_rows<O, KORD_CONTIG>(&sm.Mst[0][0], PQ, cw, 32 * kk, lane);  // G[kappa][c]
+      const Frag<O> gc = tile_cols<O, KORD_CONTIG>(&sm.u3.Gm[0][0], PQ, 32 * kk, cw, lane);  // G[c][kappa]
+      const Frag<O> gr = tile_rows<O, KORD_CONTIG>(&sm.u3.Gm[0][0], PQ, cw, 32 * kk, lane);  // G[kappa][c]
       Frag<O> b;
 #pragma unroll
       for (int e = 0; e < 8; ++e) b.v[e] = cvt<O>(to_f32(gc.v[e]) + to_f32(gr.v[e]));
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) mma(kg[ti], tile_rows<O, KORD_CONTIG>(&sm.u1.in.K[0][0], PQ, 16 * ti, 32 * kk, lane), b);
+    }
+  }
+  // colsum(S_c * dS_end): this thread's blocks, then the lanes and waves that share its columns
+  {
+    float cs[EPU];
+#pragma unroll
+    for (int e = 0; e < EPU; ++e) cs[e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int row = tid / UR + (NT / UR) * p;
+      float sc[EPU], de[EPU];
+      unpack16<T>(scb[p], sc);
+      unpack16<T>(*reinterpret_cast<const uint4*>(&sm.Mst[row][EPU * (tid % UR)]), de);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) cs[e] += sc[e] * de[e];
+    }
+#pragma unroll
+    for (int off = UR; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) cs[e] += __shfl_xor(cs[e], off, 64);
+    if (lane < UR) {
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) sm.red[w][EPU * lane + e] = cs[e];
     }
   }
   f32x4 qh[4], ebn[4];
@@ -513,23 +569,22 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
       ebn[ti][r] = __expf(-bs[ti][r]);
     }
   __syncthreads();  // key, log-decay and G tiles fully read
-  load_rows<D, D, T, PQ>(sm.Mst, dSe, D, tid, NT);
   {
     f32x4 kh[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) kh[ti] = ks[ti] * ebn[ti];
     write_strip(&sm.u1.Kh[0][0], PQ, cw, lane, kh);
-    write_strip(&sm.Qh[0][0], PQ, cw, lane, qh);
+    write_strip(&sm.u3.t.Qh[0][0], PQ, cw, lane, qh);
   }
   __syncthreads();
   for (int idx = w; idx < 16; idx += NW) {
     const int ti = idx >> 2, tj = idx & 3;
-    const f32x4 x = tril_tile<D, O>(&sm.Qh[0][0], PQ, &sm.u1.Kh[0][0], PQ, ti, tj, lane);
+    const f32x4 x = tril_tile<D, O>(&sm.u3.t.Qh[0][0], PQ, &sm.u1.Kh[0][0], PQ, ti, tj, lane);
     const f32x4 y = tril_tile<D, O>(&sm.dO[0][0], PQ, &sm.V[0][0], PQ, ti, tj, lane);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sm.A[16 * ti + 4 * g + r][16 * tj + l16] = (T)x[r];
-      sm.Dm[16 * ti + 4 * g + r][16 * tj + l16] = (T)y[r];
+      sm.u3.t.A[16 * ti + 4 * g + r][16 * tj + l16] = (T)x[r];
+      sm.u3.t.Dm[16 * ti + 4 * g + r][16 * tj + l16] = (T)y[r];
     }
   }
   __syncthreads();
@@ -539,7 +594,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    trilT_times_strip<O>(&sm.A[0][0], PTO, dos, lane, z);
+    trilT_times_strip<O>(&sm.u3.t.A[0][0], PTO, dos, lane, z);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       const Frag<O> br = tile_rows<O, KORD_CONTIG>(&sm.Mst[0][0], PQ, cw, 32 * kk, lane);  // dS_end[cw + l][kappa]
@@ -555,7 +610,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   f32x4 dkr[4], dks[4];
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) dkr[ti] = dks[ti] = zero4();
-  trilT_times_strip<O>(&sm.Dm[0][0], PTO, qh, lane, dkr);
+  trilT_times_strip<O>(&sm.u3.t.Dm[0][0], PTO, qh, lane, dkr);
   strip_times_tile<D, O>(&sm.V[0][0], PQ, &sm.Mst[0][0], PQ, cw, lane, dks);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) {
@@ -563,27 +618,24 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
     dkr[ti] = dkr[ti] * ebn[ti] + dks[ti];
   }
   {
-    f32x4 part[4], dk[4];
-    load_strip_vec(L.dkp + sv, lane, part);
+    f32x4 dk[4];
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) dk[ti] = dkr[ti] + kg[ti] + part[ti] + dma;
+    for (int ti = 0; ti < 4; ++ti) dk[ti] = dkr[ti] + kg[ti] + dkp[ti] + dma;
     store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, dk);
   }
   // dlog alpha = revcumsum(qc dqc - k dk_rule) + e^{B_L} colsum(S_c dS_end) + sum_j k_j dk_state_j
   {
-    f32x4 z[4], out[4];
-    load_strip_vec(L.qdq + sv, lane, z);
+    f32x4 out[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-      z[ti] -= ks[ti] * dkr[ti];
+      qdq[ti] -= ks[ti] * dkr[ti];
       out[ti] = zero4();
       dks[ti] *= ks[ti];
     }
-    strip_revcumsum_add<O, false>(z, out, lane);
+    strip_revcumsum_add<O, false>(qdq, out, lane);
     float cs = 0.f;
-    for (int row = g; row < D; row += 4) cs += to_f32(Sc[(size_t)row * D + cw + l16]) * to_f32(sm.Mst[row][cw + l16]);
-    cs += __shfl_xor(cs, 16, 64);
-    cs += __shfl_xor(cs, 32, 64);
+#pragma unroll
+    for (int v = 0; v < NW; ++v) cs += sm.red[v][cw + l16];
     const float after = eBLv * cs + token_sum(dks);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) out[ti] += after;
