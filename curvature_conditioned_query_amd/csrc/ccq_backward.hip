@@ -154,7 +154,8 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   using O = T;
   constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PF = SM::PF, NA = D / 16;
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), cw = 16 * w;
   const int NC = a.nchunks;
   const int chain = blockIdx.x / NC, c = blockIdx.x % NC, h = chain % a.H;
   const int t0 = c * kL, Lc = min(kL, a.T - t0);
@@ -169,16 +170,30 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   const size_t sv = (slot * NW + w) * kL * 16;  // this wave's strip in the strip-major buffers
   const int64_t nc = (a.n0 != nullptr ? a.n0[chain] : 0) + t0;
 
-  load_tile<D, T, PQ>(sm.Q, static_cast<const T*>(a.q) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.u2.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.u1.in.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.u1.in.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
-  load_rows<D, D, T, PQ>(sm.Sst, Sc, D, tid, NT);
+  // every read of the chunk, issued at once: the token tiles and S_c straight from HBM into LDS, the
+  // wave's fragments of C_c (both products with it take them from registers) and the scalars
+  dma_tile<D, T, PQ>(sm.Q, static_cast<const T*>(a.q) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.K, static_cast<const T*>(a.k) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.u2.G, static_cast<const T*>(a.log_alpha) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.u1.in.V, static_cast<const T*>(a.v) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.u1.in.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, w, NW, lane);
+#pragma unroll
+  for (int hh = 0; hh < D / kL; ++hh) dma_tile<D, T, PQ>(&sm.Sst[kL * hh], Sc + (size_t)kL * hh * D, kL, w, NW, lane);
+  Frag<O> cf[D / 32];
+  sym_frags<D, O>(Cc, cw, lane, cf);
   const float wv = a.w_lambda[(size_t)h * D + cw + l16];
   const float mv = mc[cw + l16];
   const float b_lam = a.b_lambda[h];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
+    zero_tail<D, T, PQ>(sm.Q, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.K, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.u2.G, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.u1.in.V, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.u1.in.dO, Lc, tid, NT);
+    __syncthreads();
+  }
 
   f32x4 qs[4], ks[4], bs[4];
   {
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   }
   // the read recomputed: token scalars, P = tril(Q K^T), u and the cleaned query
   f32x4 us[4], qc[4];
-  read_forward<D, O, NW>(&sm.Q[0][0], &sm.K[0][0], PQ, sm.P, sm.red, sm.tok, Cc, wv, mv, b_lam, nc, qs, ks, tid, us,
+  read_forward<D, O, NW>(&sm.Q[0][0], &sm.K[0][0], PQ, sm.P, sm.red, sm.tok, cf, wv, mv, b_lam, nc, qs, ks, tid, us,
                          qc);
   store_strip_vec(L.qc + sv, lane, qc);
 
@@ -242,7 +257,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   }
   // the read's adjoint: dq, the chunk's statistics part of dk, dG_c = dR^T Q and the chunk sums (dR
   // is written over the V and dO tiles, tril(dR K^T) over D: none is read after this)
-  read_adjoint<D, O, NW, PF>(&sm.K[0][0], PQ, sm.P, sm.u1.dR, sm.u2.Dm, sm.red, sm.tok, sm.tok2, Cc, wv, mv, qs, ks,
+  read_adjoint<D, O, NW, PF>(&sm.K[0][0], PQ, sm.P, sm.u1.dR, sm.u2.Dm, sm.red, sm.tok, sm.tok2, cf, wv, mv, qs, ks,
                              us, dqc, tid, Lc, a.dq + row0 * D, L.dkp + sv, bmat + (size_t)D * D, tail);
   if (g == 3) tail[3 * D + cw + l16] = bs[3][3];
 }

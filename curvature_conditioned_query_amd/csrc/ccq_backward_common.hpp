@@ -235,6 +235,45 @@ __device__ __forceinline__ void strip_times_sym(const TX* X, int px, const TM* M
   }
 }
 
+// The B-operand fragments strip_times_sym takes from a symmetric D x D matrix in global memory (rows
+// cw .. cw + 15: lane (g, l) gets row cw + l, columns 32 kk + 8 g .. + 7), loaded once, with one
+// 16-byte load per fragment for bf16 (two for fp32), so that several products can share them and the
+// loads can go out long before the first product.
+template <int D, typename O>
+__device__ __forceinline__ void sym_frags(const O* M, int cw, int lane, Frag<O> (&f)[D / 32]) {
+  const O* p = M + (size_t)(cw + (lane & 15)) * D + 8 * (lane >> 4);
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    if constexpr (sizeof(O) == 2) {
+      f[kk].v = *reinterpret_cast<const bf16x8*>(p + 32 * kk);
+    } else {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(p + 32 * kk);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(p + 32 * kk + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[kk].v[e] = a[e];
+        f[kk].v[4 + e] = b[e];
+      }
+    }
+  }
+}
+
+// out += X C for the statistic carry C: from global memory (strip_times_sym), or from the wave's
+// fragments of it already in registers (sym_frags).
+template <int D, typename O, typename TX>
+__device__ __forceinline__ void strip_times_carry(const TX* X, int px, const O* C, int cw, int lane, f32x4 (&out)[4]) {
+  strip_times_sym<D, O>(X, px, C, cw, lane, out);
+}
+template <int D, typename O, typename TX>
+__device__ __forceinline__ void strip_times_carry(const TX* X, int px, const Frag<O> (&f)[D / 32], int cw, int lane,
+                                                  f32x4 (&out)[4]) {
+  (void)cw;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) mma(out[ti], tile_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), f[kk]);
+}
+
 // As strip_times_mat for a D x D matrix staged in LDS (pitch pm).
 template <int D, typename O, typename TX, typename TM>
 __device__ __forceinline__ void strip_times_tile(const TX* X, int px, const TM* M, int pm, int cw, int lane,
@@ -335,12 +374,12 @@ constexpr int pf() { return D + 4; }  // pitch of fp32 [64][D] tiles
 
 // The read of a chunk recomputed: per-token gate lambda, 1/n_i and sq_i / n_i into tok; the masked Gram
 // tile P = tril(Q K^T) (fp32) into Pt; the wave's strips of u and of the cleaned query qc.  Qt, Kt: the
-// chunk's q and k row tiles (pitch pq); Cc: the statistic carry C_c at the chunk start in global memory
-// (symmetric D x D, operand dtype); wv, mv: w_lambda and m_c at the lane's channel cw + l; nc: tokens
+// chunk's q and k row tiles (pitch pq); Cc: the statistic carry C_c at the chunk start, symmetric D x D
+// (operand dtype), in global memory or as the wave's fragments of it (sym_frags); wv, mv: w_lambda and m_c at the lane's channel cw + l; nc: tokens
 // before the chunk; qs, ks: the wave's strips of q and k.  Every thread of the workgroup calls it.
-template <int D, typename O, int NW, typename TQ>
+template <int D, typename O, int NW, typename TQ, typename CS>
 __device__ __forceinline__ void read_forward(const TQ* Qt, const TQ* Kt, int pq, float (*Pt)[PT],
-                                             float (*red)[kL][2], f32x4* tok, const O* Cc, float wv, float mv,
+                                             float (*red)[kL][2], f32x4* tok, const CS& Cc, float wv, float mv,
                                              float b_lam, int64_t nc, const f32x4 (&qs)[4], const f32x4 (&ks)[4],
                                              int tid, f32x4 (&us)[4], f32x4 (&qc)[4]) {
   constexpr int NT = 64 * NW;
@@ -389,7 +428,7 @@ __device__ __forceinline__ void read_forward(const TQ* Qt, const TQ* Kt, int pq,
   // u = (Q C_c + tril(P) K - (m_c + cumsum K) sq / n) / n,  qc = q - lambda u
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti) us[ti] = zero4();
-  strip_times_sym<D, O>(Qt, pq, Cc, cw, lane, us);
+  strip_times_carry<D, O>(Qt, pq, Cc, cw, lane, us);
   tril_times_strip<O>(&Pt[0][0], PT, ks, lane, us);
   f32x4 ck[4];  // cumulative key sum (recomputed where it is needed again: registers are short)
   strip_cumsum<O, true>(ks, ck, lane);
@@ -410,10 +449,10 @@ __device__ __forceinline__ void read_forward(const TQ* Qt, const TQ* Kt, int pq,
 // (per channel, tail[0..D), tail[D..2D)) and dlogit (tail[2D]).  dRt: fp32 [64][PF] LDS tile, written
 // after the first barrier here (so it may alias tiles the caller reads before calling); Mt: fp32
 // [64][PT] LDS tile for tril(dR K^T).  Every thread of the workgroup calls it.
-template <int D, typename O, int NW, int PF, typename TK>
+template <int D, typename O, int NW, int PF, typename TK, typename CS>
 __device__ __forceinline__ void read_adjoint(const TK* Kt, int pq, const float (*Pt)[PT], float (*dRt)[PF],
                                              float (*Mt)[PT], float (*red)[kL][2], const f32x4* tok,
-                                             float (*tok2)[2], const O* Cc, float wv, float mv,
+                                             float (*tok2)[2], const CS& Cc, float wv, float mv,
                                              const f32x4 (&qs)[4], const f32x4 (&ks)[4], const f32x4 (&us)[4],
                                              const f32x4 (&dqc)[4], int tid, int Lc, float* dq_rows, float* dkp,
                                              O* Gs, float* tail) {
@@ -479,7 +518,7 @@ __device__ __forceinline__ void read_adjoint(const TK* Kt, int pq, const float (
     f32x4 z[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) z[ti] = zero4();
-    strip_times_sym<D, O>(&dRt[0][0], PF, Cc, cw, lane, z);
+    strip_times_carry<D, O>(&dRt[0][0], PF, Cc, cw, lane, z);
     tril_times_strip<O>(&Mt[0][0], PT, ks, lane, z);
     f32x4 ck2[4];
     strip_cumsum<O, true>(ks, ck2, lane);
