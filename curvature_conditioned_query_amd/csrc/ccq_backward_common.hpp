@@ -274,6 +274,19 @@ __device__ __forceinline__ void strip_times_carry(const TX* X, int px, const Fra
     for (int ti = 0; ti < 4; ++ti) mma(out[ti], tile_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), f[kk]);
 }
 
+// As strip_times_sym for a D x D matrix staged in LDS (pitch pm): out += X M[cw .. cw + 15][:]^T, the
+// B operand read as rows of M.
+template <int D, typename O, typename TX, typename TM>
+__device__ __forceinline__ void strip_times_tile_rows(const TX* X, int px, const TM* M, int pm, int cw, int lane,
+                                                      f32x4 (&out)[4]) {
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const Frag<O> b = tile_rows<O, KORD_CONTIG>(M, pm, cw, 32 * kk, lane);
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) mma(out[ti], tile_rows<O, KORD_CONTIG>(X, px, 16 * ti, 32 * kk, lane), b);
+  }
+}
+
 // As strip_times_mat for a D x D matrix staged in LDS (pitch pm).
 template <int D, typename O, typename TX, typename TM>
 __device__ __forceinline__ void strip_times_tile(const TX* X, int px, const TM* M, int pm, int cw, int lane,

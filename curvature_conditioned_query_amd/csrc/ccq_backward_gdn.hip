@@ -358,7 +358,8 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
   using O = T;
   constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PF = SM::PF, PE = SM::PE, NA = D / 16;
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), cw = 16 * w;
   const int NC = a.nchunks;
   const int chain = blockIdx.x / NC, c = blockIdx.x % NC, h = chain % a.H;
   const int t0 = c * kL, Lc = min(kL, a.T - t0);
@@ -373,24 +374,36 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
   const size_t sv = (slot * NW + w) * kL * 16;  // this wave's strip in the strip-major buffers
   const int64_t nc = (a.n0 != nullptr ? a.n0[chain] : 0) + t0;
 
-  load_tile<D, T, PQ>(sm.u0.Q, static_cast<const T*>(a.q) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.u1.in.vq.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.u1.in.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
-  if (w == 0)
-    chunk_gates<T>(static_cast<const T*>(a.log_alpha), static_cast<const T*>(a.beta), row0, Lc, lane, sm.lg, sm.gam,
-                   sm.beta, sm.bgam, nullptr);
+  // the chunk's reads, issued together: token tiles straight from HBM into LDS, the wave's fragments of
+  // C_c (both products with it take them from registers), the gates and scalars
+  dma_tile<D, T, PQ>(sm.u0.Q, static_cast<const T*>(a.q) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.K, static_cast<const T*>(a.k) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.u1.in.vq.V, static_cast<const T*>(a.v) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.u1.in.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, w, NW, lane);
+  Frag<O> cf[D / 32];
+  sym_frags<D, O>(Cc, cw, lane, cf);
   const float wv = a.w_lambda[(size_t)h * D + cw + l16];
   const float mv = mc[cw + l16];
   const float b_lam = a.b_lambda[h];
+  if (w == 0)
+    chunk_gates<T>(static_cast<const T*>(a.log_alpha), static_cast<const T*>(a.beta), row0, Lc, lane, sm.lg, sm.gam,
+                   sm.beta, sm.bgam, nullptr);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
+    zero_tail<D, T, PQ>(sm.u0.Q, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.K, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.u1.in.vq.V, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.u1.in.dO, Lc, tid, NT);
+    __syncthreads();
+  }
 
   f32x4 qs[4], ks[4];
   read_strip(&sm.u0.Q[0][0], PQ, cw, lane, qs);
   read_strip(&sm.K[0][0], PQ, cw, lane, ks);
   // the read recomputed: token scalars, P = tril(Q K^T), u and the cleaned query
   f32x4 us[4], qc[4];
-  read_forward<D, O, NW>(&sm.u0.Q[0][0], &sm.K[0][0], PQ, sm.P, sm.red, sm.tok, Cc, wv, mv, b_lam, nc, qs, ks, tid, us,
+  read_forward<D, O, NW>(&sm.u0.Q[0][0], &sm.K[0][0], PQ, sm.P, sm.red, sm.tok, cf, wv, mv, b_lam, nc, qs, ks, tid, us,
                          qc);
   store_strip_vec(L.qc + sv, lane, qc);
   __syncthreads();  // the q tile is no longer read
@@ -513,7 +526,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
   }
   // the read's adjoint: dq, the chunk's statistics part of dk, dG_c and the chunk sums (dR is
   // written over the Qc and dO tiles, tril(dR K^T) over Z': none is read after this)
-  read_adjoint<D, O, NW, PF>(&sm.K[0][0], PQ, sm.P, sm.u1.dR, sm.u3.M2, sm.red, sm.tok, sm.tok2, Cc, wv, mv, qs, ks,
+  read_adjoint<D, O, NW, PF>(&sm.K[0][0], PQ, sm.P, sm.u1.dR, sm.u3.M2, sm.red, sm.tok, sm.tok2, cf, wv, mv, qs, ks,
                              us, dqc, tid, Lc, a.dq + row0 * D, L.dkp + sv, bmat + (size_t)D * D, tail);
 }
 
@@ -743,6 +756,7 @@ struct SmemGB {
     T AK[kL][PE];  // then strict_tril(Gam K K^T)
   } u1;
   T dM[kL][PE];    // tril(dO Delta^T), then * Gam
+  T Scs[D][PQ];    // S_c
   float red[NW][kL][4];
   float lg[kL], gam[kL], beta[kL], bgam[kL], dd[kL];
   float dlg[kL], db2[kL];
@@ -756,7 +770,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
   using O = T;
   constexpr int NW = D / 16, NT = 64 * NW, PQ = SM::PQ, PE = SM::PE;
   __shared__ SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
+  constexpr int EPU = 16 / (int)sizeof(T), NP = D * D / (EPU * NT);  // dS_end blocks per thread (the dot below)
+  static_assert(NP * EPU * NT == D * D, "dS_end splits evenly over the workgroup");
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), cw = 16 * w;
   const int NC = a.nchunks;
   const int chain = blockIdx.x / NC, c = blockIdx.x % NC;
   const int t0 = c * kL, Lc = min(kL, a.T - t0);
@@ -771,17 +788,46 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
   const size_t sv = (slot * NW + w) * kL * 16;
   const int rtok = 16 * (l16 >> 2) + 4 * g + (l16 & 3);  // the token chan_reduce16 leaves here
 
-  load_tile<D, T, PQ>(sm.K, static_cast<const T*>(a.k) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, tid, NT);
-  load_tile<D, T, PQ>(sm.vq.V, static_cast<const T*>(a.v) + row0 * D, Lc, tid, NT);
-  load_rows<kL, kL, T, PE>(sm.u0.Tm, L.tinv + slot * kTT, kL, tid, NT);
+  // the chunk's reads, issued together: token tiles, the inverse and S_c straight from HBM into LDS,
+  // the cleaned-query strip and this thread's 16-byte blocks of dS_end (for <dS_L, S_c>) into registers
+  dma_tile<D, T, PQ>(sm.K, static_cast<const T*>(a.k) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.dO, static_cast<const T*>(a.d_o) + row0 * D, Lc, w, NW, lane);
+  dma_tile<D, T, PQ>(sm.vq.V, static_cast<const T*>(a.v) + row0 * D, Lc, w, NW, lane);
+  dma_tile<kL, T, PE>(sm.u0.Tm, L.tinv + slot * kTT, kL, w, NW, lane);
+#pragma unroll
+  for (int hh = 0; hh < D / kL; ++hh) dma_tile<D, T, PQ>(&sm.Scs[kL * hh], Sc + (size_t)kL * hh * D, kL, w, NW, lane);
+  uint4 dsb[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) dsb[p] = *reinterpret_cast<const uint4*>(dSe + (size_t)(tid + NT * p) * EPU);
+  f32x4 qcs[4];
+  load_strip_vec(L.qc + sv, lane, qcs);
   float gL = 0.f;
   if (w == 0)
     gL = chunk_gates<T>(static_cast<const T*>(a.log_alpha), static_cast<const T*>(a.beta), row0, Lc, lane, sm.lg, sm.gam,
                         sm.beta, sm.bgam, sm.dd);
-  f32x4 qcs[4];
-  load_strip_vec(L.qc + sv, lane, qcs);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
+    zero_tail<D, T, PQ>(sm.K, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.dO, Lc, tid, NT);
+    zero_tail<D, T, PQ>(sm.vq.V, Lc, tid, NT);
+    __syncthreads();
+  }
+  // <dS_L, S_c>: this thread's blocks, summed over the wave (the waves' sums are added at the end)
+  {
+    float s = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int f = (tid + NT * p) * EPU;
+      float x[EPU], y[EPU];
+      unpack16<T>(dsb[p], x);
+      unpack16<T>(*reinterpret_cast<const uint4*>(&sm.Scs[f / D][f % D]), y);
+#pragma unroll
+      for (int e = 0; e < EPU; ++e) s += x[e] * y[e];
+    }
+    s = group_sum<64>(s);
+    if (lane == 0) sm.dot[w] = s;
+  }
 
   f32x4 ks[4], dos[4];
   read_strip(&sm.K[0][0], PQ, cw, lane, ks);
@@ -808,7 +854,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
     f32x4 vs[4], x[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) KS[ti] = dl[ti] = zero4();
-    strip_times_rowsT<D, O>(&sm.K[0][0], PQ, Sc, cw, lane, KS);
+    strip_times_tile_rows<D, O>(&sm.K[0][0], PQ, &sm.Scs[0][0], PQ, cw, lane, KS);
     read_strip(&sm.vq.V[0][0], PQ, cw, lane, vs);
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
@@ -904,7 +950,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
   trilT_times_strip<O>(&sm.dM[0][0], PE, qcs, lane, dkr);
   tril_times_strip<O>(&sm.u0.dA[0][0], PE, ks, lane, dkr);
   trilT_times_strip<O>(&sm.u0.dA[0][0], PE, ks, lane, dkr);
-  strip_times_mat<D, O>(&sm.dXt[0][0], PQ, Sc, cw, lane, xs);
+  strip_times_tile<D, O>(&sm.dXt[0][0], PQ, &sm.Scs[0][0], PQ, cw, lane, xs);
   strip_times_mat<D, O>(&sm.Dt[0][0], PQ, dSe, cw, lane, dsl);
 #pragma unroll
   for (int ti = 0; ti < 4; ++ti)
@@ -915,10 +961,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
       dkr[ti][r] += dsl[ti][r] - sm.bgam[i] * xs[ti][r];
     }
   {
-    f32x4 part[4], dk[4];
-    load_strip_vec(L.dkp + sv, lane, part);
+    f32x4 dkp[4], dk[4];
+    load_strip_vec(L.dkp + sv, lane, dkp);
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) dk[ti] = dkr[ti] + kg[ti] + part[ti] + dma;
+    for (int ti = 0; ti < 4; ++ti) dk[ti] = dkr[ti] + kg[ti] + dkp[ti] + dma;
     store_strip_rows<D>(a.dk + row0 * D, Lc, cw, lane, dk);
   }
   // per-token channel sums: dX . xr (dbeta), dX . KS, dO . (Qc S_c^T), k . (D Delta dS_L) (dlg)
@@ -926,7 +972,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
     f32x4 qS[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) qS[ti] = zero4();
-    strip_times_rowsT<D, O>(&sm.vq.Qc[0][0], PQ, Sc, cw, lane, qS);
+    strip_times_tile_rows<D, O>(&sm.vq.Qc[0][0], PQ, &sm.Scs[0][0], PQ, cw, lane, qS);
     float v0[16], v1[16], v2[16], v3[16];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
@@ -941,13 +987,6 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
     sm.red[w][rtok][1] = chan_reduce16(v1, l16);
     sm.red[w][rtok][2] = chan_reduce16(v2, l16);
     sm.red[w][rtok][3] = chan_reduce16(v3, l16);
-  }
-  // <dS_L, S_c>
-  {
-    float s = 0.f;
-    for (size_t e = tid; e < DD; e += NT) s += to_f32(dSe[e]) * to_f32(Sc[e]);
-    s = group_sum<64>(s);
-    if (lane == 0) sm.dot[w] = s;
   }
   __syncthreads();
   if (w == 0) {
