@@ -589,6 +589,23 @@ __device__ __forceinline__ void read_adjoint(const TK* Kt, int pq, const float (
   }
 }
 
+// Four consecutive elements of T as raw bits (8 bytes for bf16, 16 for fp32) and their fp32 values:
+// a prefetch kept raw is converted where it is used, so the load need not complete before then.
+template <typename T> struct Raw4Of { using type = uint2; };
+template <> struct Raw4Of<float> { using type = uint4; };
+template <typename T> using raw4_t = typename Raw4Of<T>::type;
+template <typename T>
+__device__ __forceinline__ raw4_t<T> ld_raw4(const T* p) { return *reinterpret_cast<const raw4_t<T>*>(p); }
+template <typename T>
+__device__ __forceinline__ f32x4 raw4_f32(const raw4_t<T>& r) {
+  if constexpr (sizeof(T) == 2) {
+    return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u), __uint_as_float(r.y << 16),
+                 __uint_as_float(r.y & 0xffff0000u)};
+  } else {
+    return f32x4{__uint_as_float(r.x), __uint_as_float(r.y), __uint_as_float(r.z), __uint_as_float(r.w)};
+  }
+}
+
 // ---- reverse scans over the chunks of a chain (the carried-back adjoints)
 
 // The 16 / sizeof(E) elements of a 16-byte vector of type E as fp32, and back (bf16 rounded to nearest

@@ -538,22 +538,25 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
 // chain), two waves of 16 rows each; a wave keeps its rows transposed in MFMA accumulators
 // (dSt[a][r] at lane (g, l) = dS[v0 + l][16 a + 4 g + r]), so the running adjoint never leaves the
 // registers.  dS_end(c) replaces R_c in the workspace (input dtype).
-// The walk is software-pipelined one chunk ahead: while chunk c is applied, chunk c-1's key tile
-// and inverse stream into the other half of two LDS buffers (direct HBM -> LDS loads), its R block
-// into registers, and wave 0 forms its gates after chunk c's products; one wait and one barrier
-// per chunk.
+// The walk is software-pipelined one chunk ahead, and every read goes straight from HBM into LDS
+// (direct loads the compiler does not wait for): while chunk c is applied, chunk c-1's key tile,
+// inverse, R block and raw gates stream into the other half of two LDS buffers.  Each wave forms the
+// chunk's gates itself (a 64-lane scan into its own LDS slots), so one wait and one barrier per
+// chunk suffice, and the wait leaves the chunk's dS_end stores in flight.
 template <int D, typename T>
 __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
   using O = T;
   constexpr int PQ = Cfg<D, T>::PQ, PE = kL + 16 / (int)sizeof(T), NA = D / 16;
+  constexpr int EPU = 16 / (int)sizeof(T), NU = kL / EPU;  // 16-byte units of a 64-token gate row
   __shared__ T Ks[2][kL][PQ];
   __shared__ T Tm[2][kL][PE];
-  __shared__ __align__(16) float dd[2][kL];
+  __shared__ T Rs[2][32][PQ];   // the workgroup's 32 rows of R_c
+  __shared__ T Gr[2][2][kL];    // raw log alpha, beta
+  __shared__ __align__(16) float dd[2][kL];    // per wave: D, beta gamma (its own copies)
   __shared__ __align__(16) float bgam[2][kL];
-  __shared__ float gLs[2];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int chain = blockIdx.y, v0 = 32 * blockIdx.x + 16 * w;
+  const int chain = blockIdx.y, r0 = 32 * blockIdx.x, v0 = r0 + 16 * w;
   const int NC = a.nchunks;
   const size_t DD = (size_t)D * D;
   const GdnBwdLayout<T> L = gdn_layout<T>(a);
@@ -562,43 +565,43 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
   const T* bg = static_cast<const T*>(a.beta);
   auto chunk_len = [&](int c) { return min(kL, a.T - c * kL); };
   auto row0_of = [&](int c) { return (size_t)chain * a.T + (size_t)c * kL; };
-  auto rblock = [&](int c) { return L.mat + ((size_t)chain * NC + c) * 2 * DD + (size_t)(v0 + l16) * D + 4 * g; };
-  auto issue_tiles = [&](int c, int ln) {  // chunk c's key tile and inverse into buffer c & 1
+  auto rmat = [&](int c) { return L.mat + ((size_t)chain * NC + c) * 2 * DD; };
+  // chunk c's key tile, inverse and R block into buffer c & 1 (both waves), its raw gates (wave 0;
+  // a whole chunk only: the ragged last chunk's gates are written in the prologue)
+  auto issue = [&](int c, int ln) {
     dma_tile<D, T, PQ>(Ks[c & 1], kg + row0_of(c) * D, chunk_len(c), w, 2, ln);
     dma_tile<kL, T, PE>(Tm[c & 1], L.tinv + ((size_t)chain * NC + c) * kTT, kL, w, 2, ln);
-  };
-  auto gates = [&](int c, int ln, float x, float b) {  // wave 0: chunk c's D and beta gamma, gamma_L
-    const float gl = chunk_gates_from(x, b, ln, nullptr, nullptr, nullptr, bgam[c & 1], dd[c & 1]);
-    if (ln == 0) gLs[c & 1] = gl;
-  };
-  auto gate_in = [&](int c, int ln, float& x, float& b) {  // wave 0: chunk c's log alpha, beta
-    const bool ok = ln < chunk_len(c);
-    const size_t i = row0_of(c) + (ok ? ln : 0);
-    const float x_ = ldf(gg, i), b_ = ldf(bg, i);
-    x = ok ? x_ : 0.f;
-    b = ok ? b_ : 0.f;
+    dma_block<D, T, PQ, 32>(Rs[c & 1], rmat(c) + (size_t)r0 * D, w, 2, ln);
+    if (w == 0 && ln < 2 * NU) {
+      const T* src = ln < NU ? gg + row0_of(c) + EPU * ln : bg + row0_of(c) + EPU * (ln - NU);
+      dma_lane(&Gr[c & 1][0][0], src);
+    }
   };
 
-  f32x4 dSt[NA], Rv[NA];
+  f32x4 dSt[NA];
 #pragma unroll
   for (int t = 0; t < NA; ++t)
     dSt[t] = a.dS_T ? *reinterpret_cast<const f32x4*>(a.dS_T + (size_t)chain * DD + (size_t)(v0 + l16) * D + 16 * t + 4 * g)
                     : zero4();
   if (NC > 0) {
-    const int c = NC - 1;
-    issue_tiles(c, lane);
-    const T* R = rblock(c);
-#pragma unroll
-    for (int t = 0; t < NA; ++t) Rv[t] = ld4<T>(R + 16 * t);
-    if (w == 0) {
-      float x, b;
-      gate_in(c, lane, x, b);
-      gates(c, lane, x, b);
+    const int c = NC - 1, Lc = chunk_len(c);
+    if (Lc == kL) {
+      issue(c, lane);
+    } else {  // the ragged last chunk: gates written here (zero past the end), key rows zeroed below
+      dma_tile<D, T, PQ>(Ks[c & 1], kg + row0_of(c) * D, Lc, w, 2, lane);
+      dma_tile<kL, T, PE>(Tm[c & 1], L.tinv + ((size_t)chain * NC + c) * kTT, kL, w, 2, lane);
+      dma_block<D, T, PQ, 32>(Rs[c & 1], rmat(c) + (size_t)r0 * D, w, 2, lane);
+      if (w == 0) {
+        const bool ok = lane < Lc;
+        const size_t i = row0_of(c) + (ok ? lane : 0);
+        const T x = gg[i], b = bg[i];
+        Gr[c & 1][0][lane] = ok ? x : T(0.f);
+        Gr[c & 1][1][lane] = ok ? b : T(0.f);
+      }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int Lc = chunk_len(c);
-    if (Lc < kL) {  // the ragged last chunk: rows past the end of the sequence read as zeros
+    if (Lc < kL) {
       zero_tail<D, T, PQ>(Ks[c & 1], Lc, tid, 128);
       __syncthreads();
     }
@@ -608,70 +611,72 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const int gq = ln >> 4, lq = ln & 15;
-    // chunk c - 1 streams in; its R block (read before dS_end(c - 1) is stored over it) too
-    f32x4 Rn[NA];
-    float gx = 0.f, gb = 0.f;
-    if (c > 0) {
-      if (w == 0) gate_in(c - 1, ln, gx, gb);
-      issue_tiles(c - 1, ln);
-      const T* R = L.mat + ((size_t)chain * NC + c - 1) * 2 * DD + (size_t)(v0 + lq) * D + 4 * gq;
-#pragma unroll
-      for (int t = 0; t < NA; ++t) Rn[t] = ld4<T>(R + 16 * t);
-    }
+    if (c > 0) issue(c - 1, ln);  // buffers (c - 1) & 1 were last read in the chunk before
     {
-      T* R = L.mat + ((size_t)chain * NC + c) * 2 * DD + (size_t)(v0 + lq) * D + 4 * gq;
+      T* R = rmat(c) + (size_t)(v0 + lq) * D + 4 * gq;
 #pragma unroll
-      for (int t = 0; t < NA; ++t) st4<T>(R + 16 * t, dSt[t]);  // dS_end(c)
+      for (int t = 0; t < NA; ++t) st4<T>(R + 16 * t, dSt[t]);  // dS_end(c), over R_c (read from LDS)
     }
-    const T (*Kc)[PQ] = Ks[c & 1];
-    const T (*Tc)[PE] = Tm[c & 1];
-    const float* ddc = dd[c & 1];
-    const float* bgc = bgam[c & 1];
-    const float gL = gLs[c & 1];
+    const int b = c & 1;
+    // this wave's copy of the chunk's gates: lg = inclusive scan of log alpha, D = e^{lg_L - lg},
+    // beta gamma = beta e^{lg}, gamma_L
+    float gL;
+    {
+      float lg = to_f32(Gr[b][0][ln]);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(lg, off, 64);
+        if (ln >= off) lg += y;
+      }
+      const float lgL = __shfl(lg, 63, 64);
+      dd[w][ln] = __expf(lgL - lg);
+      bgam[w][ln] = to_f32(Gr[b][1][ln]) * __expf(lg);
+      gL = __expf(lgL);
+    }
+    const T (*Kc)[PQ] = Ks[b];
+    const T (*Tc)[PE] = Tm[b];
     // Y^T = K dS^T (token rows), scaled by D
     f32x4 y[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) y[ti] = zero4();
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const Frag<O> b = acc_frag<O>(dSt[2 * kk], dSt[2 * kk + 1]);
+      const Frag<O> bf = acc_frag<O>(dSt[2 * kk], dSt[2 * kk + 1]);
 #pragma unroll
-      for (int ti = 0; ti < 4; ++ti) mma(y[ti], lds_frag<O, KORD_ACC>(&Kc[0][0], PQ, 16 * ti, 32 * kk, ln), b);
+      for (int ti = 0; ti < 4; ++ti) mma(y[ti], lds_frag<O, KORD_ACC>(&Kc[0][0], PQ, 16 * ti, 32 * kk, ln), bf);
     }
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const f32x4 s = *reinterpret_cast<const f32x4*>(&ddc[16 * ti + 4 * gq]);
-      y[ti] *= s;
-    }
+    for (int ti = 0; ti < 4; ++ti) y[ti] *= *reinterpret_cast<const f32x4*>(&dd[w][16 * ti + 4 * gq]);
     // Y'^T = T^T (D Y^T), scaled by beta gamma
     f32x4 yp[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) yp[ti] = zero4();
     trilT_times_strip<O>(&Tc[0][0], PE, y, ln, yp);
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      const f32x4 s = *reinterpret_cast<const f32x4*>(&bgc[16 * ti + 4 * gq]);
-      yp[ti] *= s;
-    }
+    for (int ti = 0; ti < 4; ++ti) yp[ti] *= *reinterpret_cast<const f32x4*>(&bgam[w][16 * ti + 4 * gq]);
     // dS^T = gamma_L dS^T - K^T Y'^T + R_c^T
 #pragma unroll
-    for (int t = 0; t < NA; ++t) dSt[t] = gL * dSt[t] + Rv[t];
+    for (int t = 0; t < NA; ++t) dSt[t] = gL * dSt[t] + ld4<T>(&Rs[b][16 * w + lq][16 * t + 4 * gq]);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const Frag<O> b = acc_frag<O>(yp[2 * kk], yp[2 * kk + 1]);
+      const Frag<O> bf = acc_frag<O>(yp[2 * kk], yp[2 * kk + 1]);
 #pragma unroll
       for (int t = 0; t < NA; ++t) {
         f32x4 acc = zero4();
-        mma(acc, tile_cols<O, KORD_ACC>(&Kc[0][0], PQ, 32 * kk, 16 * t, ln), b);
+        mma(acc, tile_cols<O, KORD_ACC>(&Kc[0][0], PQ, 32 * kk, 16 * t, ln), bf);
         dSt[t] -= acc;
       }
     }
     if (c > 0) {
-      if (w == 0) gates(c - 1, ln, gx, gb);
-#pragma unroll
-      for (int t = 0; t < NA; ++t) Rv[t] = Rn[t];
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // chunk c - 1 has landed; chunk c's buffers are free
+      // chunk c - 1 has landed once only this chunk's NA stores (issued after its loads) may be
+      // outstanding; the barrier also frees chunk c's buffers for chunk c - 2
+      if constexpr (NA == 8) {
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      } else {
+        static_assert(NA == 4, "store count per chunk");
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      }
+      lds_barrier();
     }
   }
   if (a.dS0 != nullptr) {

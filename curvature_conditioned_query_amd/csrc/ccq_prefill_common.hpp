@@ -168,6 +168,34 @@ __device__ __forceinline__ void dma_tile(T (*dst)[PQ], const T* src, int Lc, int
   for (int j = w; j < U; j += nw) dma_unit<D, T, PQ>(dst, src, Lc, j, lane);
 }
 
+// All ROWS rows (row stride D elements) of a block into an LDS tile of pitch PQ, every row valid:
+// ceil(ROWS * U / 64) instructions, the last one with only the lanes that have a unit.  Waves w,
+// w + nw, ... issue them.  Same untracked loads as dma_unit (the caller waits).
+template <int D, typename T, int PQ, int ROWS>
+__device__ __forceinline__ void dma_block(T (*dst)[PQ], const T* src, int w, int nw, int lane) {
+  constexpr int U = PQ * (int)sizeof(T) / 16, DU = D * (int)sizeof(T) / 16, EPU = 16 / (int)sizeof(T);
+  constexpr int NI = (ROWS * U + 63) / 64;
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) T*)&dst[0][0];
+  for (int j = w; j < NI; j += nw) {
+    const int u = 64 * j + lane;
+    if (u < ROWS * U) {
+      const int row = u / U, slot = u - row * U;
+      const T* p = src + (slot < DU ? row * D + slot * EPU : 0);
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)j);
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p) : "memory", "m0");
+    }
+  }
+}
+
+// One direct load of 16 bytes per calling lane from p into dst + 16 * lane bytes (the lanes that do
+// not call write nothing).  Untracked, as above.
+template <typename T>
+__device__ __forceinline__ void dma_lane(T* dst, const T* p) {
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) T*)dst;
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p) : "memory", "m0");
+}
+
 // The same tile loads with the lane's part of every instruction worked out once: instruction
 // j = w + NWAVES m of wave w reads row[m] (kL for a padding unit, so it always falls back to
 // row 0) at element offset off[m] of the chunk.  A tile load then costs a compare, a select
