@@ -244,8 +244,10 @@ template <int D, typename T>
 __global__ __launch_bounds__(4 * D) void gdn_bwd_walk_kernel(BwdArgs a, int P, int cps) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ, NT = 64 * NW;
+  constexpr int EPU = 16 / (int)sizeof(T), NU = kL / EPU;  // 16-byte units of a 64-token gate row
   __shared__ GdnSmem<D, T> sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15, cw = 16 * w;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), cw = 16 * w;
   const int NC = a.nchunks;
   const int chain = blockIdx.x / P, seg = blockIdx.x % P;
   const int c0 = seg * cps, c1 = min(NC, c0 + cps);
@@ -262,6 +264,23 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_walk_kernel(BwdArgs a, int P, i
     C_in = a.C0 + (size_t)chain * DD;
     m_in = a.ksum0 + (size_t)chain * D;
   }
+  const T* kg = static_cast<const T*>(a.k);
+  const T* vg = static_cast<const T*>(a.v);
+  const T* gg = static_cast<const T*>(a.log_alpha);
+  const T* bg = static_cast<const T*>(a.beta);
+  T* gr = &sm.Qa[0][0];  // raw log alpha | beta of chunk c at gr + 2 kL (c & 1) (the walk reads no query)
+  auto row0_of = [&](int c) { return (size_t)chain * a.T + (size_t)c * kL; };
+  // Only the chunks before the segment's last are applied, and those are whole: the chain's last
+  // chunk, the only one that can be ragged, is never applied (the carry after it is not needed).
+  auto issue_kg = [&](int c) {  // chunk c's keys and raw gates
+    dma_tile<D, T, PQ>(sm.Ks[c & 1], kg + row0_of(c) * D, kL, w, NW, lane);
+    if (w == 0 && lane < 2 * NU) {
+      const T* src = lane < NU ? gg + row0_of(c) + EPU * lane : bg + row0_of(c) + EPU * (lane - NU);
+      dma_lane(gr + 2 * kL * (c & 1), src);
+    }
+  };
+  auto issue_v = [&](int c) { dma_tile<D, T, PQ>(sm.Vs, vg + row0_of(c) * D, kL, w, NW, lane); };
+
   // Sacc[t] = S^T[16 t + 4 g + r][cw + l16], Cacc[t] = C[16 t + 4 g + r][cw + l16] (C symmetric)
   f32x4 Sacc[NA], Cacc[NA];
 #pragma unroll
@@ -271,12 +290,13 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_walk_kernel(BwdArgs a, int P, i
     Cacc[t] = C_in ? *reinterpret_cast<const f32x4*>(C_in + o) : zero4();
   }
   if (tid < D) sm.m0[tid] = m_in ? m_in[tid] : 0.f;
+  if (c0 < c1 - 1) {
+    issue_kg(c0);
+    issue_v(c0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  const T* kg = static_cast<const T*>(a.k);
-  const T* vg = static_cast<const T*>(a.v);
-  const T* gg = static_cast<const T*>(a.log_alpha);
-  const T* bg = static_cast<const T*>(a.beta);
-  for (int c = c0; c < c1; ++c) {
+  auto store_carry = [&](int c) {  // the carry at chunk c's start: S_c, C_c (input dtype), m_c
     const size_t cs = (size_t)chain * NC + c;
     T* Sd = L.car + cs * 2 * DD;
     T* Cd = Sd + DD;
@@ -287,26 +307,45 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_walk_kernel(BwdArgs a, int P, i
       st4<T>(Cd + o, Cacc[t]);
     }
     if (tid < D) L.carm[cs * D + tid] = sm.m0[tid];
-    if (c == c1 - 1) break;
-    const size_t row0 = (size_t)chain * a.T + (size_t)c * kL;
-    load_tile<D, T, PQ>(sm.Ks[0], kg + row0 * D, kL, tid, NT);
-    load_tile<D, T, PQ>(sm.Vs, vg + row0 * D, kL, tid, NT);
-    if (w == 1) gdn_gates<D, T>(sm, ldf(gg, row0 + lane), ldf(bg, row0 + lane), lane);
-    __syncthreads();
-    gdn_build_A<D, T>(sm, sm.Ks[0], w, NW, lane);
-    if (tid >= 2 * D) gdn_key_sums<D, T>(sm, sm.Ks[0], tid - 2 * D);
-    __syncthreads();
+  };
+  for (int c = c0; c < c1; ++c) {
+    if (c == c1 - 1) {
+      store_carry(c);
+      break;
+    }
+    const bool more = c + 1 < c1 - 1;  // chunk c + 1 is applied too: its tiles stream in meanwhile
+    if (more) issue_kg(c + 1);  // buffers (c + 1) & 1 were last read in the chunk before
+    T (*Ks)[PQ] = sm.Ks[c & 1];
+    if (w == 1) {
+      const T* gc = gr + 2 * kL * (c & 1);
+      gdn_gates<D, T>(sm, to_f32(gc[lane]), to_f32(gc[kL + lane]), lane);
+    }
+    lds_barrier();
+    gdn_build_A<D, T>(sm, Ks, w, NW, lane);
+    if (tid >= 2 * D) gdn_key_sums<D, T>(sm, Ks, tid - 2 * D);
+    lds_barrier();
     if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
     f32x4 X[4];
-    gdn_rhs<D, T, true>(sm, sm.Ks[0], [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, X);
-    __syncthreads();
+    gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, X);
+    lds_barrier();  // the value tile is read
+    if (more) issue_v(c + 1);
+    // the carry at chunk c's start, issued after every load of the step so that the step's closing
+    // wait need not wait for these stores
+    store_carry(c);
     f32x4 Dl[4];
     gdn_solve<D, T>(sm, X, lane, Dl);
-    gdn_state_update<D, T>(sm, sm.Ks[0], [&](int t) -> f32x4& { return Sacc[t]; }, Dl, lane);
-    gdn_cov_update<D, T>(sm.Ks[0], Cacc, cw, lane);
-    __syncthreads();  // every wave is done with the chunk's tiles and m1
+    gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Sacc[t]; }, Dl, lane);
+    gdn_cov_update<D, T>(Ks, Cacc, cw, lane);
+    lds_barrier();  // every wave is done with the chunk's tiles and m1
     if (tid < D) sm.m0[tid] = sm.m1[tid];
-    __syncthreads();
+    // chunk c + 1 has landed once at most this step's 2 NA (+ 1) carry stores are outstanding
+    if constexpr (NA == 8) {
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+      static_assert(NA == 4, "store count per chunk");
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    }
+    lds_barrier();
   }
 }
 
