@@ -57,8 +57,11 @@ def library_sha256() -> str:
                 h.update(os.path.relpath(path, ROOT).encode())
                 with open(path, "rb") as f:
                     h.update(f.read())
+    # the flags name the include directories by absolute path: hash them relative to the repository
+    # root, so that the same tree gives the same hash wherever it is checked out
     for src in SOURCES:
-        h.update(" ".join([src, *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, [])]).encode())
+        flags = [f.replace(ROOT, "<root>") for f in (src, *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, []))]
+        h.update(" ".join(flags).encode())
     return h.hexdigest()
 
 

@@ -97,6 +97,25 @@ def test_library_hash_covers_sources_headers_and_flags(tmp_path, monkeypatch):
     assert len({h1, h2, h3}) == 3
 
 
+def test_library_hash_does_not_depend_on_where_the_tree_is(tmp_path, monkeypatch):
+    """The same sources and flags give the same hash in another checkout directory (records are
+    taken on one machine and read on another)."""
+    import shutil
+    base = build.library_sha256()
+    root2 = tmp_path / "elsewhere"
+    csrc2 = root2 / os.path.relpath(build.CSRC, build.ROOT)
+    inc2 = root2 / os.path.relpath(build.INCLUDE, build.ROOT)
+    shutil.copytree(build.CSRC, csrc2)
+    shutil.copytree(build.INCLUDE, inc2)
+    common2 = [f.replace(build.ROOT, str(root2)) for f in build.COMMON]
+    assert common2 != build.COMMON  # the flags do name the directories
+    monkeypatch.setattr(build, "ROOT", str(root2))
+    monkeypatch.setattr(build, "CSRC", str(csrc2))
+    monkeypatch.setattr(build, "INCLUDE", str(inc2))
+    monkeypatch.setattr(build, "COMMON", common2)
+    assert build.library_sha256() == base
+
+
 def test_committed_records_are_read_only_for_the_library_they_were_taken_on():
     names = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "traffic_*.json")))
     for path in names:
