@@ -17,7 +17,9 @@ from .binding import (  # noqa: F401
     ccq_fwd_workspace_bytes,
     ccq_key_subspace,
     ccq_bwd_chunked,
+    ccq_chunk_carry_bytes,
     ccq_step_backward,
+    new_chunk_carry,
     library_path,
     load_library,
 )

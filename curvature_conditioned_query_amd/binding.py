@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "ccq_step_backward",
     "ccq_bwd_chunked",
     "ccq_bwd_workspace_bytes",
+    "ccq_chunk_carry_bytes",
     "ccq_status_string",
     "ccq_abi_version",
 )
@@ -60,6 +61,7 @@ class FwdParams(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("phase_events", ctypes.c_void_p),
         ("flags", ctypes.c_int32),
+        ("chunk_carry", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +84,7 @@ class BwdParams(ctypes.Structure):
         ("phase_events", ctypes.c_void_p),
         ("flags", ctypes.c_int32),
         ("beta", ctypes.c_void_p), ("dbeta", ctypes.c_void_p),
+        ("chunk_carry", ctypes.c_void_p),
     ]
 
 
@@ -118,6 +121,8 @@ def load_library():
     lib.ccq_bwd_chunked.restype = ctypes.c_int
     lib.ccq_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BwdParams)]
     lib.ccq_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ccq_chunk_carry_bytes.argtypes = [i32] * 5
+    lib.ccq_chunk_carry_bytes.restype = ctypes.c_size_t
     lib.ccq_status_string.argtypes = [i32]
     lib.ccq_status_string.restype = ctypes.c_char_p
     lib.ccq_abi_version.argtypes = []
@@ -242,15 +247,31 @@ def ccq_fwd_workspace_bytes(p: FwdParams) -> int:
     return int(load_library().ccq_fwd_workspace_bytes(ctypes.byref(p)))
 
 
+def ccq_chunk_carry_bytes(dtype_code: int, B: int, H: int, T: int, d: int) -> int:
+    """Bytes of the chunk-carry buffer (ccq_chunk_carry_bytes)."""
+    return int(load_library().ccq_chunk_carry_bytes(dtype_code, B, H, T, d))
+
+
+def new_chunk_carry(q):
+    """A chunk-carry buffer (uint8 device tensor) for a prefill / backward of q's shape and dtype."""
+    import torch
+    B, H, T, d = q.shape
+    n = ccq_chunk_carry_bytes(_dtype_code(q), B, H, T, d)
+    if n == 0:
+        raise ValueError("unsupported shape or dtype for chunk carries")
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
                     carry_in=None, carry_out=None, segments: int = 0, chunk: int = 64,
                     workspace=None, stream=None, phase_events=None, normalize_keys: bool = False,
-                    packed_cov: bool = False):
+                    packed_cov: bool = False, chunk_carry=None):
     """Chunked CCQ prefill through the C ABI.  Allocates o (and the workspace if not
     given) with torch; returns o.  ``phase_events``: optional ctypes array of 4 hipEvent_t
     handles recorded around the kernels of the pass.  ``normalize_keys``: the kernels scale
     every key to unit L2 norm first (CCQ_FLAG_NORMALIZE_KEYS).  ``packed_cov``: the carry's
-    C is the packed upper triangle (CCQ_FLAG_PACKED_COV)."""
+    C is the packed upper triangle (CCQ_FLAG_PACKED_COV).  ``chunk_carry``: optional buffer
+    (``new_chunk_carry``) that receives the carry at every chunk start, for ccq_bwd_chunked."""
     import torch
     lib = load_library()
     if o is None:
@@ -265,10 +286,21 @@ def ccq_fwd_chunked(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
             p.workspace_bytes = nbytes
     if phase_events is not None:
         p.phase_events = ctypes.cast(phase_events, ctypes.c_void_p)
+    if chunk_carry is not None:
+        _check_chunk_carry(chunk_carry, q)
+        p.chunk_carry = chunk_carry.data_ptr()
     st = lib.ccq_fwd_chunked(ctypes.byref(p), _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_fwd_chunked")
     return o
+
+
+def _check_chunk_carry(buf, q):
+    _check_dev("chunk_carry", buf)
+    B, H, T, d = q.shape
+    need = ccq_chunk_carry_bytes(_dtype_code(q), B, H, T, d)
+    if buf.numel() * buf.element_size() < need:
+        raise ValueError(f"chunk_carry must hold {need} bytes")
 
 
 def ccq_fwd_chunked_noalloc(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, o=None,
@@ -399,14 +431,16 @@ def ccq_step_backward(rule, q, k, v, log_alpha, beta, w_lambda, b_lambda, S, C, 
 
 
 def ccq_bwd_chunked(rule, q, k, v, log_alpha, w_lambda, b_lambda, d_o, carry_in=None, carry_out_adjoint=None,
-                    want_carry_in_adjoint: bool = False, workspace=None, stream=None, phase_events=None, beta=None):
+                    want_carry_in_adjoint: bool = False, workspace=None, stream=None, phase_events=None, beta=None,
+                    chunk_carry=None):
     """Chunked backward of the prefill through the C ABI (see ``ccq_bwd_chunked`` in ccq.h).
     q, k, v, d_o: [B, H, T, d] of one dtype; log_alpha: [B, H, T, d] (GLA) or [B, H, T] (Gated
     DeltaNet, with beta [B, H, T]); carry_in: (S0, C0, ksum0, n0) or None; carry_out_adjoint:
     (dS_T, dC_T, dksum_T) fp32 or None.  Returns a dict of fp32 tensors dq, dk, dv, dlog_alpha (the
     shape of log_alpha), dbeta (Gated DeltaNet), dw_lambda [B, H, d], db_lambda [B, H] and, with
     want_carry_in_adjoint, dS0, dC0, dksum0.  ``phase_events``: optional ctypes array of 5
-    hipEvent_t handles recorded around the passes."""
+    hipEvent_t handles recorded around the passes.  ``chunk_carry``: the buffer a ccq_fwd_chunked of
+    the same inputs filled; the chunk carries are then read from it instead of recomputed."""
     import torch
     lib = load_library()
     B, H, T, d_k = q.shape
@@ -464,6 +498,9 @@ def ccq_bwd_chunked(rule, q, k, v, log_alpha, w_lambda, b_lambda, d_o, carry_in=
         p.workspace_bytes = workspace.numel() * workspace.element_size()
     if phase_events is not None:
         p.phase_events = ctypes.cast(phase_events, ctypes.c_void_p)
+    if chunk_carry is not None:
+        _check_chunk_carry(chunk_carry, q)
+        p.chunk_carry = chunk_carry.data_ptr()
     st = lib.ccq_bwd_chunked(ctypes.byref(p), _stream_handle(stream))
     if st != 0:
         raise CcqError(st, "ccq_bwd_chunked")

@@ -43,7 +43,8 @@ int validate_fwd(const ccq_fwd_params* p, int* segments_out, int* chunks_per_seg
   const int nout = (p->S_out != nullptr) + (p->C_out != nullptr) + (p->ksum_out != nullptr) + (p->n_out != nullptr);
   if ((nin != 0 && nin != 4) || (nout != 0 && nout != 4)) return CCQ_ERR_INVALID_ARG;
   const void* ptrs[] = {p->q, p->k, p->v, p->log_alpha, p->beta, p->w_lambda, p->b_lambda, p->S0, p->C0,
-                        p->ksum0, p->n0, p->o, p->S_out, p->C_out, p->ksum_out, p->n_out, p->workspace};
+                        p->ksum0, p->n0, p->o, p->S_out, p->C_out, p->ksum_out, p->n_out, p->workspace,
+                        p->chunk_carry};
   for (const void* q : ptrs)
     if (misaligned(q)) return CCQ_ERR_MISALIGNED;
   const long long chains = (long long)p->B * p->H;
@@ -120,6 +121,7 @@ int fwd_launch(const ccq_fwd_params* p, int seg, int cps, void* workspace, hipSt
   a.events = p->phase_events;
   a.flags = p->flags;
   a.snapshot = (seg > 1 && carry_overlaps(p)) ? 1 : 0;
+  a.chunk_carry = p->chunk_carry;
   const hipError_t e = ccq::launch_fwd(a, stream);
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }
@@ -150,7 +152,8 @@ int validate_bwd(const ccq_bwd_params* p) {
   if ((nin != 0 && nin != 4) || (nadj != 0 && nadj != 3) || (nout != 0 && nout != 3)) return CCQ_ERR_INVALID_ARG;
   const void* ptrs[] = {p->q, p->k, p->v, p->log_alpha, p->w_lambda, p->b_lambda, p->S0, p->C0, p->ksum0, p->n0,
                         p->d_o, p->dS_T, p->dC_T, p->dksum_T, p->dq, p->dk, p->dv, p->dlog_alpha, p->dw_lambda,
-                        p->db_lambda, p->dS0, p->dC0, p->dksum0, p->workspace, p->beta, p->dbeta};
+                        p->db_lambda, p->dS0, p->dC0, p->dksum0, p->workspace, p->beta, p->dbeta,
+                        p->chunk_carry};
   for (const void* q : ptrs)
     if (misaligned(q)) return CCQ_ERR_MISALIGNED;
   return CCQ_OK;
@@ -165,7 +168,7 @@ size_t bwd_ws_bytes(const ccq_bwd_params* p) {
 
 extern "C" {
 
-int32_t ccq_abi_version(void) { return 10; }
+int32_t ccq_abi_version(void) { return 11; }
 
 const char* ccq_status_string(int32_t status) {
   switch (status) {
@@ -264,6 +267,13 @@ int ccq_step_backward(int32_t rule, int32_t dtype, int32_t N, int32_t H, int32_t
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }
 
+size_t ccq_chunk_carry_bytes(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d) {
+  if ((dtype != CCQ_DTYPE_F32 && dtype != CCQ_DTYPE_BF16) || B <= 0 || H <= 0 || T <= 0 || !supported_d(dtype, d))
+    return 0;
+  return ccq::chunk_carry_bytes((size_t)B * H, (size_t)((T + kChunk - 1) / kChunk), (size_t)d,
+                                dtype == CCQ_DTYPE_BF16 ? 2 : 4);
+}
+
 size_t ccq_bwd_workspace_bytes(const ccq_bwd_params* p) {
   if (validate_bwd(p) != CCQ_OK) return 0;
   return bwd_ws_bytes(p);
@@ -309,6 +319,7 @@ int ccq_bwd_chunked(const ccq_bwd_params* p, void* hip_stream) {
   a.dksum0 = p->dksum0;
   a.workspace = p->workspace;
   a.events = p->phase_events;
+  a.chunk_carry = p->chunk_carry;
   const hipError_t e = ccq::launch_bwd(a, static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? CCQ_OK : CCQ_ERR_LAUNCH;
 }

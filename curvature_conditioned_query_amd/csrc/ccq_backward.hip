@@ -112,10 +112,16 @@ template <typename T>
 __device__ __forceinline__ BwdLayout<T> layout(const BwdArgs& a) {
   const BwdLayoutBytes b = bwd_layout_bytes((size_t)a.B * a.H, (size_t)a.nchunks, (size_t)a.d, sizeof(T));
   char* w = static_cast<char*>(a.workspace);
-  return BwdLayout<T>{reinterpret_cast<float*>(w + b.sum), reinterpret_cast<T*>(w + b.car),
-                      reinterpret_cast<float*>(w + b.carm), reinterpret_cast<T*>(w + b.mat),
-                      reinterpret_cast<float*>(w + b.tail), reinterpret_cast<float*>(w + b.qc),
-                      reinterpret_cast<float*>(w + b.qdq), reinterpret_cast<float*>(w + b.dkp)};
+  BwdLayout<T> L{reinterpret_cast<float*>(w + b.sum), reinterpret_cast<T*>(w + b.car),
+                 reinterpret_cast<float*>(w + b.carm), reinterpret_cast<T*>(w + b.mat),
+                 reinterpret_cast<float*>(w + b.tail), reinterpret_cast<float*>(w + b.qc),
+                 reinterpret_cast<float*>(w + b.qdq), reinterpret_cast<float*>(w + b.dkp)};
+  if (a.chunk_carry != nullptr) {  // the chunk carries the forward wrote (same layout, own buffer)
+    char* cc = static_cast<char*>(const_cast<void*>(a.chunk_carry));
+    L.car = reinterpret_cast<T*>(cc);
+    L.carm = reinterpret_cast<float*>(cc + chunk_carry_mat_bytes((size_t)a.B * a.H, (size_t)a.nchunks, (size_t)a.d, sizeof(T)));
+  }
+  return L;
 }
 
 template <typename T>
@@ -697,9 +703,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   f.segments = P;
   f.chunks_per_segment = cps;
   if (record_bwd_event(a, 0, s) != hipSuccess) return hipErrorLaunchFailure;
-  hipError_t e = P > 1 ? launch_gla_segment_carries(f, s) : hipSuccess;
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_carry_walk_kernel<D, T>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a, P, cps);
+  hipError_t e = hipSuccess;
+  if (a.chunk_carry == nullptr) {  // else the forward wrote them and layout() points at its buffer
+    e = P > 1 ? launch_gla_segment_carries(f, s) : hipSuccess;
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_carry_walk_kernel<D, T>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a, P, cps);
+  }
   if (record_bwd_event(a, 1, s) != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_chunk_a_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
   if (record_bwd_event(a, 2, s) != hipSuccess) return hipErrorLaunchFailure;

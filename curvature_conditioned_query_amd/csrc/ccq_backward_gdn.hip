@@ -115,10 +115,16 @@ template <typename T>
 __device__ __forceinline__ GdnBwdLayout<T> gdn_layout(const BwdArgs& a) {
   const GdnBwdBytes b = gdn_bwd_bytes((size_t)a.B * a.H, a.nchunks, (size_t)a.d, sizeof(T));
   char* w = static_cast<char*>(a.workspace);
-  return GdnBwdLayout<T>{reinterpret_cast<float*>(w + b.seg), reinterpret_cast<T*>(w + b.car),
-                         reinterpret_cast<float*>(w + b.carm), reinterpret_cast<T*>(w + b.tinv),
-                         reinterpret_cast<T*>(w + b.mat), reinterpret_cast<float*>(w + b.tail),
-                         reinterpret_cast<float*>(w + b.qc), reinterpret_cast<float*>(w + b.dkp)};
+  GdnBwdLayout<T> L{reinterpret_cast<float*>(w + b.seg), reinterpret_cast<T*>(w + b.car),
+                    reinterpret_cast<float*>(w + b.carm), reinterpret_cast<T*>(w + b.tinv),
+                    reinterpret_cast<T*>(w + b.mat), reinterpret_cast<float*>(w + b.tail),
+                    reinterpret_cast<float*>(w + b.qc), reinterpret_cast<float*>(w + b.dkp)};
+  if (a.chunk_carry != nullptr) {  // the chunk carries the forward wrote (same layout, own buffer)
+    char* cc = static_cast<char*>(const_cast<void*>(a.chunk_carry));
+    L.car = reinterpret_cast<T*>(cc);
+    L.carm = reinterpret_cast<float*>(cc + chunk_carry_mat_bytes((size_t)a.B * a.H, (size_t)a.nchunks, (size_t)a.d, sizeof(T)));
+  }
+  return L;
 }
 
 // The chunk's gates into LDS (one wave, lane = token): beta, the chunk-local cumulative log decay lg
@@ -1097,14 +1103,16 @@ static hipError_t launch_gdn_bwd_t(const BwdArgs& a, hipStream_t s) {
   f.n0 = a.n0;
   f.workspace = a.workspace;  // the segment slots come first in the workspace
   if (rec(0) != hipSuccess) return hipErrorLaunchFailure;
-  if (P > 1) {
-    const hipError_t es = launch_gdn_summary(f, s);
-    if (es != hipSuccess) return es;
-    hipLaunchKernelGGL((gdn_scan_state_kernel<D>), dim3(D / 16, (unsigned)chains), dim3(2 * D), 0, s, f);
-    hipLaunchKernelGGL((gdn_scan_sum_kernel<D>), dim3((unsigned)((D * D + D + 255) / 256), (unsigned)chains), dim3(256),
-                       0, s, f);
+  if (a.chunk_carry == nullptr) {  // else the forward wrote them and gdn_layout() points at its buffer
+    if (P > 1) {
+      const hipError_t es = launch_gdn_summary(f, s);
+      if (es != hipSuccess) return es;
+      hipLaunchKernelGGL((gdn_scan_state_kernel<D>), dim3(D / 16, (unsigned)chains), dim3(2 * D), 0, s, f);
+      hipLaunchKernelGGL((gdn_scan_sum_kernel<D>), dim3((unsigned)((D * D + D + 255) / 256), (unsigned)chains),
+                         dim3(256), 0, s, f);
+    }
+    hipLaunchKernelGGL((gdn_bwd_walk_kernel<D, T>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a, P, cps);
   }
-  hipLaunchKernelGGL((gdn_bwd_walk_kernel<D, T>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a, P, cps);
   if (rec(1) != hipSuccess) return hipErrorLaunchFailure;
   // 2. pass A
   hipLaunchKernelGGL((gdn_bwd_a_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);

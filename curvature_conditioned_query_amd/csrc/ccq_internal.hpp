@@ -50,7 +50,19 @@ struct FwdArgs {
   // the main kernel reads those copies, so no workgroup can read a carry another one has
   // already overwritten.
   int snapshot;
+  // Optional: the carry at every chunk start, written for the chunked backward (chunk_carry_*).
+  void* chunk_carry;
 };
+
+// The carry at the start of every 64-token chunk, as the chunked backward reads it: S_c then C_c
+// (d x d each, row-major, the input dtype; C symmetric) per (chain, chunk), chains x NC x 2 d^2
+// elements, then m_c (the key sum, d fp32) per (chain, chunk).
+__host__ __device__ inline size_t chunk_carry_mat_bytes(size_t chains, size_t NC, size_t d, size_t E) {
+  return chains * NC * 2 * d * d * E;
+}
+__host__ __device__ inline size_t chunk_carry_bytes(size_t chains, size_t NC, size_t d, size_t E) {
+  return chunk_carry_mat_bytes(chains, NC, d, E) + chains * NC * d * 4;
+}
 
 // The workspace of a prefill with more than one segment: chains x P slots, then one int64
 // token count per chain (the snapshot of n0, written only when `snapshot` is set).
@@ -110,6 +122,9 @@ struct BwdArgs {
   float *dS0, *dC0, *dksum0;
   void* workspace;
   void* const* events;  // optional: 5 hipEvent_t around the passes
+  // Optional: the chunk carries a prefill of the same inputs wrote (chunk_carry_*); the backward
+  // then reads them instead of recomputing them.
+  const void* chunk_carry;
 };
 size_t bwd_workspace_bytes(int B, int H, int T, int d, int dtype);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);

@@ -68,7 +68,9 @@ struct Smem {
 
 // Full read (o for every token) of one (chain, segment) from the segment's carry-in, carry
 // out at the end of the chain.
-template <int D, typename T>
+// CC: this instantiation writes the carry at every chunk start (FwdArgs::chunk_carry); the one
+// without it carries no trace of that code.
+template <int D, typename T, bool CC>
 __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, NK = C_::NK;
@@ -168,6 +170,11 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
     dma_rows(sm.Y[cbeg & 1], vg, cbeg);
   }
 
+  if (CC && cbeg < cend) {  // the carry at the segment's first chunk, for the backward
+    put_carry_row<D, T, NA>(a, chain, cbeg, 0, cw + l16, g, Sacc);
+    put_carry_row<D, T, NA>(a, chain, cbeg, 1, cw + l16, g, Cacc);
+    if (tid < D) put_carry_ksum<D, T>(a, chain, cbeg, tid, sm.m0[tid]);  // this thread's own m0 entry
+  }
   const Frag<T> Ih = ident_frag<T>(hb, lane);
 
   // One chunk.  bf16: the intra-chunk attention takes hi + lo operands in the first chunk of a
@@ -380,6 +387,11 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
     }
     nb += Lc;
     lds_barrier();
+    if (CC && ch + 1 < cend) {  // the carry at the next chunk's start, for the backward
+      put_carry_row<D, T, NA>(a, chain, ch + 1, 0, cw + l16, g, Sacc);
+      put_carry_row<D, T, NA>(a, chain, ch + 1, 1, cw + l16, g, Cacc);
+      if (tid < D) put_carry_ksum<D, T>(a, chain, ch + 1, tid, sm.m0[tid]);
+    }
   };
   int ch = cbeg;
   if (kSplit && ch < cend && nb == 0) chunk(ch++, std::true_type{});
@@ -428,7 +440,10 @@ static hipError_t launch_gla(const FwdArgs& a, hipStream_t s) {
   if (D == 128 && sizeof(T) == 2 && !(a.flags & kFlagNormalizeKeys)) {
     e = launch_gla_pipe(a, s);
   } else {
-    hipLaunchKernelGGL((gla_main_kernel<D, T>), dim3((unsigned)(chains * P)), block, 0, s, a);
+    if (a.chunk_carry != nullptr)
+      hipLaunchKernelGGL((gla_main_kernel<D, T, true>), dim3((unsigned)(chains * P)), block, 0, s, a);
+    else
+      hipLaunchKernelGGL((gla_main_kernel<D, T, false>), dim3((unsigned)(chains * P)), block, 0, s, a);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;

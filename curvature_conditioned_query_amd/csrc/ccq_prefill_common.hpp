@@ -38,6 +38,26 @@ __device__ __forceinline__ void st4(T* p, const f32x4& v) {
   }
 }
 
+// The carry at the start of chunk ch of a chain into the chunk-carry buffer (the chunked backward's
+// layout): `row` of S (mat 0) or of the symmetric C (mat 1), from NA accumulator tiles whose element
+// r of lane (g, .) is column 16 t + 4 g + r of that row.
+template <int D, typename T, int NA>
+__device__ __forceinline__ void put_carry_row(const FwdArgs& a, int chain, int ch, int mat, int row, int g,
+                                              const f32x4 (&acc)[NA]) {
+  const size_t NC = (size_t)((a.T + kL - 1) / kL);
+  T* base = static_cast<T*>(a.chunk_carry) + ((size_t)chain * NC + ch) * 2 * D * D + (size_t)mat * D * D +
+            (size_t)row * D + 4 * g;
+#pragma unroll
+  for (int t = 0; t < NA; ++t) st4<T>(base + 16 * t, acc[t]);
+}
+// m_c (the key sum before chunk ch), channel c.
+template <int D, typename T>
+__device__ __forceinline__ void put_carry_ksum(const FwdArgs& a, int chain, int ch, int c, float m) {
+  const size_t chains = (size_t)a.B * a.H, NC = (size_t)((a.T + kL - 1) / kL);
+  float* km = reinterpret_cast<float*>(static_cast<char*>(a.chunk_carry) + chunk_carry_mat_bytes(chains, NC, D, sizeof(T)));
+  km[((size_t)chain * NC + ch) * D + c] = m;
+}
+
 template <typename T>
 __device__ __forceinline__ f32x4 ld4(const T* p) {
   if constexpr (sizeof(T) == 2) {

@@ -26,7 +26,10 @@ static hipError_t launch_gdn_t(const FwdArgs& a, hipStream_t s) {
     return hipErrorLaunchFailure;
   }
   if (rec(2) != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((gdn_main_kernel<D, T>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a);
+  if (a.chunk_carry != nullptr)
+    hipLaunchKernelGGL((gdn_main_kernel<D, T, true>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a);
+  else
+    hipLaunchKernelGGL((gdn_main_kernel<D, T, false>), dim3((unsigned)(chains * P)), dim3(4 * D), 0, s, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return rec(3);

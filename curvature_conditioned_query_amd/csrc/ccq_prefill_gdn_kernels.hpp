@@ -273,7 +273,8 @@ __device__ __forceinline__ void gdn_cov_update(const T (*Ks)[Cfg<D, T>::PQ], f32
 
 // ---------------------------------------------------------------- main kernel
 
-template <int D, typename T>
+// CC: this instantiation writes the carry at every chunk start (FwdArgs::chunk_carry).
+template <int D, typename T, bool CC>
 __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, NK = C_::NK;
@@ -394,6 +395,11 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     // ---- this chunk's tiles have landed; gates; rows past the end of the sequence zeroed
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (w == 1) gdn_gates<D, T>(sm, sg, sb, lane);
+    if (CC) {  // the carry at this chunk's start, for the chunked backward
+      put_carry_row<D, T, NA>(a, chain, ch, 0, cw + l16, g, Sacc);
+      put_carry_row<D, T, NA>(a, chain, ch, 1, cw + l16, g, Cacc);
+      if (tid < D) put_carry_ksum<D, T>(a, chain, ch, tid, sm.m0[tid]);
+    }
     lds_barrier();
     if (Lc < kL) {
       zero_tail<D, T, PQ>(sm.Qs, Lc, tid, 64 * NW);

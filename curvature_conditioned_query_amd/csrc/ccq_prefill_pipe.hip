@@ -102,7 +102,8 @@ struct PipeCtx {
   static constexpr int NWC = 8, NWS = 4, NWT = NWC + NWS;  // C-waves, S-waves, all
 };
 
-template <int D, typename T>
+// CC: this instantiation writes the carry at every chunk start (FwdArgs::chunk_carry).
+template <int D, typename T, bool CC>
 __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
   using X_ = PipeCtx<D, T>;
   constexpr int NA = X_::NA, NK = X_::NK, PQ = X_::PQ, PT = X_::PT;
@@ -230,6 +231,12 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
+    // C and the key sum at every chunk start of the segment, for the chunked backward: the first
+    // one here, each later one at the end of the step that updated C to it
+    if (CC && n > 0) {
+      put_carry_row<D, T, NA>(a, chain, cbeg, 1, cw + l16, g, Cacc);
+      if (tid < D) put_carry_ksum<D, T>(a, chain, cbeg, tid, sm.m0[p0][tid]);
+    }
     typedef __attribute__((address_space(1))) const bf16x8 gbf16x8;  // global loads, not flat ones
     for (int s = 0; s < nsteps; ++s) {
       CCQ_PIPE_STEP_LANE()
@@ -358,6 +365,12 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every tile of the next step has landed
       lds_barrier();
+      // C and the key sum at the next chunk's start, for the chunked backward (after the step's
+      // wait: the stores complete during the next step); the key sum was formed in phase A
+      if (CC && cc >= 0 && cc + 1 < cend) {
+        put_carry_row<D, T, NA>(a, chain, cc + 1, 1, cw + l16_, g_, Cacc);
+        if (tid < D) put_carry_ksum<D, T>(a, chain, cc + 1, tid, sm.m0[(cc + 1) & 1][tid]);
+      }
     }
     // ---- carry C out (last segment of the chain)
     if (seg == P - 1 && a.S_out != nullptr) {
@@ -387,6 +400,13 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
+    // S at every chunk start of the segment, for the chunked backward: the first one here, each
+    // later one at the end of the step that updated S to it (after the step's wait, so that the
+    // stores complete during the next step)
+    if (CC && n > 0) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) put_carry_row<D, T, NA>(a, chain, cbeg, 0, cw + 16 * hh + l16, g, Sacc[hh]);
+    }
     for (int s = 0; s < nsteps; ++s) {
       CCQ_PIPE_STEP_LANE()
       const int sc = s_at(s), nC = c_at(s + 1), nS = s_at(s + 1);
@@ -496,6 +516,10 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       lds_barrier();
+      if (CC && sc >= 0 && sc + 1 < cend) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) put_carry_row<D, T, NA>(a, chain, sc + 1, 0, cw + 16 * hh + l16_, g_, Sacc[hh]);
+      }
     }
     // ---- carry S out (last segment of the chain)
     if (seg == P - 1 && a.S_out != nullptr) {
@@ -511,7 +535,11 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
 }
 
 hipError_t launch_gla_pipe(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gla_pipe_kernel<128, __bf16>), dim3((unsigned)(a.B * a.H * a.segments)), dim3(768), 0, s, a);
+  if (a.chunk_carry != nullptr)
+    hipLaunchKernelGGL((gla_pipe_kernel<128, __bf16, true>), dim3((unsigned)(a.B * a.H * a.segments)), dim3(768), 0, s, a);
+  else
+    hipLaunchKernelGGL((gla_pipe_kernel<128, __bf16, false>), dim3((unsigned)(a.B * a.H * a.segments)), dim3(768), 0, s,
+                       a);
   return hipGetLastError();
 }
 

@@ -118,7 +118,22 @@ typedef struct {
   void *const *phase_events;
 
   int32_t flags;          /* ccq_flag bits; unknown bits are CCQ_ERR_INVALID_ARG            */
+
+  /* Optional (training): NULL, or ccq_chunk_carry_bytes(dtype, B, H, T, d_k) bytes of device
+   * memory that receive the carry at the start of every 64-token chunk c of every chain
+   * i = b H + h, for a later ccq_bwd_chunked of the same inputs (its chunk_carry): S_c then C_c,
+   * each [d][d] row-major in dtype, at element offset (i NC + c) 2 d^2 (NC = ceil(T / 64); C full,
+   * whatever the flags say about the carry in and out), followed by the key sums m_c, [d] fp32
+   * each, at float offset (i NC + c) d of the region after all of them.  The chunk carries are
+   * those of the keys as used (normalised in the kernel if the flag asks for it).  16-byte
+   * aligned (else CCQ_ERR_MISALIGNED). */
+  void *chunk_carry;
 } ccq_fwd_params;
+
+/* Bytes of the chunk-carry buffer of ccq_fwd_params.chunk_carry / ccq_bwd_params.chunk_carry for
+ * these sizes (0 for an unsupported dtype, non-positive sizes or d_k != d_v shapes the chunked
+ * calls reject): B H ceil(T / 64) (2 d^2 sizeof(dtype) + 4 d). */
+size_t ccq_chunk_carry_bytes(int32_t dtype, int32_t B, int32_t H, int32_t T, int32_t d);
 
 /*
  * Chunked prefill of one CCQ layer: o for every token and, optionally, the final carry.
@@ -278,6 +293,12 @@ typedef struct {
    * gradient dbeta [B, H, T] (fp32, written). */
   const void *beta;
   float *dbeta;
+  /* Optional: NULL (the backward recomputes the forward carry at every chunk start), or the
+   * chunk_carry buffer a ccq_fwd_chunked call with the same inputs and carry in filled (layout
+   * there); the backward then reads the chunk carries from it and skips their recomputation
+   * (the segment summary, scan and chunk walk).  Results agree with the recomputing path up to
+   * rounding.  16-byte aligned (else CCQ_ERR_MISALIGNED). */
+  const void *chunk_carry;
 } ccq_bwd_params;
 
 /*
@@ -288,7 +309,7 @@ typedef struct {
  * of the forward with the same inputs and carry in, it writes dL/dq, dL/dk, dL/dv,
  * dL/dlog_alpha (and dL/dbeta for Gated DeltaNet), the per-sequence gate-parameter gradients and,
  * when asked for, the adjoint of the carry in.  The forward carry at every 64-token chunk start is
- * recomputed (not read from the forward), and each chunk's gradients follow from it and the
+ * recomputed, or read from the forward's chunk_carry when given, and each chunk's gradients follow from it and the
  * adjoint carried back from later chunks: for GLA through the diagonal decay, for Gated DeltaNet
  * through the transpose of each chunk's d_k x d_k state transition.  Results equal
  * backpropagation through the per-token recurrence up to rounding; the forward's precondition on

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(binding.EXPORTED_SYMBOLS)
     for name in names:
         assert hasattr(lib, name), f"libccq.so does not export {name}"
-    assert lib.ccq_abi_version() == 10
+    assert lib.ccq_abi_version() == 11
 
 
 def test_status_strings(lib):
@@ -233,3 +233,54 @@ def test_gdn_bwd_workspace_sizing(lib):
     p.workspace, p.workspace_bytes = FAKE, need - 16
     assert lib.ccq_bwd_chunked(ctypes.byref(p), None) == WORKSPACE
 
+
+
+def test_chunk_carry_bytes(lib):
+    """B H ceil(T / 64) (2 d^2 sizeof(dtype) + 4 d); 0 for what the chunked calls reject."""
+    f = lib.ccq_chunk_carry_bytes
+    assert f(1, 4, 16, 4096, 128) == 64 * 64 * (2 * 128 * 128 * 2 + 4 * 128)
+    assert f(0, 1, 2, 200, 64) == 2 * 4 * (2 * 64 * 64 * 4 + 4 * 64)
+    assert f(1, 1, 1, 65, 64) == 2 * (2 * 64 * 64 * 2 + 4 * 64)
+    for args in ((2, 1, 1, 64, 64), (1, 0, 1, 64, 64), (1, 1, 1, 0, 64), (1, 1, 1, 64, 96), (0, 1, 1, 64, 128)):
+        assert f(*args) == 0
+
+
+def test_chunk_carry_must_be_aligned(lib):
+    p = _params(chunk_carry=FAKE + 8)
+    assert _fwd(lib, p) == MISALIGNED
+    b = BwdParams()
+    b.rule, b.dtype, b.B, b.H, b.T, b.d_k, b.d_v, b.chunk = 0, 1, 1, 2, 256, 128, 128, 64
+    for name in ("q", "k", "v", "log_alpha", "w_lambda", "b_lambda", "d_o", "dq", "dk", "dv", "dlog_alpha",
+                 "dw_lambda", "db_lambda"):
+        setattr(b, name, FAKE)
+    b.chunk_carry = FAKE + 8
+    assert lib.ccq_bwd_chunked(ctypes.byref(b), None) == MISALIGNED
+
+
+def test_param_structs_match_the_header(tmp_path):
+    """Every field of the ctypes mirrors sits where the C compiler puts it, and the sizes agree."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ["#include <stddef.h>", "#include <stdio.h>", '#include "ccq.h"', "int main(void) {"]
+    for cname, cls in (("ccq_fwd_params", FwdParams), ("ccq_bwd_params", BwdParams)):
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            cname, field, value = line.split()
+            got[(cname, field)] = int(value)
+    for cname, cls in (("ccq_fwd_params", FwdParams), ("ccq_bwd_params", BwdParams)):
+        assert got[(cname, "size")] == ctypes.sizeof(cls)
+        for field, _ in cls._fields_:
+            assert got[(cname, field)] == getattr(cls, field).offset, (cname, field)
