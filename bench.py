@@ -556,9 +556,35 @@ def time_bwd_chunked(steps, warmup, rule="gla"):
     phases = {name: float(np.mean([hip.elapsed_ms(5 * i + a, 5 * i + a + 1) for i in range(steps)]))
               for a, name in enumerate(("carries", "pass_a", "scan", "pass_b"))}
     hip.destroy()
-    del out
+    # training with the forward's chunk carries: the prefill writing them (against the plain
+    # prefill), then the backward reading them instead of recomputing them
+    from curvature_conditioned_query_amd import ccq_fwd_chunked, new_chunk_carry
+    from curvature_conditioned_query_amd.binding import ccq_fwd_workspace_bytes, make_fwd_params
+    o = torch.empty_like(do)
+    fws_n = ccq_fwd_workspace_bytes(make_fwd_params(rule, q, k, v, g, beta, w, b, o))
+    fws = torch.empty(max(fws_n, 1), dtype=torch.uint8, device="cuda") if fws_n else None
+    cc = new_chunk_carry(q)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        for _ in range(steps):
+            fn()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        return a0.elapsed_time(a1) / steps
+
+    fwd_ms = timed(lambda: ccq_fwd_chunked(rule, q, k, v, g, beta, w, b, o=o, workspace=fws))
+    fwd_cc_ms = timed(lambda: ccq_fwd_chunked(rule, q, k, v, g, beta, w, b, o=o, workspace=fws, chunk_carry=cc))
+    bwd_cc_ms = timed(lambda: ccq_bwd_chunked(rule, q, k, v, g, w, b, do, workspace=ws, beta=beta, chunk_carry=cc))
+    del out, cc
     return dict(name=f"ccq-{rule}-bwd-chunked-B{B}H{H}T{T}d{dk}-bf16", shape=(B, H, T, dk, dv), ms=ms,
-                phase_ms=phases, chunks=B * H * ((T + CHUNK - 1) // CHUNK), rule=rule)
+                phase_ms=phases, chunks=B * H * ((T + CHUNK - 1) // CHUNK), rule=rule,
+                with_chunk_carries=dict(forward_ms=fwd_ms, forward_writing_carries_ms=fwd_cc_ms,
+                                        backward_reading_carries_ms=bwd_cc_ms))
 
 
 def _ws_bytes_bwd(B, H, T, d, rule="gla"):
@@ -588,7 +614,12 @@ def bwd_chunked_entry(cres, lib_sha):
     print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass, {cB * cT / (cres['ms'] * 1e-3):.4g} tokens/s; "
           "passes (ms) " + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items())
           + f"; pass A {a_gbs:.1f} GB/s alg, {a_tf:.1f} TFLOP/s, pass B {b_tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+    wc = cres["with_chunk_carries"]
+    print(f"#   with the forward's chunk carries: forward {wc['forward_ms']:.3f} -> {wc['forward_writing_carries_ms']:.3f} "
+          f"ms, backward {wc['backward_reading_carries_ms']:.3f} ms (forward + backward {wc['forward_ms'] + cres['ms']:.3f} "
+          f"-> {wc['forward_writing_carries_ms'] + wc['backward_reading_carries_ms']:.3f} ms)", file=sys.stderr, flush=True)
     return {
+        "with_chunk_carries": {k: round(v, 4) for k, v in wc.items()},
         "workload": cres["name"], "ms_per_step": round(cres["ms"], 4),
         "tokens_per_s": round(cB * cT / (cres["ms"] * 1e-3), 1),
         "pass_ms": {k: round(v, 4) for k, v in cres["phase_ms"].items()},
@@ -793,10 +824,9 @@ def main(argv=None):
                   flush=True)
         return 0
     if args.bwd_chunked_only:
+        lib_sha = library_sha()
         for rule in ("gla", "gdn"):
-            cres = time_bwd_chunked(args.steps, args.warmup, rule=rule)
-            print(f"# {cres['name']}: {cres['ms']:.3f} ms/pass; passes (ms) "
-                  + ", ".join(f"{k} {v:.4f}" for k, v in cres["phase_ms"].items()), file=sys.stderr, flush=True)
+            bwd_chunked_entry(time_bwd_chunked(args.steps, args.warmup, rule=rule), lib_sha)  # prints its lines
         return 0
     if args.subspace_only:
         sres = time_subspace(5, 1)
