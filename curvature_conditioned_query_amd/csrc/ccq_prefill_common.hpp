@@ -121,8 +121,17 @@ template <typename T>
 __device__ __forceinline__ Frag<T> ident_frag(int h, int lane) {
   Frag<T> f;
   const int l = lane & 15, g = lane >> 4;
+  if constexpr (sizeof(T) == 2) {
+    // at most one element is one: e = l + 16h - 8g, in dword e / 2, half e % 2 (bf16 1.0 = 0x3F80)
+    const int e = l + 16 * h - 8 * g;
+    const unsigned one = (e & 1) ? 0x3F800000u : 0x3F80u;
+    const int j = e >> 1;
+    const u32x4 x{j == 0 ? one : 0u, j == 1 ? one : 0u, j == 2 ? one : 0u, j == 3 ? one : 0u};
+    f.v = __builtin_bit_cast(bf16x8, x);
+  } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = cvt<T>((8 * g + e == l + 16 * h) ? 1.0f : 0.0f);
+    for (int e = 0; e < 8; ++e) f.v[e] = cvt<T>((8 * g + e == l + 16 * h) ? 1.0f : 0.0f);
+  }
   return f;
 }
 
@@ -132,10 +141,22 @@ template <typename T>
 __device__ __forceinline__ Frag<T> ltri_frag(int ti, int kk, int lane) {
   Frag<T> f;
   const int t = 16 * ti + (lane & 15), g = lane >> 4;
+  if constexpr (sizeof(T) == 2) {
+    // element 4 hf + r is one where r <= d = t - 32 kk - 16 hf - 4 g: two bf16 ones per dword
+    u32x4 x;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int tp = 32 * kk + 16 * (e >> 2) + 4 * g + (e & 3);
-    f.v[e] = cvt<T>(tp <= t ? 1.0f : 0.0f);
+    for (int hf = 0; hf < 2; ++hf) {
+      const int d = t - 32 * kk - 16 * hf - 4 * g;
+      x[2 * hf] = d >= 1 ? 0x3F803F80u : (d >= 0 ? 0x3F80u : 0u);
+      x[2 * hf + 1] = d >= 3 ? 0x3F803F80u : (d >= 2 ? 0x3F80u : 0u);
+    }
+    f.v = __builtin_bit_cast(bf16x8, x);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tp = 32 * kk + 16 * (e >> 2) + 4 * g + (e & 3);
+      f.v[e] = cvt<T>(tp <= t ? 1.0f : 0.0f);
+    }
   }
   return f;
 }

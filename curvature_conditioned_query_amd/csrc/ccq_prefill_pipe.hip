@@ -59,21 +59,20 @@ struct PipeView {
   float (&m0)[D];
 };
 
-// Tile loads as DmaPlan's, 16 waves, rows at or past Lc (and the padding units) from the zero
-// row.
+// Tile loads as DmaPlan's: instruction j = w + NWAVES m of wave w loads the lane's unit from
+// element offset off[m] of the chunk.  A padding unit holds kL * D, so one compare against
+// Lc * D sends both it and the rows at or past Lc to the zero row.
 template <int D, typename T, int PQ, int NWAVES>
 struct PipeDma {
   static constexpr int U = PQ * (int)sizeof(T) / 16, DU = D * (int)sizeof(T) / 16, EPU = 16 / (int)sizeof(T);
   static constexpr int M = (U + NWAVES - 1) / NWAVES;
-  int row[M];
   int off[M];
   __device__ __forceinline__ PipeDma(int w, int lane) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const int u = 64 * (w + NWAVES * m) + lane;
       const int r = u / U, slot = u - r * U;
-      row[m] = slot < DU ? r : kL;
-      off[m] = slot < DU ? r * D + slot * EPU : 0;
+      off[m] = slot < DU ? r * D + slot * EPU : kL * D;
     }
   }
   __device__ __forceinline__ void load(T (*dst)[PQ], const T* src, int Lc, int w) const {
@@ -82,7 +81,7 @@ struct PipeDma {
       const int j = w + NWAVES * m;
       if (j >= U) continue;
       const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) T*)&dst[0][0];
-      const void* p = row[m] < Lc ? static_cast<const void*>(src + off[m]) : static_cast<const void*>(g_zero16);
+      const void* p = off[m] < Lc * D ? static_cast<const void*>(src + off[m]) : static_cast<const void*>(g_zero16);
       const unsigned m0 = __builtin_amdgcn_readfirstlane(base + 1024u * (unsigned)j);
       asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(p) : "memory", "m0");
     }
@@ -191,15 +190,16 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
   };
   const int nsteps = n <= 0 ? 0 : n + (split0 ? 2 : 1);
 
-  // tile loads; the lane's plan is rebuilt from the lane index passed in (inside the step loops
-  // a per-step opaque copy), so no per-lane plan stays live across a loop
-  auto dma = [&](T (*dst)[PQ], const T* src, int ch, int ln) {
-    const PipeDma<D, T, PQ, NWT> plan(wv, ln);
+  // tile loads; inside the step loops the lane's plan is built once per step from the step's
+  // opaque lane index, so no per-lane plan stays live across a loop
+  using Plan = PipeDma<D, T, PQ, NWT>;
+  auto dma = [&](T (*dst)[PQ], const T* src, int ch, const Plan& plan) {
     plan.load(dst, src + (tok0 + (size_t)ch * kL) * D, chunk_len(ch), wv);
   };
   if (n > 0) {
-    dma(sm.QB[cbeg & 1], qg, cbeg, lane);
-    dma(sm.KB[cbeg & 1], kg, cbeg, lane);
+    const Plan plan(wv, lane);
+    dma(sm.QB[cbeg & 1], qg, cbeg, plan);
+    dma(sm.KB[cbeg & 1], kg, cbeg, plan);
   }
   // Each side runs its own step loop (so that each is register-allocated on its own) with the
   // same barriers: one before the loop, two per step (s_barrier counts arrivals wherever they
@@ -209,7 +209,8 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
 #define CCQ_PIPE_STEP_LANE()                                                                      \
   int lane_;                                                                                     \
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_)); \
-  const int g_ = lane_ >> 4, l16_ = lane_ & 15;
+  const int g_ = lane_ >> 4, l16_ = lane_ & 15;                                                  \
+  const Plan plan(wv, lane_);
 
   if (cside) {
     // ======================= statistics side: 16 channels of C per wave
@@ -333,11 +334,11 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
           for (int r = 0; r < 4; ++r) sm.eBL[pc][c + r] = __expf(BT[3][r]);
         }
       }
-      if (nC >= 0) dma(sm.KB[nC & 1], kg, nC, lane_);
-      if (nS >= 0) dma(sm.VB[nS & 1], vg, nS, lane_);
+      if (nC >= 0) dma(sm.KB[nC & 1], kg, nC, plan);
+      if (nS >= 0) dma(sm.VB[nS & 1], vg, nS, plan);
       lds_barrier();
       // ---- phase B: cleaned query -> Qc e^B in place of q, C += K^T K
-      if (nC >= 0) dma(sm.QB[nC & 1], qg, nC, lane_);  // its buffer's Qc e^B (or low part) is consumed
+      if (nC >= 0) dma(sm.QB[nC & 1], qg, nC, plan);  // its buffer's Qc e^B (or low part) is consumed
       if (cc >= 0) {
         const int pc = cc & 1;
         T (*Ks)[PQ] = sm.KB[pc];
@@ -412,8 +413,8 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
       const int sc = s_at(s), nC = c_at(s + 1), nS = s_at(s + 1);
       f32x4 O[2][4];  // O^T for its value rows cw + 16 hh ..
       // ---- phase A: O = S0 (Qc e^B)^T, intra-chunk attention -> Am
-      if (nC >= 0) dma(sm.KB[nC & 1], kg, nC, lane_);
-      if (nS >= 0) dma(sm.VB[nS & 1], vg, nS, lane_);
+      if (nC >= 0) dma(sm.KB[nC & 1], kg, nC, plan);
+      if (nS >= 0) dma(sm.VB[nS & 1], vg, nS, plan);
       if (sc >= 0) {
         const int ps = sc & 1;
 #pragma unroll
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
       }
       lds_barrier();
       // ---- phase B: O += V^T A^T, o out, S <- diag(e^{B_63}) (S + (K e^-B)^T V)
-      if (nC >= 0) dma(sm.QB[nC & 1], qg, nC, lane_);
+      if (nC >= 0) dma(sm.QB[nC & 1], qg, nC, plan);
       if (sc >= 0) {
         const int ps = sc & 1;
         const int Lc = chunk_len(sc);
