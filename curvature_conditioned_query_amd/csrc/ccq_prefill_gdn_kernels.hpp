@@ -59,12 +59,15 @@ struct GdnSmem {
   float Tb[4][16][16 + 4]; // (I + A_bb)^{-1} of the four diagonal 16-token blocks
   float m0[D], m1[D];
   float lgam[kL], beta[kL];  // chunk-local log gamma_i, beta_i
+  float gam[kL], gdec[kL];   // gamma_i = e^{lgam_i} and gamma_L / gamma_i = e^{lgam_L - lgam_i}
   f32x4 tok[kL];             // lambda, 1/n, sq/n^2, gate logit + b
 };
 
 // ---------------------------------------------------------------- steps shared by the kernels
 
-// Wave 1: chunk-local log gamma (inclusive scan over lanes = tokens) and beta into LDS.
+// Wave 1: chunk-local log gamma (inclusive scan over lanes = tokens), beta, and the per-token
+// factors gamma_i and gamma_L / gamma_i into LDS (formed once here rather than by every lane
+// that scales by them).
 template <int D, typename T>
 __device__ __forceinline__ void gdn_gates(GdnSmem<D, T>& sm, float sg, float sb, int lane) {
   float x = sg;
@@ -75,6 +78,8 @@ __device__ __forceinline__ void gdn_gates(GdnSmem<D, T>& sm, float sg, float sb,
   }
   sm.lgam[lane] = x;
   sm.beta[lane] = sb;
+  sm.gam[lane] = __expf(x);
+  sm.gdec[lane] = __expf(__shfl(x, kL - 1, 64) - x);
 }
 
 // A = beta Gam (K K^T) below the diagonal, lower 16x16 tiles idx = i0, i0 + step, ... < 10.
@@ -200,12 +205,12 @@ __device__ __forceinline__ void gdn_rhs(const GdnSmem<D, T>& sm, const T (*Ks)[C
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int j0 = 16 * b + 4 * g;
-    const f32x4 lg = *reinterpret_cast<const f32x4*>(&sm.lgam[j0]);
+    const f32x4 gm = *reinterpret_cast<const f32x4*>(&sm.gam[j0]);
     const f32x4 bt = *reinterpret_cast<const f32x4*>(&sm.beta[j0]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float v = WITH_V ? to_f32(sm.Vs[j0 + r][cw + l16]) : 0.f;
-      X[b][r] = bt[r] * (v - __expf(lg[r]) * X[b][r]);
+      X[b][r] = bt[r] * (v - gm[r] * X[b][r]);
     }
   }
 }
@@ -237,20 +242,14 @@ __device__ __forceinline__ void gdn_state_update(const GdnSmem<D, T>& sm, const 
   using C_ = Cfg<D, T>;
   constexpr int NA = C_::NA, PQ = C_::PQ;
   const int g = lane >> 4;
-  const float lgL = sm.lgam[kL - 1];
-  const float gL = __expf(lgL);
+  const float gL = sm.gam[kL - 1];
 #pragma unroll
   for (int t = 0; t < NA; ++t) stile(t) *= gL;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     f32x4 d0 = Dl[2 * kk], d1 = Dl[2 * kk + 1];
-    const f32x4 lg0 = *reinterpret_cast<const f32x4*>(&sm.lgam[32 * kk + 4 * g]);
-    const f32x4 lg1 = *reinterpret_cast<const f32x4*>(&sm.lgam[32 * kk + 16 + 4 * g]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      d0[r] *= __expf(lgL - lg0[r]);
-      d1[r] *= __expf(lgL - lg1[r]);
-    }
+    d0 *= *reinterpret_cast<const f32x4*>(&sm.gdec[32 * kk + 4 * g]);
+    d1 *= *reinterpret_cast<const f32x4*>(&sm.gdec[32 * kk + 16 + 4 * g]);
     const Frag<T> Bd = acc_frag<T>(d0, d1);  // diag(gamma_L / gamma) Delta, own columns
 #pragma unroll
     for (int t = 0; t < NA; ++t) mma(stile(t), tr_frag_acc<T>(&Ks[0][0], PQ, 32 * kk, 16 * t, lane), Bd);
@@ -472,7 +471,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
       for (int ti = 0; ti < 4; ++ti) mma(O[ti], A, lds_frag<T, KORD_ACC>(&sm.Qa[0][0], PQ, 16 * ti, 32 * kk, lane));
     }
 #pragma unroll
-    for (int ti = 0; ti < 4; ++ti) O[ti] *= __expf(sm.lgam[16 * ti + l16]);
+    for (int ti = 0; ti < 4; ++ti) O[ti] *= sm.gam[16 * ti + l16];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const Frag<T> A = acc_frag<T>(Dl[2 * kk], Dl[2 * kk + 1]);  // Delta^T, own rows
