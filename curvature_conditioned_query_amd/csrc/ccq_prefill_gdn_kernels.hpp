@@ -215,9 +215,12 @@ __device__ __forceinline__ void gdn_rhs(const GdnSmem<D, T>& sm, const T (*Ks)[C
   }
 }
 
-// Delta = (I + A)^{-1} X by 16-token blocks (fp32 MFMAs), on the wave's columns.
+// Delta = (I + A)^{-1} X by 16-token blocks on the wave's columns:
+//   Delta_b = T_b (X_b - sum_{b' < b} A_bb' Delta_b'),  T_b = (I + A_bb)^{-1}  (in sm.Tb),
+// fp32 operands (A and T from LDS, Delta in the accumulators).
+// fp32 tiles: v_mfma_f32_16x16x4_f32, one K-slice of 4 per instruction.
 template <int D, typename T>
-__device__ __forceinline__ void gdn_solve(const GdnSmem<D, T>& sm, const f32x4 (&X)[4], int lane, f32x4 (&Dl)[4]) {
+__device__ __forceinline__ void gdn_solve_f32(const GdnSmem<D, T>& sm, const f32x4 (&X)[4], int lane, f32x4 (&Dl)[4]) {
   const int g = lane >> 4, l16 = lane & 15;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -233,6 +236,90 @@ __device__ __forceinline__ void gdn_solve(const GdnSmem<D, T>& sm, const f32x4 (
 #pragma unroll
     for (int r = 0; r < 4; ++r) Dl[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(t4[r], Z[r], Dl[b], 0, 0, 0);
   }
+}
+
+// bf16 hi + lo split of 8 fp32 values (x0 then x1, negated when NEG) into a KORD_ACC fragment
+// pair: elements 0..3 from x0, 4..7 from x1.
+template <bool NEG>
+__device__ __forceinline__ void split_hl(const f32x4& x0, const f32x4& x1, Frag<__bf16>& h, Frag<__bf16>& l) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = NEG ? -(e < 4 ? x0[e] : x1[e - 4]) : (e < 4 ? x0[e] : x1[e - 4]);
+    h.v[e] = (__bf16)v;
+    l.v[e] = (__bf16)(v - (float)h.v[e]);
+  }
+}
+
+// The same for NR right-hand sides at once on bf16 tiles: every product is three
+// v_mfma_f32_16x16x32_bf16 on hi + lo splits of its fp32 operands (hi.hi + hi.lo + lo.hi, about
+// 16 significant bits, against 8 for a plain bf16 product), with two 16-token blocks of the
+// reduction per instruction: a third of the matrix-core time of the fp32 form.  The systems
+// share the split A and T fragments, and their chains interleave.  KORD_ACC pairs: A's element
+// e of lane (g, i) is A[16 b + i][16 p0 + 4 g + e] (e < 4) or [16 p1 + 4 g + e - 4]; Delta's is
+// Delta[16 p0 + 4 g + e][i] or [16 p1 + 4 g + e - 4][i], exactly the accumulator rows of blocks
+// p0 and p1.
+template <int D, typename T, int NR>
+__device__ __forceinline__ void gdn_solve_n(const GdnSmem<D, T>& sm, const f32x4 (&X)[NR][4], int lane,
+                                            f32x4 (&Dl)[NR][4]) {
+  if constexpr (sizeof(T) != 2) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) gdn_solve_f32<D, T>(sm, X[r], lane, Dl[r]);
+  } else {
+    const int g = lane >> 4, l16 = lane & 15;
+    Frag<T> Bh[NR][2], Bl[NR][2];  // Delta pairs (0, 1) and (2, -), hi and lo, as blocks complete
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        Bh[r][p].v = bf16x8{};
+        Bl[r][p].v = bf16x8{};
+      }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      f32x4 Z[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) Z[r] = X[r][b];
+#pragma unroll
+      for (int pr = 0; 2 * pr < b; ++pr) {  // block pairs with a block before b: -A_b,pair Delta_pair
+        const int p0 = 2 * pr, p1 = 2 * pr + 1;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(&sm.As[16 * b + l16][16 * p0 + 4 * g]);
+        const f32x4 a1 = p1 < b ? *reinterpret_cast<const f32x4*>(&sm.As[16 * b + l16][16 * p1 + 4 * g]) : zero4();
+        Frag<T> Ah, Al;
+        split_hl<true>(a0, a1, Ah, Al);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          mma(Z[r], Ah, Bh[r][pr]);
+          mma(Z[r], Ah, Bl[r][pr]);
+          mma(Z[r], Al, Bh[r][pr]);
+        }
+      }
+      Frag<T> Th, Tl;
+      split_hl<false>(*reinterpret_cast<const f32x4*>(&sm.Tb[b][l16][4 * g]), zero4(), Th, Tl);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        Frag<T> zh, zl;
+        split_hl<false>(Z[r], zero4(), zh, zl);
+        Dl[r][b] = zero4();
+        mma(Dl[r][b], Th, zh);
+        mma(Dl[r][b], Th, zl);
+        mma(Dl[r][b], Tl, zh);
+        if (b < 3) {  // into half b % 2 of pair b / 2
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = Dl[r][b][e];
+            const __bf16 hv = (__bf16)v;
+            Bh[r][b / 2].v[4 * (b % 2) + e] = hv;
+            Bl[r][b / 2].v[4 * (b % 2) + e] = (__bf16)(v - (float)hv);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int D, typename T>
+__device__ __forceinline__ void gdn_solve(const GdnSmem<D, T>& sm, const f32x4 (&X)[4], int lane, f32x4 (&Dl)[4]) {
+  gdn_solve_n<D, T, 1>(sm, *reinterpret_cast<const f32x4(*)[1][4]>(&X), lane, *reinterpret_cast<f32x4(*)[1][4]>(&Dl));
 }
 
 // S^T = gamma_L S^T + K^T diag(gamma_L / gamma) Delta on the wave's state tiles.
@@ -598,9 +685,9 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
     lds_barrier();
 
     if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
-    f32x4 XS[4], XM[4];
-    gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, XS);
-    gdn_rhs<D, T, false>(sm, Ks, [&](int t) -> const f32x4& { return Macc[t]; }, cw, lane, XM);
+    f32x4 XSM[2][4];  // right-hand sides of the S and M recurrences
+    gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, XSM[0]);
+    gdn_rhs<D, T, false>(sm, Ks, [&](int t) -> const f32x4& { return Macc[t]; }, cw, lane, XSM[1]);
     lds_barrier();
     if (ch + 1 < cend) {
       dma_rows(sm.Vs, vg, ch + 1, lane);
@@ -608,14 +695,10 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
     }
 
     {
-      f32x4 Dl[4];
-      gdn_solve<D, T>(sm, XS, lane, Dl);
-      gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Sacc[t]; }, Dl, lane);
-    }
-    {
-      f32x4 Dl[4];
-      gdn_solve<D, T>(sm, XM, lane, Dl);
-      gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Macc[t]; }, Dl, lane);
+      f32x4 Dl[2][4];
+      gdn_solve_n<D, T, 2>(sm, XSM, lane, Dl);
+      gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Sacc[t]; }, Dl[0], lane);
+      gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Macc[t]; }, Dl[1], lane);
     }
     gdn_cov_update<D, T>(Ks, Cacc, cw, lane);
     if (tid < D) sm.m0[tid] = sm.m1[tid];
