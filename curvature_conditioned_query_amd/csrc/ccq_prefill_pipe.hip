@@ -408,6 +408,27 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) put_carry_row<D, T, NA>(a, chain, cbeg, 0, cw + 16 * hh + l16, g, Sacc[hh]);
     }
+    // S += (K e^-B)^T V over tokens 32 kk .. 32 kk + 31 of chunk parity ps (each k e^-B fragment
+    // serves both row halves); the decay e^{B_63} follows once both halves are in
+    auto s_update = [&](int ps, int kk) {
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      T (*Vs)[PQ] = sm.VB[ps];
+      const Frag<T> Bv0 = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, ln);
+      const Frag<T> Bv1 = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw + 16, ln);
+#pragma unroll
+      for (int t0_ = 0; t0_ < NA; t0_ += 4) {
+        Frag<T> Ap[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Ap[u] = tr_frag<T>(&sm.PB[ps][0][0], PQ, 32 * kk, 16 * (t0_ + u), ln);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          mma(Sacc[0][t0_ + u], Ap[u], Bv0);
+          mma(Sacc[1][t0_ + u], Ap[u], Bv1);
+        }
+      }
+    };
     for (int s = 0; s < nsteps; ++s) {
       CCQ_PIPE_STEP_LANE()
       const int sc = s_at(s), nC = c_at(s + 1), nS = s_at(s + 1);
@@ -463,6 +484,10 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
           for (int r = 0; r < 4; ++r) acc[r] = (16 * tj + 4 * g_ + r <= i) ? acc[r] : 0.f;
           st4<T>(&sm.Am[i][16 * tj + 4 * g_], acc);
         }
+        // the state update's first half (tokens 0..31) here, where the state side would wait for
+        // the statistics side's Gram rows; O above has read S0 already.  k e^-B and v of chunk sc
+        // have been in LDS since the previous step.
+        s_update(ps, 0);
       }
       lds_barrier();
       // ---- phase B: O += V^T A^T, o out, S <- diag(e^{B_63}) (S + (K e^-B)^T V)
@@ -491,23 +516,7 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
             const int i = 16 * ti + l16_;
             if (i < Lc) st4<T>(og + (t0 + i) * D + cw + 16 * hh + 4 * g_, O[hh][ti]);
           }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {  // each k e^-B fragment serves both row halves
-          const Frag<T> Bv0 = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane_);
-          const Frag<T> Bv1 = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw + 16, lane_);
-#pragma unroll
-          for (int t0_ = 0; t0_ < NA; t0_ += 4) {
-            Frag<T> Ap[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) Ap[u] = tr_frag<T>(&sm.PB[ps][0][0], PQ, 32 * kk, 16 * (t0_ + u), lane_);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              mma(Sacc[0][t0_ + u], Ap[u], Bv0);
-              mma(Sacc[1][t0_ + u], Ap[u], Bv1);
-            }
-          }
-        }
+        s_update(ps, 1);  // tokens 32..63 (tokens 0..31 went in phase A)
 #pragma unroll
         for (int t = 0; t < NA; ++t) {
           const f32x4 e4 = *reinterpret_cast<const f32x4*>(&sm.eBL[ps][16 * t + 4 * g_]);
