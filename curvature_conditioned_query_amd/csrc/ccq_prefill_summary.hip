@@ -30,16 +30,16 @@ struct SumSmem {
   float eBL[2][D];      // e^{B_63} per key channel
 };
 
-template <int D, typename T>
-__global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
+// WITH_C: the workgroup also accumulates C = sum K^T K (otherwise gla_csum_body does, beside it).
+template <int D, typename T, bool WITH_C>
+__device__ __forceinline__ void gla_summary_body(const FwdArgs& a, SumSmem<D, T>& sm, int bid) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
-  __shared__ SumSmem<D, T> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
   const int cw = 16 * w, hb = w & 1, cb = cw - 16 * hb;
   const int P = a.segments, n = a.chunks_per_segment;
-  const int chain = blockIdx.x / (P - 1), seg = blockIdx.x % (P - 1);
+  const int chain = bid / (P - 1), seg = bid % (P - 1);
   const int cbeg = seg * n;
   const size_t tok0 = (size_t)chain * (size_t)a.T;
   const T* kg = static_cast<const T*>(a.k);
@@ -153,20 +153,21 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
     T (*Vs)[PQ] = sm.Vs[i & 1];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);
+      Frag<T> Bk{};
+      if constexpr (WITH_C) Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);
       const Frag<T> Bv = tr_frag<T>(&Vs[0][0], PQ, 32 * kk, cw, lane);
 #pragma unroll
       for (int t0_ = 0; t0_ < NA; t0_ += 4) {
         Frag<T> Ak[4], Ap[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          Ak[u] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
+          if constexpr (WITH_C) Ak[u] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
           Ap[u] = tr_frag<T>(&Kp[0][0], PQ, 32 * kk, 16 * (t0_ + u), lane);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          mma(Cacc[t0_ + u], Ak[u], Bk);
+          if constexpr (WITH_C) mma(Cacc[t0_ + u], Ak[u], Bk);
           mma(Sacc[t0_ + u], Ap[u], Bv);
         }
         if (2 * kParts + kk * (NA / 4) + t0_ / 4 < 3 * kParts) issue(i, 2 * kParts + kk * (NA / 4) + t0_ / 4);
@@ -193,12 +194,94 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
     for (int t = 0; t < NA; ++t) {
       const int col = 16 * t + 4 * g;
       *reinterpret_cast<f32x4*>(slot + (size_t)row * D + col) = Sacc[t];
-      *reinterpret_cast<f32x4*>(slot + (size_t)D * D + (size_t)row * D + col) = Cacc[t];
+      if constexpr (WITH_C) *reinterpret_cast<f32x4*>(slot + (size_t)D * D + (size_t)row * D + col) = Cacc[t];
     }
     const int c = cw + 4 * g;
     if (l16 == 0) *reinterpret_cast<f32x4*>(slot + 2 * (size_t)D * D + c) = ksum;
     if (l16 == 15) *reinterpret_cast<f32x4*>(slot + 2 * (size_t)D * D + D + c) = ldec;
   }
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
+  __shared__ SumSmem<D, T> sm;
+  gla_summary_body<D, T, true>(a, sm, blockIdx.x);
+}
+
+// The C part of the segment summaries, C_seg = sum over the segment's chunks of K^T K, on its own:
+// workgroup j (of Wc) takes units (chain, segment) j, j + Wc, ...; key tiles stream through two LDS
+// buffers; the products are the summary kernel's own, in its order, so the sums are the same.
+template <int D, typename T>
+struct CSumSmem {
+  T Ks[2][kL][Cfg<D, T>::PQ];
+};
+template <int D, typename T>
+__device__ __forceinline__ void gla_csum_body(const FwdArgs& a, CSumSmem<D, T>& sm, int j, int Wc) {
+  using C_ = Cfg<D, T>;
+  constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int cw = 16 * w;
+  const int P = a.segments, n = a.chunks_per_segment;
+  const int units = a.B * a.H * (P - 1);
+  const T* kg = static_cast<const T*>(a.k);
+  const bool norm = (a.flags & kFlagNormalizeKeys) != 0;
+  const DmaPlan<D, T, PQ, NW> plan(w, lane);
+  const size_t slot_f = 2 * (size_t)D * D + 2 * D;
+  for (int u = j; u < units; u += Wc) {
+    const int chain = u / (P - 1), seg = u % (P - 1);
+    const T* src = kg + ((size_t)chain * (size_t)a.T + (size_t)seg * n * kL) * D;  // whole chunks
+    f32x4 Cacc[NA];
+#pragma unroll
+    for (int t = 0; t < NA; ++t) Cacc[t] = zero4();
+    plan.load(sm.Ks[0], src, kL, w);
+    for (int i = 0; i < n; ++i) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();  // chunk i has landed; chunk i-1's buffer is free
+      if (i + 1 < n) plan.load(sm.Ks[(i + 1) & 1], src + (size_t)(i + 1) * kL * D, kL, w);
+      T (*Ks)[PQ] = sm.Ks[i & 1];
+      if (norm) {
+        normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
+        lds_barrier();
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);
+#pragma unroll
+        for (int t0_ = 0; t0_ < NA; t0_ += 4) {
+          Frag<T> Ak[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Ak[v] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + v), lane);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mma(Cacc[t0_ + v], Ak[v], Bk);
+        }
+      }
+    }
+    float* slot = static_cast<float*>(a.workspace) + ((size_t)chain * P + seg) * slot_f + (size_t)D * D;
+    const int row = cw + l16;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) *reinterpret_cast<f32x4*>(slot + (size_t)row * D + 16 * t + 4 * g) = Cacc[t];
+    lds_barrier();  // the last chunk's buffer is read before the next unit loads over it
+  }
+}
+
+// The summary in two roles of one launch: workgroups 0 .. chains (P-1) - 1 summarise S (and the key
+// sums and log decays) without C, the rest accumulate C on compute units the summary would leave
+// idle.  The C products are a fifth of a summary chunk's latency chain; moving them out of it
+// leaves the S workgroups a shorter step.
+template <int D, typename T>
+union SplitSumSmem {
+  SumSmem<D, T> s;
+  CSumSmem<D, T> c;
+};
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gla_summary_split_kernel(FwdArgs a) {
+  __shared__ SplitSumSmem<D, T> sm;
+  const int nS = a.B * a.H * (a.segments - 1);
+  if ((int)blockIdx.x < nS)
+    gla_summary_body<D, T, false>(a, sm.s, blockIdx.x);
+  else
+    gla_csum_body<D, T>(a, sm.c, blockIdx.x - nS, gridDim.x - nS);
 }
 
 // Exclusive scan of segment summaries into carry-ins, in place.  Slot p holds the summary
@@ -265,10 +348,19 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
   }
 }
 
+// Compute units of the device the split summary counts on (MI355X).
+constexpr int kSummaryCUs = 256;
+
 template <int D, typename T>
 static void launch_summary_t(const FwdArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gla_summary_kernel<D, T>), dim3((unsigned)(a.B * a.H * (a.segments - 1))), dim3(4 * D), 0,
-                     s, a);
+  const int nS = a.B * a.H * (a.segments - 1);
+  // Split when the summary leaves compute units idle, and enough of them that no C workgroup takes
+  // more than three segments (its step is about a third of the summary's).
+  const int Wc = nS < kSummaryCUs - nS ? nS : kSummaryCUs - nS;
+  if (Wc > 0 && 3 * Wc >= nS)
+    hipLaunchKernelGGL((gla_summary_split_kernel<D, T>), dim3((unsigned)(nS + Wc)), dim3(4 * D), 0, s, a);
+  else
+    hipLaunchKernelGGL((gla_summary_kernel<D, T>), dim3((unsigned)nS), dim3(4 * D), 0, s, a);
 }
 
 template <int D>
