@@ -320,6 +320,72 @@ __device__ __forceinline__ void normalize_rows(T (*K)[PQ], int tid, int nthreads
   }
 }
 
+// Workgroups for the C part when a summary runs in two roles (0: the fused summary): one per
+// compute unit the nS summary workgroups leave idle on the 256 of an MI355X, if that gives no C
+// workgroup more than three segments (its step is about a third of a summary step).
+__host__ __device__ inline int summary_c_groups(int nS) {
+  constexpr int kCUs = 256;
+  const int Wc = nS < kCUs - nS ? nS : kCUs - nS;
+  return (Wc > 0 && 3 * Wc >= nS) ? Wc : 0;
+}
+
+// The C part of the segment summaries (both rules), C_seg = sum over the segment's chunks of K^T K,
+// on its own: workgroup j (of Wc) takes units (chain, segment) j, j + Wc, ...; key tiles stream
+// through two LDS buffers; the products are the summary kernels' own, in their order, so the sums
+// are the same.  C goes to the unit's workspace slot (slot_f floats each) at offset D^2.
+template <int D, typename T>
+struct CSumSmem {
+  T Ks[2][kL][Cfg<D, T>::PQ];
+};
+template <int D, typename T>
+__device__ __forceinline__ void csum_body(const FwdArgs& a, CSumSmem<D, T>& sm, int j, int Wc, size_t slot_f) {
+  using C_ = Cfg<D, T>;
+  constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
+  const int cw = 16 * w;
+  const int P = a.segments, n = a.chunks_per_segment;
+  const int units = a.B * a.H * (P - 1);
+  const T* kg = static_cast<const T*>(a.k);
+  const bool norm = (a.flags & kFlagNormalizeKeys) != 0;
+  const DmaPlan<D, T, PQ, NW> plan(w, lane);
+  for (int u = j; u < units; u += Wc) {
+    const int chain = u / (P - 1), seg = u % (P - 1);
+    const T* src = kg + ((size_t)chain * (size_t)a.T + (size_t)seg * n * kL) * D;  // whole chunks
+    f32x4 Cacc[NA];
+#pragma unroll
+    for (int t = 0; t < NA; ++t) Cacc[t] = zero4();
+    plan.load(sm.Ks[0], src, kL, w);
+    for (int i = 0; i < n; ++i) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();  // chunk i has landed; chunk i-1's buffer is free
+      if (i + 1 < n) plan.load(sm.Ks[(i + 1) & 1], src + (size_t)(i + 1) * kL * D, kL, w);
+      T (*Ks)[PQ] = sm.Ks[i & 1];
+      if (norm) {
+        normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
+        lds_barrier();
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);
+#pragma unroll
+        for (int t0_ = 0; t0_ < NA; t0_ += 4) {
+          Frag<T> Ak[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Ak[v] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + v), lane);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mma(Cacc[t0_ + v], Ak[v], Bk);
+        }
+      }
+    }
+    float* slot = static_cast<float*>(a.workspace) + ((size_t)chain * P + seg) * slot_f + (size_t)D * D;
+    const int row = cw + l16;
+#pragma unroll
+    for (int t = 0; t < NA; ++t) *reinterpret_cast<f32x4*>(slot + (size_t)row * D + 16 * t + 4 * g) = Cacc[t];
+    lds_barrier();  // the last chunk's buffer is read before the next unit loads over it
+  }
+}
+
 // Gate logit and m0 . q, then the row tile of P = Q K^T, its inclusive row sums and
 // Pm = tril(P - c 1^T), for the 16-token row tiles it = w, w + NWAVES, ... < 4.  Writes
 // sm.Pm and sm.tok[i] = {lambda_i, 1/n_i, sq_i / n_i^2, logit_i}; nb is the number of tokens

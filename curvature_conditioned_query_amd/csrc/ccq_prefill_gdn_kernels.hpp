@@ -614,17 +614,17 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
 // the transition recurrence (state starting at I, v = 0), M_p, side by side, sharing the
 // staged keys, A and the diagonal inverses; writes both to slot p.  Summary segments are
 // whole chunks.
-template <int D, typename T>
-__global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
+// WITH_C: the workgroup also accumulates dC = sum K^T K (otherwise csum_body does, beside it).
+template <int D, typename T, bool WITH_C>
+__device__ __forceinline__ void gdn_summary_body(const FwdArgs& a, GdnSmem<D, T>& sm, int bid) {
   using C_ = Cfg<D, T>;
   constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
-  __shared__ GdnSmem<D, T> sm;
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int cw = 16 * w;
   const int P = a.segments, cps = a.chunks_per_segment;
-  const int chain = blockIdx.x / (P - 1), seg = blockIdx.x % (P - 1);
+  const int chain = bid / (P - 1), seg = bid % (P - 1);
   const int nchunks = (a.T + kL - 1) / kL;
   const int cbeg = seg * cps;
   const int cend = min(nchunks, cbeg + cps);
@@ -700,7 +700,7 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
       gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Sacc[t]; }, Dl[0], lane);
       gdn_state_update<D, T>(sm, Ks, [&](int t) -> f32x4& { return Macc[t]; }, Dl[1], lane);
     }
-    gdn_cov_update<D, T>(Ks, Cacc, cw, lane);
+    if constexpr (WITH_C) gdn_cov_update<D, T>(Ks, Cacc, cw, lane);
     if (tid < D) sm.m0[tid] = sm.m1[tid];
     lds_barrier();
   }
@@ -711,10 +711,33 @@ __global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
   for (int t = 0; t < NA; ++t) {
     const size_t o = (size_t)row * D + 16 * t + 4 * g;
     *reinterpret_cast<f32x4*>(slot + o) = Sacc[t];
-    *reinterpret_cast<f32x4*>(slot + (size_t)D * D + o) = Cacc[t];
+    if constexpr (WITH_C) *reinterpret_cast<f32x4*>(slot + (size_t)D * D + o) = Cacc[t];
     *reinterpret_cast<f32x4*>(slot + 2 * (size_t)D * D + D + o) = Macc[t];
   }
   if (tid < D) slot[2 * (size_t)D * D + tid] = sm.m0[tid];
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gdn_summary_kernel(FwdArgs a) {
+  __shared__ GdnSmem<D, T> sm;
+  gdn_summary_body<D, T, true>(a, sm, blockIdx.x);
+}
+
+// The summary in two roles of one launch (as gla_summary_split_kernel): summary workgroups without
+// dC, and dC workgroups on the compute units the summary leaves idle.
+template <int D, typename T>
+union GdnSplitSmem {
+  GdnSmem<D, T> s;
+  CSumSmem<D, T> c;
+};
+template <int D, typename T>
+__global__ __launch_bounds__(4 * D) void gdn_summary_split_kernel(FwdArgs a) {
+  __shared__ GdnSplitSmem<D, T> sm;
+  const int nS = a.B * a.H * (a.segments - 1);
+  if ((int)blockIdx.x < nS)
+    gdn_summary_body<D, T, false>(a, sm.s, blockIdx.x);
+  else
+    csum_body<D, T>(a, sm.c, blockIdx.x - nS, gridDim.x - nS, gdn_slot_floats(D));
 }
 
 // ---------------------------------------------------------------- scans over segments

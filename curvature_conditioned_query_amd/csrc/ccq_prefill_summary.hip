@@ -30,7 +30,7 @@ struct SumSmem {
   float eBL[2][D];      // e^{B_63} per key channel
 };
 
-// WITH_C: the workgroup also accumulates C = sum K^T K (otherwise gla_csum_body does, beside it).
+// WITH_C: the workgroup also accumulates C = sum K^T K (otherwise csum_body does, beside it).
 template <int D, typename T, bool WITH_C>
 __device__ __forceinline__ void gla_summary_body(const FwdArgs& a, SumSmem<D, T>& sm, int bid) {
   using C_ = Cfg<D, T>;
@@ -208,63 +208,6 @@ __global__ __launch_bounds__(4 * D) void gla_summary_kernel(FwdArgs a) {
   gla_summary_body<D, T, true>(a, sm, blockIdx.x);
 }
 
-// The C part of the segment summaries, C_seg = sum over the segment's chunks of K^T K, on its own:
-// workgroup j (of Wc) takes units (chain, segment) j, j + Wc, ...; key tiles stream through two LDS
-// buffers; the products are the summary kernel's own, in its order, so the sums are the same.
-template <int D, typename T>
-struct CSumSmem {
-  T Ks[2][kL][Cfg<D, T>::PQ];
-};
-template <int D, typename T>
-__device__ __forceinline__ void gla_csum_body(const FwdArgs& a, CSumSmem<D, T>& sm, int j, int Wc) {
-  using C_ = Cfg<D, T>;
-  constexpr int NW = C_::NW, NA = C_::NA, PQ = C_::PQ;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
-  const int cw = 16 * w;
-  const int P = a.segments, n = a.chunks_per_segment;
-  const int units = a.B * a.H * (P - 1);
-  const T* kg = static_cast<const T*>(a.k);
-  const bool norm = (a.flags & kFlagNormalizeKeys) != 0;
-  const DmaPlan<D, T, PQ, NW> plan(w, lane);
-  const size_t slot_f = 2 * (size_t)D * D + 2 * D;
-  for (int u = j; u < units; u += Wc) {
-    const int chain = u / (P - 1), seg = u % (P - 1);
-    const T* src = kg + ((size_t)chain * (size_t)a.T + (size_t)seg * n * kL) * D;  // whole chunks
-    f32x4 Cacc[NA];
-#pragma unroll
-    for (int t = 0; t < NA; ++t) Cacc[t] = zero4();
-    plan.load(sm.Ks[0], src, kL, w);
-    for (int i = 0; i < n; ++i) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lds_barrier();  // chunk i has landed; chunk i-1's buffer is free
-      if (i + 1 < n) plan.load(sm.Ks[(i + 1) & 1], src + (size_t)(i + 1) * kL * D, kL, w);
-      T (*Ks)[PQ] = sm.Ks[i & 1];
-      if (norm) {
-        normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
-        lds_barrier();
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const Frag<T> Bk = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, cw, lane);
-#pragma unroll
-        for (int t0_ = 0; t0_ < NA; t0_ += 4) {
-          Frag<T> Ak[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v) Ak[v] = tr_frag<T>(&Ks[0][0], PQ, 32 * kk, 16 * (t0_ + v), lane);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) mma(Cacc[t0_ + v], Ak[v], Bk);
-        }
-      }
-    }
-    float* slot = static_cast<float*>(a.workspace) + ((size_t)chain * P + seg) * slot_f + (size_t)D * D;
-    const int row = cw + l16;
-#pragma unroll
-    for (int t = 0; t < NA; ++t) *reinterpret_cast<f32x4*>(slot + (size_t)row * D + 16 * t + 4 * g) = Cacc[t];
-    lds_barrier();  // the last chunk's buffer is read before the next unit loads over it
-  }
-}
-
 // The summary in two roles of one launch: workgroups 0 .. chains (P-1) - 1 summarise S (and the key
 // sums and log decays) without C, the rest accumulate C on compute units the summary would leave
 // idle.  The C products are a fifth of a summary chunk's latency chain; moving them out of it
@@ -281,7 +224,7 @@ __global__ __launch_bounds__(4 * D) void gla_summary_split_kernel(FwdArgs a) {
   if ((int)blockIdx.x < nS)
     gla_summary_body<D, T, false>(a, sm.s, blockIdx.x);
   else
-    gla_csum_body<D, T>(a, sm.c, blockIdx.x - nS, gridDim.x - nS);
+    csum_body<D, T>(a, sm.c, blockIdx.x - nS, gridDim.x - nS, 2 * (size_t)D * D + 2 * D);
 }
 
 // Exclusive scan of segment summaries into carry-ins, in place.  Slot p holds the summary
@@ -348,16 +291,11 @@ __global__ __launch_bounds__(256) void gla_scan_kernel(FwdArgs a) {
   }
 }
 
-// Compute units of the device the split summary counts on (MI355X).
-constexpr int kSummaryCUs = 256;
-
 template <int D, typename T>
 static void launch_summary_t(const FwdArgs& a, hipStream_t s) {
   const int nS = a.B * a.H * (a.segments - 1);
-  // Split when the summary leaves compute units idle, and enough of them that no C workgroup takes
-  // more than three segments (its step is about a third of the summary's).
-  const int Wc = nS < kSummaryCUs - nS ? nS : kSummaryCUs - nS;
-  if (Wc > 0 && 3 * Wc >= nS)
+  const int Wc = summary_c_groups(nS);
+  if (Wc > 0)
     hipLaunchKernelGGL((gla_summary_split_kernel<D, T>), dim3((unsigned)(nS + Wc)), dim3(4 * D), 0, s, a);
   else
     hipLaunchKernelGGL((gla_summary_kernel<D, T>), dim3((unsigned)nS), dim3(4 * D), 0, s, a);
