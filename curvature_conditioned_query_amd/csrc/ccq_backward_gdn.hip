@@ -583,6 +583,10 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
 // chain), two waves of 16 rows each; a wave keeps its rows transposed in MFMA accumulators
 // (dSt[a][r] at lane (g, l) = dS[v0 + l][16 a + 4 g + r]), so the running adjoint never leaves the
 // registers.  dS_end(c) replaces R_c in the workspace (input dtype).
+// The same walk carries the additive adjoints: G(c) = dC_T + sum over later chunks of dG (the second
+// half of each chunk's adjoint matrices, replaced in place) on the workgroup's 32 rows, and, on the
+// first row block of a chain, dm_after(c) (replacing the chunk's dm) with dw and db summed; their
+// loads go out at the top of a chunk's step and the sums at its end, in the shadow of the dS chain.
 // The walk is software-pipelined one chunk ahead, and every read goes straight from HBM into LDS
 // (direct loads the compiler does not wait for): while chunk c is applied, chunk c-1's key tile,
 // inverse, R block and raw gates stream into the other half of two LDS buffers.  Each wave forms the
@@ -628,6 +632,35 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
   for (int t = 0; t < NA; ++t)
     dSt[t] = a.dS_T ? *reinterpret_cast<const f32x4*>(a.dS_T + (size_t)chain * DD + (size_t)(v0 + l16) * D + 16 * t + 4 * g)
                     : zero4();
+  // G on rows r0 .. r0 + 31: thread tid owns 16-byte vectors tid + 128 j
+  constexpr int EPV = 16 / (int)sizeof(T), GV = 32 * D / EPV / 128;
+  static_assert(GV * 128 * EPV == 32 * D, "whole vectors per thread");
+  T* gmat = L.mat + (size_t)chain * NC * 2 * DD + DD + (size_t)r0 * D;  // chunk 0's G block
+  float grun[GV][EPV];
+#pragma unroll
+  for (int j = 0; j < GV; ++j) {
+    const float* src = a.dC_T ? a.dC_T + (size_t)chain * DD + (size_t)r0 * D + (size_t)(tid + 128 * j) * EPV : nullptr;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) grun[j][e] = src ? src[e] : 0.f;
+  }
+  // tails dm | dw | db (first row block): thread tid < 3D/4 owns 4 floats of part (4 tid) / D
+  const bool tails = blockIdx.x == 0 && tid < 3 * D / 4;
+  const int tpart = (4 * tid) / D;  // 0 dm (scanned), 1 dw, 2 db (summed)
+  // (every thread reads a whole-block address, so the loads below need no branch: 4 (tid mod D) < 4 D)
+  float* tbase = L.tail + (size_t)chain * NC * 4 * D + 4 * (tid & (D - 1));
+  f32x4 trun = (tails && tpart == 0 && a.dksum_T) ? *reinterpret_cast<const f32x4*>(a.dksum_T + (size_t)chain * D + 4 * tid)
+                                                   : zero4();
+  // chunk c's dG on the workgroup's rows and its tails, loaded one step ahead of their use so that
+  // the wait for them never waits for the direct loads issued after them
+  auto load_sums = [&](int c, u32x4 (&gx)[GV], f32x4& tx) {
+#pragma unroll
+    for (int j = 0; j < GV; ++j) gx[j] = *reinterpret_cast<const u32x4*>(gmat + (size_t)c * 2 * DD + (size_t)(tid + 128 * j) * EPV);
+    const f32x4 t = *reinterpret_cast<const f32x4*>(tbase + (size_t)c * 4 * D);
+    tx = tails ? t : zero4();
+  };
+  u32x4 gx[GV];
+  f32x4 tx = zero4();
+  if (NC > 0) load_sums(NC - 1, gx, tx);
   if (NC > 0) {
     const int c = NC - 1, Lc = chunk_len(c);
     if (Lc == kL) {
@@ -651,11 +684,17 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
       __syncthreads();
     }
   }
+  // no load is pending at the walk's start (a wait the compiler sees, so that it places none for the
+  // prologue's loads inside the walk, where it would also wait for the direct loads)
+  __builtin_amdgcn_s_waitcnt(0);
   for (int c = NC - 1; c >= 0; --c) {
     // lane index recomputed per chunk (opaque), so lane-derived addresses are not held across the loop
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
     const int gq = ln >> 4, lq = ln & 15;
+    u32x4 gxn[GV];  // chunk c - 1's (chunk 0's again on the last step: not used)
+    f32x4 txn;
+    load_sums(c > 0 ? c - 1 : 0, gxn, txn);
     if (c > 0) issue(c - 1, ln);  // buffers (c - 1) & 1 were last read in the chunk before
     {
       T* R = rmat(c) + (size_t)(v0 + lq) * D + 4 * gq;
@@ -712,14 +751,42 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
         dSt[t] -= acc;
       }
     }
+    // G(c) and dm_after(c) in place, then the chunk's own terms join the running sums (the loaded
+    // terms pass through an empty asm here, so nothing reads them, and no wait for them falls,
+    // before this point)
+#pragma unroll
+    for (int j = 0; j < GV; ++j) asm volatile("" : "+v"(gx[j]));
+    asm volatile("" : "+v"(tx));
+#pragma unroll
+    for (int j = 0; j < GV; ++j) {
+      *reinterpret_cast<uint4*>(gmat + (size_t)c * 2 * DD + (size_t)(tid + 128 * j) * EPV) = pack16<T>(grun[j]);
+      float x[EPV];
+      unpack16<T>(__builtin_bit_cast(uint4, gx[j]), x);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        grun[j][e] += x[e];
+        asm volatile("" : "+v"(grun[j][e]));  // the sums stay in this step, ahead of the wait below
+      }
+    }
+    if (tails) {
+      if (tpart == 0) *reinterpret_cast<f32x4*>(tbase + (size_t)c * 4 * D) = trun;
+      trun += tx;
+    }
+#pragma unroll
+    for (int j = 0; j < GV; ++j) gx[j] = gxn[j];
+    tx = txn;
     if (c > 0) {
-      // chunk c - 1 has landed once only this chunk's NA stores (issued after its loads) may be
-      // outstanding; the barrier also frees chunk c's buffers for chunk c - 2
-      if constexpr (NA == 8) {
+      // chunk c - 1 has landed once only the stores issued after its loads (NA of dS_end, GV of G,
+      // and on some waves one tail) may be outstanding; the barrier also frees chunk c's buffers
+      // for chunk c - 2
+      constexpr int after = NA + GV;
+      if constexpr (after == 12) {
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      } else if constexpr (after == 8) {
         asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       } else {
-        static_assert(NA == 4, "store count per chunk");
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        static_assert(after == 6, "store count per chunk");
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
       }
       lds_barrier();
     }
@@ -729,57 +796,16 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
     for (int t = 0; t < NA; ++t)
       *reinterpret_cast<f32x4*>(a.dS0 + (size_t)chain * DD + (size_t)(v0 + l16) * D + 16 * t + 4 * g) = dSt[t];
   }
-}
-
-// The additive adjoints: G(c) = dC_T + sum over later chunks of dG (input dtype, the second half of
-// each chunk's adjoint matrices), dm_after(c) = dksum_T + sum over later chunks of dm (each replacing
-// the chunk's own), and dw, db summed over every chunk.  What is left after chunk 0 is the adjoint of
-// the carry in.  Blocks 0 .. nmb-1 take G, one 16-byte vector per thread; the last block the fp32
-// tails dm | dw | db, 4 floats per thread (the part is uniform over a block).
-template <int D, typename T>
-__global__ __launch_bounds__(256) void gdn_bwd_scan_sums_kernel(BwdArgs a) {
-  constexpr int EPV = 16 / (int)sizeof(T);
-  constexpr int NMV = D * D / EPV;
-  constexpr int NMB = (NMV + 255) / 256;
-  const int chain = blockIdx.y;
-  const int NC = a.nchunks;
-  const GdnBwdLayout<T> L = gdn_layout<T>(a);
-  const size_t DD = (size_t)D * D;
-  if ((int)blockIdx.x < NMB) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= NMV) return;
-    const size_t f = (size_t)idx * EPV;
-    float run[EPV];
-    const float* src = a.dC_T ? a.dC_T + (size_t)chain * DD + f : nullptr;
+  if (a.dC0 != nullptr) {
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) run[e] = src ? src[e] : 0.f;
-    rev_scan_vec<T, false>(L.mat + (size_t)chain * NC * 2 * DD + DD + f, 2 * DD, NC, nullptr, 0, run);
-    if (a.dC0) {
+    for (int j = 0; j < GV; ++j)
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) a.dC0[(size_t)chain * DD + f + e] = run[e];
-    }
-    return;
+      for (int e = 0; e < EPV; ++e) a.dC0[(size_t)chain * DD + (size_t)r0 * D + (size_t)(tid + 128 * j) * EPV + e] = grun[j][e];
   }
-  const int idx = threadIdx.x;
-  if (idx >= 3 * D / 4) return;
-  const size_t o = (size_t)idx * 4;
-  const int part = (int)(o / D);  // 0 dm, 1 dw, 2 db
-  float run[4];
-  const float* src = (part == 0 && a.dksum_T) ? a.dksum_T + (size_t)chain * D + o : nullptr;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) run[e] = src ? src[e] : 0.f;
-  float* x0 = L.tail + (size_t)chain * NC * 4 * D + o;
-  if (part == 0) {
-    rev_scan_vec<float, false>(x0, 4 * (size_t)D, NC, nullptr, 0, run);
-    if (a.dksum0) *reinterpret_cast<f32x4*>(a.dksum0 + (size_t)chain * D + o) = f32x4{run[0], run[1], run[2], run[3]};
-  } else {
-    for (int c = 0; c < NC; ++c) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(x0 + (size_t)c * 4 * D);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) run[e] += v[e];
-    }
-    if (part == 1) *reinterpret_cast<f32x4*>(a.dw + (size_t)chain * D + (o - D)) = f32x4{run[0], run[1], run[2], run[3]};
-    if (part == 2 && o == 2 * (size_t)D) a.db[chain] = run[0];
+  if (tails) {
+    if (tpart == 0 && a.dksum0) *reinterpret_cast<f32x4*>(a.dksum0 + (size_t)chain * D + 4 * tid) = trun;
+    if (tpart == 1) *reinterpret_cast<f32x4*>(a.dw + (size_t)chain * D + (4 * tid - D)) = trun;
+    if (tpart == 2 && 4 * tid == 2 * D) a.db[chain] = trun[0];
   }
 }
 
@@ -1119,9 +1145,6 @@ static hipError_t launch_gdn_bwd_t(const BwdArgs& a, hipStream_t s) {
   if (rec(2) != hipSuccess) return hipErrorLaunchFailure;
   // 3. reverse scans
   hipLaunchKernelGGL((gdn_bwd_scan_s_kernel<D, T>), dim3(D / 32, (unsigned)chains), dim3(128), 0, s, a);
-  const int nmb = (D * D / (16 / (int)sizeof(T)) + 255) / 256;  // G blocks, then one tail block
-  hipLaunchKernelGGL((gdn_bwd_scan_sums_kernel<D, T>), dim3((unsigned)(nmb + 1), (unsigned)chains), dim3(256), 0,
-                     s, a);
   if (rec(3) != hipSuccess) return hipErrorLaunchFailure;
   // 4. pass B
   hipLaunchKernelGGL((gdn_bwd_b_kernel<D, T>), dim3((unsigned)(chains * NC)), dim3(4 * D), 0, s, a);
