@@ -190,7 +190,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_a_kernel(BwdArgs a) {
   const float wv = a.w_lambda[(size_t)h * D + cw + l16];
   const float mv = mc[cw + l16];
   const float b_lam = a.b_lambda[h];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   __syncthreads();
   if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
     zero_tail<D, T, PQ>(sm.Q, Lc, tid, NT);
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(4 * D) void bwd_carry_walk_kernel(BwdArgs a, int P,
     if (g == 0) L.carm[cs * D + cw + l16] = mv;
     if (c >= cu) break;
     const int b = (c - c0) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_wait_all();
     lds_barrier();  // chunk c's tiles have landed; the other buffer is free
     if (c + 1 < cu) issue(c + 1, b ^ 1);
     f32x4 ks[4], bs[4];
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(4 * D) void bwd_chunk_b_kernel(BwdArgs a) {
   for (int p = 0; p < NP; ++p)
     scb[p] = *reinterpret_cast<const uint4*>(Sc + (size_t)(tid / UR + (NT / UR) * p) * D + EPU * (tid % UR));
   const float dma = L.tail[slot * 4 * D + cw + l16];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   __syncthreads();
   if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
     zero_tail<D, T, PQ>(sm.u1.in.K, Lc, tid, NT);

@@ -300,7 +300,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_walk_kernel(BwdArgs a, int P, i
     issue_kg(c0);
     issue_v(c0);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   __syncthreads();
   auto store_carry = [&](int c) {  // the carry at chunk c's start: S_c, C_c (input dtype), m_c
     const size_t cs = (size_t)chain * NC + c;
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
   if (w == 0)
     chunk_gates<T>(static_cast<const T*>(a.log_alpha), static_cast<const T*>(a.beta), row0, Lc, lane, sm.lg, sm.gam,
                    sm.beta, sm.bgam, nullptr);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   __syncthreads();
   if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
     zero_tail<D, T, PQ>(sm.u0.Q, Lc, tid, NT);
@@ -677,16 +677,14 @@ __global__ __launch_bounds__(128) void gdn_bwd_scan_s_kernel(BwdArgs a) {
         Gr[c & 1][1][lane] = ok ? b : T(0.f);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_wait_all();
     __syncthreads();
     if (Lc < kL) {
       zero_tail<D, T, PQ>(Ks[c & 1], Lc, tid, 128);
       __syncthreads();
     }
   }
-  // no load is pending at the walk's start (a wait the compiler sees, so that it places none for the
-  // prologue's loads inside the walk, where it would also wait for the direct loads)
-  __builtin_amdgcn_s_waitcnt(0);
+  vm_wait_all();  // also on the path that skipped the prologue's loads: none is pending in the walk
   for (int c = NC - 1; c >= 0; --c) {
     // lane index recomputed per chunk (opaque), so lane-derived addresses are not held across the loop
     int ln;
@@ -881,7 +879,7 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
   if (w == 0)
     gL = chunk_gates<T>(static_cast<const T*>(a.log_alpha), static_cast<const T*>(a.beta), row0, Lc, lane, sm.lg, sm.gam,
                         sm.beta, sm.bgam, sm.dd);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   __syncthreads();
   if (Lc < kL) {  // a ragged last chunk: rows past the end of the sequence read as zeros
     zero_tail<D, T, PQ>(sm.K, Lc, tid, NT);

@@ -54,6 +54,17 @@ __device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcp
 // compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Waits for every vector memory access of the wave (direct loads into LDS included) and tells the
+// compiler so.  A wait written in inline asm is opaque to the compiler's own wait placement: a loop
+// entered after one carries the loads issued before it as still pending into every iteration, and
+// the compiler then waits for them at their first use inside the loop, where its wait also waits
+// for the direct loads issued since, which it cannot see.  The immediate is vmcnt(0) with the
+// export and LDS counters left alone (their fields at their maxima, 7 and 15).
+__device__ __forceinline__ void vm_wait_all() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 // ---------------------------------------------------------------- MFMA tiles
 
 enum KOrder { KORD_CONTIG = 0, KORD_ACC = 1 };

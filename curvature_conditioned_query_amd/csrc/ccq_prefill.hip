@@ -133,7 +133,7 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
     }
   }
   // the carry-in loads complete here, so nothing in the chunk loop waits on them
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   int64_t nb = (int64_t)cbeg * kL;  // tokens before this chunk (count base)
   if (a.n0 != nullptr)
     nb += a.snapshot ? reinterpret_cast<const int64_t*>(reinterpret_cast<const char*>(a.workspace) +
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(4 * D) void gla_main_kernel(FwdArgs a) {
 
     // ---- this chunk's tiles have landed (own loads, then everyone's); rows past the end of
     // the sequence are zeroed
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_wait_all();
     lds_barrier();
     if (Lc < kL) {
       zero_tail<D, T, PQ>(sm.Qs, Lc, tid, 64 * NW);

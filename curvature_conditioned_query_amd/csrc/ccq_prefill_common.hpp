@@ -356,7 +356,7 @@ __device__ __forceinline__ void csum_body(const FwdArgs& a, CSumSmem<D, T>& sm, 
     for (int t = 0; t < NA; ++t) Cacc[t] = zero4();
     plan.load(sm.Ks[0], src, kL, w);
     for (int i = 0; i < n; ++i) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      vm_wait_all();
       lds_barrier();  // chunk i has landed; chunk i-1's buffer is free
       if (i + 1 < n) plan.load(sm.Ks[(i + 1) & 1], src + (size_t)(i + 1) * kL * D, kL, w);
       T (*Ks)[PQ] = sm.Ks[i & 1];

@@ -418,7 +418,7 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
         Cacc[t] = *reinterpret_cast<const f32x4*>(Cin + (size_t)row * D + col);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   int64_t nb = (int64_t)cbeg * kL;
   if (a.n0 != nullptr)
     nb += a.snapshot ? reinterpret_cast<const int64_t*>(static_cast<const char*>(a.workspace) +
@@ -448,15 +448,20 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
   auto dma_rows = [&](T (*dst)[PQ], const T* src, int c, int ln) {
     dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, ln);
   };
-  float sg = 0.f, sb = 0.f;
+  // wave 1: the raw log alpha and beta of token `lane` of the next chunk (token 0 again past the
+  // end).  They stay as loaded until the chunk top, after its wait, where tokens past the end
+  // read zero: anything done with them here would wait for the tile loads issued just before.
+  T sg = T(0.f), sb = T(0.f);
   auto load_gates = [&](int c, int ln) {
     if (w == 1) {
-      const bool ok = ln < chunk_len(c);
-      const size_t i = tok0 + (size_t)c * kL + (ok ? ln : 0);
-      const float x = ldf(gg, i), y = ldf(bg, i);
-      sg = ok ? x : 0.f;
-      sb = ok ? y : 0.f;
+      const size_t i = tok0 + (size_t)c * kL + (ln < chunk_len(c) ? ln : 0);
+      sg = gg[i];
+      sb = bg[i];
     }
+  };
+  auto put_gates = [&](int c, int ln) {
+    const bool ok = ln < chunk_len(c);
+    gdn_gates<D, T>(sm, ok ? to_f32(sg) : 0.f, ok ? to_f32(sb) : 0.f, ln);
   };
   if (cbeg < cend) {
     dma_rows(sm.Qs, qg, cbeg, lane);
@@ -479,8 +484,8 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     T (*Ks)[PQ] = sm.Ks[ch & 1];
 
     // ---- this chunk's tiles have landed; gates; rows past the end of the sequence zeroed
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (w == 1) gdn_gates<D, T>(sm, sg, sb, lane);
+    vm_wait_all();
+    if (w == 1) put_gates(ch, lane);
     if (CC) {  // the carry at this chunk's start, for the chunked backward
       put_carry_row<D, T, NA>(a, chain, ch, 0, cw + l16, g, Sacc);
       put_carry_row<D, T, NA>(a, chain, ch, 1, cw + l16, g, Cacc);
@@ -512,8 +517,11 @@ __global__ __launch_bounds__(4 * D) void gdn_main_kernel(FwdArgs a) {
     lds_barrier();
 
     // ---- inverses of the diagonal blocks (the last four waves, one block each), cleaned query
+    // (the inverse waves carry the longer path here: they take issue priority until the barrier)
+    if (w >= NW - 4) __builtin_amdgcn_s_setprio(2);
     if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
     ccq_clean_query<D, T, 1, kSplit>(sm, Ks, sm.Qalo, R, cw, lane, [](int, int, int) { return 1.0f; });
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
     if (ch + 1 < cend) dma_rows(sm.Qs, qg, ch + 1, lane);  // q of this chunk is no longer read
 
@@ -649,15 +657,20 @@ __device__ __forceinline__ void gdn_summary_body(const FwdArgs& a, GdnSmem<D, T>
   auto dma_rows = [&](T (*dst)[PQ], const T* src, int c, int ln) {
     dma_tile<D, T, PQ>(dst, src + (tok0 + (size_t)c * kL) * D, chunk_len(c), w, NW, ln);
   };
-  float sg = 0.f, sb = 0.f;
+  // wave 1: the raw log alpha and beta of token `lane` of the next chunk (token 0 again past the
+  // end).  They stay as loaded until the chunk top, after its wait, where tokens past the end
+  // read zero: anything done with them here would wait for the tile loads issued just before.
+  T sg = T(0.f), sb = T(0.f);
   auto load_gates = [&](int c, int ln) {
     if (w == 1) {
-      const bool ok = ln < chunk_len(c);
-      const size_t i = tok0 + (size_t)c * kL + (ok ? ln : 0);
-      const float x = ldf(gg, i), y = ldf(bg, i);
-      sg = ok ? x : 0.f;
-      sb = ok ? y : 0.f;
+      const size_t i = tok0 + (size_t)c * kL + (ln < chunk_len(c) ? ln : 0);
+      sg = gg[i];
+      sb = bg[i];
     }
+  };
+  auto put_gates = [&](int c, int ln) {
+    const bool ok = ln < chunk_len(c);
+    gdn_gates<D, T>(sm, ok ? to_f32(sg) : 0.f, ok ? to_f32(sb) : 0.f, ln);
   };
   if (cbeg < cend) {
     dma_rows(sm.Ks[cbeg & 1], kg, cbeg, lane);
@@ -671,8 +684,8 @@ __device__ __forceinline__ void gdn_summary_body(const FwdArgs& a, GdnSmem<D, T>
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_opaque));
     const int lane = lane_opaque;
     T (*Ks)[PQ] = sm.Ks[ch & 1];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (w == 1) gdn_gates<D, T>(sm, sg, sb, lane);
+    vm_wait_all();
+    if (w == 1) put_gates(ch, lane);
     lds_barrier();
     if (a.flags & kFlagNormalizeKeys) {
       normalize_rows<D, T, PQ>(Ks, tid, 64 * NW);
@@ -684,10 +697,12 @@ __device__ __forceinline__ void gdn_summary_body(const FwdArgs& a, GdnSmem<D, T>
     if (tid >= 2 * D) gdn_key_sums<D, T>(sm, Ks, tid - 2 * D);
     lds_barrier();
 
+    if (w >= NW - 4) __builtin_amdgcn_s_setprio(2);  // the inverse waves' longer path, to the barrier
     if (w >= NW - 4) gdn_diag_inverse_mfma<D, T>(sm, w - (NW - 4), lane);
     f32x4 XSM[2][4];  // right-hand sides of the S and M recurrences
     gdn_rhs<D, T, true>(sm, Ks, [&](int t) -> const f32x4& { return Sacc[t]; }, cw, lane, XSM[0]);
     gdn_rhs<D, T, false>(sm, Ks, [&](int t) -> const f32x4& { return Macc[t]; }, cw, lane, XSM[1]);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
     if (ch + 1 < cend) {
       dma_rows(sm.Vs, vg, ch + 1, lane);

@@ -124,7 +124,7 @@ __device__ __forceinline__ void gla_summary_body(const FwdArgs& a, SumSmem<D, T>
     dma(sm.Ks[1], kg, 1);
     dma(sm.Gs[1], gg, 1);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait_all();
   lds_barrier();
   if (norm) {
     normalize_rows<D, T, PQ>(sm.Ks[0], tid, 64 * NW);
@@ -178,7 +178,7 @@ __device__ __forceinline__ void gla_summary_body(const FwdArgs& a, SumSmem<D, T>
 #pragma unroll
     for (int t = 0; t < NA; ++t) Sacc[t] *= *reinterpret_cast<const f32x4*>(&sm.eBL[i & 1][16 * t + 4 * g]);
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_wait_all();
     lds_barrier();
     if (norm && i + 2 < n) {  // chunk i+2's keys have landed: unit rows before their first use
       normalize_rows<D, T, PQ>(sm.Ks[(i + 2) % 3], tid, 64 * NW);
