@@ -187,10 +187,11 @@ __device__ __forceinline__ int offd(int i, int j) { return (i - j == 1) ? j : (i
 // (lane = (block, row)); off-diagonal ones from T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, one block per
 // wave and diagonal, the nearest diagonal first.  Results: Tb (diagonal blocks), To (off-diagonal,
 // indexed by offd), both [.][16][20] fp32.  Every thread of the workgroup calls it; it ends with a
-// barrier.
-template <int NW>
+// barrier.  `between` runs on every wave after the diagonal blocks are out, before the off-diagonal
+// rounds (work for the forming wave, which takes no part in those).
+template <int NW, typename Between>
 __device__ __forceinline__ void chunk_inverse(const float (*As)[PT], float (*Tb)[16][20], float (*To)[16][20], int w,
-                                              int lane) {
+                                              int lane, Between&& between) {
   static_assert(NW >= 4, "the off-diagonal blocks of the first diagonal take three waves");
   if (w == NW - 1) {
     const int blk = lane >> 4, i = lane & 15, base = 16 * blk;
@@ -207,6 +208,7 @@ __device__ __forceinline__ void chunk_inverse(const float (*As)[PT], float (*Tb)
     for (int j = 0; j < 16; ++j) Tb[blk][i][j] = trow[j];
   }
   __syncthreads();
+  between();
   const int g = lane >> 4, l = lane & 15;
   for (int dgl = 1; dgl <= 3; ++dgl) {
     if (w < 4 - dgl) {
@@ -467,21 +469,12 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
       sm.u0.As[i][j0 + r] = (j0 + r < i) ? sm.beta[i] * __expf(sm.lg[i] - sm.lg[j0 + r]) * acc[r] : 0.f;
   }
   __syncthreads();
-  chunk_inverse<NW>(sm.u0.As, sm.u2.inv.Tb, sm.u2.inv.To, w, lane);
-  // (I + A)^{-1} in the operand dtype: to LDS for the products here and to the workspace for the
-  // reverse scan and pass B
-  {
-    T* tw = L.tinv + slot * kTT;
-    for (int e = tid; e < kTT; e += NT) {
-      const T x = (T)inv_at(sm.u2.inv.Tb, sm.u2.inv.To, e >> 6, e & 63);
-      sm.Tm[e >> 6][e & 63] = x;
-      tw[e] = x;
-    }
-  }
-  // X = beta (V - gamma K S_c^T) on the wave's value channels, Delta = T X
-  f32x4 dl[4];
-  {
-    f32x4 x[4], vs[4];
+  // X = beta (V - gamma K S_c^T) on the wave's value channels: on the waves that do not form the
+  // diagonal blocks' inverses while that runs, on the wave that does while the others form the
+  // off-diagonal blocks (which it takes no part in)
+  f32x4 x[4];
+  auto form_x = [&]() {
+    f32x4 vs[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) x[ti] = zero4();
     strip_times_rowsT<D, O>(&sm.K[0][0], PQ, Sc, cw, lane, x);  // (K S_c^T)[i][cw + l]
@@ -495,6 +488,24 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
       }
     // the wave's v columns are read: the cleaned query takes their place (same columns)
     write_strip(&sm.u1.in.vq.Qc[0][0], PQ, cw, lane, qc);
+  };
+  if (w != NW - 1) form_x();
+  chunk_inverse<NW>(sm.u0.As, sm.u2.inv.Tb, sm.u2.inv.To, w, lane, [&]() {
+    if (w == NW - 1) form_x();
+  });
+  // (I + A)^{-1} in the operand dtype: to LDS for the products here and to the workspace for the
+  // reverse scan and pass B
+  {
+    T* tw = L.tinv + slot * kTT;
+    for (int e = tid; e < kTT; e += NT) {
+      const T x = (T)inv_at(sm.u2.inv.Tb, sm.u2.inv.To, e >> 6, e & 63);
+      sm.Tm[e >> 6][e & 63] = x;
+      tw[e] = x;
+    }
+  }
+  // Delta = T X
+  f32x4 dl[4];
+  {
     __syncthreads();  // Tm complete
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) dl[ti] = zero4();
