@@ -183,30 +183,18 @@ __device__ __forceinline__ f32x4 neg_mm16_acc(const float* X, int px, const f32x
 __device__ __forceinline__ int offd(int i, int j) { return (i - j == 1) ? j : (i - j == 2) ? 3 + j : 5; }
 
 // (I + A)^{-1} of a chunk in fp32 by 16-token blocks, A strictly lower triangular in the LDS tile As
-// (pitch PT; only its lower blocks are read).  Diagonal blocks by forward substitution on one wave
-// (lane = (block, row)); off-diagonal ones from T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, one block per
-// wave and diagonal, the nearest diagonal first.  Results: Tb (diagonal blocks), To (off-diagonal,
+// (pitch PT; its lower blocks are read, its upper blocks serve as scratch).  Diagonal blocks on the
+// last four waves, one each, by the product form of the prefill (diag_block_inverse_mfma);
+// off-diagonal ones from T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, one block per wave and diagonal,
+// the nearest diagonal first, on waves 0..2.  Results: Tb (diagonal blocks), To (off-diagonal,
 // indexed by offd), both [.][16][20] fp32.  Every thread of the workgroup calls it; it ends with a
 // barrier.  `between` runs on every wave after the diagonal blocks are out, before the off-diagonal
-// rounds (work for the forming wave, which takes no part in those).
+// rounds (work for the last waves, which take no part in those).
 template <int NW, typename Between>
-__device__ __forceinline__ void chunk_inverse(const float (*As)[PT], float (*Tb)[16][20], float (*To)[16][20], int w,
-                                              int lane, Between&& between) {
-  static_assert(NW >= 4, "the off-diagonal blocks of the first diagonal take three waves");
-  if (w == NW - 1) {
-    const int blk = lane >> 4, i = lane & 15, base = 16 * blk;
-    float trow[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) trow[j] = (j == i) ? 1.f : 0.f;
-#pragma unroll
-    for (int k = 0; k < 15; ++k) {
-      const float coef = (i > k) ? As[base + i][base + k] : 0.f;
-#pragma unroll
-      for (int j = 0; j <= k; ++j) trow[j] -= coef * __shfl(trow[j], k, 16);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) Tb[blk][i][j] = trow[j];
-  }
+__device__ __forceinline__ void chunk_inverse(float (*As)[PT], float (*Tb)[16][20], float (*To)[16][20], int w, int lane,
+                                              Between&& between) {
+  static_assert(NW >= 4, "the diagonal blocks take four waves, the first off-diagonal round three");
+  if (w >= NW - 4) diag_block_inverse_mfma(As, Tb, w - (NW - 4), lane);
   __syncthreads();
   between();
   const int g = lane >> 4, l = lane & 15;
@@ -470,8 +458,8 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
   }
   __syncthreads();
   // X = beta (V - gamma K S_c^T) on the wave's value channels: on the waves that do not form the
-  // diagonal blocks' inverses while that runs, on the wave that does while the others form the
-  // off-diagonal blocks (which it takes no part in)
+  // diagonal blocks' inverses while that runs, on the waves that do while waves 0..2 form the
+  // off-diagonal blocks
   f32x4 x[4];
   auto form_x = [&]() {
     f32x4 vs[4];
@@ -489,9 +477,9 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_a_kernel(BwdArgs a) {
     // the wave's v columns are read: the cleaned query takes their place (same columns)
     write_strip(&sm.u1.in.vq.Qc[0][0], PQ, cw, lane, qc);
   };
-  if (w != NW - 1) form_x();
+  if (w < NW - 4) form_x();
   chunk_inverse<NW>(sm.u0.As, sm.u2.inv.Tb, sm.u2.inv.To, w, lane, [&]() {
-    if (w == NW - 1) form_x();
+    if (w >= NW - 4) form_x();
   });
   // (I + A)^{-1} in the operand dtype: to LDS for the products here and to the workspace for the
   // reverse scan and pass B

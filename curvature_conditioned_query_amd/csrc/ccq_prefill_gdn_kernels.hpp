@@ -151,14 +151,13 @@ __device__ __forceinline__ void gdn_diag_inverse(GdnSmem<D, T>& sm, int lane) {
 // operand from LDS: the powers are written to Tb[blk] (which receives the inverse at the end) and to an
 // upper block of As, which the kernels never use (A is strictly lower triangular).  The LDS traffic
 // stays inside the wave, whose LDS instructions complete in order, so no barrier is needed.
-template <int D, typename T>
-__device__ __forceinline__ void gdn_diag_inverse_mfma(GdnSmem<D, T>& sm, int blk, int lane) {
+__device__ __forceinline__ void diag_block_inverse_mfma(float (*As)[kL + 4], float (*Tb)[16][20], int blk, int lane) {
   const int g = lane >> 4, l = lane & 15, base = 16 * blk;
   constexpr int PA = kL + 4;
-  const float* N = &sm.As[base][base];
-  float* s1 = &sm.Tb[blk][0][0];                                            // pitch 20
+  const float* N = &As[base][base];
+  float* s1 = &Tb[blk][0][0];                                              // pitch 20
   // upper blocks (0,1) (0,2) (0,3) (1,2) for blocks 0..3
-  float* s2 = &sm.As[blk == 3 ? 16 : 0][blk == 3 ? 32 : 16 * (blk + 1)];   // pitch PA
+  float* s2 = &As[blk == 3 ? 16 : 0][blk == 3 ? 32 : 16 * (blk + 1)];      // pitch PA
   auto mm = [&](const float* X, int px, const f32x4& y, f32x4 acc) {        // acc + X Y
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[l * px + 4 * g + r], y[r], acc, 0, 0, 0);
@@ -184,6 +183,10 @@ __device__ __forceinline__ void gdn_diag_inverse_mfma(GdnSmem<D, T>& sm, int blk
   put(s1, 20, n8);
   e = mm(s1, 20, e, e);                     // ... (I + N^8)
   put(s1, 20, e);
+}
+template <int D, typename T>
+__device__ __forceinline__ void gdn_diag_inverse_mfma(GdnSmem<D, T>& sm, int blk, int lane) {
+  diag_block_inverse_mfma(sm.As, sm.Tb, blk, lane);
 }
 
 // X = beta (V - gamma K S0^T) on the wave's 16 state rows (WITH_V false: V = 0).  X[b][r] at
