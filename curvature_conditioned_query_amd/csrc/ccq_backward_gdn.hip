@@ -955,11 +955,15 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // dlg from Gam in M: rowsum_i - colsum_i of dM * M
-  for (int i = tid; i < kL; i += NT) {
+  // dlg from Gam in M: rowsum_i - colsum_i of dM * M, token i = lane, each wave over its share of
+  // j (partial sums parked in red, which the channel sums at the end are the first to write again)
+  constexpr int JW = kL / NW;
+  {
     float s = 0.f;
-    for (int j = 0; j < kL; ++j) s += to_f32(sm.dM[i][j]) * to_f32(sm.u1.Mt[i][j]) - to_f32(sm.dM[j][i]) * to_f32(sm.u1.Mt[j][i]);
-    sm.dlg[i] = s;
+#pragma unroll 1
+    for (int j = JW * w; j < JW * (w + 1); ++j)
+      s += to_f32(sm.dM[lane][j]) * to_f32(sm.u1.Mt[lane][j]) - to_f32(sm.dM[j][lane]) * to_f32(sm.u1.Mt[j][lane]);
+    sm.red[w][lane][0] = s;
   }
   // dDelta = M^T dO + D (K dS_L^T), dX = T^T dDelta, dv = beta dX
   f32x4 dX[4];
@@ -997,17 +1001,29 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
   }
   __syncthreads();
   // dlg from Gam in A (A = beta_i AK): rowsum_i - colsum_i of dA * A; dbeta's second term
-  // sum_j dA_ij AK_ij
-  for (int i = tid; i < kL; i += NT) {
+  // sum_j dA_ij AK_ij (the same split over waves)
+  {
     float rs = 0.f, cs = 0.f;
-    for (int j = 0; j < kL; ++j) {
-      rs += to_f32(sm.u0.dA[i][j]) * to_f32(sm.u1.AK[i][j]);
-      cs += sm.beta[j] * to_f32(sm.u0.dA[j][i]) * to_f32(sm.u1.AK[j][i]);
+#pragma unroll 1
+    for (int j = JW * w; j < JW * (w + 1); ++j) {
+      rs += to_f32(sm.u0.dA[lane][j]) * to_f32(sm.u1.AK[lane][j]);
+      cs += sm.beta[j] * to_f32(sm.u0.dA[j][lane]) * to_f32(sm.u1.AK[j][lane]);
     }
-    sm.db2[i] = rs;
-    sm.dlg[i] += sm.beta[i] * rs - cs;
+    sm.red[w][lane][1] = rs;
+    sm.red[w][lane][2] = cs;
   }
   __syncthreads();  // dA, AK and dM are read for the sums
+  if (tid < kL) {  // the waves' partial sums
+    float s1 = 0.f, rs = 0.f, cs = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      s1 += sm.red[v][tid][0];
+      rs += sm.red[v][tid][1];
+      cs += sm.red[v][tid][2];
+    }
+    sm.db2[tid] = rs;
+    sm.dlg[tid] = s1 + sm.beta[tid] * rs - cs;
+  }
   // W_A = dA * beta_i Gam_ij (over dA), dM * Gam (over dM)
   for (int e = tid; e < kL * kL; e += NT) {
     const int i = e >> 6, j = e & 63;
