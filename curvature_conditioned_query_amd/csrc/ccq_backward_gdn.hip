@@ -898,7 +898,13 @@ __global__ __launch_bounds__(4 * D) void gdn_bwd_b_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < EPU; ++e) s += x[e] * y[e];
     }
-    s = group_sum<64>(s);
+    {  // wave sum, lane index taken opaque here so that its shuffle addresses are not kept to the end
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1)
+        s += __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((ln ^ off) << 2, __builtin_bit_cast(int, s)));
+    }
     if (lane == 0) sm.dot[w] = s;
   }
 
