@@ -334,11 +334,9 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
           for (int r = 0; r < 4; ++r) sm.eBL[pc][c + r] = __expf(BT[3][r]);
         }
       }
-      if (nC >= 0) dma(sm.KB[nC & 1], kg, nC, plan);
-      if (nS >= 0) dma(sm.VB[nS & 1], vg, nS, plan);
       lds_barrier();
       // ---- phase B: cleaned query -> Qc e^B in place of q, C += K^T K
-      if (nC >= 0) dma(sm.QB[nC & 1], qg, nC, plan);  // its buffer's Qc e^B (or low part) is consumed
+      (void)plan;  // the state waves issue every tile load of the step (below)
       if (cc >= 0) {
         const int pc = cc & 1;
         T (*Ks)[PQ] = sm.KB[pc];
@@ -434,8 +432,16 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
       const int sc = s_at(s), nC = c_at(s + 1), nS = s_at(s + 1);
       f32x4 O[2][4];  // O^T for its value rows cw + 16 hh ..
       // ---- phase A: O = S0 (Qc e^B)^T, intra-chunk attention -> Am
-      if (nC >= 0) dma(sm.KB[nC & 1], kg, nC, plan);
-      if (nS >= 0) dma(sm.VB[nS & 1], vg, nS, plan);
+      // The state waves issue every tile load of the step (k and v here, q at phase B's start): the
+      // statistics waves, whose phase A is the step's longest path, then issue none (3-5 % off the
+      // kernel against all twelve waves sharing each tile's instructions).  The shared barrier after
+      // both sides' closing waits still publishes the tiles to every wave.
+      const PipeDma<D, T, PQ, NWS> splan(w, lane_);
+      auto sdma = [&](T (*dst)[PQ], const T* src, int ch) {
+        splan.load(dst, src + (tok0 + (size_t)ch * kL) * D, chunk_len(ch), w);
+      };
+      if (nC >= 0) sdma(sm.KB[nC & 1], kg, nC);
+      if (nS >= 0) sdma(sm.VB[nS & 1], vg, nS);
       if (sc >= 0) {
         const int ps = sc & 1;
 #pragma unroll
@@ -494,7 +500,7 @@ __global__ __launch_bounds__(768) void gla_pipe_kernel(FwdArgs a) {
       // The state side is phase B's longest path: its waves take issue priority over the
       // statistics waves that share their SIMDs until the step's end (measured ~2% on the pass).
       __builtin_amdgcn_s_setprio(2);
-      if (nC >= 0) dma(sm.QB[nC & 1], qg, nC, plan);
+      if (nC >= 0) sdma(sm.QB[nC & 1], qg, nC);
       if (sc >= 0) {
         const int ps = sc & 1;
         const int Lc = chunk_len(sc);
